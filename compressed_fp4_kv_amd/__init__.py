@@ -1,0 +1,232 @@
+"""Python binding of the CSA2 hot-path library (libcsa2.so, include/csa2.h).
+
+Argument marshalling only: every function takes torch device tensors (or
+None), checks dtype / contiguity / device, passes raw pointers, the sizes and
+the current HIP stream to the C entry point of the same name, and raises
+``CSA2Error`` on a non-zero status.  All computation happens in the HIP
+kernels of the library; there is no fallback path.  Importing this package
+fails loudly when the library has not been built.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "CSA2Error", "lib", "csa2_index_full", "csa2_index_full_workspace_bytes", "csa2_reindex",
+    "csa2_reindex_workspace_bytes", "csa2_sparse_attn_decode", "csa2_decode_workspace_bytes",
+    "csa2_sparse_attn_prefill_chunk", "csa2_prefill_workspace_bytes", "profile_enable",
+    "profile_read", "profile_reset", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+EXPORTED_SYMBOLS = [
+    "csa2_status_str", "csa2_last_hip_error",
+    "csa2_index_full_workspace_bytes", "csa2_index_full",
+    "csa2_reindex_workspace_bytes", "csa2_reindex",
+    "csa2_decode_workspace_bytes", "csa2_sparse_attn_decode",
+    "csa2_prefill_workspace_bytes", "csa2_sparse_attn_prefill_chunk",
+    "csa2_profile_enable", "csa2_profile_read", "csa2_profile_reset",
+    "csa2_debug_decode_tables",
+]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(hipcc, gfx950); there is no non-HIP implementation")
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
+
+lib = ctypes.CDLL(LIB_PATH)
+lib.csa2_status_str.restype = ctypes.c_char_p
+lib.csa2_status_str.argtypes = [ctypes.c_int]
+lib.csa2_last_hip_error.restype = ctypes.c_int
+lib.csa2_index_full_workspace_bytes.restype = _SZ
+lib.csa2_index_full_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
+lib.csa2_index_full.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32,
+                                _I32, _P, _P, _SZ, _P]
+lib.csa2_reindex_workspace_bytes.restype = _SZ
+lib.csa2_reindex_workspace_bytes.argtypes = [_I32, _I32, _I32]
+lib.csa2_reindex.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                             _P, _SZ, _P]
+lib.csa2_decode_workspace_bytes.restype = _SZ
+lib.csa2_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
+lib.csa2_sparse_attn_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
+                                        _I32, _F32, _P, _P, _P, _SZ, _P]
+lib.csa2_prefill_workspace_bytes.restype = _SZ
+lib.csa2_prefill_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
+lib.csa2_sparse_attn_prefill_chunk.argtypes = [_P, _I64, _P, _P, _P, _I32, _P, _P, _I32, _I32,
+                                               _I32, _I32, _F32, _P, _P, _P, _SZ, _P]
+lib.csa2_profile_enable.argtypes = [ctypes.c_int]
+lib.csa2_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                  ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
+lib.csa2_debug_decode_tables.argtypes = [_P, _P, _P, _P, _P]
+
+
+class CSA2Error(RuntimeError):
+    def __init__(self, status, where):
+        msg = lib.csa2_status_str(status).decode()
+        if status == 5:
+            msg += f" (hipError {lib.csa2_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def _check(status, where):
+    if status != 0:
+        raise CSA2Error(status, where)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous tensor (None -> NULL)."""
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws, name="ws"), ws.numel() * ws.element_size()
+
+
+def _dt():
+    import torch
+    return torch.float32, torch.int32, torch.int64, torch.uint8
+
+
+# ------------------------------------------------------------------ indexer
+
+def csa2_index_full_workspace_bytes(Q, max_nvis, topk, pool_blocks=0, block_size=8):
+    return int(lib.csa2_index_full_workspace_bytes(Q, max_nvis, topk, pool_blocks, block_size))
+
+
+def csa2_index_full(qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,
+                    pool_blocks=0, block_size=8, pool_block_idx=None, ws=None, stream=None):
+    """qI [Q,Hi,Di] f32; kI [rows,Hk,Di] f32; seq_row_off [S] i64; q_seq [Q] i32 or None;
+    q_nvis [Q] i32; topk_idx [Q,topk] i32 out; pool_block_idx [Q,pool_blocks] i32 out."""
+    f32, i32, i64, _ = _dt()
+    Q, Hi, Di = qI.shape
+    Hk = kI.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib.csa2_index_full(
+        _ptr(qI, f32, "qI"), _ptr(kI, f32, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
+        _ptr(q_seq, i32, "q_seq"), _ptr(q_nvis, i32, "q_nvis"), Q, Hi, Hk, Di, max_nvis, topk,
+        _ptr(topk_idx, i32, "topk_idx"), pool_blocks, block_size,
+        _ptr(pool_block_idx, i32, "pool_block_idx"), wp, wn, _stream(stream)), "csa2_index_full")
+
+
+def csa2_reindex_workspace_bytes(Q, pool_blocks, block_size):
+    return int(lib.csa2_reindex_workspace_bytes(Q, pool_blocks, block_size))
+
+
+def csa2_reindex(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, block_size, topk, topk_idx,
+                 ws=None, stream=None):
+    f32, i32, i64, _ = _dt()
+    Q, Hi, Di = qI.shape
+    Hk = kI.shape[1]
+    P = pool_block_idx.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib.csa2_reindex(
+        _ptr(qI, f32, "qI"), _ptr(kI, f32, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
+        _ptr(q_seq, i32, "q_seq"), _ptr(q_nvis, i32, "q_nvis"),
+        _ptr(pool_block_idx, i32, "pool_block_idx"), P, block_size, Q, Hi, Hk, Di, topk,
+        _ptr(topk_idx, i32, "topk_idx"), wp, wn, _stream(stream)), "csa2_reindex")
+
+
+# ---------------------------------------------------------------- attention
+
+def csa2_decode_workspace_bytes(B, H, D, topk, W):
+    return int(lib.csa2_decode_workspace_bytes(B, H, D, topk, W))
+
+
+def csa2_sparse_attn_decode(q, kv_codes, kv_scales, seq_row_off, topk_idx, swa_k, swa_v, swa_len,
+                            softmax_scale, out, lse=None, ws=None, stream=None):
+    """q [B,H,D] f32; kv_codes [rows,D/2] u8; kv_scales [rows,D/16] u8; topk_idx [B,topk] i32;
+    swa_k/swa_v [B,W,D] u8; swa_len [B] i32; out [B,H,D] f32; lse [B,H] f32 or None."""
+    f32, i32, i64, u8 = _dt()
+    B, H, D = q.shape
+    topk = topk_idx.shape[1] if topk_idx is not None else 0
+    W = swa_k.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib.csa2_sparse_attn_decode(
+        _ptr(q, f32, "q"), _ptr(kv_codes, u8, "kv_codes"), _ptr(kv_scales, u8, "kv_scales"),
+        _ptr(seq_row_off, i64, "seq_row_off"), _ptr(topk_idx, i32, "topk_idx"), topk,
+        _ptr(swa_k, u8, "swa_k"), _ptr(swa_v, u8, "swa_v"), _ptr(swa_len, i32, "swa_len"), W, B,
+        H, D, float(softmax_scale), _ptr(out, f32, "out"), _ptr(lse, f32, "lse"), wp, wn,
+        _stream(stream)), "csa2_sparse_attn_decode")
+
+
+def csa2_prefill_workspace_bytes(Qn, H, D, topk, W):
+    return int(lib.csa2_prefill_workspace_bytes(Qn, H, D, topk, W))
+
+
+def csa2_sparse_attn_prefill_chunk(q, p0, kv_codes, kv_scales, topk_idx, swa_k, swa_v, W,
+                                   softmax_scale, out, lse=None, ws=None, stream=None):
+    """q [Qn,H,D] f32; topk_idx [Qn,topk] i32; swa_k/swa_v [Qn+W-1,D] u8; out [Qn,H,D]."""
+    f32, i32, i64, u8 = _dt()
+    Qn, H, D = q.shape
+    topk = topk_idx.shape[1] if topk_idx is not None else 0
+    wp, wn = _ws(ws)
+    _check(lib.csa2_sparse_attn_prefill_chunk(
+        _ptr(q, f32, "q"), int(p0), _ptr(kv_codes, u8, "kv_codes"),
+        _ptr(kv_scales, u8, "kv_scales"), _ptr(topk_idx, i32, "topk_idx"), topk,
+        _ptr(swa_k, u8, "swa_k"), _ptr(swa_v, u8, "swa_v"), W, Qn, H, D, float(softmax_scale),
+        _ptr(out, f32, "out"), _ptr(lse, f32, "lse"), wp, wn, _stream(stream)),
+        "csa2_sparse_attn_prefill_chunk")
+
+
+# ----------------------------------------------------------------- profiling
+
+def profile_enable(on=True):
+    _check(lib.csa2_profile_enable(1 if on else 0), "csa2_profile_enable")
+
+
+def profile_reset():
+    _check(lib.csa2_profile_reset(), "csa2_profile_reset")
+
+
+def profile_read():
+    """{kernel name: (launches, total_ms)} of the launches since the last reset."""
+    res = {}
+    i = 0
+    while True:
+        name, n, ms = ctypes.c_char_p(), ctypes.c_int(), ctypes.c_double()
+        if lib.csa2_profile_read(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)) != 0:
+            break
+        res[name.value.decode()] = (n.value, ms.value)
+        i += 1
+    return res
+
+
+def debug_decode_tables(stream=None):
+    """Device decodes of all 256 FP4 byte pairs and FP8 bytes (hardware and
+    definition paths), for the codec tests."""
+    import torch
+    dev = torch.device("cuda")
+    fp4_hw = torch.empty(512, dtype=torch.float32, device=dev)
+    fp4_ref = torch.empty(512, dtype=torch.float32, device=dev)
+    fp8_hw = torch.empty(256, dtype=torch.float32, device=dev)
+    fp8_ref = torch.empty(256, dtype=torch.float32, device=dev)
+    _check(lib.csa2_debug_decode_tables(_ptr(fp4_hw), _ptr(fp4_ref), _ptr(fp8_hw), _ptr(fp8_ref),
+                                        _stream(stream)), "csa2_debug_decode_tables")
+    return fp4_hw, fp4_ref, fp8_hw, fp8_ref

@@ -1,0 +1,628 @@
+// Full-mode indexer (score stream + exact Top-K + candidate pool) and the
+// Reindex step of CSA2, for gfx950.
+//
+// Method (jaehun.me review of arXiv 2609.19969, section "2) CSA2" and the
+// worked example of the modes): a Full layer scores every visible compressed
+// entry with its indexer and keeps the Top-K; the decoder's first Full layer
+// also keeps the best 2,048 blocks of 8 positions as a candidate pool; a
+// Reindex layer rescores only the pool with its own indexer query.
+//
+// Structure on the GPU
+//   1. k_score_stream: one pass over the key rows at HBM speed.  A wave
+//      takes 8 rows at a time (each lane holds 2 float4 of every 2 KB row,
+//      fully coalesced), dots them with the query held in registers and
+//      reduces the 8 sums across the wave with a transpose-reduction.  The
+//      order-preserving uint32 key of each score goes to workspace, together
+//      with a 4096-bin histogram of its top 12 bits (LDS, flushed once per
+//      workgroup) and, for the pool, the block maximum and its histogram.
+//   2. k_filter: the histogram gives the bin holding the K-th key; entries
+//      above it are certain winners, entries in it are candidates (their
+//      composite key score|~index goes to a short list).
+//   3. k_finalize: one workgroup per query selects the remaining winners
+//      among the candidates with a register-resident 64-bit radix select,
+//      sorts the K winners by index and writes them.  If the candidate bin
+//      holds more than 16,384 entries (degenerate score distributions) it
+//      falls back to an exact select over the whole key row.
+//   Reindex: k_reindex_score gathers the pool rows (8 contiguous 2 KB rows
+//   per block) with the same 8-row dot, k_reindex_select selects among the
+//   <= 16,384 composite keys of a query in one workgroup.
+#include <limits.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace csa2 {
+namespace {
+
+constexpr int kHistBins = 4096;      // first-level digit: top 12 bits of the key
+constexpr int kDigitShift = 20;
+constexpr int kCandCap = 16384;      // candidates a selecting workgroup holds
+constexpr int kSelThreads = 1024;
+constexpr int kSelItems = kCandCap / kSelThreads;
+constexpr int kStreamThreads = 256;
+constexpr int kRowsPerWG = 1024;     // score stream: rows per workgroup
+constexpr int kFilterElems = 16384;  // filter: keys per workgroup
+constexpr int kReindexPerWG = 1024;  // reindex: candidates per workgroup
+
+// ------------------------------------------------------------ row dots
+
+// Lane-resident slice of the query vector: chunk j of lane l holds floats
+// [4(l + 64 j), 4(l + 64 j) + 4) of the RW = 256*VPR-float query row.  With
+// one shared key head (Hk == 1) the query heads are summed first.
+template <int VPR>
+__device__ __forceinline__ void load_qvec(const float* __restrict__ qI, int q, int Hi, int Hk,
+                                          int Di, float4 (&qv)[VPR]) {
+    const int lane = lane_id();
+    if (Hk == Hi) {
+        const float4* p = reinterpret_cast<const float4*>(qI + (size_t)q * Hi * Di);
+#pragma unroll
+        for (int j = 0; j < VPR; ++j) qv[j] = p[lane + 64 * j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPR; ++j) {
+            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int h = 0; h < Hi; ++h) {
+                float4 v = reinterpret_cast<const float4*>(qI + ((size_t)q * Hi + h) * Di)[lane + 64 * j];
+                s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+            }
+            qv[j] = s;
+        }
+    }
+}
+
+// Dot products of the query with 8 key rows.  Returns, in every lane, the
+// full sum for row (lane >> 3) & 7.  Invalid rows (ok[i] false) read nothing.
+template <int VPR>
+__device__ __forceinline__ float dot8(const float* const (&rows)[8], const bool (&ok)[8],
+                                      const float4 (&qv)[VPR]) {
+    const int lane = lane_id();
+    float4 k[8][VPR];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < VPR; ++j)
+            k[i][j] = ok[i] ? reinterpret_cast<const float4*>(rows[i])[lane + 64 * j]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < VPR; ++j)
+            s += qv[j].x * k[i][j].x + qv[j].y * k[i][j].y + qv[j].z * k[i][j].z +
+                 qv[j].w * k[i][j].w;
+        a[i] = s;
+    }
+    // transpose-reduction: after the xor-32/16/8 steps lane l holds a partial
+    // of row (l>>3)&7 summed over 8 lanes; xor-4/2/1 completes the sum.
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float send = b5 ? a[i] : a[i + 4];
+        float keep = b5 ? a[i + 4] : a[i];
+        a[i] = keep + __shfl_xor(send, 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float send = b4 ? a[i] : a[i + 2];
+        float keep = b4 ? a[i + 2] : a[i];
+        a[i] = keep + __shfl_xor(send, 16);
+    }
+    {
+        float send = b3 ? a[0] : a[1];
+        float keep = b3 ? a[1] : a[0];
+        a[0] = keep + __shfl_xor(send, 8);
+    }
+    a[0] += __shfl_xor(a[0], 4);
+    a[0] += __shfl_xor(a[0], 2);
+    a[0] += __shfl_xor(a[0], 1);
+    return a[0];
+}
+
+// ------------------------------------------------------- score stream
+
+template <int VPR>
+__global__ __launch_bounds__(kStreamThreads) void k_score_stream(
+    const float* __restrict__ qI, const float* __restrict__ kI,
+    const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
+    int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
+    int64_t bstride, int bs_log2, uint32_t* __restrict__ hist_b) {
+    __shared__ uint32_t s_he[kHistBins];
+    __shared__ uint32_t s_hb[kHistBins];
+    constexpr int RW = 256 * VPR;
+    const int q = blockIdx.y;
+    const int nvis = q_nvis[q];
+    const int r0 = blockIdx.x * kRowsPerWG;
+    if (r0 >= nvis) return;
+    const int r1 = min(nvis, r0 + kRowsPerWG);
+    const bool pool = bkeys != nullptr;
+    for (int i = threadIdx.x; i < kHistBins; i += kStreamThreads) { s_he[i] = 0; s_hb[i] = 0; }
+    __syncthreads();
+
+    float4 qv[VPR];
+    load_qvec<VPR>(qI, q, Hi, Hk, Di, qv);
+    const int64_t row0 = seq_row_off[q_seq ? q_seq[q] : 0];
+    const float* kb = kI + row0 * RW;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int myrow = (lane >> 3) & 7;
+    const uint32_t bmask = (1u << bs_log2) - 1u;
+    uint32_t* krow = keys + (size_t)q * kstride;
+
+    for (int g0 = r0 + 8 * wave; g0 < r1; g0 += 8 * (kStreamThreads / kWave)) {
+        const float* rows[8];
+        bool ok[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ok[i] = g0 + i < r1;
+            rows[i] = kb + (int64_t)(g0 + i) * RW;
+        }
+        const float s = dot8<VPR>(rows, ok, qv);
+        const int row = g0 + myrow;
+        const bool valid = row < r1;
+        const uint32_t k = ord_key(s);
+        if ((lane & 7) == 0 && valid) {
+            krow[row] = k;
+            atomicAdd(&s_he[k >> kDigitShift], 1u);
+        }
+        if (pool) {
+            uint32_t bk = valid ? k : 0u;
+            if (bs_log2 >= 1) bk = max(bk, (uint32_t)__shfl_xor(bk, 8));
+            if (bs_log2 >= 2) bk = max(bk, (uint32_t)__shfl_xor(bk, 16));
+            if (bs_log2 >= 3) bk = max(bk, (uint32_t)__shfl_xor(bk, 32));
+            if ((lane & 7) == 0 && valid && ((uint32_t)myrow & bmask) == 0) {
+                bkeys[(size_t)q * bstride + (row >> bs_log2)] = bk;
+                atomicAdd(&s_hb[bk >> kDigitShift], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kHistBins; i += kStreamThreads) {
+        if (s_he[i]) atomicAdd(&hist_e[(size_t)q * kHistBins + i], s_he[i]);
+        if (pool && s_hb[i]) atomicAdd(&hist_b[(size_t)q * kHistBins + i], s_hb[i]);
+    }
+}
+
+__global__ void k_zero_u32(uint32_t* __restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// ------------------------------------------------------------- filter
+
+__global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ keys, int64_t stride,
+                                                const int32_t* __restrict__ q_nvis, int bs_log2,
+                                                int K, const uint32_t* __restrict__ hist,
+                                                uint32_t* __restrict__ cnt,
+                                                int32_t* __restrict__ above,
+                                                uint64_t* __restrict__ cand) {
+    __shared__ uint32_t s_tmp[256 / kWave + 3];
+    const int q = blockIdx.y;
+    const int nvis = q_nvis[q];
+    const int n = (nvis + (1 << bs_log2) - 1) >> bs_log2;
+    const int e0 = blockIdx.x * kFilterElems;
+    if (n <= K || e0 >= n) return;
+    uint32_t b1, nabove;
+    find_digit_4096<256>(hist + (size_t)q * kHistBins, (uint32_t)K, s_tmp, b1, nabove);
+    const int e1 = min(n, e0 + kFilterElems);
+    const uint32_t* row = keys + (size_t)q * stride;
+    for (int base = e0; base < e1; base += 256) {
+        const int e = base + threadIdx.x;
+        const bool ok = e < e1;
+        const uint32_t k = ok ? row[e] : 0u;
+        const uint32_t d = k >> kDigitShift;
+        const bool pa = ok && d > b1, pc = ok && d == b1;
+        const uint32_t sa = wave_append(pa, &cnt[2 * q]);
+        if (pa && sa < (uint32_t)K) above[(size_t)q * K + sa] = e;
+        const uint32_t sc = wave_append(pc, &cnt[2 * q + 1]);
+        if (pc && sc < (uint32_t)kCandCap) cand[(size_t)q * kCandCap + sc] = comp_key(k, (uint32_t)e);
+    }
+}
+
+// ------------------------------------------------------------ selects
+
+// Radix select over NT*IPT register-resident 64-bit keys (0 = empty slot;
+// non-empty keys distinct): returns T such that exactly `k` keys are >= T.
+// 1 <= k <= number of non-empty keys.
+template <int NT, int IPT>
+__device__ uint64_t block_select_kth(const uint64_t (&it)[IPT], uint32_t k, uint32_t* s_hist,
+                                     uint32_t* s_dig) {
+    uint64_t prefix = 0, mask = 0;
+    uint32_t want = k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += NT) s_hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+            const uint64_t v = it[j];
+            const bool m = v != 0 && (v & mask) == prefix;
+            const uint32_t d = (uint32_t)(v >> shift) & 255u;
+            // one atomic per wave when all matching lanes share the digit
+            const uint64_t mm = __ballot(m);
+            if (mm) {
+                const int lead = __builtin_ctzll(mm);
+                const uint32_t d0 = __shfl(d, lead);
+                const uint64_t same = __ballot(m && d == d0);
+                if (same == mm) {
+                    if (lane_id() == lead) atomicAdd(&s_hist[d0], (uint32_t)__popcll(mm));
+                } else if (m) {
+                    atomicAdd(&s_hist[d], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        find_digit_256(s_hist, want, s_dig);
+        const uint32_t d = s_dig[0], above = s_dig[1];
+        __syncthreads();
+        prefix |= (uint64_t)d << shift;
+        mask |= 0xFFull << shift;
+        want -= above;
+    }
+    return prefix;
+}
+
+// Exact Top-K over a whole row of uint32 keys (n > K) by one workgroup,
+// written in ascending index order: radix-select the K-th key value T, then
+// an ordered pass keeps every key > T and the lowest-index ties of T.
+template <int NT>
+__device__ void select_global_row(const uint32_t* __restrict__ keys, int n, int K,
+                                  int32_t* __restrict__ out, uint32_t* s_hist, uint32_t* s_dig,
+                                  uint32_t* s_tmp) {
+    uint32_t prefix = 0, mask = 0, want = (uint32_t)K;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += NT) s_hist[i] = 0u;
+        __syncthreads();
+        for (int base = 0; base < n; base += NT) {
+            const int i = base + threadIdx.x;
+            const uint32_t v = i < n ? keys[i] : 0u;
+            const bool m = i < n && (v & mask) == prefix;
+            const uint32_t d = (v >> shift) & 255u;
+            const uint64_t mm = __ballot(m);
+            if (mm) {
+                const int lead = __builtin_ctzll(mm);
+                const uint32_t d0 = __shfl(d, lead);
+                const uint64_t same = __ballot(m && d == d0);
+                if (same == mm) {
+                    if (lane_id() == lead) atomicAdd(&s_hist[d0], (uint32_t)__popcll(mm));
+                } else if (m) {
+                    atomicAdd(&s_hist[d], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        find_digit_256(s_hist, want, s_dig);
+        const uint32_t d = s_dig[0], above = s_dig[1];
+        __syncthreads();
+        prefix |= d << shift;
+        mask |= 0xFFu << shift;
+        want -= above;
+    }
+    const uint32_t T = prefix, need = want;  // keys > T: K - need of them
+    uint32_t tie_run = 0, sel_run = 0;
+    for (int base = 0; base < n; base += NT) {
+        const int i = base + threadIdx.x;
+        const uint32_t v = i < n ? keys[i] : 0u;
+        const bool eq = i < n && v == T, gt = i < n && v > T;
+        uint32_t tie_tot, sel_tot;
+        const uint32_t tie_ex = block_exclusive_sum<NT>(eq ? 1u : 0u, s_tmp, tie_tot);
+        const bool sel = gt || (eq && tie_run + tie_ex < need);
+        const uint32_t sel_ex = block_exclusive_sum<NT>(sel ? 1u : 0u, s_tmp, sel_tot);
+        if (sel && sel_run + sel_ex < (uint32_t)K) out[sel_run + sel_ex] = i;
+        tie_run += tie_tot;
+        sel_run += sel_tot;
+    }
+    for (int i = (int)sel_run + threadIdx.x; i < K; i += NT) out[i] = -1;
+}
+
+__device__ __forceinline__ int next_pow2(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+// Sorts the `count` indices in s_out ascending and writes K slots (-1 padded).
+__device__ void sort_and_write(int32_t* s_out, int count, int K, int32_t* __restrict__ o) {
+    const int P = next_pow2(K);
+    for (int i = count + threadIdx.x; i < P; i += kSelThreads) s_out[i] = INT_MAX;
+    __syncthreads();
+    block_bitonic_sort<kSelThreads>(s_out, P);
+    for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < count ? s_out[i] : -1;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_finalize(
+    const uint32_t* __restrict__ keys, int64_t stride, const int32_t* __restrict__ q_nvis,
+    int bs_log2, int K, const uint32_t* __restrict__ cnt, const int32_t* __restrict__ above,
+    const uint64_t* __restrict__ cand, int32_t* __restrict__ out) {
+    __shared__ int32_t s_out[CSA2_MAX_TOPK];
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
+    __shared__ uint32_t s_count;
+    const int q = blockIdx.x;
+    const int nvis = q_nvis[q];
+    const int n = (nvis + (1 << bs_log2) - 1) >> bs_log2;
+    int32_t* o = out + (size_t)q * K;
+    if (n <= K) {
+        for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
+        return;
+    }
+    const uint32_t na = min(cnt[2 * q], (uint32_t)K - 1u), nc = cnt[2 * q + 1];
+    if (nc > (uint32_t)kCandCap) {
+        select_global_row<kSelThreads>(keys + (size_t)q * stride, n, K, o, s_hist, s_dig, s_tmp);
+        return;
+    }
+    uint64_t it[kSelItems];
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        const uint32_t i = threadIdx.x + j * kSelThreads;
+        it[j] = i < nc ? cand[(size_t)q * kCandCap + i] : 0ull;
+    }
+    const uint64_t T = block_select_kth<kSelThreads, kSelItems>(it, (uint32_t)K - na, s_hist, s_dig);
+    if (threadIdx.x == 0) s_count = na;
+    for (int i = threadIdx.x; i < (int)na; i += kSelThreads) s_out[i] = above[(size_t)q * K + i];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        if (it[j] != 0 && it[j] >= T) {
+            const uint32_t pos = atomicAdd(&s_count, 1u);
+            if (pos < (uint32_t)K) s_out[pos] = (int32_t)comp_idx(it[j]);
+        }
+    }
+    __syncthreads();
+    sort_and_write(s_out, min((int)s_count, K), K, o);
+}
+
+// ------------------------------------------------------------- reindex
+
+template <int VPR>
+__global__ __launch_bounds__(kStreamThreads) void k_reindex_score(
+    const float* __restrict__ qI, const float* __restrict__ kI,
+    const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, const int32_t* __restrict__ pool,
+    int P, int bs, uint64_t* __restrict__ ckeys) {
+    constexpr int RW = 256 * VPR;
+    const int q = blockIdx.y;
+    const int ncand = P * bs;
+    const int c0 = blockIdx.x * kReindexPerWG;
+    if (c0 >= ncand) return;
+    const int c1 = min(ncand, c0 + kReindexPerWG);
+    float4 qv[VPR];
+    load_qvec<VPR>(qI, q, Hi, Hk, Di, qv);
+    const int nvis = q_nvis[q];
+    const int64_t row0 = seq_row_off[q_seq ? q_seq[q] : 0];
+    const float* kb = kI + row0 * RW;
+    const int32_t* prow = pool + (size_t)q * P;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int myrow = (lane >> 3) & 7;
+    for (int g0 = c0 + 8 * wave; g0 < c1; g0 += 8 * (kStreamThreads / kWave)) {
+        const float* rows[8];
+        bool ok[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = g0 + i;
+            int64_t t = -1;
+            if (c < c1) {
+                const int b = prow[c / bs];
+                t = b >= 0 ? (int64_t)b * bs + c % bs : -1;
+            }
+            ok[i] = t >= 0 && t < nvis;
+            rows[i] = kb + (ok[i] ? t : 0) * RW;
+        }
+        const float s = dot8<VPR>(rows, ok, qv);
+        const int c = g0 + myrow;
+        if ((lane & 7) == 0 && c < c1) {
+            const int b = prow[c / bs];
+            const int64_t t = b >= 0 ? (int64_t)b * bs + c % bs : -1;
+            const bool v = t >= 0 && t < nvis;
+            ckeys[(size_t)q * ncand + c] = v ? comp_key(ord_key(s), (uint32_t)t) : 0ull;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_reindex_select(
+    const uint64_t* __restrict__ ckeys, int ncand, int K, int32_t* __restrict__ out) {
+    __shared__ int32_t s_out[CSA2_MAX_TOPK];
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
+    __shared__ uint32_t s_count;
+    const int q = blockIdx.x;
+    uint64_t it[kSelItems];
+    uint32_t nv = 0;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        const int i = threadIdx.x + j * kSelThreads;
+        it[j] = i < ncand ? ckeys[(size_t)q * ncand + i] : 0ull;
+        nv += it[j] != 0;
+    }
+    uint32_t total;
+    (void)block_exclusive_sum<kSelThreads>(nv, s_tmp, total);
+    const int k = min((int)total, K);
+    int32_t* o = out + (size_t)q * K;
+    if (k == 0) {
+        for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
+        return;
+    }
+    const uint64_t T = block_select_kth<kSelThreads, kSelItems>(it, (uint32_t)k, s_hist, s_dig);
+    if (threadIdx.x == 0) s_count = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        if (it[j] != 0 && it[j] >= T) {
+            const uint32_t pos = atomicAdd(&s_count, 1u);
+            if (pos < (uint32_t)K) s_out[pos] = (int32_t)comp_idx(it[j]);
+        }
+    }
+    __syncthreads();
+    sort_and_write(s_out, min((int)s_count, K), K, o);
+}
+
+// ------------------------------------------------------ host helpers
+
+struct IndexWs {
+    uint32_t *keys_e, *keys_b, *hist_e, *hist_b, *cnt_e, *cnt_b;
+    int32_t *above_e, *above_b;
+    uint64_t *cand_e, *cand_b;
+    int64_t se, sb;
+    size_t zero_words;
+    size_t bytes;
+};
+
+inline int ilog2(int x) {
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return l;
+}
+
+IndexWs carve_index(void* ws, int Q, int max_nvis, int topk, int pool_blocks, int block_size) {
+    IndexWs w{};
+    Carver c(ws);
+    const int bs = pool_blocks > 0 ? block_size : 1;
+    w.se = ((int64_t)max_nvis + 63) / 64 * 64;
+    w.sb = pool_blocks > 0 ? (((int64_t)max_nvis + bs - 1) / bs + 63) / 64 * 64 : 0;
+    // zeroed region first: histograms and counters
+    w.hist_e = c.take<uint32_t>((size_t)Q * kHistBins);
+    w.hist_b = c.take<uint32_t>(pool_blocks > 0 ? (size_t)Q * kHistBins : 0);
+    w.cnt_e = c.take<uint32_t>((size_t)Q * 2);
+    w.cnt_b = c.take<uint32_t>((size_t)Q * 2);
+    w.zero_words = c.bytes() / 4;
+    w.keys_e = c.take<uint32_t>((size_t)Q * w.se);
+    w.keys_b = c.take<uint32_t>((size_t)Q * w.sb);
+    w.above_e = c.take<int32_t>((size_t)Q * topk);
+    w.above_b = c.take<int32_t>((size_t)Q * pool_blocks);
+    w.cand_e = c.take<uint64_t>(topk > 0 ? (size_t)Q * kCandCap : 0);
+    w.cand_b = c.take<uint64_t>(pool_blocks > 0 ? (size_t)Q * kCandCap : 0);
+    w.bytes = c.bytes();
+    return w;
+}
+
+// Shared argument checks of the indexer entry points.
+int check_indexer_shape(int Q, int Hi, int Hk, int Di, int* vpr) {
+    if (Q < 0 || Hi <= 0 || Hk <= 0 || Di <= 0) return CSA2_ERR_SHAPE;
+    if (Hk != Hi && Hk != 1) return CSA2_ERR_UNSUPPORTED;
+    const long rw = (long)Hk * Di;
+    if (rw == 256) *vpr = 1;
+    else if (rw == 512) *vpr = 2;
+    else if (rw == 1024) *vpr = 4;
+    else return CSA2_ERR_UNSUPPORTED;
+    if (Q > 65535) return CSA2_ERR_UNSUPPORTED;
+    return CSA2_OK;
+}
+
+}  // namespace
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
+                                                  int32_t pool_blocks, int32_t block_size) {
+    if (Q < 0 || max_nvis < 0 || topk < 0 || pool_blocks < 0) return 0;
+    if (pool_blocks > 0 && block_size <= 0) return 0;
+    return carve_index(nullptr, Q, max_nvis, topk, pool_blocks, block_size).bytes;
+}
+
+extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* seq_row_off,
+                               const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
+                               int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk,
+                               int32_t* topk_idx, int32_t pool_blocks, int32_t block_size,
+                               int32_t* pool_block_idx, void* ws, size_t ws_bytes,
+                               void* stream_) {
+    int vpr = 0;
+    int st = check_indexer_shape(Q, Hi, Hk, Di, &vpr);
+    if (st != CSA2_OK) return st;
+    if (max_nvis < 0 || topk < 0 || pool_blocks < 0) return CSA2_ERR_SHAPE;
+    if (topk > CSA2_MAX_TOPK || pool_blocks > CSA2_MAX_TOPK) return CSA2_ERR_UNSUPPORTED;
+    if (pool_blocks > 0 && block_size != 1 && block_size != 2 && block_size != 4 && block_size != 8)
+        return block_size <= 0 ? CSA2_ERR_SHAPE : CSA2_ERR_UNSUPPORTED;
+    if (Q == 0 || (topk == 0 && pool_blocks == 0)) return CSA2_OK;
+    if (!qI || !kI || !seq_row_off || !q_nvis || !ws) return CSA2_ERR_NULL;
+    if ((topk > 0 && !topk_idx) || (pool_blocks > 0 && !pool_block_idx)) return CSA2_ERR_NULL;
+    if (((uintptr_t)qI | (uintptr_t)kI) & 15) return CSA2_ERR_UNSUPPORTED;
+    IndexWs w = carve_index(ws, Q, max_nvis, topk, pool_blocks, block_size);
+    if (ws_bytes < w.bytes) return CSA2_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream_;
+    const int bs_log2 = pool_blocks > 0 ? ilog2(block_size) : 0;
+
+    st = CSA2_LAUNCH("zero", k_zero_u32, dim3(256), dim3(256), s, w.hist_e, w.zero_words);
+    if (st) return st;
+    if (max_nvis == 0) {
+        // no visible entries anywhere: the finalize kernels write -1 rows
+    } else {
+        dim3 grid((max_nvis + kRowsPerWG - 1) / kRowsPerWG, Q);
+        uint32_t* bk = pool_blocks > 0 ? w.keys_b : nullptr;
+#define CSA2_STREAM(V)                                                                        \
+    CSA2_LAUNCH("score_stream", k_score_stream<V>, grid, dim3(kStreamThreads), s, qI, kI,     \
+                seq_row_off, q_seq, q_nvis, Hi, Hk, Di, w.keys_e, w.se, w.hist_e, bk, w.sb,   \
+                bs_log2, w.hist_b)
+        st = vpr == 1 ? CSA2_STREAM(1) : vpr == 2 ? CSA2_STREAM(2) : CSA2_STREAM(4);
+#undef CSA2_STREAM
+        if (st) return st;
+    }
+    if (topk > 0) {
+        if (max_nvis > 0) {
+            dim3 g((max_nvis + kFilterElems - 1) / kFilterElems, Q);
+            st = CSA2_LAUNCH("filter", k_filter, g, dim3(256), s, w.keys_e, w.se, q_nvis, 0, topk,
+                             w.hist_e, w.cnt_e, w.above_e, w.cand_e);
+            if (st) return st;
+        }
+        st = CSA2_LAUNCH("finalize", k_finalize, dim3(Q), dim3(kSelThreads), s, w.keys_e, w.se,
+                         q_nvis, 0, topk, w.cnt_e, w.above_e, w.cand_e, topk_idx);
+        if (st) return st;
+    }
+    if (pool_blocks > 0) {
+        const int nb = (max_nvis + block_size - 1) / block_size;
+        if (nb > 0) {
+            dim3 g((nb + kFilterElems - 1) / kFilterElems, Q);
+            st = CSA2_LAUNCH("filter", k_filter, g, dim3(256), s, w.keys_b, w.sb, q_nvis, bs_log2,
+                             pool_blocks, w.hist_b, w.cnt_b, w.above_b, w.cand_b);
+            if (st) return st;
+        }
+        st = CSA2_LAUNCH("finalize", k_finalize, dim3(Q), dim3(kSelThreads), s, w.keys_b, w.sb,
+                         q_nvis, bs_log2, pool_blocks, w.cnt_b, w.above_b, w.cand_b,
+                         pool_block_idx);
+        if (st) return st;
+    }
+    return CSA2_OK;
+}
+
+extern "C" size_t csa2_reindex_workspace_bytes(int32_t Q, int32_t pool_blocks, int32_t block_size) {
+    if (Q < 0 || pool_blocks < 0 || block_size <= 0) return 0;
+    Carver c(nullptr);
+    c.take<uint64_t>((size_t)Q * pool_blocks * block_size);
+    return c.bytes();
+}
+
+extern "C" int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
+                            const int32_t* q_seq, const int32_t* q_nvis,
+                            const int32_t* pool_block_idx, int32_t pool_blocks, int32_t block_size,
+                            int32_t Q, int32_t Hi, int32_t Hk, int32_t Di, int32_t topk,
+                            int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream_) {
+    int vpr = 0;
+    int st = check_indexer_shape(Q, Hi, Hk, Di, &vpr);
+    if (st != CSA2_OK) return st;
+    if (pool_blocks < 0 || block_size <= 0 || topk < 0) return CSA2_ERR_SHAPE;
+    if (topk > CSA2_MAX_TOPK || (int64_t)pool_blocks * block_size > CSA2_MAX_POOL_CAND)
+        return CSA2_ERR_UNSUPPORTED;
+    if (Q == 0 || topk == 0) return CSA2_OK;
+    if (!qI || !kI || !seq_row_off || !q_nvis || !topk_idx || !ws) return CSA2_ERR_NULL;
+    if (pool_blocks > 0 && !pool_block_idx) return CSA2_ERR_NULL;
+    if (((uintptr_t)qI | (uintptr_t)kI) & 15) return CSA2_ERR_UNSUPPORTED;
+    if (ws_bytes < csa2_reindex_workspace_bytes(Q, pool_blocks, block_size))
+        return CSA2_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream_;
+    uint64_t* ck = static_cast<uint64_t*>(ws);
+    const int ncand = pool_blocks * block_size;
+    if (ncand > 0) {
+        dim3 g((ncand + kReindexPerWG - 1) / kReindexPerWG, Q);
+#define CSA2_RS(V)                                                                             \
+    CSA2_LAUNCH("reindex_score", k_reindex_score<V>, g, dim3(kStreamThreads), s, qI, kI,       \
+                seq_row_off, q_seq, q_nvis, Hi, Hk, Di, pool_block_idx, pool_blocks,           \
+                block_size, ck)
+        st = vpr == 1 ? CSA2_RS(1) : vpr == 2 ? CSA2_RS(2) : CSA2_RS(4);
+#undef CSA2_RS
+        if (st) return st;
+    }
+    return CSA2_LAUNCH("reindex_select", k_reindex_select, dim3(Q), dim3(kSelThreads), s, ck,
+                       ncand, topk, topk_idx);
+}

@@ -1,0 +1,48 @@
+// Host-side helpers shared by the CSA2 entry points: status plumbing,
+// workspace carving and optional per-kernel event timing.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+
+namespace csa2 {
+
+// Records the HIP error of a failed launch for csa2_last_hip_error().
+void set_last_hip_error(hipError_t e);
+
+// Returns CSA2_OK or CSA2_ERR_HIP for the last launch on this thread.
+int check_launch();
+
+// Kernel timing hooks (no-ops unless csa2_profile_enable(1)).
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+// Linear bump allocator over a caller-provided workspace; every piece is
+// 256-byte aligned.  With base == nullptr it only measures.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(size_t count) {
+        off = (off + 255) & ~size_t(255);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+    size_t bytes() const { return (off + 255) & ~size_t(255); }
+};
+
+}  // namespace csa2
+
+// Launch helper: kernel<<<grid, block, 0, stream>>>(args...) bracketed by the
+// timing hooks; evaluates to the launch status.
+#define CSA2_LAUNCH(name, kernel, grid, block, stream, ...)                \
+    ([&]() -> int {                                                        \
+        ::csa2::prof_begin(name, stream);                                  \
+        kernel<<<grid, block, 0, stream>>>(__VA_ARGS__);                   \
+        ::csa2::prof_end(stream);                                          \
+        return ::csa2::check_launch();                                     \
+    }())

@@ -1,0 +1,194 @@
+/*
+ * csa2.h -- C ABI of the CSA2 sparse-attention hot path on MI355X (gfx950).
+ *
+ * The method (arXiv 2609.19969, "DeepSeek-V4.1-Flash: Pushing the Limits of
+ * KV Cache Compression"), as described by the jaehun.me review of that paper
+ * (sections "2) CSA2" and "3) FP4 main KV + SWA Bounded Replay", and the
+ * worked example of the three modes) and by the ainewsway.com article on it:
+ *   - every CSA2 layer has a static mode.  Full: scores all compressed
+ *     main-KV entries with an indexer and keeps the Top-K (K = 512); the
+ *     decoder's first Full layer also builds a candidate pool of 2,048
+ *     blocks x 8 positions.  Reindex: rescores only the pool with its own
+ *     indexer query and keeps 512.  Reuse: takes the latest Full layer's
+ *     main KV and indices as they are.  Every mode has its own query and its
+ *     own sliding-window (SWA) KV.
+ *   - main KV is stored as FP4 E2M1 with one E4M3 scale per 16 channels; the
+ *     window KV (n_win = 128 tokens) is FP8 E4M3.
+ *
+ * Layer modes map onto calls: Full = csa2_index_full + attention; Reindex =
+ * csa2_reindex (with the Full layer's pool and key cache) + attention; Reuse =
+ * attention with the same topk_idx / kv pointers and no indexer call.
+ *
+ * Conventions for every call
+ *   - All array arguments are DEVICE pointers owned by the caller; `stream` is
+ *     a hipStream_t (NULL = the null stream).  The library never allocates,
+ *     frees or synchronises: it checks its scalar arguments on the host,
+ *     enqueues kernels on `stream` and returns.  Device-side contents are
+ *     trusted (see the preconditions of each call).
+ *   - Workspace `ws` (>= the size the matching *_workspace_bytes returns,
+ *     256-byte aligned) is scratch owned by the caller; its contents need no
+ *     initialisation and are meaningless after the call.  Calls that overlap
+ *     on different streams need different workspaces.
+ *   - Entry indices are int32 and local to their sequence; row offsets are
+ *     int64.  Index outputs are written in ascending order, padded with -1,
+ *     and fully overwritten.  Outputs must not alias inputs.
+ *   - Selection order: higher score first, ties to the lower index (lower
+ *     block id for the pool).  With integer-valued indexer inputs whose dot
+ *     products stay below 2^24 the fp32 scores are exact and the selection
+ *     is exactly the one of the definition.
+ *   - Return value: a csa2_status.  No C++ exception crosses this boundary.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    CSA2_ERR_SHAPE = 2,       /* a size is negative or inconsistent              */
+    CSA2_ERR_UNSUPPORTED = 3, /* valid, but outside what the kernels implement   */
+    CSA2_ERR_WORKSPACE = 4,   /* ws_bytes below the *_workspace_bytes figure     */
+    CSA2_ERR_HIP = 5          /* a launch failed; see csa2_last_hip_error()      */
+} csa2_status;
+
+/* Name of a status code (static string). */
+const char* csa2_status_str(int status);
+/* hipError_t of the last CSA2_ERR_HIP returned on this host thread. */
+int csa2_last_hip_error(void);
+
+/* Limits of this implementation. */
+#define CSA2_MAX_TOPK 2048          /* topk and pool_blocks                     */
+#define CSA2_MAX_POOL_CAND 16384    /* pool_blocks * block_size (2,048 x 8)    */
+
+/* ------------------------------------------------------------------------
+ * Full-mode indexer: scoring + Top-K (+ candidate pool).
+ *
+ * Defines (jaehun.me review, section "2) CSA2" and the worked example; the
+ * pages give no score formula, the plain head sum is used):
+ *   s(q, t) = sum_{h < Hi} sum_{d < Di} qI[q,h,d] * kI[row0(q) + t, h mod Hk, d]
+ * for every visible entry t < q_nvis[q], row0(q) = seq_row_off[q_seq[q]].
+ * topk_idx[q] = the min(topk, q_nvis[q]) entries of highest score.
+ * With pool_blocks > 0 (decoder's first Full layer, 2,048 blocks x 8
+ * positions): block b covers entries [b*block_size, (b+1)*block_size) ∩
+ * [0, q_nvis); it scores the maximum of its entries' scores;
+ * pool_block_idx[q] = the min(pool_blocks, #blocks) best blocks.
+ *
+ *   qI             [Q, Hi, Di] fp32
+ *   kI             [rows, Hk, Di] fp32, Hk == Hi or Hk == 1 (one key row
+ *                  shared by all indexer heads); Hk*Di must be 256, 512 or
+ *                  1024 (Hk == Hi) or Di must be (Hk == 1)
+ *   seq_row_off    [S] int64: first kI row of each sequence
+ *   q_seq          [Q] int32: sequence of each query.  May be NULL: then all
+ *                  queries belong to sequence 0 (a chunk of prefill queries
+ *                  of one prompt) and the call is scheduled as a
+ *                  query-tile x key-tile contraction instead of one key
+ *                  stream per query.
+ *   q_nvis         [Q] int32: visible entries of each query (causality; for
+ *                  an encoder chunk with m tokens per entry the caller passes
+ *                  floor((p+1)/m)).  0 <= q_nvis[q] <= max_nvis.
+ *   max_nvis       host bound on q_nvis (sizes the grid and the workspace)
+ *   topk           0..CSA2_MAX_TOPK; topk_idx [Q, topk] int32 (may be NULL iff 0)
+ *   pool_blocks    0..CSA2_MAX_TOPK; block_size in {1,2,4,8};
+ *                  pool_block_idx [Q, pool_blocks] int32 (NULL iff pool_blocks 0)
+ * Preconditions (device data): rows read stay inside kI.
+ * ---------------------------------------------------------------------- */
+size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
+                                       int32_t pool_blocks, int32_t block_size);
+int csa2_index_full(const float* qI, const float* kI, const int64_t* seq_row_off,
+                    const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
+                    int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk, int32_t* topk_idx,
+                    int32_t pool_blocks, int32_t block_size, int32_t* pool_block_idx, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Reindex mode (jaehun.me review, section "2) CSA2"; paper 2.3.2): rescore
+ * only the candidate pool with this layer's own indexer query against the
+ * shared key cache and keep the Top-K.  Candidates of query q:
+ *   { b*block_size + j : b = pool_block_idx[q, i] >= 0, j < block_size,
+ *     b*block_size + j < q_nvis[q] }
+ * at most pool_blocks * block_size <= CSA2_MAX_POOL_CAND (2,048 x 8).
+ * Score as in csa2_index_full; ties go to the lower ENTRY index.
+ *   pool_block_idx [Q, pool_blocks] int32, -1 = empty slot.
+ * Preconditions (device data): the valid block ids of a row are distinct.
+ * ---------------------------------------------------------------------- */
+size_t csa2_reindex_workspace_bytes(int32_t Q, int32_t pool_blocks, int32_t block_size);
+int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
+                 const int32_t* q_seq, const int32_t* q_nvis, const int32_t* pool_block_idx,
+                 int32_t pool_blocks, int32_t block_size, int32_t Q, int32_t Hi, int32_t Hk,
+                 int32_t Di, int32_t topk, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention, decode (one query token per sequence; any layer mode).
+ * (jaehun.me review, sections "2) CSA2" and "3) FP4 main KV"; ainewsway.com
+ * article: window and global sparse retrieval form one attention.)
+ * For sequence b and head h, one softmax over the union of
+ *   - main-KV entries t = topk_idx[b, i] >= 0: key = value = dequantised row
+ *     seq_row_off[b] + t, v[c] = E2M1(code[c]) * E4M3(scale[c/16]) (channel
+ *     c = low nibble of byte c/2 for even c, high nibble for odd c);
+ *   - window tokens w < min(swa_len[b], W): key E4M3(swa_k[b,w,:]),
+ *     value E4M3(swa_v[b,w,:]);
+ * with logits softmax_scale * q.k:  out[b,h] = sum_j p_j v_j,
+ * lse[b,h] = log sum_j exp(logit_j).  No key at all: out = 0, lse = -inf.
+ *   q        [B, H, D] fp32          kv_codes [rows, D/2] u8
+ *   kv_scales [rows, D/16] u8        topk_idx [B, topk] int32 (-1 skipped)
+ *   swa_k/swa_v [B, W, D] u8 (E4M3FN)  swa_len [B] int32
+ *   out [B, H, D] fp32; lse [B, H] fp32 or NULL
+ * Supported: D == 512, H a multiple of 16 up to 64... (any H % 16 == 0),
+ * 0 <= topk <= CSA2_MAX_TOPK, 0 <= W <= 1024.
+ * Preconditions (device data): every valid index addresses a row of kv.
+ * ---------------------------------------------------------------------- */
+size_t csa2_decode_workspace_bytes(int32_t B, int32_t H, int32_t D, int32_t topk, int32_t W);
+int csa2_sparse_attn_decode(const float* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                            const int64_t* seq_row_off, const int32_t* topk_idx, int32_t topk,
+                            const uint8_t* swa_k, const uint8_t* swa_v, const int32_t* swa_len,
+                            int32_t W, int32_t B, int32_t H, int32_t D, float softmax_scale,
+                            float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention over a prefill chunk of ONE sequence: query i sits at
+ * position p = p0 + i and equals a decode query with index row topk_idx[i]
+ * and the window of the W tokens ending at p (those at positions >= 0).
+ * (jaehun.me review: encoder CSA2 layers, m = 2; window n_win = 128.)
+ *   q [Qn, H, D] fp32; kv_codes/kv_scales: this sequence's rows
+ *   topk_idx [Qn, topk] int32 (-1 skipped)
+ *   swa_k/swa_v [Qn + W - 1, D] u8: row r holds position p0 - W + 1 + r;
+ *   rows of negative position are never read.
+ *   out [Qn, H, D]; lse [Qn, H] or NULL.   Supported shapes as for decode.
+ * ---------------------------------------------------------------------- */
+size_t csa2_prefill_workspace_bytes(int32_t Qn, int32_t H, int32_t D, int32_t topk, int32_t W);
+int csa2_sparse_attn_prefill_chunk(const float* q, int64_t p0, const uint8_t* kv_codes,
+                                   const uint8_t* kv_scales, const int32_t* topk_idx,
+                                   int32_t topk, const uint8_t* swa_k, const uint8_t* swa_v,
+                                   int32_t W, int32_t Qn, int32_t H, int32_t D,
+                                   float softmax_scale, float* out, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Optional per-kernel timing (for measurement tools).  While enabled, every
+ * kernel the library launches is bracketed by hipEvents recorded on the
+ * launch stream; csa2_profile_read synchronises on the last event and
+ * returns, per kernel name, the launch count and summed milliseconds.
+ * Not thread-safe; disabled by default.
+ * ---------------------------------------------------------------------- */
+int csa2_profile_enable(int enable);
+int csa2_profile_read(int slot, const char** name, int* launches, double* total_ms);
+int csa2_profile_reset(void);
+
+/* Test hook: decodes every byte value with the device codecs the attention
+ * kernels use.  fp4_hw/fp4_ref [512]: entry 2b / 2b+1 = low / high nibble of
+ * byte b through the gfx950 FP4 conversion / through the E2M1 definition;
+ * fp8_hw/fp8_ref [256]: byte b through the gfx950 FP8 conversion / the
+ * E4M3FN definition.  Device pointers. */
+int csa2_debug_decode_tables(float* fp4_hw, float* fp4_ref, float* fp8_hw, float* fp8_ref,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

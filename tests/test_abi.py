@@ -1,0 +1,100 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    import compressed_fp4_kv_amd as p
+    return p
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(pkg):
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(pkg.lib, n), n
+    assert sorted(pkg.EXPORTED_SYMBOLS) == names
+
+
+def test_status_strings(pkg):
+    for s in range(6):
+        assert pkg.lib.csa2_status_str(s).decode().startswith("CSA2")
+
+
+NULL = None
+
+
+def _idx(pkg, **kw):
+    a = dict(qI=1, kI=1, off=1, qseq=1, nvis=1, Q=1, Hi=4, Hk=4, Di=128, maxn=100, topk=8,
+             out=1, P=0, bs=8, pool=NULL, ws=1, wsb=1 << 30)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(16 * x)
+    return pkg.lib.csa2_index_full(v(a["qI"]), v(a["kI"]), v(a["off"]), v(a["qseq"]), v(a["nvis"]),
+                                   a["Q"], a["Hi"], a["Hk"], a["Di"], a["maxn"], a["topk"],
+                                   v(a["out"]), a["P"], a["bs"], v(a["pool"]), v(a["ws"]), a["wsb"],
+                                   None)
+
+
+def test_index_full_argument_checks(pkg):
+    assert _idx(pkg, qI=NULL) == 1
+    assert _idx(pkg, out=NULL) == 1
+    assert _idx(pkg, P=16, pool=NULL) == 1
+    assert _idx(pkg, Q=-1) == 2
+    assert _idx(pkg, topk=-3) == 2
+    assert _idx(pkg, Hk=2) == 3            # neither 1 nor Hi
+    assert _idx(pkg, Di=100) == 3          # row width not 256/512/1024
+    assert _idx(pkg, topk=4096) == 3
+    assert _idx(pkg, P=16, bs=3, pool=1) == 3
+    assert _idx(pkg, P=16, bs=0, pool=1) == 2
+    assert _idx(pkg, wsb=10) == 4
+    assert _idx(pkg, Q=0) == 0             # nothing to do, nothing launched
+    need = pkg.csa2_index_full_workspace_bytes(1, 100, 8, 0, 8)
+    assert need > 0 and _idx(pkg, wsb=need - 1) == 4
+
+
+def test_reindex_argument_checks(pkg):
+    v = lambda x: None if x is None else ctypes.c_void_p(16 * x)
+    f = pkg.lib.csa2_reindex
+    base = [v(1), v(1), v(1), v(1), v(1), v(1), 2048, 8, 4, 4, 4, 128, 512, v(1), v(1), 1 << 30, None]
+    assert f(*base[:5], None, *base[6:]) == 1
+    b = list(base); b[6] = 4096
+    assert f(*b) == 3                       # 4096 x 8 > 16,384 candidates
+    b = list(base); b[7] = 0
+    assert f(*b) == 2
+    b = list(base); b[15] = 8
+    assert f(*b) == 4
+
+
+def test_attention_argument_checks(pkg):
+    v = lambda x: None if x is None else ctypes.c_void_p(16 * x)
+    f = pkg.lib.csa2_sparse_attn_decode
+    base = [v(1), v(1), v(1), v(1), v(1), 512, v(1), v(1), v(1), 128, 4, 64, 512, 0.04, v(1), None,
+            v(1), 1 << 30, None]
+    b = list(base); b[12] = 256
+    assert f(*b) == 3                       # D != 512
+    b = list(base); b[11] = 24
+    assert f(*b) == 3                       # H not a multiple of 16
+    b = list(base); b[0] = None
+    assert f(*b) == 1
+    b = list(base); b[10] = -1
+    assert f(*b) == 2
+    b = list(base); b[17] = 0
+    assert f(*b) == 4                       # needs split workspace at B=4
+    g = pkg.lib.csa2_sparse_attn_prefill_chunk
+    pb = [v(1), -5, v(1), v(1), v(1), 512, v(1), v(1), 128, 64, 64, 512, 0.04, v(1), None, v(1),
+          1 << 30, None]
+    assert g(*pb) == 2                      # negative position

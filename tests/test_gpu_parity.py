@@ -1,0 +1,277 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI, on
+the five workloads at reduced context (several tiles and ragged tails) and on
+edge cases.  Indices: bit-exact.  Attention: max-abs 2e-3 and rel-L2 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from gen import host_ints  # noqa: E402
+from gen.workloads import (T_QI_FULL, T_QI_REINDEX, Workload, build_device, host_kI_rows,  # noqa: E402
+                           host_qI, workload)
+
+import _cases as C  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def csa2():
+    assert torch.cuda.is_available(), "needs an MI355X"
+    import compressed_fp4_kv_amd as m
+    return m
+
+
+def teardown_module(module):
+    torch.cuda.empty_cache()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ codecs
+
+def test_device_codecs_match_oracle_tables(csa2):
+    fp4_hw, fp4_ref, fp8_hw, fp8_ref = [x.cpu().numpy() for x in csa2.debug_decode_tables()]
+    torch.cuda.synchronize()
+    exp4 = np.array([oracle.e2m1(b & 15) if j == 0 else oracle.e2m1(b >> 4)
+                     for b in range(256) for j in range(2)])
+    exp8 = np.array([oracle.e4m3(b) for b in range(256)])
+    assert np.array_equal(fp4_ref, exp4)
+    assert np.array_equal(fp4_hw, exp4), "gfx950 FP4 conversion disagrees with E2M1"
+    nan = np.isnan(exp8)
+    assert np.array_equal(np.isnan(fp8_ref), nan) and np.array_equal(fp8_ref[~nan], exp8[~nan])
+    assert np.array_equal(np.isnan(fp8_hw), nan), "gfx950 FP8 NaN codes differ from E4M3FN"
+    assert np.array_equal(fp8_hw[~nan], exp8[~nan]), "gfx950 FP8 conversion differs from E4M3FN"
+
+
+# ----------------------------------------------------------- decode groups
+
+def _check_decode_group(csa2, w, t, idx_gpu, idx_ref_rows, layers, queries):
+    for layer in range(layers):
+        out, lse = C.gpu_attn(w, t, layer, idx_gpu)
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        for b in queries:
+            ro, rl = C.oracle_attn_query(w, b, layer, idx_ref_rows[b])
+            C.assert_attn_close(out[b], ro[0], f"{w.name} layer {layer} query {b}")
+            C.assert_lse_close(lse[b], rl[0], f"{w.name} layer {layer} query {b}")
+
+
+@pytest.mark.parametrize("wid", [0, 1])
+def test_full_then_reuse_group(csa2, wid):
+    w = workload(wid, small=True)
+    _say(f"[{w.name}] B={w.B} ctx={w.ctx[0]} topk={w.topk}")
+    t = build_device(w)
+    idx, _ = C.gpu_index_full(w, t)
+    idx = idx.cpu().numpy()
+    ref = {}
+    for b in range(w.B):
+        r, _ = C.oracle_index_query(w, b)
+        assert np.array_equal(idx[b], r[0]), f"{w.name}: Top-K of query {b} differs"
+        ref[b] = r[0]
+    # Full layer + Reuse layers: same indices, same KV, own q and window
+    _check_decode_group(csa2, w, t, torch.from_numpy(idx).cuda(), ref, w.layers, range(w.B))
+
+
+def test_hierarchical_pool_reindex_group(csa2):
+    w = workload(3, small=True)
+    _say(f"[{w.name}] ctx={w.ctx}")
+    t = build_device(w)
+    idx, pool = C.gpu_index_full(w, t, pool_blocks=w.pool_blocks)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    ref_re = {}
+    for b in range(w.B):
+        r, p = C.oracle_index_query(w, b, pool_blocks=w.pool_blocks)
+        assert np.array_equal(idx[b], r[0]), f"Top-K of query {b}"
+        assert np.array_equal(pool[b], p[0]), f"pool of query {b}"
+        ref_re[b] = C.oracle_reindex_query(w, b, p[0])[0]
+    re = C.gpu_reindex(w, t, torch.from_numpy(pool).cuda()).cpu().numpy()
+    for b in range(w.B):
+        assert np.array_equal(re[b], ref_re[b]), f"reindex of query {b}"
+    _check_decode_group(csa2, w, t, torch.from_numpy(re).cuda(), ref_re, w.layers, range(w.B))
+
+
+def test_mixed_length_reindex_group(csa2):
+    w = workload(4, small=True)
+    _say(f"[{w.name}] ctx={w.ctx}")
+    t = build_device(w, with_kI=True)
+    re = C.gpu_reindex(w, t, t["pool"]).cpu().numpy()
+    ref = {}
+    for b in range(w.B):
+        ref[b] = C.oracle_reindex_query(w, b, w.pool[b])[0]
+        assert np.array_equal(re[b], ref[b]), f"reindex of query {b} (ctx {w.ctx[b]})"
+    _check_decode_group(csa2, w, t, torch.from_numpy(re).cuda(), ref, w.layers, range(w.B))
+
+
+def test_prefill_chunk(csa2):
+    w = workload(2, small=True)
+    _say(f"[{w.name}] Qn={w.Qn} p0={w.p0}")
+    t = build_device(w)
+    idx, _ = C.gpu_index_full(w, t)
+    idx = idx.cpu().numpy()
+    kI = host_kI_rows(w, 0, w.ctx[0])
+    qI = host_qI(w, T_QI_FULL)
+    ref, _ = oracle.index_full(qI, kI, [0], np.zeros(w.Qn, np.int32), w.q_nvis(), w.Hi, w.Hk, w.Di,
+                               w.topk)
+    assert np.array_equal(idx, ref)
+    idx_d = torch.from_numpy(idx).cuda()
+    rows = list(range(w.Qn))
+    for layer in range(w.layers):
+        out, lse = C.gpu_attn(w, t, layer, idx_d)
+        ro, rl = C.oracle_prefill_rows(w, layer, ref, rows)
+        C.assert_attn_close(out.cpu().numpy(), ro, f"prefill layer {layer}")
+        C.assert_lse_close(lse.cpu().numpy(), rl, f"prefill layer {layer}")
+
+
+# ------------------------------------------------------------- edge cases
+
+def _edge(ctx, **kw):
+    w = Workload("edge", 9, "decode_full", list(ctx), **kw)
+    return w
+
+
+@pytest.mark.parametrize("ctx,topk", [([10, 64, 65, 3000, 0, 1], 64),
+                                      ([1, 2, 7, 5000], 512),
+                                      ([2049, 2047, 4097], 2048)])
+def test_index_ragged_and_short(csa2, ctx, topk):
+    w = _edge(ctx, topk=topk)
+    t = build_device(w, layers=0, with_kv=False)
+    idx, _ = C.gpu_index_full(w, t)
+    idx = idx.cpu().numpy()
+    for b in range(w.B):
+        if w.ctx[b] == 0:
+            assert np.all(idx[b] == -1)
+            continue
+        r, _ = C.oracle_index_query(w, b)
+        assert np.array_equal(idx[b], r[0]), f"query {b} ctx {w.ctx[b]}"
+
+
+def test_index_all_ties_takes_lowest_indices(csa2):
+    # qI = 0: every score is 0; more candidates than one workgroup holds, so
+    # the whole-row exact select runs
+    w = _edge([20000, 70000], topk=512)
+    t = build_device(w, layers=0, with_kv=False)
+    zero = torch.zeros_like(t["qI_full"])
+    idx, pool = C.gpu_index_full(w, t, qI=zero, pool_blocks=2048)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for b in range(2):
+        assert np.array_equal(idx[b], np.arange(512))
+        assert np.array_equal(pool[b], np.arange(2048))
+
+
+def test_index_heavy_ties_narrow_values(csa2):
+    # indexer values in [-1, 1]: scores take few distinct values
+    w = _edge([30000, 12345], topk=512)
+    t = build_device(w, layers=0, with_kv=False)
+    n = sum(w.ctx) * w.row_width
+    kI = torch.from_numpy(host_ints(77, 1, 0, n, -1, 1).reshape(-1, w.Hk, w.Di)).cuda()
+    qI = torch.from_numpy(host_ints(77, 2, 0, w.B * w.Hi * w.Di, -1, 1).reshape(w.B, w.Hi, w.Di)).cuda()
+    t["kI"] = kI
+    idx, pool = C.gpu_index_full(w, t, qI=qI, pool_blocks=2048)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    kh, qh = kI.cpu().numpy(), qI.cpu().numpy()
+    for b in range(w.B):
+        off = int(w.seq_row_off[b])
+        r, p = oracle.index_full(qh[b:b + 1], kh[off:off + w.ctx[b]], [0], [0], [w.ctx[b]], w.Hi,
+                                 w.Hk, w.Di, 512, 2048, 8)
+        assert np.array_equal(idx[b], r[0]) and np.array_equal(pool[b], p[0])
+
+
+@pytest.mark.parametrize("bs", [1, 2, 4])
+def test_pool_block_sizes(csa2, bs):
+    w = _edge([9000, 3001], topk=64, pool_blocks=300, block_size=bs)
+    t = build_device(w, layers=0, with_kv=False)
+    idx, pool = C.gpu_index_full(w, t, pool_blocks=300)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for b in range(w.B):
+        r, p = C.oracle_index_query(w, b, pool_blocks=300)
+        assert np.array_equal(idx[b], r[0]) and np.array_equal(pool[b], p[0])
+    re = C.gpu_reindex(w, t, torch.from_numpy(pool).cuda(), qI=t["qI_full"], topk=64).cpu().numpy()
+    for b in range(w.B):
+        r = C.oracle_reindex_query(w, b, pool[b], tensor=T_QI_FULL, topk=64)
+        assert np.array_equal(re[b], r[0])
+
+
+def test_shared_key_head_and_narrow_rows(csa2):
+    # Hk = 1 with Di = 256 (one key row shared by the 4 indexer heads), and
+    # Hi x Di = 4 x 64 rows of 1 KB
+    for kw in (dict(Hi=4, Hk=1, Di=256), dict(Hi=4, Hk=4, Di=64)):
+        w = _edge([5000, 777], topk=128, **kw)
+        t = build_device(w, layers=0, with_kv=False)
+        idx, _ = C.gpu_index_full(w, t)
+        idx = idx.cpu().numpy()
+        for b in range(w.B):
+            r, _ = C.oracle_index_query(w, b)
+            assert np.array_equal(idx[b], r[0]), f"{kw} query {b}"
+
+
+def test_index_is_deterministic(csa2):
+    w = workload(3, small=True)
+    t = build_device(w, layers=0, with_kv=False)
+    a = [x.cpu() for x in C.gpu_index_full(w, t, pool_blocks=2048)]
+    b = [x.cpu() for x in C.gpu_index_full(w, t, pool_blocks=2048)]
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("H", [16, 32, 48, 64])
+def test_attention_heads_padding_and_short_windows(csa2, H):
+    w = _edge([300, 50, 1000], H=H, topk=96, W=128)
+    t = build_device(w, layers=1, with_kI=False)
+    rng = np.random.default_rng(H)
+    idx = np.full((w.B, w.topk), -1, np.int32)
+    idx[0, :90] = np.sort(rng.choice(300, 90, replace=False))      # ragged tail of -1
+    idx[1, :40] = np.arange(40)                                     # short sequence
+    idx[2] = np.sort(rng.choice(1000, 96, replace=False))
+    sl = torch.tensor([128, 50, 7], dtype=torch.int32, device="cuda")
+    out, lse = C.gpu_attn(w, t, 0, torch.from_numpy(idx).cuda(), swa_len=sl)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b, s in zip(range(3), [128, 50, 7]):
+        ro, rl = C.oracle_attn_query(w, b, 0, idx[b], swa_len=s)
+        C.assert_attn_close(out[b], ro[0], f"H={H} query {b}")
+        C.assert_lse_close(lse[b], rl[0], f"H={H} query {b}")
+
+
+def test_attention_window_only_main_only_and_empty(csa2):
+    w = _edge([400, 400], H=64, topk=32, W=128)
+    t = build_device(w, layers=1, with_kI=False)
+    none = torch.full((2, 32), -1, dtype=torch.int32, device="cuda")
+    some = torch.from_numpy(np.tile(np.arange(0, 320, 10, dtype=np.int32), (2, 1))).cuda()
+    cases = [(none, [128, 0], "window only / nothing"), (some, [0, 0], "main only")]
+    for idx, sl, what in cases:
+        out, lse = C.gpu_attn(w, t, 0, idx, swa_len=torch.tensor(sl, dtype=torch.int32, device="cuda"))
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        for b in range(2):
+            ro, rl = C.oracle_attn_query(w, b, 0, idx[b].cpu().numpy(), swa_len=sl[b])
+            C.assert_attn_close(out[b], ro[0], what)
+            C.assert_lse_close(lse[b], rl[0], what)
+    # no key at all: zeros and -inf
+    out, lse = C.gpu_attn(w, t, 0, none, swa_len=torch.zeros(2, dtype=torch.int32, device="cuda"))
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_attention_is_deterministic(csa2):
+    w = workload(1, small=True)
+    t = build_device(w, layers=1, with_kI=False)
+    rng = np.random.default_rng(5)
+    idx = torch.from_numpy(np.stack([np.sort(rng.choice(w.ctx[0], 512, replace=False))
+                                     for _ in range(w.B)]).astype(np.int32)).cuda()
+    a = C.gpu_attn(w, t, 0, idx)
+    b = C.gpu_attn(w, t, 0, idx)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_prefill_window_before_position_zero(csa2):
+    w = Workload("edge_prefill", 9, "prefill", [40], H=16, topk=8, W=128, layers=1, p0=3, Qn=20,
+                 m=2)
+    t = build_device(w)
+    idx, _ = C.gpu_index_full(w, t)
+    idx_h = idx.cpu().numpy()
+    kI = host_kI_rows(w, 0, w.ctx[0])
+    ref, _ = oracle.index_full(host_qI(w, T_QI_FULL), kI, [0], np.zeros(w.Qn, np.int32),
+                               w.q_nvis(), w.Hi, w.Hk, w.Di, w.topk)
+    assert np.array_equal(idx_h, ref)
+    out, lse = C.gpu_attn(w, t, 0, idx)
+    ro, rl = C.oracle_prefill_rows(w, 0, ref, list(range(w.Qn)))
+    C.assert_attn_close(out.cpu().numpy(), ro, "prefill near position 0")
+    C.assert_lse_close(lse.cpu().numpy(), rl, "prefill near position 0")
