@@ -26,6 +26,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per score-stream launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration),
+    or None if the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "score_stream_c1_traffic.md")
+    try:
+        for line in open(path):
+            if line.startswith("traffic_record:"):
+                rec = json.loads(line.split(":", 1)[1])
+                src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+                if hashlib.sha256(src).hexdigest()[:16] == rec["source_sha256_16"]:
+                    return rec["traffic_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
 def make_step(csa2, w, t, torch):
     Q = w.B
     max_nvis = int(max(w.ctx))
@@ -81,6 +99,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (reference "
+                         "kernel of known traffic for the hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path is single-GPU "
@@ -88,6 +109,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4,
+                          "calibrate_copy_bytes_written": dst.numel() * 4, "launches": 3}))
+        return
     import compressed_fp4_kv_amd as csa2
     from gen.workloads import build_device, workload
 
@@ -151,7 +181,8 @@ def main():
         "kernels": kern,
         "roofline": {"bound": "hbm", "kernel": "score_stream", "achieved": ach,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (ach / HBM_PEAK_GBS) if ach else None, "traffic": None},
+                     "frac": (ach / HBM_PEAK_GBS) if ach else None,
+                     "traffic": measured_traffic()},
     }
     del t
     torch.cuda.empty_cache()

@@ -11,7 +11,7 @@
 // query, the two contractions (S = Q K^T over channels, O = P V over keys)
 // are dense, so they run on the fp32 matrix cores
 // (V_MFMA_F32_16X16X4_F32: exact fp32 products, fp32 accumulation).
-//   - a workgroup owns one query (token), 16*NW heads (16 per wave) and a
+//   - a workgroup owns one query (token), up to 64 heads (16 per wave) and a
 //     range of 16-key tiles; splits of the key range across workgroups are
 //     merged by k_attn_combine (log-sum-exp weights).
 //   - per tile the workgroup dequantises 16 keys x 512 channels into LDS
@@ -62,62 +62,89 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Dequantises tile `t` (16 keys) of query `qi` into sK (row-major) and sVt
-// (transposed); sValid[k] = 1 for a real key, 0 for padding.
-template <int NT>
-__device__ __forceinline__ void load_tile(const AttnArgs& a, int qi, int64_t row0, int wlo,
-                                          int whi, int t, float* sK, float* sVt,
-                                          int* sValid) {
+// Raw bytes of one tile for one thread: ITEMS items of 4 keys x 8 channels.
+// Main keys: k.x = 4 code bytes (8 channels), k.y = scale byte.  Window
+// keys: k = 8 K bytes, v = 8 V bytes.
+template <int ITEMS>
+struct TileRaw {
+    uint2 k[ITEMS][4];
+    uint2 v[ITEMS][4];
+    uint32_t ok[ITEMS];   // bit j: key 4*kq + j is real
+};
+
+// Global loads of tile t (issued early; consumed by store_tile).
+template <int NT, int ITEMS>
+__device__ __forceinline__ void fetch_tile(const AttnArgs& a, const int32_t* s_idx, int t0,
+                                           int64_t row0, int wlo, int whi, int t,
+                                           TileRaw<ITEMS>& r) {
     const bool main = t < a.ntiles_main;
-    for (int item = threadIdx.x; item < 256; item += NT) {
-        const int c8 = item >> 2, kq = item & 3;   // channels 8*c8.., keys 4*kq..
-        float v[4][8], kk[4][8];
-        bool ok[4];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int item = threadIdx.x + it * NT;
+        const int c8 = item >> 2, kq = item & 3;
+        r.ok[it] = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = 4 * kq + j;
+            r.k[it][j] = make_uint2(0, 0);
+            r.v[it][j] = make_uint2(0, 0);
             if (main) {
-                const int slot = kTK * t + key;
-                int32_t idx = slot < a.topk ? a.topk_idx[(size_t)qi * a.topk + slot] : -1;
-                ok[j] = idx >= 0;
-                if (ok[j]) {
+                const int32_t idx = s_idx[kTK * (t - t0) + key];
+                if (idx >= 0) {
                     const int64_t row = row0 + idx;
-                    const uint32_t w = *reinterpret_cast<const uint32_t*>(
-                        a.kv_codes + row * (kD / 2) + 4 * c8);
-                    const float sc = e4m3_to_f32(a.kv_scales[row * (kD / 16) + (c8 >> 1)]);
-                    float2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
-                    float2 p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
-                    v[j][0] = p0.x * sc; v[j][1] = p0.y * sc; v[j][2] = p1.x * sc; v[j][3] = p1.y * sc;
-                    v[j][4] = p2.x * sc; v[j][5] = p2.y * sc; v[j][6] = p3.x * sc; v[j][7] = p3.y * sc;
-                } else {
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) v[j][x] = 0.f;
+                    r.k[it][j].x = *reinterpret_cast<const uint32_t*>(a.kv_codes + row * (kD / 2) + 4 * c8);
+                    r.k[it][j].y = a.kv_scales[row * (kD / 16) + (c8 >> 1)];
+                    r.ok[it] |= 1u << j;
                 }
-#pragma unroll
-                for (int x = 0; x < 8; ++x) kk[j][x] = v[j][x];
             } else {
                 const int w_ = kTK * (t - a.ntiles_main) + key;
-                ok[j] = w_ >= wlo && w_ < whi;
-                if (ok[j]) {
+                if (w_ >= wlo && w_ < whi) {
                     const size_t off = (size_t)w_ * kD + 8 * c8;
-                    const uint2 kb = *reinterpret_cast<const uint2*>(a.swa_k + off);
-                    const uint2 vb = *reinterpret_cast<const uint2*>(a.swa_v + off);
-                    float2 k0 = fp8x2_to_f32<false>(kb.x), k1 = fp8x2_to_f32<true>(kb.x);
-                    float2 k2 = fp8x2_to_f32<false>(kb.y), k3 = fp8x2_to_f32<true>(kb.y);
-                    float2 v0 = fp8x2_to_f32<false>(vb.x), v1 = fp8x2_to_f32<true>(vb.x);
-                    float2 v2 = fp8x2_to_f32<false>(vb.y), v3 = fp8x2_to_f32<true>(vb.y);
-                    kk[j][0] = k0.x; kk[j][1] = k0.y; kk[j][2] = k1.x; kk[j][3] = k1.y;
-                    kk[j][4] = k2.x; kk[j][5] = k2.y; kk[j][6] = k3.x; kk[j][7] = k3.y;
-                    v[j][0] = v0.x; v[j][1] = v0.y; v[j][2] = v1.x; v[j][3] = v1.y;
-                    v[j][4] = v2.x; v[j][5] = v2.y; v[j][6] = v3.x; v[j][7] = v3.y;
-                } else {
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) { v[j][x] = 0.f; kk[j][x] = 0.f; }
+                    r.k[it][j] = *reinterpret_cast<const uint2*>(a.swa_k + off);
+                    r.v[it][j] = *reinterpret_cast<const uint2*>(a.swa_v + off);
+                    r.ok[it] |= 1u << j;
                 }
             }
+        }
+    }
+}
+
+// Dequantises the fetched tile into sK (row-major K) and sVt (transposed V);
+// sValid[k] = 1 for a real key, 0 for padding.
+template <int NT, int ITEMS>
+__device__ __forceinline__ void store_tile(bool main, const TileRaw<ITEMS>& r, float* sK,
+                                           float* sVt, int* sValid) {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int item = threadIdx.x + it * NT;
+        const int c8 = item >> 2, kq = item & 3;
+        float v[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float kk[8];
+            if (main) {
+                const uint32_t w = r.k[it][j].x;
+                const float sc = e4m3_to_f32(r.k[it][j].y);
+                const float2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
+                const float2 p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
+                v[j][0] = p0.x * sc; v[j][1] = p0.y * sc; v[j][2] = p1.x * sc; v[j][3] = p1.y * sc;
+                v[j][4] = p2.x * sc; v[j][5] = p2.y * sc; v[j][6] = p3.x * sc; v[j][7] = p3.y * sc;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) kk[x] = v[j][x];
+            } else {
+                const uint2 kb = r.k[it][j], vb = r.v[it][j];
+                const float2 k0 = fp8x2_to_f32<false>(kb.x), k1 = fp8x2_to_f32<true>(kb.x);
+                const float2 k2 = fp8x2_to_f32<false>(kb.y), k3 = fp8x2_to_f32<true>(kb.y);
+                const float2 v0 = fp8x2_to_f32<false>(vb.x), v1 = fp8x2_to_f32<true>(vb.x);
+                const float2 v2 = fp8x2_to_f32<false>(vb.y), v3 = fp8x2_to_f32<true>(vb.y);
+                kk[0] = k0.x; kk[1] = k0.y; kk[2] = k1.x; kk[3] = k1.y;
+                kk[4] = k2.x; kk[5] = k2.y; kk[6] = k3.x; kk[7] = k3.y;
+                v[j][0] = v0.x; v[j][1] = v0.y; v[j][2] = v1.x; v[j][3] = v1.y;
+                v[j][4] = v2.x; v[j][5] = v2.y; v[j][6] = v3.x; v[j][7] = v3.y;
+            }
             float4* dk = reinterpret_cast<float4*>(sK + (4 * kq + j) * kKStr + 8 * c8);
-            dk[0] = make_float4(kk[j][0], kk[j][1], kk[j][2], kk[j][3]);
-            dk[1] = make_float4(kk[j][4], kk[j][5], kk[j][6], kk[j][7]);
+            dk[0] = make_float4(kk[0], kk[1], kk[2], kk[3]);
+            dk[1] = make_float4(kk[4], kk[5], kk[6], kk[7]);
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x)
@@ -125,23 +152,33 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int qi, int64_t row
                 make_float4(v[0][x], v[1][x], v[2][x], v[3][x]);
         if (c8 == 0) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sValid[4 * kq + j] = ok[j] ? 1 : 0;
+            for (int j = 0; j < 4; ++j) sValid[4 * kq + j] = (r.ok[it] >> j) & 1u;
         }
     }
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a) {
-    constexpr int NT = NW * 64;
+// Rescale threshold (log2 units): the running maximum used for the
+// exponentials is only moved when a new logit exceeds it by more than this,
+// so p <= 2^8 and most tiles skip the rescale of the accumulators.
+constexpr float kRescale = 8.f;
+
+// One workgroup = 4 waves = up to 64 heads of one query; with fewer heads
+// (H not a multiple of 64) the surplus waves only help load the tiles.
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+    constexpr int NT = 256;
+    constexpr int ITEMS = 1;
     __shared__ __attribute__((aligned(16))) float sK[kTK * kKStr];
     __shared__ __attribute__((aligned(16))) float sVt[kD * kVStr];
     __shared__ int sValid[kTK];
+    __shared__ int32_t s_idx[CSA2_MAX_TOPK];
 
     const int split = blockIdx.x;
     const int qi = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, hl = lane & 15;
-    const int h = (blockIdx.y * NW + wave) * 16 + hl;
+    const int h0 = (blockIdx.y * 4 + wave) * 16;
+    const bool active = h0 < a.H;          // wave-uniform
+    const int h = active ? h0 + hl : hl;   // idle waves read head hl, write nothing
 
     int64_t row0 = 0;
     int wlo = 0, whi = 0;
@@ -161,6 +198,16 @@ __global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a) {
         aa.swa_k = a.swa_k + (size_t)qi * a.W * kD;
         aa.swa_v = a.swa_v + (size_t)qi * a.W * kD;
     }
+    const int t0 = split * a.tiles_per_split;
+    const int t1 = min(a.ntiles, t0 + a.tiles_per_split);
+    // this split's main-KV indices, staged once
+    {
+        const int nslot = kTK * (min(t1, a.ntiles_main) - t0);
+        for (int i = threadIdx.x; i < nslot; i += NT) {
+            const int slot = kTK * t0 + i;
+            s_idx[i] = slot < a.topk ? a.topk_idx[(size_t)qi * a.topk + slot] : -1;
+        }
+    }
 
     // query slice: qreg[4u + i] = q[h][16u + 4g + i]
     float qreg[128];
@@ -177,12 +224,17 @@ __global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a) {
     for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
-    const int t0 = split * a.tiles_per_split;
-    const int t1 = min(a.ntiles, t0 + a.tiles_per_split);
+    __syncthreads();
+    TileRaw<ITEMS> raw;
+    if (t0 < t1) fetch_tile<NT, ITEMS>(aa, s_idx, t0, row0, wlo, whi, t0, raw);
     for (int t = t0; t < t1; ++t) {
+        __syncthreads();   // previous tile's LDS reads are done
+        store_tile<NT, ITEMS>(t < a.ntiles_main, raw, sK, sVt, sValid);
         __syncthreads();
-        load_tile<NT>(aa, qi, row0, wlo, whi, t, sK, sVt, sValid);
-        __syncthreads();
+        // next tile's global loads overlap this tile's matrix work
+        if (t + 1 < t1) fetch_tile<NT, ITEMS>(aa, s_idx, t0, row0, wlo, whi, t + 1, raw);
+
+        if (!active) continue;
         // S^T[key 4g+i][head hl] over all channels.  Eight independent
         // accumulation chains (channel block u mod 8) summed as a tree keep
         // the fp32 rounding error of the 512-term dot well below the error
@@ -212,21 +264,27 @@ __global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a) {
         }
         tm = fmaxf(tm, __shfl_xor(tm, 16));
         tm = fmaxf(tm, __shfl_xor(tm, 32));
-        const float mn = fmaxf(m, tm);
-        const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
+        const bool bump = tm > m + kRescale;   // true for any finite tm while m = -inf
+        if (__ballot(bump)) {
+            const float mn = bump ? tm : m;
+            const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < 32; ++cb) o[cb] = o[cb] * alpha;
+            m = mn;
+        }
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - mn);
+            p[i] = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m);
             ps += p[i];
         }
-        l = l * alpha + ps;
-        m = mn;
+        l += ps;
         // O^T[channel 16cb + 4g + r][head hl] += sum_keys V^T P^T
         const float* vr = sVt + hl * kVStr + 4 * g;
 #pragma unroll
         for (int cb = 0; cb < 32; ++cb) {
-            f32x4 acc = o[cb] * alpha;
+            f32x4 acc = o[cb];
             const float4 vv = *reinterpret_cast<const float4*>(vr + 16 * cb * kVStr);
             acc = mfma4(vv.x, p[0], acc);
             acc = mfma4(vv.y, p[1], acc);
@@ -235,6 +293,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a) {
             o[cb] = acc;
         }
     }
+    if (!active) return;
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     const size_t orow = ((size_t)qi * a.H + h) * kD;
@@ -306,7 +365,7 @@ __global__ void k_decode_tables(float* fp4_hw, float* fp4_ref, float* fp8_hw, fl
 }
 
 struct AttnPlan {
-    int nw, hgroups, ntiles_main, ntiles, nsplit, tps;
+    int hgroups, ntiles_main, ntiles, nsplit, tps;
     size_t ws_bytes;
 };
 
@@ -314,14 +373,13 @@ int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnP
     if (rows_q < 0 || H <= 0 || D <= 0 || topk < 0 || W < 0) return CSA2_ERR_SHAPE;
     if (D != kD || H % 16 != 0 || topk > CSA2_MAX_TOPK || W > 1024 || rows_q > 65535)
         return CSA2_ERR_UNSUPPORTED;
-    p->nw = (H % 64 == 0) ? 4 : (H % 32 == 0) ? 2 : 1;
-    p->hgroups = H / (16 * p->nw);
+    p->hgroups = (H + 63) / 64;
     p->ntiles_main = (topk + kTK - 1) / kTK;
     p->ntiles = p->ntiles_main + (W + kTK - 1) / kTK;
     int nsplit = 1;
     if (allow_split && p->ntiles > 1) {
         const long wgs = (long)rows_q * p->hgroups;
-        const long target = 512;
+        const long target = 256;
         if (wgs < target) nsplit = (int)((target + wgs - 1) / wgs);
         if (nsplit > p->ntiles) nsplit = p->ntiles;
     }
@@ -348,10 +406,7 @@ int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_q, void* ws, hipStream_
         a.part_ml = c.take<float>((size_t)pl.nsplit * rows_q * a.H * 2);
     }
     dim3 grid(pl.nsplit, pl.hgroups, rows_q);
-    int st;
-    if (pl.nw == 4) st = CSA2_LAUNCH("attn", k_attn<4>, grid, dim3(256), s, a);
-    else if (pl.nw == 2) st = CSA2_LAUNCH("attn", k_attn<2>, grid, dim3(128), s, a);
-    else st = CSA2_LAUNCH("attn", k_attn<1>, grid, dim3(64), s, a);
+    int st = CSA2_LAUNCH("attn", k_attn, grid, dim3(256), s, a);
     if (st || pl.nsplit == 1) return st;
     return CSA2_LAUNCH("attn_combine", k_attn_combine, dim3(rows_q * a.H), dim3(128), s,
                        a.part_o, a.part_ml, pl.nsplit, rows_q, a.H, a.out, a.lse);

@@ -17,12 +17,15 @@
 //      workgroup) and, for the pool, the block maximum and its histogram.
 //   2. k_filter: the histogram gives the bin holding the K-th key; entries
 //      above it are certain winners, entries in it are candidates (their
-//      composite key score|~index goes to a short list).
+//      composite key score|~index goes to a short list); one atomic per
+//      workgroup and list.
 //   3. k_finalize: one workgroup per query selects the remaining winners
-//      among the candidates with a register-resident 64-bit radix select,
-//      sorts the K winners by index and writes them.  If the candidate bin
-//      holds more than 16,384 entries (degenerate score distributions) it
-//      falls back to an exact select over the whole key row.
+//      among the candidates (direct ranking, or a register-resident 64-bit
+//      radix select) and writes the K winners in index order.  If the
+//      candidate bin holds more than 16,384 entries (degenerate score
+//      distributions) it falls back to an exact select over the whole row.
+//   (Kernel boundaries order the phases: a grid-wide "last workgroup" hand-
+//   off would need agent-scope fences, which write back L2 on this part.)
 //   Reindex: k_reindex_score gathers the pool rows (8 contiguous 2 KB rows
 //   per block) with the same 8-row dot, k_reindex_select selects among the
 //   <= 16,384 composite keys of a query in one workgroup.
@@ -39,10 +42,12 @@ constexpr int kDigitShift = 20;
 constexpr int kCandCap = 16384;      // candidates a selecting workgroup holds
 constexpr int kSelThreads = 1024;
 constexpr int kSelItems = kCandCap / kSelThreads;
-constexpr int kStreamThreads = 256;
-constexpr int kRowsPerWG = 1024;     // score stream: rows per workgroup
-constexpr int kFilterElems = 16384;  // filter: keys per workgroup
+constexpr int kStreamThreads = 512;
+constexpr int kRowsPerWG = 2048;     // score stream: rows per workgroup
+constexpr int kSelElems = 4096;     // filter: keys per workgroup (16 per thread)
+constexpr int kRankMax = 2048;      // candidates selected by direct ranking
 constexpr int kReindexPerWG = 1024;  // reindex: candidates per workgroup
+constexpr int kReindexThreads = 256;
 
 // ------------------------------------------------------------ row dots
 
@@ -70,31 +75,21 @@ __device__ __forceinline__ void load_qvec(const float* __restrict__ qI, int q, i
     }
 }
 
-// Dot products of the query with 8 key rows.  Returns, in every lane, the
-// full sum for row (lane >> 3) & 7.  Invalid rows (ok[i] false) read nothing.
-template <int VPR>
-__device__ __forceinline__ float dot8(const float* const (&rows)[8], const bool (&ok)[8],
-                                      const float4 (&qv)[VPR]) {
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Streaming load of one float4 of a key row: each key byte is read once, so
+// the load is marked nontemporal (no reuse expected in the caches).
+__device__ __forceinline__ float4 load_stream(const float* p) {
+    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Sums 8 per-lane partials across the wave (transpose-reduction): returns in
+// every lane the full sum of partial (lane >> 3) & 7.  After the xor-32/16/8
+// steps lane l holds a partial of row (l>>3)&7 summed over 8 lanes; xor-4/2/1
+// completes it.
+__device__ __forceinline__ float reduce8(float (&a)[8]) {
     const int lane = lane_id();
-    float4 k[8][VPR];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < VPR; ++j)
-            k[i][j] = ok[i] ? reinterpret_cast<const float4*>(rows[i])[lane + 64 * j]
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-    float a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < VPR; ++j)
-            s += qv[j].x * k[i][j].x + qv[j].y * k[i][j].y + qv[j].z * k[i][j].z +
-                 qv[j].w * k[i][j].w;
-        a[i] = s;
-    }
-    // transpose-reduction: after the xor-32/16/8 steps lane l holds a partial
-    // of row (l>>3)&7 summed over 8 lanes; xor-4/2/1 completes the sum.
     const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -119,6 +114,37 @@ __device__ __forceinline__ float dot8(const float* const (&rows)[8], const bool 
     return a[0];
 }
 
+// Dot products of the query with ROWS key rows (all loads issued first).
+// Returns in out[h] the full sum of row 8h + ((lane >> 3) & 7).  Invalid
+// rows (ok[i] false) read nothing.
+template <int VPR, int ROWS>
+__device__ __forceinline__ void dot_rows(const float* const (&rows)[ROWS], const bool (&ok)[ROWS],
+                                         const float4 (&qv)[VPR], float (&out)[ROWS / 8]) {
+    const int lane = lane_id();
+    float4 k[ROWS][VPR];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+        for (int j = 0; j < VPR; ++j)
+            k[i][j] = ok[i] ? load_stream(rows[i] + 4 * (lane + 64 * j))
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int h = 0; h < ROWS / 8; ++h) {
+        float a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < VPR; ++j) {
+                const float4 x = k[8 * h + i][j];
+                s += qv[j].x * x.x + qv[j].y * x.y + qv[j].z * x.z + qv[j].w * x.w;
+            }
+            a[i] = s;
+        }
+        out[h] = reduce8(a);
+    }
+}
+
 // ------------------------------------------------------- score stream
 
 template <int VPR>
@@ -131,6 +157,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     __shared__ uint32_t s_he[kHistBins];
     __shared__ uint32_t s_hb[kHistBins];
     constexpr int RW = 256 * VPR;
+    constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (64 KB in flight per 4 waves)
     const int q = blockIdx.y;
     const int nvis = q_nvis[q];
     const int r0 = blockIdx.x * kRowsPerWG;
@@ -149,30 +176,34 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     const uint32_t bmask = (1u << bs_log2) - 1u;
     uint32_t* krow = keys + (size_t)q * kstride;
 
-    for (int g0 = r0 + 8 * wave; g0 < r1; g0 += 8 * (kStreamThreads / kWave)) {
-        const float* rows[8];
-        bool ok[8];
+    for (int g0 = r0 + kStreamRows * wave; g0 < r1; g0 += kStreamRows * (kStreamThreads / kWave)) {
+        const float* rows[kStreamRows];
+        bool ok[kStreamRows];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kStreamRows; ++i) {
             ok[i] = g0 + i < r1;
             rows[i] = kb + (int64_t)(g0 + i) * RW;
         }
-        const float s = dot8<VPR>(rows, ok, qv);
-        const int row = g0 + myrow;
-        const bool valid = row < r1;
-        const uint32_t k = ord_key(s);
-        if ((lane & 7) == 0 && valid) {
-            krow[row] = k;
-            atomicAdd(&s_he[k >> kDigitShift], 1u);
-        }
-        if (pool) {
-            uint32_t bk = valid ? k : 0u;
-            if (bs_log2 >= 1) bk = max(bk, (uint32_t)__shfl_xor(bk, 8));
-            if (bs_log2 >= 2) bk = max(bk, (uint32_t)__shfl_xor(bk, 16));
-            if (bs_log2 >= 3) bk = max(bk, (uint32_t)__shfl_xor(bk, 32));
-            if ((lane & 7) == 0 && valid && ((uint32_t)myrow & bmask) == 0) {
-                bkeys[(size_t)q * bstride + (row >> bs_log2)] = bk;
-                atomicAdd(&s_hb[bk >> kDigitShift], 1u);
+        float sc[kStreamRows / 8];
+        dot_rows<VPR, kStreamRows>(rows, ok, qv, sc);
+#pragma unroll
+        for (int hh = 0; hh < kStreamRows / 8; ++hh) {
+            const int row = g0 + 8 * hh + myrow;
+            const bool valid = row < r1;
+            const uint32_t k = ord_key(sc[hh]);
+            if ((lane & 7) == 0 && valid) {
+                krow[row] = k;
+                atomicAdd(&s_he[k >> kDigitShift], 1u);
+            }
+            if (pool) {
+                uint32_t bk = valid ? k : 0u;
+                if (bs_log2 >= 1) bk = max(bk, (uint32_t)__shfl_xor(bk, 8));
+                if (bs_log2 >= 2) bk = max(bk, (uint32_t)__shfl_xor(bk, 16));
+                if (bs_log2 >= 3) bk = max(bk, (uint32_t)__shfl_xor(bk, 32));
+                if ((lane & 7) == 0 && valid && ((uint32_t)myrow & bmask) == 0) {
+                    bkeys[(size_t)q * bstride + (row >> bs_log2)] = bk;
+                    atomicAdd(&s_hb[bk >> kDigitShift], 1u);
+                }
             }
         }
     }
@@ -189,48 +220,34 @@ __global__ void k_zero_u32(uint32_t* __restrict__ p, size_t n) {
         p[i] = 0u;
 }
 
-// ------------------------------------------------------------- filter
-
-__global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ keys, int64_t stride,
-                                                const int32_t* __restrict__ q_nvis, int bs_log2,
-                                                int K, const uint32_t* __restrict__ hist,
-                                                uint32_t* __restrict__ cnt,
-                                                int32_t* __restrict__ above,
-                                                uint64_t* __restrict__ cand) {
-    __shared__ uint32_t s_tmp[256 / kWave + 3];
-    const int q = blockIdx.y;
-    const int nvis = q_nvis[q];
-    const int n = (nvis + (1 << bs_log2) - 1) >> bs_log2;
-    const int e0 = blockIdx.x * kFilterElems;
-    if (n <= K || e0 >= n) return;
-    uint32_t b1, nabove;
-    find_digit_4096<256>(hist + (size_t)q * kHistBins, (uint32_t)K, s_tmp, b1, nabove);
-    const int e1 = min(n, e0 + kFilterElems);
-    const uint32_t* row = keys + (size_t)q * stride;
-    for (int base = e0; base < e1; base += 256) {
-        const int e = base + threadIdx.x;
-        const bool ok = e < e1;
-        const uint32_t k = ok ? row[e] : 0u;
-        const uint32_t d = k >> kDigitShift;
-        const bool pa = ok && d > b1, pc = ok && d == b1;
-        const uint32_t sa = wave_append(pa, &cnt[2 * q]);
-        if (pa && sa < (uint32_t)K) above[(size_t)q * K + sa] = e;
-        const uint32_t sc = wave_append(pc, &cnt[2 * q + 1]);
-        if (pc && sc < (uint32_t)kCandCap) cand[(size_t)q * kCandCap + sc] = comp_key(k, (uint32_t)e);
-    }
-}
-
 // ------------------------------------------------------------ selects
 
 // Radix select over NT*IPT register-resident 64-bit keys (0 = empty slot;
 // non-empty keys distinct): returns T such that exactly `k` keys are >= T.
 // 1 <= k <= number of non-empty keys.
+// Digits are taken from bit `top_shift` down; bits above top_shift + 8 must
+// already be equal across all keys.  Stops early once the chosen digit's
+// bucket holds exactly the keys still wanted.
 template <int NT, int IPT>
 __device__ uint64_t block_select_kth(const uint64_t (&it)[IPT], uint32_t k, uint32_t* s_hist,
-                                     uint32_t* s_dig) {
+                                     uint32_t* s_dig, int top_shift) {
     uint64_t prefix = 0, mask = 0;
     uint32_t want = k;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    if (top_shift < 56) {
+        // common high bits: take them from any non-empty key
+        uint64_t any = 0;
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) any = it[j] ? it[j] : any;
+        if (threadIdx.x == 0) s_dig[0] = 0;
+        __syncthreads();
+        if (any) { s_dig[0] = (uint32_t)(any >> 32); }
+        __syncthreads();
+        const uint64_t hi_mask = ~((1ull << (top_shift + 8)) - 1ull);
+        prefix = ((uint64_t)s_dig[0] << 32) & hi_mask;
+        mask = hi_mask;
+        __syncthreads();
+    }
+    for (int shift = top_shift; shift >= 0; shift -= 8) {
         for (int i = threadIdx.x; i < 256; i += NT) s_hist[i] = 0u;
         __syncthreads();
 #pragma unroll
@@ -254,10 +271,12 @@ __device__ uint64_t block_select_kth(const uint64_t (&it)[IPT], uint32_t k, uint
         __syncthreads();
         find_digit_256(s_hist, want, s_dig);
         const uint32_t d = s_dig[0], above = s_dig[1];
+        const uint32_t bucket = s_hist[d];
         __syncthreads();
         prefix |= (uint64_t)d << shift;
         mask |= 0xFFull << shift;
         want -= above;
+        if (bucket == want) break;   // every key of this bucket is selected
     }
     return prefix;
 }
@@ -315,26 +334,95 @@ __device__ void select_global_row(const uint32_t* __restrict__ keys, int n, int 
     for (int i = (int)sel_run + threadIdx.x; i < K; i += NT) out[i] = -1;
 }
 
-__device__ __forceinline__ int next_pow2(int x) {
-    int p = 1;
-    while (p < x) p <<= 1;
-    return p;
-}
-
-// Sorts the `count` indices in s_out ascending and writes K slots (-1 padded).
-__device__ void sort_and_write(int32_t* s_out, int count, int K, int32_t* __restrict__ o) {
-    const int P = next_pow2(K);
-    for (int i = count + threadIdx.x; i < P; i += kSelThreads) s_out[i] = INT_MAX;
+// Writes the `count` distinct indices of s_list (unordered, followed by room
+// for 3 pad slots) to o in ascending order, each at its rank, and pads the K
+// slots with -1.
+__device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __restrict__ o) {
+    if (threadIdx.x < 4) s_list[count + threadIdx.x] = INT_MAX;
     __syncthreads();
-    block_bitonic_sort<kSelThreads>(s_out, P);
-    for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < count ? s_out[i] : -1;
+    const int4* l4 = reinterpret_cast<const int4*>(s_list);
+    for (int i = threadIdx.x; i < count; i += kSelThreads) {
+        const int32_t e = s_list[i];
+        int r = 0;
+        for (int j = 0; j < (count + 3) / 4; ++j) {
+            const int4 v = l4[j];
+            r += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
+        }
+        o[r] = e;
+    }
+    for (int i = count + threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
 }
 
+// Filter of one key row per query (entries or blocks): every workgroup
+// classifies kSelElems keys against the bin b1 that holds the K-th largest
+// key (from the first-level histogram).  Keys above b1 are winners, keys in
+// b1 are candidates (composite key score|~index); both lists grow by one
+// atomic per workgroup.  cnt[2q + 0/1]: winners, candidates (zeroed first).
+__global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ keys, int64_t stride,
+                                                const int32_t* __restrict__ q_nvis, int bs_log2,
+                                                int K, const uint32_t* __restrict__ hist,
+                                                uint32_t* __restrict__ cnt,
+                                                int32_t* __restrict__ above,
+                                                uint64_t* __restrict__ cand) {
+    __shared__ uint32_t s_tmp[256 / kWave + 3];
+    __shared__ uint32_t s_bc[2];
+    const int q = blockIdx.y;
+    const int nvis = q_nvis[q];
+    const int n = (nvis + (1 << bs_log2) - 1) >> bs_log2;
+    const int e0 = blockIdx.x * kSelElems;
+    if (n <= K || e0 >= n) return;
+    // 16 keys per thread (4 coalesced uint4 loads), in flight during the search
+    const uint32_t* row = keys + (size_t)q * stride;
+    uint32_t kk[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 4 * (threadIdx.x + 256 * j);
+        const uint4 v = e < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
+        kk[4 * j] = v.x; kk[4 * j + 1] = v.y; kk[4 * j + 2] = v.z; kk[4 * j + 3] = v.w;
+    }
+    uint32_t b1, nabove;
+    find_digit_4096<256>(hist + (size_t)q * kHistBins, (uint32_t)K, s_tmp, b1, nabove);
+    uint32_t na = 0, nc = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = e0 + 4 * (threadIdx.x + 256 * (i >> 2)) + (i & 3);
+        const uint32_t d = kk[i] >> kDigitShift;
+        na += e < n && d > b1;
+        nc += e < n && d == b1;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_sum<256>((na << 16) | nc, s_tmp, tot);
+    if (threadIdx.x == 0) {
+        s_bc[0] = (tot >> 16) ? atomicAdd(&cnt[2 * q], tot >> 16) : 0u;
+        s_bc[1] = (tot & 0xFFFFu) ? atomicAdd(&cnt[2 * q + 1], tot & 0xFFFFu) : 0u;
+    }
+    __syncthreads();
+    uint32_t pa = s_bc[0] + (ex >> 16), pc = s_bc[1] + (ex & 0xFFFFu);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = e0 + 4 * (threadIdx.x + 256 * (i >> 2)) + (i & 3);
+        const uint32_t d = kk[i] >> kDigitShift;
+        if (e < n && d > b1) {
+            if (pa < (uint32_t)K) above[(size_t)q * K + pa] = e;
+            ++pa;
+        } else if (e < n && d == b1) {
+            if (pc < (uint32_t)kCandCap) cand[(size_t)q * kCandCap + pc] = comp_key(kk[i], (uint32_t)e);
+            ++pc;
+        }
+    }
+}
+
+// Final selection, one workgroup per query: picks the K - #winners best
+// candidates -- by direct ranking when there are at most kRankMax of them,
+// else by a register-resident radix select, else (more than kCandCap:
+// degenerate ties) by an exact select over the whole row -- and writes the K
+// indices in ascending order.
 __global__ __launch_bounds__(kSelThreads) void k_finalize(
     const uint32_t* __restrict__ keys, int64_t stride, const int32_t* __restrict__ q_nvis,
     int bs_log2, int K, const uint32_t* __restrict__ cnt, const int32_t* __restrict__ above,
     const uint64_t* __restrict__ cand, int32_t* __restrict__ out) {
-    __shared__ int32_t s_out[CSA2_MAX_TOPK];
+    __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
+    __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
@@ -343,40 +431,60 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
     const int nvis = q_nvis[q];
     const int n = (nvis + (1 << bs_log2) - 1) >> bs_log2;
     int32_t* o = out + (size_t)q * K;
-    if (n <= K) {
+    if (n <= K) {  // everything is selected
         for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
         return;
     }
-    const uint32_t na = min(cnt[2 * q], (uint32_t)K - 1u), nc = cnt[2 * q + 1];
-    if (nc > (uint32_t)kCandCap) {
+    const uint32_t NA = min(cnt[2 * q], (uint32_t)K - 1u);
+    const uint32_t NC = cnt[2 * q + 1];
+    const uint32_t need = (uint32_t)K - NA;
+    if (NC > (uint32_t)kCandCap) {
         select_global_row<kSelThreads>(keys + (size_t)q * stride, n, K, o, s_hist, s_dig, s_tmp);
         return;
     }
-    uint64_t it[kSelItems];
-#pragma unroll
-    for (int j = 0; j < kSelItems; ++j) {
-        const uint32_t i = threadIdx.x + j * kSelThreads;
-        it[j] = i < nc ? cand[(size_t)q * kCandCap + i] : 0ull;
-    }
-    const uint64_t T = block_select_kth<kSelThreads, kSelItems>(it, (uint32_t)K - na, s_hist, s_dig);
-    if (threadIdx.x == 0) s_count = na;
-    for (int i = threadIdx.x; i < (int)na; i += kSelThreads) s_out[i] = above[(size_t)q * K + i];
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kSelItems; ++j) {
-        if (it[j] != 0 && it[j] >= T) {
-            const uint32_t pos = atomicAdd(&s_count, 1u);
-            if (pos < (uint32_t)K) s_out[pos] = (int32_t)comp_idx(it[j]);
+    for (int i = threadIdx.x; i < (int)NA; i += kSelThreads) s_out[i] = above[(size_t)q * K + i];
+    if (NC <= (uint32_t)kRankMax) {
+        for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) s_cand[i] = cand[(size_t)q * kCandCap + i];
+        if (threadIdx.x == 0) s_cand[NC] = 0ull;  // pad for the paired reads
+        __syncthreads();
+        // candidate i has rank r = #{larger candidates}; the best `need` ranks win
+        const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s_cand);
+        for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) {
+            const uint64_t ci = s_cand[i];
+            uint32_t r = 0;
+            for (int j = 0; j < ((int)NC + 1) / 2; ++j) {
+                const ulonglong2 w = c2[j];
+                r += (w.x > ci) + (w.y > ci);
+            }
+            if (r < need) s_out[NA + r] = (int32_t)comp_idx(ci);
         }
+        __syncthreads();
+    } else {
+        uint64_t it[kSelItems];
+#pragma unroll
+        for (int j = 0; j < kSelItems; ++j) {
+            const uint32_t i = threadIdx.x + j * kSelThreads;
+            it[j] = i < NC ? cand[(size_t)q * kCandCap + i] : 0ull;
+        }
+        const uint64_t T = block_select_kth<kSelThreads, kSelItems>(it, need, s_hist, s_dig, 48);
+        if (threadIdx.x == 0) s_count = NA;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kSelItems; ++j) {
+            if (it[j] != 0 && it[j] >= T) {
+                const uint32_t pos = atomicAdd(&s_count, 1u);
+                if (pos < (uint32_t)K) s_out[pos] = (int32_t)comp_idx(it[j]);
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    sort_and_write(s_out, min((int)s_count, K), K, o);
+    rank_and_write(s_out, K, K, o);
 }
 
 // ------------------------------------------------------------- reindex
 
 template <int VPR>
-__global__ __launch_bounds__(kStreamThreads) void k_reindex_score(
+__global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
     const float* __restrict__ qI, const float* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, const int32_t* __restrict__ pool,
@@ -395,7 +503,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_reindex_score(
     const int32_t* prow = pool + (size_t)q * P;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int myrow = (lane >> 3) & 7;
-    for (int g0 = c0 + 8 * wave; g0 < c1; g0 += 8 * (kStreamThreads / kWave)) {
+    for (int g0 = c0 + 8 * wave; g0 < c1; g0 += 8 * (kReindexThreads / kWave)) {
         const float* rows[8];
         bool ok[8];
 #pragma unroll
@@ -409,7 +517,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_reindex_score(
             ok[i] = t >= 0 && t < nvis;
             rows[i] = kb + (ok[i] ? t : 0) * RW;
         }
-        const float s = dot8<VPR>(rows, ok, qv);
+        float sv[1];
+        dot_rows<VPR, 8>(rows, ok, qv, sv);
+        const float s = sv[0];
         const int c = g0 + myrow;
         if ((lane & 7) == 0 && c < c1) {
             const int b = prow[c / bs];
@@ -422,7 +532,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_reindex_score(
 
 __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
     const uint64_t* __restrict__ ckeys, int ncand, int K, int32_t* __restrict__ out) {
-    __shared__ int32_t s_out[CSA2_MAX_TOPK];
+    __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
@@ -444,7 +554,7 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
         for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
         return;
     }
-    const uint64_t T = block_select_kth<kSelThreads, kSelItems>(it, (uint32_t)k, s_hist, s_dig);
+    const uint64_t T = block_select_kth<kSelThreads, kSelItems>(it, (uint32_t)k, s_hist, s_dig, 56);
     if (threadIdx.x == 0) s_count = 0;
     __syncthreads();
 #pragma unroll
@@ -455,7 +565,7 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
         }
     }
     __syncthreads();
-    sort_and_write(s_out, min((int)s_count, K), K, o);
+    rank_and_write(s_out, min((int)s_count, K), K, o);
 }
 
 // ------------------------------------------------------ host helpers
@@ -561,7 +671,7 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
     }
     if (topk > 0) {
         if (max_nvis > 0) {
-            dim3 g((max_nvis + kFilterElems - 1) / kFilterElems, Q);
+            dim3 g((max_nvis + kSelElems - 1) / kSelElems, Q);
             st = CSA2_LAUNCH("filter", k_filter, g, dim3(256), s, w.keys_e, w.se, q_nvis, 0, topk,
                              w.hist_e, w.cnt_e, w.above_e, w.cand_e);
             if (st) return st;
@@ -573,7 +683,7 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
     if (pool_blocks > 0) {
         const int nb = (max_nvis + block_size - 1) / block_size;
         if (nb > 0) {
-            dim3 g((nb + kFilterElems - 1) / kFilterElems, Q);
+            dim3 g((nb + kSelElems - 1) / kSelElems, Q);
             st = CSA2_LAUNCH("filter", k_filter, g, dim3(256), s, w.keys_b, w.sb, q_nvis, bs_log2,
                              pool_blocks, w.hist_b, w.cnt_b, w.above_b, w.cand_b);
             if (st) return st;
@@ -616,7 +726,7 @@ extern "C" int csa2_reindex(const float* qI, const float* kI, const int64_t* seq
     if (ncand > 0) {
         dim3 g((ncand + kReindexPerWG - 1) / kReindexPerWG, Q);
 #define CSA2_RS(V)                                                                             \
-    CSA2_LAUNCH("reindex_score", k_reindex_score<V>, g, dim3(kStreamThreads), s, qI, kI,       \
+    CSA2_LAUNCH("reindex_score", k_reindex_score<V>, g, dim3(kReindexThreads), s, qI, kI,       \
                 seq_row_off, q_seq, q_nvis, Hi, Hk, Di, pool_block_idx, pool_blocks,           \
                 block_size, ck)
         st = vpr == 1 ? CSA2_RS(1) : vpr == 2 ? CSA2_RS(2) : CSA2_RS(4);
