@@ -21,6 +21,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+WORKLOAD_NAMES = {
+    "c0_tiny_full": "decode Full layer: 1 sequence x 4,096 entries, indexer 4x64, Top-64, 16 heads",
+    "c1_full_reuse3": "decode Full + 3 Reuse layers: 32 sequences x 65,536 entries, indexer 4x128 "
+                      "fp32, Top-512, 64 heads x 512 ch, FP4 main KV, 128-token FP8 window",
+    "c2_prefill_m2": "prefill chunk, m=2: 4,096 queries over 65,536 entries, Full + 5 Reuse layers",
+    "c3_hier_1m": "decode, 8 sequences x 1,048,576 entries: Full indexer + 2,048x8 pool, Reindex "
+                  "+ 3 Reuse layers",
+    "c4_mixed_reindex": "decode, 64 sequences of 8K..1M entries: Reindex over inherited pools + "
+                        "3 Reuse layers",
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -45,25 +56,83 @@ def measured_traffic():
 
 
 def make_step(csa2, w, t, torch):
-    Q = w.B
-    max_nvis = int(max(w.ctx))
-    idx = torch.empty((Q, w.topk), dtype=torch.int32, device="cuda")
-    ws_i = torch.empty(csa2.csa2_index_full_workspace_bytes(Q, max_nvis, w.topk, 0, 8),
-                       dtype=torch.uint8, device="cuda")
-    ws_a = torch.empty(max(256, csa2.csa2_decode_workspace_bytes(Q, w.H, w.D, w.topk, w.W)),
-                       dtype=torch.uint8, device="cuda")
-    outs = [torch.empty((Q, w.H, w.D), dtype=torch.float32, device="cuda") for _ in range(w.layers)]
-    lses = [torch.empty((Q, w.H), dtype=torch.float32, device="cuda") for _ in range(w.layers)]
+    """One pass of the workload's call sequence (all of its layers)."""
+    Q = w.Q
+    max_nvis = int(w.q_nvis().max())
+    dev = "cuda"
+    idx = torch.empty((Q, w.topk), dtype=torch.int32, device=dev)
+    ridx = torch.empty((Q, w.topk), dtype=torch.int32, device=dev)
+    pool = t.get("pool")
+    if w.kind == "decode_hier":
+        pool = torch.empty((Q, w.pool_blocks), dtype=torch.int32, device=dev)
+    P = w.pool_blocks if w.kind == "decode_hier" else 0
+    ws_i = torch.empty(max(256, csa2.csa2_index_full_workspace_bytes(Q, max_nvis, w.topk, P,
+                                                                       w.block_size)),
+                       dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(max(256, csa2.csa2_reindex_workspace_bytes(Q, w.pool_blocks, w.block_size)),
+                       dtype=torch.uint8, device=dev)
+    if w.kind == "prefill":
+        nb = csa2.csa2_prefill_workspace_bytes(Q, w.H, w.D, w.topk, w.W)
+    else:
+        nb = csa2.csa2_decode_workspace_bytes(Q, w.H, w.D, w.topk, w.W)
+    ws_a = torch.empty(max(256, nb), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((Q, w.H, w.D), dtype=torch.float32, device=dev) for _ in range(w.layers)]
+    lses = [torch.empty((Q, w.H), dtype=torch.float32, device=dev) for _ in range(w.layers)]
 
-    def step():
-        csa2.csa2_index_full(t["qI_full"], t["kI"], t["seq_row_off"], t["q_seq"], t["q_nvis"],
-                             max_nvis, w.topk, idx, ws=ws_i)
-        for layer in range(w.layers):   # Full layer, then Reuse layers: same idx and KV
+    def attn(layer, ix):
+        if w.kind == "prefill":
+            csa2.csa2_sparse_attn_prefill_chunk(t["q"][layer], w.p0, t["kv_codes"], t["kv_scales"],
+                                                ix, t["swa_k"][layer], t["swa_v"][layer], w.W,
+                                                w.scale, outs[layer], lses[layer], ws=ws_a)
+        else:
             csa2.csa2_sparse_attn_decode(t["q"][layer], t["kv_codes"], t["kv_scales"],
-                                         t["seq_row_off"], idx, t["swa_k"][layer],
+                                         t["seq_row_off"], ix, t["swa_k"][layer],
                                          t["swa_v"][layer], t["swa_len"], w.scale, outs[layer],
                                          lses[layer], ws=ws_a)
+
+    def step():
+        if w.kind in ("decode_full", "prefill"):
+            # Full layer: indexer, then Full + Reuse layers on the same indices and KV
+            csa2.csa2_index_full(t["qI_full"], t["kI"], t["seq_row_off"],
+                                 None if w.kind == "prefill" else t["q_seq"], t["q_nvis"],
+                                 max_nvis, w.topk, idx, ws=ws_i)
+            for layer in range(w.layers):
+                attn(layer, idx)
+            return
+        if w.kind == "decode_hier":
+            # the Full layer's indexer builds Top-K and the candidate pool
+            csa2.csa2_index_full(t["qI_full"], t["kI"], t["seq_row_off"], t["q_seq"], t["q_nvis"],
+                                 max_nvis, w.topk, idx, P, w.block_size, pool, ws=ws_i)
+        # Reindex layer over the pool, then Reindex + Reuse layers' attention
+        csa2.csa2_reindex(t["qI_reindex"], t["kI"], t["seq_row_off"], t["q_seq"], t["q_nvis"],
+                          pool, w.block_size, w.topk, ridx, ws=ws_r)
+        for layer in range(w.layers):
+            attn(layer, ridx)
     return step, idx
+
+
+def dominant_roofline(w, kern):
+    """Roofline record of the workload's dominant kernel (algorithmic work per
+    launch / measured average launch time)."""
+    if w.kind in ("decode_full", "decode_hier") and "score_stream" in kern:
+        alg = float(w.rows) * w.row_width * 4 + float(w.Q) * w.Hi * w.Di * 4
+        ach = alg / (kern["score_stream"]["avg_us"] * 1e-6) / 1e9
+        return {"bound": "hbm", "kernel": "score_stream", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": measured_traffic() if w.name.startswith("c1") else None}
+    if w.kind == "decode_reindex" and "reindex_score" in kern:
+        import numpy as np
+        rows = sum(min(int(np.sum(w.pool[b] >= 0)) * w.block_size, w.ctx[b]) for b in range(w.B))
+        alg = float(rows) * w.row_width * 4
+        ach = alg / (kern["reindex_score"]["avg_us"] * 1e-6) / 1e9
+        return {"bound": "hbm", "kernel": "reindex_score", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    if "attn" in kern:
+        flops = 4.0 * w.H * (w.topk + w.W) * w.D * w.Q
+        ach = flops / (kern["attn"]["avg_us"] * 1e-6) / 1e12
+        return {"bound": "mfma", "kernel": "attn (fp32 MFMA)", "achieved": ach, "peak": 157.3,
+                "unit": "TFLOP/s", "frac": ach / 157.3, "traffic": None}
+    return None
 
 
 def cpu_baseline(w, max_threads):
@@ -98,6 +167,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", type=int, default=1,
+                    help="workload number (1 = the decode workload the metric is quoted on)")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (reference "
@@ -121,7 +192,7 @@ def main():
     import compressed_fp4_kv_amd as csa2
     from gen.workloads import build_device, workload
 
-    w = workload(1)
+    w = workload(args.workload)
     log(f"building inputs: {w.name} B={w.B} ctx={w.ctx[0]} H={w.H} topk={w.topk}")
     t = build_device(w)
     step, idx = make_step(csa2, w, t, torch)
@@ -152,15 +223,9 @@ def main():
     kern = {k: {"launches": n, "avg_us": 1000.0 * ms / n} for k, (n, ms) in prof.items()}
     log("kernels:", json.dumps(kern))
 
-    key_bytes = float(w.rows) * w.row_width * 4
-    q_bytes = float(w.B) * w.Hi * w.Di * 4
-    alg = key_bytes + q_bytes
-    ss = kern.get("score_stream")
-    ach = alg / (ss["avg_us"] * 1e-6) / 1e9 if ss else None
-
     res = {
         "metric": "CSA2 decode queries/sec and achieved HBM GB/s (% of peak) at 1 MI355X",
-        "value": w.B / (ms_step * 1e-3),
+        "value": w.Q / (ms_step * 1e-3),
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -172,21 +237,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded integer indexer inputs, FP4 E2M1/E4M3 KV, N(0,1) queries, "
                 "FP8 window)",
-        "config": {"workload": "decode Full + 3 Reuse layers: 32 sequences x 65,536 entries, "
-                               "indexer 4x128 fp32, Top-512, 64 heads x 512 ch, FP4 main KV, "
-                               "128-token FP8 window",
-                   "global_batch": w.B, "seq_len": int(w.ctx[0]), "parallelism": "single GPU"},
-        "step_hbm_gbs": (alg + w.layers * w.B * (512 * 288 + 2 * 128 * 512 + 2 * w.H * w.D * 4))
-                        / (ms_step * 1e-3) / 1e9,
+        "config": {"workload": WORKLOAD_NAMES.get(w.name, w.name),
+                   "global_batch": w.Q, "seq_len": int(max(w.ctx)), "parallelism": "single GPU"},
         "kernels": kern,
-        "roofline": {"bound": "hbm", "kernel": "score_stream", "achieved": ach,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (ach / HBM_PEAK_GBS) if ach else None,
-                     "traffic": measured_traffic()},
+        "roofline": dominant_roofline(w, kern),
     }
     del t
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == 1:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_threads)
     print(json.dumps(res), flush=True)

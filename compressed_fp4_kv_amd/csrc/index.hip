@@ -46,7 +46,7 @@ constexpr int kStreamThreads = 512;
 constexpr int kRowsPerWG = 2048;     // score stream: rows per workgroup
 constexpr int kSelElems = 4096;     // filter: keys per workgroup (16 per thread)
 constexpr int kRankMax = 2048;      // candidates selected by direct ranking
-constexpr int kReindexPerWG = 1024;  // reindex: candidates per workgroup
+constexpr int kReindexPerWG = 256;   // reindex: candidates per workgroup
 constexpr int kReindexThreads = 256;
 
 // ------------------------------------------------------------ row dots
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     constexpr int RW = 256 * VPR;
     constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (64 KB in flight per 4 waves)
     const int q = blockIdx.y;
-    const int nvis = q_nvis[q];
+    const int nvis = min(q_nvis[q], (int)kstride);   // q_nvis <= max_nvis <= kstride
     const int r0 = blockIdx.x * kRowsPerWG;
     if (r0 >= nvis) return;
     const int r1 = min(nvis, r0 + kRowsPerWG);
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ key
     __shared__ uint32_t s_bc[2];
     const int q = blockIdx.y;
     const int nvis = q_nvis[q];
-    const int n = (nvis + (1 << bs_log2) - 1) >> bs_log2;
+    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, (int)stride);
     const int e0 = blockIdx.x * kSelElems;
     if (n <= K || e0 >= n) return;
     // 16 keys per thread (4 coalesced uint4 loads), in flight during the search
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
     __shared__ uint32_t s_count;
     const int q = blockIdx.x;
     const int nvis = q_nvis[q];
-    const int n = (nvis + (1 << bs_log2) - 1) >> bs_log2;
+    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, (int)stride);
     int32_t* o = out + (size_t)q * K;
     if (n <= K) {  // everything is selected
         for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
@@ -478,6 +478,233 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
         }
         __syncthreads();
     }
+    rank_and_write(s_out, K, K, o);
+}
+
+// -------------------------------------------------- prefill indexer
+
+// A prefill chunk of Q queries of one sequence scores the same key rows for
+// every query, so it is a dense contraction S = Qi K^T ([Q x RW] x [RW x N])
+// on the bf16 matrix cores.  Integer-valued inputs of magnitude <= 256 are
+// exact in bf16 and every partial sum of the fp32 accumulation is an integer
+// below 2^24, so the scores equal the definition bit for bit.  Other fp32
+// inputs are split x = hi + lo (two bf16); a K-chunk whose lo parts are not
+// all zero adds the hi*lo and lo*hi products (about 16 significand bits).
+// Workgroup tile: 128 queries x 128 keys, 4 waves of 64 x 64, K in chunks of
+// 64 staged through LDS (rows padded to 144 B so 16 lanes hit 16 bank groups).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPM = 128, kPN = 128, kPK = 64, kPStr = kPK + 8;
+
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+__device__ __forceinline__ float4 load_qrow4(const float* __restrict__ qI, int q, int Hi, int Hk,
+                                             int Di, int c) {
+    if (Hk == Hi) return *reinterpret_cast<const float4*>(qI + (size_t)q * Hi * Di + c);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int h = 0; h < Hi; ++h) {
+        const float4 v = *reinterpret_cast<const float4*>(qI + ((size_t)q * Hi + h) * Di + c);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    return s;
+}
+
+__global__ __launch_bounds__(256) void k_prefill_scores(
+    const float* __restrict__ qI, const float* __restrict__ kI, const int64_t* __restrict__ seq_row_off,
+    const int32_t* __restrict__ q_nvis, int Q, int Hi, int Hk, int Di, int max_nvis,
+    uint32_t* __restrict__ keys, int64_t kstride) {
+    __shared__ __attribute__((aligned(16))) __bf16 sA[2][kPM * kPStr];
+    __shared__ __attribute__((aligned(16))) __bf16 sB[2][kPN * kPStr];
+    const int RW = Hk * Di;
+    const int n0 = blockIdx.x * kPN, m0 = blockIdx.y * kPM;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+    const float* kb = kI + seq_row_off[0] * (int64_t)RW;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // register stage of one K-chunk: 8 float4 of the query tile, 8 of the key tile
+    float4 ra[8], rb[8];
+    auto fetch = [&](int kc) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int f = threadIdx.x + 256 * j;       // float4 id in the 128 x 16 chunk
+            const int r = f >> 4, c = kc + 4 * (f & 15);
+            const int q = m0 + r, t = n0 + r;
+            ra[j] = q < Q ? load_qrow4(qI, q, Hi, Hk, Di, c) : make_float4(0.f, 0.f, 0.f, 0.f);
+            rb[j] = t < max_nvis ? *reinterpret_cast<const float4*>(kb + (int64_t)t * RW + c)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    fetch(0);
+    for (int kc = 0; kc < RW; kc += kPK) {
+        // split into bf16 hi/lo in registers; lo tiles are only staged (and
+        // only multiplied) when some value of this chunk is not exact in bf16
+        uint2 ah[8], bh[8], al[8], bl[8];
+        int any_lo = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float av[4] = {ra[j].x, ra[j].y, ra[j].z, ra[j].w};
+            const float bv[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
+            uint32_t hw[4], lw[4], hb[4], lb[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                __bf16 h, lo;
+                split_bf16(av[x], h, lo);
+                hw[x] = __builtin_bit_cast(uint16_t, h);
+                lw[x] = __builtin_bit_cast(uint16_t, lo);
+                any_lo |= (lw[x] & 0x7FFFu) != 0;
+                split_bf16(bv[x], h, lo);
+                hb[x] = __builtin_bit_cast(uint16_t, h);
+                lb[x] = __builtin_bit_cast(uint16_t, lo);
+                any_lo |= (lb[x] & 0x7FFFu) != 0;
+            }
+            ah[j] = make_uint2(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16));
+            al[j] = make_uint2(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16));
+            bh[j] = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+            bl[j] = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+        }
+        __syncthreads();   // previous chunk's LDS reads are done
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int f = threadIdx.x + 256 * j;
+            const int r = f >> 4, c = 4 * (f & 15);
+            *reinterpret_cast<uint2*>(&sA[0][r * kPStr + c]) = ah[j];
+            *reinterpret_cast<uint2*>(&sB[0][r * kPStr + c]) = bh[j];
+        }
+        const int need_lo = __syncthreads_or(any_lo);
+        if (need_lo) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int f = threadIdx.x + 256 * j;
+                const int r = f >> 4, c = 4 * (f & 15);
+                *reinterpret_cast<uint2*>(&sA[1][r * kPStr + c]) = al[j];
+                *reinterpret_cast<uint2*>(&sB[1][r * kPStr + c]) = bl[j];
+            }
+            __syncthreads();
+        }
+        if (kc + kPK < RW) fetch(kc + kPK);
+#pragma unroll
+        for (int ks = 0; ks < kPK; ks += 32) {
+            bf16x8 a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(&sA[0][(wm + 16 * i + l16) * kPStr + ks + 8 * g]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(&sB[0][(wn + 16 * j + l16) * kPStr + ks + 8 * g]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            if (need_lo) {
+                bf16x8 al[4], bl[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    al[i] = *reinterpret_cast<const bf16x8*>(&sA[1][(wm + 16 * i + l16) * kPStr + ks + 8 * g]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bl[j] = *reinterpret_cast<const bf16x8*>(&sB[1][(wn + 16 * j + l16) * kPStr + ks + 8 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
+                    }
+            }
+        }
+    }
+    // lane (g, l16) of tile (i, j) holds S[row wm + 16i + 4g + r][key wn + 16j + l16]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int q = m0 + wm + 16 * i + 4 * g + r;
+            if (q >= Q) continue;
+            const int nv = min(q_nvis[q], max_nvis);
+            uint32_t* krow = keys + (size_t)q * kstride;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = n0 + wn + 16 * j + l16;
+                if (t < nv) krow[t] = ord_key(acc[i][j][r]);
+            }
+        }
+}
+
+// Exact Top-K of one row of score keys (prefill: one workgroup per query):
+// a 4096-bin LDS histogram of the top 12 bits finds the bin b1 of the K-th
+// key; a second pass over the row keeps the keys above b1 and collects the
+// keys in b1; the best of those are picked by direct ranking.  More than
+// kRankMax keys in b1 falls back to the exact whole-row select.
+__global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __restrict__ keys,
+                                                            int64_t stride,
+                                                            const int32_t* __restrict__ q_nvis,
+                                                            int K, int32_t* __restrict__ out) {
+    __shared__ uint32_t s_h[kHistBins];
+    __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
+    __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
+    __shared__ uint32_t s_na, s_nc;
+    const int q = blockIdx.x;
+    const int n = min(q_nvis[q], (int)stride);
+    int32_t* o = out + (size_t)q * K;
+    if (n <= K) {
+        for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
+        return;
+    }
+    const uint32_t* row = keys + (size_t)q * stride;
+    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
+    if (threadIdx.x == 0) { s_na = 0; s_nc = 0; }
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += kSelThreads) atomicAdd(&s_h[row[e] >> kDigitShift], 1u);
+    __syncthreads();
+    uint32_t b1, nabove;
+    find_digit_4096<kSelThreads>(s_h, (uint32_t)K, s_tmp, b1, nabove);
+    for (int base = 0; base < n; base += kSelThreads) {
+        const int e = base + threadIdx.x;
+        const uint32_t k = e < n ? row[e] : 0u;
+        const uint32_t d = k >> kDigitShift;
+        if (e < n && d > b1) {
+            const uint32_t p = atomicAdd(&s_na, 1u);
+            if (p < (uint32_t)K) s_out[p] = e;
+        } else if (e < n && d == b1) {
+            const uint32_t p = atomicAdd(&s_nc, 1u);
+            if (p < (uint32_t)kRankMax) s_cand[p] = comp_key(k, (uint32_t)e);
+        }
+    }
+    __syncthreads();
+    const uint32_t NA = min(s_na, (uint32_t)K - 1u), NC = s_nc;
+    if (NC > (uint32_t)kRankMax) {
+        select_global_row<kSelThreads>(row, n, K, o, s_hist, s_dig, s_tmp);
+        return;
+    }
+    const uint32_t need = (uint32_t)K - NA;
+    if (threadIdx.x == 0) s_cand[NC] = 0ull;
+    __syncthreads();
+    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s_cand);
+    for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) {
+        const uint64_t ci = s_cand[i];
+        uint32_t r = 0;
+        for (int j = 0; j < ((int)NC + 1) / 2; ++j) {
+            const ulonglong2 w = c2[j];
+            r += (w.x > ci) + (w.y > ci);
+        }
+        if (r < need) s_out[NA + r] = (int32_t)comp_idx(ci);
+    }
+    __syncthreads();
     rank_and_write(s_out, K, K, o);
 }
 
@@ -654,6 +881,19 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
     hipStream_t s = (hipStream_t)stream_;
     const int bs_log2 = pool_blocks > 0 ? ilog2(block_size) : 0;
 
+    if (!q_seq) {
+        // prefill chunk of one sequence: bf16-MFMA score tiles, then one
+        // selecting workgroup per query
+        if (pool_blocks > 0) return CSA2_ERR_UNSUPPORTED;
+        if (max_nvis > 0) {
+            dim3 grid((max_nvis + kPN - 1) / kPN, (Q + kPM - 1) / kPM);
+            st = CSA2_LAUNCH("prefill_scores", k_prefill_scores, grid, dim3(256), s, qI, kI,
+                             seq_row_off, q_nvis, Q, Hi, Hk, Di, max_nvis, w.keys_e, w.se);
+            if (st) return st;
+        }
+        return CSA2_LAUNCH("row_select", k_row_select, dim3(Q), dim3(kSelThreads), s, w.keys_e,
+                           w.se, q_nvis, topk, topk_idx);
+    }
     st = CSA2_LAUNCH("zero", k_zero_u32, dim3(256), dim3(256), s, w.hist_e, w.zero_words);
     if (st) return st;
     if (max_nvis == 0) {
