@@ -7,21 +7,25 @@
 // the E2M1 row times its E4M3 per-16-channel scales) and the last 128 tokens
 // of its own FP8 window; one softmax covers both sets.
 //
-// Structure on the GPU.  With 64 heads sharing one 512-channel KV set per
-// query, the two contractions (S = Q K^T over channels, O = P V over keys)
-// are dense, so they run on the fp32 matrix cores
-// (V_MFMA_F32_16X16X4_F32: exact fp32 products, fp32 accumulation).
-//   - a workgroup owns one query (token), up to 64 heads (16 per wave) and a
-//     range of 16-key tiles; splits of the key range across workgroups are
-//     merged by k_attn_combine (log-sum-exp weights).
-//   - per tile the workgroup dequantises 16 keys x 512 channels into LDS
-//     twice: row-major K (A operand of S^T = K Q^T, one ds_read_b128 feeds 4
-//     MFMAs) and transposed V (A operand of O^T = V^T P^T, likewise).
-//   - each wave keeps its 16 heads' query slice (128 fp32 per lane) and the
-//     16 x 512 output accumulator (128 fp32 per lane) in registers.  S^T comes
-//     out of the MFMA with lane (g, h) holding keys 4g..4g+3 of head h, which
-//     is exactly the B-operand layout the P V MFMA needs: P never leaves
-//     registers.  Online softmax in base 2, one max/sum per head.
+// Structure on the GPU.  64 heads share one 512-channel key set per query,
+// so S = Q K^T (over channels) and O = P V (over keys) are dense
+// contractions; they run on the bf16 matrix cores (V_MFMA_F32_32X32X16_BF16)
+// at fp32 accuracy:
+//   - dequantised K and V are exact in bf16 (an E2M1 value times an E4M3
+//     scale has at most 6 significant bits; E4M3 itself has 4);
+//   - the fp32 query and the fp32 probabilities are split into three bf16
+//     parts (x = x1 + x2 + x3 to 24 bits), each multiplied exactly and
+//     accumulated in fp32.
+// Work split: a workgroup (8 waves, 2 per SIMD) owns one query token, 64
+// heads and a range of 32-key tiles.  Wave w handles heads 32*(w&1).. and
+// channels 128*(w>>1)..; the four channel quarters add their partial logits
+// through LDS in a fixed order, then all run the same softmax and each
+// accumulates its quarter of the output.  Per
+// tile the workgroup dequantises 32 keys into LDS twice: row-major K (A
+// operand of S^T = K Q^T) and transposed V (A operand of O^T = V^T P^T).
+// S^T leaves each lane with 16 keys of one head, exactly the B-operand
+// layout the P V product needs, so P never leaves registers.  Key-range
+// splits across workgroups are merged by k_attn_combine.
 #include <math.h>
 
 #include "common.hpp"
@@ -31,11 +35,13 @@ namespace csa2 {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 512;
-constexpr int kTK = 16;             // keys per tile
-constexpr int kKStr = kD + 4;       // LDS row stride of the K tile (floats)
-constexpr int kVStr = kTK + 4;      // LDS row stride of the transposed V tile
+constexpr int kTK = 32;             // keys per tile
+constexpr int kKStr = kD + 8;       // LDS row stride of the K tile (bf16)
+constexpr int kVStr = kTK + 8;      // LDS row stride of the transposed V tile (bf16)
 constexpr float kLn2 = 0.69314718055994530942f;
 
 struct AttnArgs {
@@ -58,30 +64,52 @@ struct AttnArgs {
     float* part_ml;              // [nsplit, rows_q, H, 2]
 };
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Raw bytes of one tile for one thread: ITEMS items of 4 keys x 8 channels.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// x (fp32) -> three bf16 parts with x == p0 + p1 + p2 to fp32 precision.
+__device__ __forceinline__ void split3(float x, uint32_t& b0, uint32_t& b1, uint32_t& b2) {
+    const __bf16 h0 = (__bf16)x;
+    const float r0 = x - (float)h0;
+    const __bf16 h1 = (__bf16)r0;
+    const float r1 = r0 - (float)h1;
+    b0 = __builtin_bit_cast(uint16_t, h0);
+    b1 = __builtin_bit_cast(uint16_t, h1);
+    b2 = bf16_bits(r1);
+}
+
+// Packs 8 bf16 bit patterns (low halves of v[0..7]) into an MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const uint32_t (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = v[2 * i] | (v[2 * i + 1] << 16);
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+constexpr int kAttnThreads = 512;   // 8 waves
+
+// Raw bytes of one tile for one thread: 1 item of 4 keys x 8 channels.
 // Main keys: k.x = 4 code bytes (8 channels), k.y = scale byte.  Window
 // keys: k = 8 K bytes, v = 8 V bytes.
-template <int ITEMS>
 struct TileRaw {
-    uint2 k[ITEMS][4];
-    uint2 v[ITEMS][4];
-    uint32_t ok[ITEMS];   // bit j: key 4*kq + j is real
+    uint2 k[1][4];
+    uint2 v[1][4];
+    uint32_t ok[1];   // bit j: key 4*kq + j is real
 };
 
-// Global loads of tile t (issued early; consumed by store_tile).
-template <int NT, int ITEMS>
+// Item i of a tile: channels 8*(i >> 3) .. +8, keys 4*(i & 7) .. +4.
 __device__ __forceinline__ void fetch_tile(const AttnArgs& a, const int32_t* s_idx, int t0,
-                                           int64_t row0, int wlo, int whi, int t,
-                                           TileRaw<ITEMS>& r) {
+                                           int64_t row0, int wlo, int whi, int t, TileRaw& r) {
     const bool main = t < a.ntiles_main;
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int item = threadIdx.x + it * NT;
-        const int c8 = item >> 2, kq = item & 3;
+    for (int it = 0; it < 1; ++it) {
+        const int item = threadIdx.x + kAttnThreads * it;
+        const int c8 = item >> 3, kq = item & 7;
         r.ok[it] = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -109,47 +137,46 @@ __device__ __forceinline__ void fetch_tile(const AttnArgs& a, const int32_t* s_i
     }
 }
 
-// Dequantises the fetched tile into sK (row-major K) and sVt (transposed V);
-// sValid[k] = 1 for a real key, 0 for padding.
-template <int NT, int ITEMS>
-__device__ __forceinline__ void store_tile(bool main, const TileRaw<ITEMS>& r, float* sK,
-                                           float* sVt, int* sValid) {
+// Dequantises the fetched tile to bf16 (exactly) into sK (row-major K) and
+// sVt (transposed V); sValid[k] = 1 for a real key, 0 for padding.
+__device__ __forceinline__ void store_tile(bool main, const TileRaw& r, uint16_t* sK,
+                                           uint16_t* sVt, int* sValid) {
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int item = threadIdx.x + it * NT;
-        const int c8 = item >> 2, kq = item & 3;
-        float v[4][8];
+    for (int it = 0; it < 1; ++it) {
+        const int item = threadIdx.x + kAttnThreads * it;
+        const int c8 = item >> 3, kq = item & 7;
+        uint32_t vb[4][8];   // bf16 bits of V, [key][channel]
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float kk[8];
+            uint32_t kb[8];
             if (main) {
                 const uint32_t w = r.k[it][j].x;
                 const float sc = e4m3_to_f32(r.k[it][j].y);
                 const float2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
                 const float2 p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
-                v[j][0] = p0.x * sc; v[j][1] = p0.y * sc; v[j][2] = p1.x * sc; v[j][3] = p1.y * sc;
-                v[j][4] = p2.x * sc; v[j][5] = p2.y * sc; v[j][6] = p3.x * sc; v[j][7] = p3.y * sc;
+                const float v[8] = {p0.x * sc, p0.y * sc, p1.x * sc, p1.y * sc,
+                                    p2.x * sc, p2.y * sc, p3.x * sc, p3.y * sc};
 #pragma unroll
-                for (int x = 0; x < 8; ++x) kk[x] = v[j][x];
+                for (int x = 0; x < 8; ++x) { kb[x] = bf16_bits(v[x]); vb[j][x] = kb[x]; }
             } else {
-                const uint2 kb = r.k[it][j], vb = r.v[it][j];
-                const float2 k0 = fp8x2_to_f32<false>(kb.x), k1 = fp8x2_to_f32<true>(kb.x);
-                const float2 k2 = fp8x2_to_f32<false>(kb.y), k3 = fp8x2_to_f32<true>(kb.y);
-                const float2 v0 = fp8x2_to_f32<false>(vb.x), v1 = fp8x2_to_f32<true>(vb.x);
-                const float2 v2 = fp8x2_to_f32<false>(vb.y), v3 = fp8x2_to_f32<true>(vb.y);
-                kk[0] = k0.x; kk[1] = k0.y; kk[2] = k1.x; kk[3] = k1.y;
-                kk[4] = k2.x; kk[5] = k2.y; kk[6] = k3.x; kk[7] = k3.y;
-                v[j][0] = v0.x; v[j][1] = v0.y; v[j][2] = v1.x; v[j][3] = v1.y;
-                v[j][4] = v2.x; v[j][5] = v2.y; v[j][6] = v3.x; v[j][7] = v3.y;
+                const uint2 kw = r.k[it][j], vw = r.v[it][j];
+                const float2 k0 = fp8x2_to_f32<false>(kw.x), k1 = fp8x2_to_f32<true>(kw.x);
+                const float2 k2 = fp8x2_to_f32<false>(kw.y), k3 = fp8x2_to_f32<true>(kw.y);
+                const float2 v0 = fp8x2_to_f32<false>(vw.x), v1 = fp8x2_to_f32<true>(vw.x);
+                const float2 v2 = fp8x2_to_f32<false>(vw.y), v3 = fp8x2_to_f32<true>(vw.y);
+                const float kf[8] = {k0.x, k0.y, k1.x, k1.y, k2.x, k2.y, k3.x, k3.y};
+                const float vf[8] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
+#pragma unroll
+                for (int x = 0; x < 8; ++x) { kb[x] = bf16_bits(kf[x]); vb[j][x] = bf16_bits(vf[x]); }
             }
-            float4* dk = reinterpret_cast<float4*>(sK + (4 * kq + j) * kKStr + 8 * c8);
-            dk[0] = make_float4(kk[0], kk[1], kk[2], kk[3]);
-            dk[1] = make_float4(kk[4], kk[5], kk[6], kk[7]);
+            *reinterpret_cast<uint4*>(sK + (4 * kq + j) * kKStr + 8 * c8) =
+                make_uint4(kb[0] | (kb[1] << 16), kb[2] | (kb[3] << 16), kb[4] | (kb[5] << 16),
+                           kb[6] | (kb[7] << 16));
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x)
-            *reinterpret_cast<float4*>(sVt + (8 * c8 + x) * kVStr + 4 * kq) =
-                make_float4(v[0][x], v[1][x], v[2][x], v[3][x]);
+            *reinterpret_cast<uint2*>(sVt + (8 * c8 + x) * kVStr + 4 * kq) =
+                make_uint2(vb[0][x] | (vb[1][x] << 16), vb[2][x] | (vb[3][x] << 16));
         if (c8 == 0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) sValid[4 * kq + j] = (r.ok[it] >> j) & 1u;
@@ -162,23 +189,22 @@ __device__ __forceinline__ void store_tile(bool main, const TileRaw<ITEMS>& r, f
 // so p <= 2^8 and most tiles skip the rescale of the accumulators.
 constexpr float kRescale = 8.f;
 
-// One workgroup = 4 waves = up to 64 heads of one query; with fewer heads
-// (H not a multiple of 64) the surplus waves only help load the tiles.
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-    constexpr int NT = 256;
-    constexpr int ITEMS = 1;
-    __shared__ __attribute__((aligned(16))) float sK[kTK * kKStr];
-    __shared__ __attribute__((aligned(16))) float sVt[kD * kVStr];
+__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kTK * kKStr];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[kD * kVStr];
+    __shared__ __attribute__((aligned(16))) float4 sS[8][4][64];   // partial logits per wave
     __shared__ int sValid[kTK];
     __shared__ int32_t s_idx[CSA2_MAX_TOPK];
 
     const int split = blockIdx.x;
     const int qi = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, hl = lane & 15;
-    const int h0 = (blockIdx.y * 4 + wave) * 16;
-    const bool active = h0 < a.H;          // wave-uniform
-    const int h = active ? h0 + hl : hl;   // idle waves read head hl, write nothing
+    const int hh = lane >> 5, l32 = lane & 31;      // lane half, lane in half
+    const int hg = wave & 1, cq = wave >> 1;         // head group, channel quarter
+    const int h = blockIdx.y * 64 + hg * 32 + l32;   // this lane's head
+    const bool hvalid = h < a.H;
+    const bool active = blockIdx.y * 64 + hg * 32 < a.H;   // wave-uniform
+    const int cbase = 128 * cq;
 
     int64_t row0 = 0;
     int wlo = 0, whi = 0;
@@ -200,69 +226,87 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
     const int t0 = split * a.tiles_per_split;
     const int t1 = min(a.ntiles, t0 + a.tiles_per_split);
-    // this split's main-KV indices, staged once
     {
         const int nslot = kTK * (min(t1, a.ntiles_main) - t0);
-        for (int i = threadIdx.x; i < nslot; i += NT) {
+        for (int i = threadIdx.x; i < nslot; i += kAttnThreads) {
             const int slot = kTK * t0 + i;
             s_idx[i] = slot < a.topk ? a.topk_idx[(size_t)qi * a.topk + slot] : -1;
         }
     }
 
-    // query slice: qreg[4u + i] = q[h][16u + 4g + i]
-    float qreg[128];
+    // query slice in three bf16 parts: step s (16 channels) of this lane is
+    // channels cbase + 16 s + 8 hh .. +8 of head h
+    bf16x8 q0[8], q1[8], q2[8];
     {
-        const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)qi * a.H + h) * kD);
+        const float* qp = a.q + ((size_t)qi * a.H + (hvalid ? h : 0)) * kD + cbase + 8 * hh;
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-            const float4 v = qp[4 * u + g];
-            qreg[4 * u + 0] = v.x; qreg[4 * u + 1] = v.y; qreg[4 * u + 2] = v.z; qreg[4 * u + 3] = v.w;
+        for (int st = 0; st < 8; ++st) {
+            float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+            if (hvalid) {
+                x0 = *reinterpret_cast<const float4*>(qp + 16 * st);
+                x1 = *reinterpret_cast<const float4*>(qp + 16 * st + 4);
+            }
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            uint32_t b0[8], b1[8], b2[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) split3(xv[x], b0[x], b1[x], b2[x]);
+            q0[st] = pack8(b0);
+            q1[st] = pack8(b1);
+            q2[st] = pack8(b2);
         }
     }
-    f32x4 o[32];
+    f32x16 o[4];
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < 4; ++ct) o[ct] = f32x16{};
     float m = -INFINITY, l = 0.f;
 
     __syncthreads();
-    TileRaw<ITEMS> raw;
-    if (t0 < t1) fetch_tile<NT, ITEMS>(aa, s_idx, t0, row0, wlo, whi, t0, raw);
+    TileRaw raw;
+    if (t0 < t1) fetch_tile(aa, s_idx, t0, row0, wlo, whi, t0, raw);
     for (int t = t0; t < t1; ++t) {
         __syncthreads();   // previous tile's LDS reads are done
-        store_tile<NT, ITEMS>(t < a.ntiles_main, raw, sK, sVt, sValid);
+        store_tile(t < a.ntiles_main, raw, sK, sVt, sValid);
         __syncthreads();
         // next tile's global loads overlap this tile's matrix work
-        if (t + 1 < t1) fetch_tile<NT, ITEMS>(aa, s_idx, t0, row0, wlo, whi, t + 1, raw);
+        if (t + 1 < t1) fetch_tile(aa, s_idx, t0, row0, wlo, whi, t + 1, raw);
 
-        if (!active) continue;
-        // S^T[key 4g+i][head hl] over all channels.  Eight independent
-        // accumulation chains (channel block u mod 8) summed as a tree keep
-        // the fp32 rounding error of the 512-term dot well below the error
-        // budget of the outputs (one sequential chain does not).
-        f32x4 sc[8];
+        // partial S^T over this wave's 128 channels (the small query parts
+        // are folded into the same chain, after the main part of each step)
+        f32x16 s0 = f32x16{};
+        if (active) {
+            const uint16_t* kr = sK + l32 * kKStr + cbase + 8 * hh;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const float* kr = sK + hl * kKStr + 4 * g;
-        for (int uo = 0; uo < 32; uo += 8) {
-#pragma unroll
-            for (int ui = 0; ui < 8; ++ui) {
-                const int u = uo + ui;
-                const float4 kv = *reinterpret_cast<const float4*>(kr + 16 * u);
-                sc[ui] = mfma4(kv.x, qreg[4 * u + 0], sc[ui]);
-                sc[ui] = mfma4(kv.y, qreg[4 * u + 1], sc[ui]);
-                sc[ui] = mfma4(kv.z, qreg[4 * u + 2], sc[ui]);
-                sc[ui] = mfma4(kv.w, qreg[4 * u + 3], sc[ui]);
+            for (int st = 0; st < 8; ++st) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr + 16 * st);
+                s0 = mfma32(ka, q0[st], s0);
+                s0 = mfma32(ka, q1[st], s0);
+                s0 = mfma32(ka, q2[st], s0);
             }
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                sS[wave][r4][lane] = make_float4(s0[4 * r4], s0[4 * r4 + 1], s0[4 * r4 + 2], s0[4 * r4 + 3]);
         }
-        const f32x4 s = ((sc[0] + sc[1]) + (sc[2] + sc[3])) + ((sc[4] + sc[5]) + (sc[6] + sc[7]));
-        float z[4], p[4];
+        __syncthreads();
+        if (!active) continue;
+        // full logits: the four channel quarters of this head group, added
+        // in the same order in every wave
+        float z[16];
         float tm = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = sValid[4 * g + i] ? s[i] * a.scale_log2 : -INFINITY;
-            tm = fmaxf(tm, z[i]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 c0 = sS[hg][r4][lane], c1 = sS[hg + 2][r4][lane];
+            const float4 c2 = sS[hg + 4][r4][lane], c3 = sS[hg + 6][r4][lane];
+            const float v0[4] = {c0.x, c0.y, c0.z, c0.w}, v1[4] = {c1.x, c1.y, c1.z, c1.w};
+            const float v2[4] = {c2.x, c2.y, c2.z, c2.w}, v3[4] = {c3.x, c3.y, c3.z, c3.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * r4 + i;
+                const int key = 8 * r4 + 4 * hh + i;
+                const float sv = (v0[i] + v1[i]) + (v2[i] + v3[i]);
+                z[r] = sValid[key] ? sv * a.scale_log2 : -INFINITY;
+                tm = fmaxf(tm, z[r]);
+            }
         }
-        tm = fmaxf(tm, __shfl_xor(tm, 16));
         tm = fmaxf(tm, __shfl_xor(tm, 32));
         const bool bump = tm > m + kRescale;   // true for any finite tm while m = -inf
         if (__ballot(bump)) {
@@ -270,51 +314,69 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
             const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
             l *= alpha;
 #pragma unroll
-            for (int cb = 0; cb < 32; ++cb) o[cb] = o[cb] * alpha;
+            for (int ct = 0; ct < 4; ++ct) o[ct] = o[ct] * alpha;
             m = mn;
         }
+        // P^T operands: MFMA u covers registers 8u..8u+7 (keys 16u + 8(j/4) + 4hh + j%4),
+        // each probability split into three bf16 parts
         float ps = 0.f;
+        bf16x8 pp[2][3];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m);
-            ps += p[i];
+        for (int u = 0; u < 2; ++u) {
+            uint32_t x0[8], x1[8], x2[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float zr = z[8 * u + j];
+                const float pv = (zr == -INFINITY) ? 0.f : exp2f(zr - m);
+                ps += pv;
+                split3(pv, x0[j], x1[j], x2[j]);
+            }
+            pp[u][0] = pack8(x0);
+            pp[u][1] = pack8(x1);
+            pp[u][2] = pack8(x2);
         }
         l += ps;
-        // O^T[channel 16cb + 4g + r][head hl] += sum_keys V^T P^T
-        const float* vr = sVt + hl * kVStr + 4 * g;
+        // O^T[channel cbase + 32 ct + m][head] += V^T P^T over the 32 keys
 #pragma unroll
-        for (int cb = 0; cb < 32; ++cb) {
-            f32x4 acc = o[cb];
-            const float4 vv = *reinterpret_cast<const float4*>(vr + 16 * cb * kVStr);
-            acc = mfma4(vv.x, p[0], acc);
-            acc = mfma4(vv.y, p[1], acc);
-            acc = mfma4(vv.z, p[2], acc);
-            acc = mfma4(vv.w, p[3], acc);
-            o[cb] = acc;
+        for (int ct = 0; ct < 4; ++ct) {
+            const uint16_t* vr = sVt + (cbase + 32 * ct + l32) * kVStr + 4 * hh;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint2 va = *reinterpret_cast<const uint2*>(vr + 16 * u);
+                const uint2 vb = *reinterpret_cast<const uint2*>(vr + 16 * u + 8);
+                const bf16x8 vv = __builtin_bit_cast(bf16x8, make_uint4(va.x, va.y, vb.x, vb.y));
+                o[ct] = mfma32(vv, pp[u][0], o[ct]);
+                o[ct] = mfma32(vv, pp[u][1], o[ct]);
+                o[ct] = mfma32(vv, pp[u][2], o[ct]);
+            }
         }
     }
     if (!active) return;
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
-    const size_t orow = ((size_t)qi * a.H + h) * kD;
+    const float lt = l + __shfl_xor(l, 32);
+    if (!hvalid) return;
+    // lane (hh, head) holds channels cbase + 32 ct + 8 q + 4 hh + 0..3, q = 0..3
+    const size_t orow = ((size_t)qi * a.H + h) * kD + cbase + 4 * hh;
     if (a.nsplit == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-        for (int cb = 0; cb < 32; ++cb) {
-            const f32x4 v = o[cb] * inv;
-            *reinterpret_cast<float4*>(a.out + orow + 16 * cb + 4 * g) =
-                make_float4(v[0], v[1], v[2], v[3]);
-        }
-        if (a.lse && g == 0)
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<float4*>(a.out + orow + 32 * ct + 8 * q4) =
+                    make_float4(o[ct][4 * q4] * inv, o[ct][4 * q4 + 1] * inv,
+                                o[ct][4 * q4 + 2] * inv, o[ct][4 * q4 + 3] * inv);
+        if (a.lse && hh == 0 && cq == 0)
             a.lse[(size_t)qi * a.H + h] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
     } else {
         const size_t rows_q = gridDim.z;
         float* po = a.part_o + ((size_t)split * rows_q * a.H) * kD + orow;
 #pragma unroll
-        for (int cb = 0; cb < 32; ++cb)
-            *reinterpret_cast<float4*>(po + 16 * cb + 4 * g) =
-                make_float4(o[cb][0], o[cb][1], o[cb][2], o[cb][3]);
-        if (g == 0) {
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<float4*>(po + 32 * ct + 8 * q4) =
+                    make_float4(o[ct][4 * q4], o[ct][4 * q4 + 1], o[ct][4 * q4 + 2], o[ct][4 * q4 + 3]);
+        if (hh == 0 && cq == 0) {
             float* pm = a.part_ml + (((size_t)split * rows_q + qi) * a.H + h) * 2;
             pm[0] = m;
             pm[1] = lt;
@@ -406,7 +468,7 @@ int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_q, void* ws, hipStream_
         a.part_ml = c.take<float>((size_t)pl.nsplit * rows_q * a.H * 2);
     }
     dim3 grid(pl.nsplit, pl.hgroups, rows_q);
-    int st = CSA2_LAUNCH("attn", k_attn, grid, dim3(256), s, a);
+    int st = CSA2_LAUNCH("attn", k_attn, grid, dim3(kAttnThreads), s, a);
     if (st || pl.nsplit == 1) return st;
     return CSA2_LAUNCH("attn_combine", k_attn_combine, dim3(rows_q * a.H), dim3(128), s,
                        a.part_o, a.part_ml, pl.nsplit, rows_q, a.H, a.out, a.lse);
