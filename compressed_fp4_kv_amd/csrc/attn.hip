@@ -41,7 +41,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kD = 512;
 constexpr int kTK = 32;             // keys per tile
 constexpr int kKStr = kD + 8;       // LDS row stride of the K tile (bf16)
-constexpr int kVStr = kTK + 8;      // LDS row stride of the transposed V tile (bf16)
+constexpr int kVStr = kTK + 4;      // LDS row stride of the transposed V tile (bf16)
 constexpr float kLn2 = 0.69314718055994530942f;
 
 struct AttnArgs {
@@ -68,26 +68,31 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> one dword of two bf16 (round to nearest even; one
+// v_cvt_pk_bf16_f32).  Element a lands in the low half.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    const bf16x2v r = __builtin_convertvector((f32x2v){a, b}, bf16x2v);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
-// x (fp32) -> three bf16 parts with x == p0 + p1 + p2 to fp32 precision.
-__device__ __forceinline__ void split3(float x, uint32_t& b0, uint32_t& b1, uint32_t& b2) {
-    const __bf16 h0 = (__bf16)x;
-    const float r0 = x - (float)h0;
-    const __bf16 h1 = (__bf16)r0;
-    const float r1 = r0 - (float)h1;
-    b0 = __builtin_bit_cast(uint16_t, h0);
-    b1 = __builtin_bit_cast(uint16_t, h1);
-    b2 = bf16_bits(r1);
+// Pair (a, b) -> three packed bf16 pairs with a == p0.lo + p1.lo + p2.lo and
+// b == p0.hi + p1.hi + p2.hi to fp32 precision (each residual is exact).
+__device__ __forceinline__ void split3_pk(float a, float b, uint32_t& p0, uint32_t& p1,
+                                          uint32_t& p2) {
+    p0 = cvt_pk_bf16(a, b);
+    a -= __uint_as_float(p0 << 16);
+    b -= __uint_as_float(p0 & 0xFFFF0000u);
+    p1 = cvt_pk_bf16(a, b);
+    a -= __uint_as_float(p1 << 16);
+    b -= __uint_as_float(p1 & 0xFFFF0000u);
+    p2 = cvt_pk_bf16(a, b);
 }
 
-// Packs 8 bf16 bit patterns (low halves of v[0..7]) into an MFMA operand.
-__device__ __forceinline__ bf16x8 pack8(const uint32_t (&v)[8]) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = v[2 * i] | (v[2 * i + 1] << 16);
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    const uint32_t w[4] = {w0, w1, w2, w3};
     return __builtin_bit_cast(bf16x8, w);
 }
 
@@ -102,14 +107,15 @@ struct TileRaw {
     uint32_t ok[1];   // bit j: key 4*kq + j is real
 };
 
-// Item i of a tile: channels 8*(i >> 3) .. +8, keys 4*(i & 7) .. +4.
+// Item i of a tile: channels 8*(i & 63) .. +8, keys 4*(i >> 6) .. +4 (consecutive
+// threads write consecutive 16 B of a K row; V rows land 2 banks apart).
 __device__ __forceinline__ void fetch_tile(const AttnArgs& a, const int32_t* s_idx, int t0,
                                            int64_t row0, int wlo, int whi, int t, TileRaw& r) {
     const bool main = t < a.ntiles_main;
 #pragma unroll
     for (int it = 0; it < 1; ++it) {
         const int item = threadIdx.x + kAttnThreads * it;
-        const int c8 = item >> 3, kq = item & 7;
+        const int c8 = item & 63, kq = item >> 6;
         r.ok[it] = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -144,39 +150,47 @@ __device__ __forceinline__ void store_tile(bool main, const TileRaw& r, uint16_t
 #pragma unroll
     for (int it = 0; it < 1; ++it) {
         const int item = threadIdx.x + kAttnThreads * it;
-        const int c8 = item >> 3, kq = item & 7;
-        uint32_t vb[4][8];   // bf16 bits of V, [key][channel]
+        const int c8 = item & 63, kq = item >> 6;
+        uint32_t vp[4][4];   // bf16 pairs of V, [key][channel pair]
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t kb[8];
+            uint32_t kp[4];
             if (main) {
                 const uint32_t w = r.k[it][j].x;
                 const float sc = e4m3_to_f32(r.k[it][j].y);
                 const float2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
                 const float2 p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
-                const float v[8] = {p0.x * sc, p0.y * sc, p1.x * sc, p1.y * sc,
-                                    p2.x * sc, p2.y * sc, p3.x * sc, p3.y * sc};
+                kp[0] = cvt_pk_bf16(p0.x * sc, p0.y * sc);
+                kp[1] = cvt_pk_bf16(p1.x * sc, p1.y * sc);
+                kp[2] = cvt_pk_bf16(p2.x * sc, p2.y * sc);
+                kp[3] = cvt_pk_bf16(p3.x * sc, p3.y * sc);
 #pragma unroll
-                for (int x = 0; x < 8; ++x) { kb[x] = bf16_bits(v[x]); vb[j][x] = kb[x]; }
+                for (int x = 0; x < 4; ++x) vp[j][x] = kp[x];
             } else {
                 const uint2 kw = r.k[it][j], vw = r.v[it][j];
                 const float2 k0 = fp8x2_to_f32<false>(kw.x), k1 = fp8x2_to_f32<true>(kw.x);
                 const float2 k2 = fp8x2_to_f32<false>(kw.y), k3 = fp8x2_to_f32<true>(kw.y);
                 const float2 v0 = fp8x2_to_f32<false>(vw.x), v1 = fp8x2_to_f32<true>(vw.x);
                 const float2 v2 = fp8x2_to_f32<false>(vw.y), v3 = fp8x2_to_f32<true>(vw.y);
-                const float kf[8] = {k0.x, k0.y, k1.x, k1.y, k2.x, k2.y, k3.x, k3.y};
-                const float vf[8] = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
-#pragma unroll
-                for (int x = 0; x < 8; ++x) { kb[x] = bf16_bits(kf[x]); vb[j][x] = bf16_bits(vf[x]); }
+                kp[0] = cvt_pk_bf16(k0.x, k0.y); kp[1] = cvt_pk_bf16(k1.x, k1.y);
+                kp[2] = cvt_pk_bf16(k2.x, k2.y); kp[3] = cvt_pk_bf16(k3.x, k3.y);
+                vp[j][0] = cvt_pk_bf16(v0.x, v0.y); vp[j][1] = cvt_pk_bf16(v1.x, v1.y);
+                vp[j][2] = cvt_pk_bf16(v2.x, v2.y); vp[j][3] = cvt_pk_bf16(v3.x, v3.y);
             }
             *reinterpret_cast<uint4*>(sK + (4 * kq + j) * kKStr + 8 * c8) =
-                make_uint4(kb[0] | (kb[1] << 16), kb[2] | (kb[3] << 16), kb[4] | (kb[5] << 16),
-                           kb[6] | (kb[7] << 16));
+                make_uint4(kp[0], kp[1], kp[2], kp[3]);
         }
+        // transposed V: row = channel, 4 consecutive keys per 8-byte store
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-            *reinterpret_cast<uint2*>(sVt + (8 * c8 + x) * kVStr + 4 * kq) =
-                make_uint2(vb[0][x] | (vb[1][x] << 16), vb[2][x] | (vb[3][x] << 16));
+        for (int x = 0; x < 4; ++x) {
+            // channel pair x: low halves are channel 2x, high halves 2x + 1
+            const uint32_t lo01 = (vp[0][x] & 0xFFFFu) | (vp[1][x] << 16);
+            const uint32_t lo23 = (vp[2][x] & 0xFFFFu) | (vp[3][x] << 16);
+            const uint32_t hi01 = (vp[0][x] >> 16) | (vp[1][x] & 0xFFFF0000u);
+            const uint32_t hi23 = (vp[2][x] >> 16) | (vp[3][x] & 0xFFFF0000u);
+            *reinterpret_cast<uint2*>(sVt + (8 * c8 + 2 * x) * kVStr + 4 * kq) = make_uint2(lo01, lo23);
+            *reinterpret_cast<uint2*>(sVt + (8 * c8 + 2 * x + 1) * kVStr + 4 * kq) = make_uint2(hi01, hi23);
+        }
         if (c8 == 0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) sValid[4 * kq + j] = (r.ok[it] >> j) & 1u;
@@ -246,13 +260,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
                 x0 = *reinterpret_cast<const float4*>(qp + 16 * st);
                 x1 = *reinterpret_cast<const float4*>(qp + 16 * st + 4);
             }
-            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            uint32_t b0[8], b1[8], b2[8];
-#pragma unroll
-            for (int x = 0; x < 8; ++x) split3(xv[x], b0[x], b1[x], b2[x]);
-            q0[st] = pack8(b0);
-            q1[st] = pack8(b1);
-            q2[st] = pack8(b2);
+            uint32_t a0[4], a1[4], a2[4];
+            split3_pk(x0.x, x0.y, a0[0], a1[0], a2[0]);
+            split3_pk(x0.z, x0.w, a0[1], a1[1], a2[1]);
+            split3_pk(x1.x, x1.y, a0[2], a1[2], a2[2]);
+            split3_pk(x1.z, x1.w, a0[3], a1[3], a2[3]);
+            q0[st] = as_bf16x8(a0[0], a0[1], a0[2], a0[3]);
+            q1[st] = as_bf16x8(a1[0], a1[1], a1[2], a1[3]);
+            q2[st] = as_bf16x8(a2[0], a2[1], a2[2], a2[3]);
         }
     }
     f32x16 o[4];
@@ -323,17 +338,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         bf16x8 pp[2][3];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            uint32_t x0[8], x1[8], x2[8];
+            float pv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float zr = z[8 * u + j];
-                const float pv = (zr == -INFINITY) ? 0.f : exp2f(zr - m);
-                ps += pv;
-                split3(pv, x0[j], x1[j], x2[j]);
+                pv[j] = (zr == -INFINITY) ? 0.f : exp2f(zr - m);
+                ps += pv[j];
             }
-            pp[u][0] = pack8(x0);
-            pp[u][1] = pack8(x1);
-            pp[u][2] = pack8(x2);
+            uint32_t x0[4], x1[4], x2[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) split3_pk(pv[2 * j], pv[2 * j + 1], x0[j], x1[j], x2[j]);
+            pp[u][0] = as_bf16x8(x0[0], x0[1], x0[2], x0[3]);
+            pp[u][1] = as_bf16x8(x1[0], x1[1], x1[2], x1[3]);
+            pp[u][2] = as_bf16x8(x2[0], x2[1], x2[2], x2[3]);
         }
         l += ps;
         // O^T[channel cbase + 32 ct + m][head] += V^T P^T over the 32 keys
