@@ -109,35 +109,39 @@ struct TileRaw {
 
 // Item i of a tile: channels 8*(i & 63) .. +8, keys 4*(i >> 6) .. +4 (consecutive
 // threads write consecutive 16 B of a K row; V rows land 2 banks apart).
-__device__ __forceinline__ void fetch_tile(const AttnArgs& a, const int32_t* s_idx, int t0,
-                                           int64_t row0, int wlo, int whi, int t, TileRaw& r) {
+// The main-KV indices of this thread's 4 keys of tile t: from `idxp` (the
+// tile's first slot; slots >= nslots are padding).
+__device__ __forceinline__ void tile_idx(const int32_t* idxp, int nslots, int32_t (&idx)[4]) {
+    const int kq = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) idx[j] = 4 * kq + j < nslots ? idxp[4 * kq + j] : -1;
+}
+
+// Global loads of tile t (issued early; consumed by store_tile).
+__device__ __forceinline__ void fetch_tile(const AttnArgs& a, const int32_t (&idx)[4], int64_t row0,
+                                           int wlo, int whi, int t, TileRaw& r) {
     const bool main = t < a.ntiles_main;
+    const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
+    r.ok[0] = 0;
 #pragma unroll
-    for (int it = 0; it < 1; ++it) {
-        const int item = threadIdx.x + kAttnThreads * it;
-        const int c8 = item & 63, kq = item >> 6;
-        r.ok[it] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = 4 * kq + j;
-            r.k[it][j] = make_uint2(0, 0);
-            r.v[it][j] = make_uint2(0, 0);
-            if (main) {
-                const int32_t idx = s_idx[kTK * (t - t0) + key];
-                if (idx >= 0) {
-                    const int64_t row = row0 + idx;
-                    r.k[it][j].x = *reinterpret_cast<const uint32_t*>(a.kv_codes + row * (kD / 2) + 4 * c8);
-                    r.k[it][j].y = a.kv_scales[row * (kD / 16) + (c8 >> 1)];
-                    r.ok[it] |= 1u << j;
-                }
-            } else {
-                const int w_ = kTK * (t - a.ntiles_main) + key;
-                if (w_ >= wlo && w_ < whi) {
-                    const size_t off = (size_t)w_ * kD + 8 * c8;
-                    r.k[it][j] = *reinterpret_cast<const uint2*>(a.swa_k + off);
-                    r.v[it][j] = *reinterpret_cast<const uint2*>(a.swa_v + off);
-                    r.ok[it] |= 1u << j;
-                }
+    for (int j = 0; j < 4; ++j) {
+        const int key = 4 * kq + j;
+        r.k[0][j] = make_uint2(0, 0);
+        r.v[0][j] = make_uint2(0, 0);
+        if (main) {
+            if (idx[j] >= 0) {
+                const int64_t row = row0 + idx[j];
+                r.k[0][j].x = *reinterpret_cast<const uint32_t*>(a.kv_codes + row * (kD / 2) + 4 * c8);
+                r.k[0][j].y = a.kv_scales[row * (kD / 16) + (c8 >> 1)];
+                r.ok[0] |= 1u << j;
+            }
+        } else {
+            const int w_ = kTK * (t - a.ntiles_main) + key;
+            if (w_ >= wlo && w_ < whi) {
+                const size_t off = (size_t)w_ * kD + 8 * c8;
+                r.k[0][j] = *reinterpret_cast<const uint2*>(a.swa_k + off);
+                r.v[0][j] = *reinterpret_cast<const uint2*>(a.swa_v + off);
+                r.ok[0] |= 1u << j;
             }
         }
     }
@@ -240,12 +244,25 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     }
     const int t0 = split * a.tiles_per_split;
     const int t1 = min(a.ntiles, t0 + a.tiles_per_split);
-    {
-        const int nslot = kTK * (min(t1, a.ntiles_main) - t0);
-        for (int i = threadIdx.x; i < nslot; i += kAttnThreads) {
-            const int slot = kTK * t0 + i;
-            s_idx[i] = slot < a.topk ? a.topk_idx[(size_t)qi * a.topk + slot] : -1;
-        }
+    const int32_t* qidx = a.topk_idx + (size_t)qi * a.topk;
+    // Prologue: the first tile's indices (global), the split's index staging
+    // and the query slice are all requested before any of them is used.
+    TileRaw raw;
+    int32_t idx[4] = {-1, -1, -1, -1};
+    if (t0 < a.ntiles_main) tile_idx(qidx + kTK * t0, a.topk - kTK * t0, idx);
+    const int nslot = kTK * (min(t1, a.ntiles_main) - t0);
+    int32_t stage[CSA2_MAX_TOPK / kAttnThreads];
+#pragma unroll
+    for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i) {
+        const int k = threadIdx.x + kAttnThreads * i;
+        const int slot = kTK * t0 + k;
+        stage[i] = (k < nslot && slot < a.topk) ? qidx[slot] : -1;
+    }
+    if (t0 < t1) fetch_tile(aa, idx, row0, wlo, whi, t0, raw);
+#pragma unroll
+    for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i) {
+        const int k = threadIdx.x + kAttnThreads * i;
+        if (k < nslot) s_idx[k] = stage[i];
     }
 
     // query slice in three bf16 parts: step s (16 channels) of this lane is
@@ -276,14 +293,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     float m = -INFINITY, l = 0.f;
 
     __syncthreads();
-    TileRaw raw;
-    if (t0 < t1) fetch_tile(aa, s_idx, t0, row0, wlo, whi, t0, raw);
     for (int t = t0; t < t1; ++t) {
         __syncthreads();   // previous tile's LDS reads are done
         store_tile(t < a.ntiles_main, raw, sK, sVt, sValid);
+        // next tile's global loads overlap the barrier and this tile's matrix work
+        if (t + 1 < t1) {
+            if (t + 1 < a.ntiles_main) tile_idx(s_idx + kTK * (t + 1 - t0), kTK, idx);
+            fetch_tile(aa, idx, row0, wlo, whi, t + 1, raw);
+        }
         __syncthreads();
-        // next tile's global loads overlap this tile's matrix work
-        if (t + 1 < t1) fetch_tile(aa, s_idx, t0, row0, wlo, whi, t + 1, raw);
 
         // partial S^T over this wave's 128 channels (the small query parts
         // are folded into the same chain, after the main part of each step)
@@ -402,6 +420,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 }
 
 // Merges the key-range splits of one (query, head): weights 2^(m_s - M).
+// All partials are requested in one round (up to kMaxSplitRegs in
+// registers), then weighted.
+constexpr int kMaxSplitRegs = 16;
+
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int nsplit, int rows_q, int H,
@@ -410,18 +432,28 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
     const int qh = blockIdx.x;  // qi * H + h
     const size_t stride_o = (size_t)rows_q * H * kD;
     const size_t stride_ml = (size_t)rows_q * H * 2;
+    float2 ml[kMaxSplitRegs];
+    float4 po[kMaxSplitRegs];
+#pragma unroll
+    for (int s = 0; s < kMaxSplitRegs; ++s) {
+        if (s < nsplit) {
+            ml[s] = *reinterpret_cast<const float2*>(part_ml + s * stride_ml + (size_t)qh * 2);
+            po[s] = reinterpret_cast<const float4*>(part_o + s * stride_o + (size_t)qh * kD)[threadIdx.x];
+        }
+    }
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[s * stride_ml + (size_t)qh * 2]);
+#pragma unroll
+    for (int s = 0; s < kMaxSplitRegs; ++s)
+        if (s < nsplit) M = fmaxf(M, ml[s].x);
     float L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nsplit; ++s) {
-        const float ms = part_ml[s * stride_ml + (size_t)qh * 2];
-        const float ls = part_ml[s * stride_ml + (size_t)qh * 2 + 1];
-        if (ms == -INFINITY || ls == 0.f) continue;
-        const float w = exp2f(ms - M);
-        L += w * ls;
-        const float4 v = reinterpret_cast<const float4*>(part_o + s * stride_o + (size_t)qh * kD)[threadIdx.x];
-        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+#pragma unroll
+    for (int s = 0; s < kMaxSplitRegs; ++s) {
+        if (s < nsplit && ml[s].x != -INFINITY && ml[s].y != 0.f) {
+            const float w = exp2f(ml[s].x - M);
+            L += w * ml[s].y;
+            acc.x += w * po[s].x; acc.y += w * po[s].y; acc.z += w * po[s].z; acc.w += w * po[s].w;
+        }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     reinterpret_cast<float4*>(out + (size_t)qh * kD)[threadIdx.x] =
@@ -461,6 +493,7 @@ int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnP
         const long target = 256;
         if (wgs < target) nsplit = (int)((target + wgs - 1) / wgs);
         if (nsplit > p->ntiles) nsplit = p->ntiles;
+        if (nsplit > kMaxSplitRegs) nsplit = kMaxSplitRegs;
     }
     p->tps = p->ntiles > 0 ? (p->ntiles + nsplit - 1) / nsplit : 0;
     if (p->tps > 0) nsplit = (p->ntiles + p->tps - 1) / p->tps;

@@ -44,8 +44,12 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelItems = kCandCap / kSelThreads;
 constexpr int kStreamThreads = 512;
 constexpr int kRowsPerWG = 2048;     // score stream: rows per workgroup
-constexpr int kSelElems = 4096;     // filter: keys per workgroup (16 per thread)
-constexpr int kRankMax = 2048;      // candidates selected by direct ranking
+constexpr int kSelElems = 16384;    // filter: keys per workgroup (64 per thread)
+constexpr int kFilterLoads = kSelElems / (4 * 256);   // uint4 loads per thread
+constexpr int kRankMax = 4096;      // candidates held in LDS by the one-workgroup selects
+constexpr int kRankDirect = 512;    // up to this many candidates are ranked directly
+constexpr int kLdsCandItems = kRankMax / kSelThreads;  // per thread, radix path
+constexpr int kSmallRow = 65536;    // rows up to this length are selected by one workgroup
 constexpr int kReindexPerWG = 256;   // reindex: candidates per workgroup
 constexpr int kReindexThreads = 256;
 
@@ -154,8 +158,13 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
     int64_t bstride, int bs_log2, uint32_t* __restrict__ hist_b) {
-    __shared__ uint32_t s_he[kHistBins];
-    __shared__ uint32_t s_hb[kHistBins];
+    // 16-bit bin counters, two per word (a workgroup sees at most
+    // kRowsPerWG keys), so that four workgroups fit a CU's LDS
+    __shared__ uint32_t s_he[kHistBins / 2];
+    __shared__ uint32_t s_hb[kHistBins / 2];
+    // this workgroup's keys, written out as whole lines at the end
+    __shared__ __attribute__((aligned(16))) uint32_t s_ke[kRowsPerWG];
+    __shared__ __attribute__((aligned(16))) uint32_t s_kb[kRowsPerWG];
     constexpr int RW = 256 * VPR;
     constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (64 KB in flight per 4 waves)
     const int q = blockIdx.y;
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     if (r0 >= nvis) return;
     const int r1 = min(nvis, r0 + kRowsPerWG);
     const bool pool = bkeys != nullptr;
-    for (int i = threadIdx.x; i < kHistBins; i += kStreamThreads) { s_he[i] = 0; s_hb[i] = 0; }
+    for (int i = threadIdx.x; i < kHistBins / 2; i += kStreamThreads) { s_he[i] = 0; s_hb[i] = 0; }
     __syncthreads();
 
     float4 qv[VPR];
@@ -192,8 +201,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
             const bool valid = row < r1;
             const uint32_t k = ord_key(sc[hh]);
             if ((lane & 7) == 0 && valid) {
-                krow[row] = k;
-                atomicAdd(&s_he[k >> kDigitShift], 1u);
+                s_ke[row - r0] = k;
+                const uint32_t d = k >> kDigitShift;
+                atomicAdd(&s_he[d >> 1], 1u << ((d & 1u) << 4));
             }
             if (pool) {
                 uint32_t bk = valid ? k : 0u;
@@ -201,16 +211,41 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
                 if (bs_log2 >= 2) bk = max(bk, (uint32_t)__shfl_xor(bk, 16));
                 if (bs_log2 >= 3) bk = max(bk, (uint32_t)__shfl_xor(bk, 32));
                 if ((lane & 7) == 0 && valid && ((uint32_t)myrow & bmask) == 0) {
-                    bkeys[(size_t)q * bstride + (row >> bs_log2)] = bk;
-                    atomicAdd(&s_hb[bk >> kDigitShift], 1u);
+                    s_kb[(row - r0) >> bs_log2] = bk;
+                    const uint32_t d = bk >> kDigitShift;
+                    atomicAdd(&s_hb[d >> 1], 1u << ((d & 1u) << 4));
                 }
             }
         }
     }
     __syncthreads();
+    // r0 and the key strides are multiples of 4 (64): whole uint4 stores,
+    // a scalar tail for the last workgroup of a row
+    const int nk = r1 - r0;
+    for (int i = 4 * threadIdx.x; i < nk; i += 4 * kStreamThreads) {
+        if (i + 4 <= nk)
+            *reinterpret_cast<uint4*>(krow + r0 + i) = *reinterpret_cast<const uint4*>(s_ke + i);
+        else
+            for (int x = i; x < nk; ++x) krow[r0 + x] = s_ke[x];
+    }
+    if (pool) {
+        const int b0 = r0 >> bs_log2, nb = ((r1 - 1) >> bs_log2) - b0 + 1;
+        uint32_t* brow = bkeys + (size_t)q * bstride + b0;
+        for (int i = 4 * threadIdx.x; i < nb; i += 4 * kStreamThreads) {
+            if (i + 4 <= nb)
+                *reinterpret_cast<uint4*>(brow + i) = *reinterpret_cast<const uint4*>(s_kb + i);
+            else
+                for (int x = i; x < nb; ++x) brow[x] = s_kb[x];
+        }
+    }
     for (int i = threadIdx.x; i < kHistBins; i += kStreamThreads) {
-        if (s_he[i]) atomicAdd(&hist_e[(size_t)q * kHistBins + i], s_he[i]);
-        if (pool && s_hb[i]) atomicAdd(&hist_b[(size_t)q * kHistBins + i], s_hb[i]);
+        const uint32_t sh = (i & 1) << 4;
+        const uint32_t ce = (s_he[i >> 1] >> sh) & 0xFFFFu;
+        if (ce) atomicAdd(&hist_e[(size_t)q * kHistBins + i], ce);
+        if (pool) {
+            const uint32_t cb = (s_hb[i >> 1] >> sh) & 0xFFFFu;
+            if (cb) atomicAdd(&hist_b[(size_t)q * kHistBins + i], cb);
+        }
     }
 }
 
@@ -334,23 +369,121 @@ __device__ void select_global_row(const uint32_t* __restrict__ keys, int n, int 
     for (int i = (int)sel_run + threadIdx.x; i < K; i += NT) out[i] = -1;
 }
 
-// Writes the `count` distinct indices of s_list (unordered, followed by room
-// for 3 pad slots) to o in ascending order, each at its rank, and pads the K
-// slots with -1.
+// Writes the `count` distinct non-negative indices of s_list (unordered, room
+// for 4 pad slots after them) to o in ascending order and pads the K slots
+// with -1.  Lists of up to 512: each index is written at its rank.  Longer
+// ones: a counting sort into kSelThreads buckets spread evenly over [min, max]
+// of the list, then each index is placed by its rank inside its bucket.
 __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __restrict__ o) {
-    if (threadIdx.x < 4) s_list[count + threadIdx.x] = INT_MAX;
-    __syncthreads();
-    const int4* l4 = reinterpret_cast<const int4*>(s_list);
-    for (int i = threadIdx.x; i < count; i += kSelThreads) {
-        const int32_t e = s_list[i];
-        int r = 0;
-        for (int j = 0; j < (count + 3) / 4; ++j) {
-            const int4 v = l4[j];
-            r += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
+    constexpr int NB = kSelThreads;
+    __shared__ uint32_t s_start[NB + 1];
+    __shared__ uint32_t s_cur[NB];
+    __shared__ int32_t s_srt[CSA2_MAX_TOPK];
+    __shared__ int32_t s_mm[2 * (kSelThreads / kWave)];
+    __shared__ uint32_t s_scan[kSelThreads / kWave + 1];
+    if (count <= 512) {
+        if (threadIdx.x < 4) s_list[count + threadIdx.x] = INT_MAX;
+        __syncthreads();
+        const int4* l4 = reinterpret_cast<const int4*>(s_list);
+        for (int i = threadIdx.x; i < count; i += kSelThreads) {
+            const int32_t e = s_list[i];
+            int r = 0;
+            for (int j = 0; j < (count + 3) / 4; ++j) {
+                const int4 v = l4[j];
+                r += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
+            }
+            o[r] = e;
         }
-        o[r] = e;
+    } else {
+        // range of the list
+        int32_t mn = INT_MAX, mx = 0;
+        for (int i = threadIdx.x; i < count; i += kSelThreads) {
+            mn = min(mn, s_list[i]);
+            mx = max(mx, s_list[i]);
+        }
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) {
+            mn = min(mn, __shfl_xor(mn, off));
+            mx = max(mx, __shfl_xor(mx, off));
+        }
+        const int wid = threadIdx.x / kWave;
+        if (lane_id() == 0) { s_mm[2 * wid] = mn; s_mm[2 * wid + 1] = mx; }
+        s_cur[threadIdx.x] = 0u;
+        __syncthreads();
+        mn = INT_MAX; mx = 0;
+        for (int w = 0; w < kSelThreads / kWave; ++w) {
+            mn = min(mn, s_mm[2 * w]);
+            mx = max(mx, s_mm[2 * w + 1]);
+        }
+        // bucket(e) is non-decreasing in e
+        const float scale = (float)NB / ((float)(mx - mn) + 1.0f);
+        auto bucket = [&](int32_t e) { return min(NB - 1, (int)((float)(e - mn) * scale)); };
+        for (int i = threadIdx.x; i < count; i += kSelThreads) atomicAdd(&s_cur[bucket(s_list[i])], 1u);
+        __syncthreads();
+        const uint32_t c = s_cur[threadIdx.x];
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_sum<kSelThreads>(c, s_scan, tot);
+        s_start[threadIdx.x] = ex;
+        s_cur[threadIdx.x] = ex;
+        if (threadIdx.x == NB - 1) s_start[NB] = ex + c;
+        __syncthreads();
+        for (int i = threadIdx.x; i < count; i += kSelThreads) {
+            const int32_t e = s_list[i];
+            s_srt[atomicAdd(&s_cur[bucket(e)], 1u)] = e;
+        }
+        __syncthreads();
+        for (int p = threadIdx.x; p < count; p += kSelThreads) {
+            const int32_t e = s_srt[p];
+            const int bk = bucket(e);
+            const int lo = (int)s_start[bk], hi = (int)s_start[bk + 1];
+            int r = 0;
+            for (int j = lo; j < hi; ++j) r += s_srt[j] < e;
+            o[lo + r] = e;
+        }
     }
     for (int i = count + threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
+}
+
+// Appends to s_out[NA ..] the indices of the `need` best of the NC distinct
+// candidate keys in s_cand (1 <= need <= NC <= kRankMax; one spare slot after
+// them): direct ranking when NC <= kRankDirect, else a register-resident radix
+// select.  Ends with a barrier.
+__device__ void pick_lds_candidates(uint64_t* s_cand, uint32_t NC, uint32_t need, uint32_t NA,
+                                    int32_t* s_out, uint32_t* s_hist, uint32_t* s_dig,
+                                    uint32_t* s_count) {
+    if (NC <= (uint32_t)kRankDirect) {
+        if (threadIdx.x == 0) s_cand[NC] = 0ull;  // pad for the paired reads
+        __syncthreads();
+        // candidate i has rank r = #{larger candidates}; the best `need` ranks win
+        const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s_cand);
+        for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) {
+            const uint64_t ci = s_cand[i];
+            uint32_t r = 0;
+            for (int j = 0; j < ((int)NC + 1) / 2; ++j) {
+                const ulonglong2 w = c2[j];
+                r += (w.x > ci) + (w.y > ci);
+            }
+            if (r < need) s_out[NA + r] = (int32_t)comp_idx(ci);
+        }
+    } else {
+        uint64_t it[kLdsCandItems];
+#pragma unroll
+        for (int j = 0; j < kLdsCandItems; ++j) {
+            const uint32_t i = threadIdx.x + j * kSelThreads;
+            it[j] = i < NC ? s_cand[i] : 0ull;
+        }
+        const uint64_t T = block_select_kth<kSelThreads, kLdsCandItems>(it, need, s_hist, s_dig, 48);
+        if (threadIdx.x == 0) *s_count = NA;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kLdsCandItems; ++j) {
+            if (it[j] != 0 && it[j] >= T) {
+                const uint32_t pos = atomicAdd(s_count, 1u);
+                if (pos < NA + need) s_out[pos] = (int32_t)comp_idx(it[j]);
+            }
+        }
+    }
+    __syncthreads();
 }
 
 // Filter of one key row per query (entries or blocks): every workgroup
@@ -371,11 +504,11 @@ __global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ key
     const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, (int)stride);
     const int e0 = blockIdx.x * kSelElems;
     if (n <= K || e0 >= n) return;
-    // 16 keys per thread (4 coalesced uint4 loads), in flight during the search
+    // the keys (coalesced uint4 loads) are in flight during the bin search
     const uint32_t* row = keys + (size_t)q * stride;
-    uint32_t kk[16];
+    uint32_t kk[4 * kFilterLoads];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kFilterLoads; ++j) {
         const int e = e0 + 4 * (threadIdx.x + 256 * j);
         const uint4 v = e < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
         kk[4 * j] = v.x; kk[4 * j + 1] = v.y; kk[4 * j + 2] = v.z; kk[4 * j + 3] = v.w;
@@ -384,7 +517,7 @@ __global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ key
     find_digit_4096<256>(hist + (size_t)q * kHistBins, (uint32_t)K, s_tmp, b1, nabove);
     uint32_t na = 0, nc = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4 * kFilterLoads; ++i) {
         const int e = e0 + 4 * (threadIdx.x + 256 * (i >> 2)) + (i & 3);
         const uint32_t d = kk[i] >> kDigitShift;
         na += e < n && d > b1;
@@ -399,7 +532,7 @@ __global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ key
     __syncthreads();
     uint32_t pa = s_bc[0] + (ex >> 16), pc = s_bc[1] + (ex & 0xFFFFu);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4 * kFilterLoads; ++i) {
         const int e = e0 + 4 * (threadIdx.x + 256 * (i >> 2)) + (i & 3);
         const uint32_t d = kk[i] >> kDigitShift;
         if (e < n && d > b1) {
@@ -413,7 +546,7 @@ __global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ key
 }
 
 // Final selection, one workgroup per query: picks the K - #winners best
-// candidates -- by direct ranking when there are at most kRankMax of them,
+// candidates -- by direct ranking when there are at most kRankDirect of them,
 // else by a register-resident radix select, else (more than kCandCap:
 // degenerate ties) by an exact select over the whole row -- and writes the K
 // indices in ascending order.
@@ -422,7 +555,7 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
     int bs_log2, int K, const uint32_t* __restrict__ cnt, const int32_t* __restrict__ above,
     const uint64_t* __restrict__ cand, int32_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
-    __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
+    __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankDirect + 2];
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
@@ -443,22 +576,9 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
         return;
     }
     for (int i = threadIdx.x; i < (int)NA; i += kSelThreads) s_out[i] = above[(size_t)q * K + i];
-    if (NC <= (uint32_t)kRankMax) {
+    if (NC <= (uint32_t)kRankDirect) {
         for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) s_cand[i] = cand[(size_t)q * kCandCap + i];
-        if (threadIdx.x == 0) s_cand[NC] = 0ull;  // pad for the paired reads
-        __syncthreads();
-        // candidate i has rank r = #{larger candidates}; the best `need` ranks win
-        const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s_cand);
-        for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) {
-            const uint64_t ci = s_cand[i];
-            uint32_t r = 0;
-            for (int j = 0; j < ((int)NC + 1) / 2; ++j) {
-                const ulonglong2 w = c2[j];
-                r += (w.x > ci) + (w.y > ci);
-            }
-            if (r < need) s_out[NA + r] = (int32_t)comp_idx(ci);
-        }
-        __syncthreads();
+        pick_lds_candidates(s_cand, NC, need, NA, s_out, s_hist, s_dig, &s_count);
     } else {
         uint64_t it[kSelItems];
 #pragma unroll
@@ -478,6 +598,68 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
         }
         __syncthreads();
     }
+    rank_and_write(s_out, K, K, o);
+}
+
+// Top-K of one key row per query by a single workgroup (rows of at most
+// kSmallRow keys: the c1 entry rows, the pool's block rows): the bin b1 of
+// the K-th key comes from the first-level histogram; one pass over the row
+// puts winners and candidates into LDS, where the best candidates are picked.
+// Replaces the filter + finalize pair where one workgroup can read the row.
+__global__ __launch_bounds__(kSelThreads) void k_select_small(
+    const uint32_t* __restrict__ keys, int64_t stride, const int32_t* __restrict__ q_nvis,
+    int bs_log2, int K, const uint32_t* __restrict__ hist, int32_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
+    __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
+    __shared__ uint32_t s_na, s_nc, s_count;
+    const int q = blockIdx.x;
+    const int nvis = q_nvis[q];
+    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, (int)stride);
+    int32_t* o = out + (size_t)q * K;
+    if (n <= K) {
+        for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
+        return;
+    }
+    const uint32_t* row = keys + (size_t)q * stride;
+    if (threadIdx.x == 0) { s_na = 0; s_nc = 0; }
+    uint32_t b1, nabove;
+    find_digit_4096<kSelThreads>(hist + (size_t)q * kHistBins, (uint32_t)K, s_tmp, b1, nabove);
+    // 32 keys per thread per pass (8 uint4 loads in flight)
+    constexpr int kVec = 8;
+    for (int base = 0; base < n; base += 4 * kVec * kSelThreads) {
+        uint4 v[kVec];
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int e = base + 4 * (threadIdx.x + kSelThreads * j);
+            v[j] = e < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int e = base + 4 * (threadIdx.x + kSelThreads * j);
+            const uint32_t kk[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t d = kk[x] >> kDigitShift;
+                if (e + x < n && d > b1) {
+                    const uint32_t p = atomicAdd(&s_na, 1u);
+                    if (p < (uint32_t)K) s_out[p] = e + x;
+                } else if (e + x < n && d == b1) {
+                    const uint32_t p = atomicAdd(&s_nc, 1u);
+                    if (p < (uint32_t)kRankMax) s_cand[p] = comp_key(kk[x], (uint32_t)(e + x));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t NA = min(s_na, (uint32_t)K - 1u), NC = s_nc;
+    if (NC > (uint32_t)kRankMax) {
+        select_global_row<kSelThreads>(row, n, K, o, s_hist, s_dig, s_tmp);
+        return;
+    }
+    pick_lds_candidates(s_cand, NC, (uint32_t)K - NA, NA, s_out, s_hist, s_dig, &s_count);
     rank_and_write(s_out, K, K, o);
 }
 
@@ -645,8 +827,8 @@ __global__ __launch_bounds__(256) void k_prefill_scores(
 // Exact Top-K of one row of score keys (prefill: one workgroup per query):
 // a 4096-bin LDS histogram of the top 12 bits finds the bin b1 of the K-th
 // key; a second pass over the row keeps the keys above b1 and collects the
-// keys in b1; the best of those are picked by direct ranking.  More than
-// kRankMax keys in b1 falls back to the exact whole-row select.
+// keys in b1, of which the best are picked in LDS.  More than kRankMax keys
+// in b1 falls back to the exact whole-row select.
 __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __restrict__ keys,
                                                             int64_t stride,
                                                             const int32_t* __restrict__ q_nvis,
@@ -657,7 +839,7 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
-    __shared__ uint32_t s_na, s_nc;
+    __shared__ uint32_t s_na, s_nc, s_count;
     const int q = blockIdx.x;
     const int n = min(q_nvis[q], (int)stride);
     int32_t* o = out + (size_t)q * K;
@@ -691,20 +873,7 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
         select_global_row<kSelThreads>(row, n, K, o, s_hist, s_dig, s_tmp);
         return;
     }
-    const uint32_t need = (uint32_t)K - NA;
-    if (threadIdx.x == 0) s_cand[NC] = 0ull;
-    __syncthreads();
-    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s_cand);
-    for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) {
-        const uint64_t ci = s_cand[i];
-        uint32_t r = 0;
-        for (int j = 0; j < ((int)NC + 1) / 2; ++j) {
-            const ulonglong2 w = c2[j];
-            r += (w.x > ci) + (w.y > ci);
-        }
-        if (r < need) s_out[NA + r] = (int32_t)comp_idx(ci);
-    }
-    __syncthreads();
+    pick_lds_candidates(s_cand, NC, (uint32_t)K - NA, NA, s_out, s_hist, s_dig, &s_count);
     rank_and_write(s_out, K, K, o);
 }
 
@@ -909,28 +1078,32 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
 #undef CSA2_STREAM
         if (st) return st;
     }
+    // selection of one row per query: a single workgroup for short rows,
+    // filter + finalize otherwise
+    auto select = [&](bool blocks, uint32_t* keys, int64_t stride, int bsl, int nmax, int K,
+                      uint32_t* hist, uint32_t* cnt, int32_t* above, uint64_t* cand,
+                      int32_t* out) -> int {
+        if (nmax <= kSmallRow)
+            return CSA2_LAUNCH(blocks ? "select_small_b" : "select_small", k_select_small,
+                               dim3(Q), dim3(kSelThreads), s, keys, stride, q_nvis, bsl, K,
+                               hist, out);
+        dim3 g((nmax + kSelElems - 1) / kSelElems, Q);
+        int r = CSA2_LAUNCH(blocks ? "filter_b" : "filter", k_filter, g, dim3(256), s, keys,
+                            stride, q_nvis, bsl, K, hist, cnt, above, cand);
+        if (r) return r;
+        return CSA2_LAUNCH(blocks ? "finalize_b" : "finalize", k_finalize, dim3(Q),
+                           dim3(kSelThreads), s, keys, stride, q_nvis, bsl, K, cnt, above, cand,
+                           out);
+    };
     if (topk > 0) {
-        if (max_nvis > 0) {
-            dim3 g((max_nvis + kSelElems - 1) / kSelElems, Q);
-            st = CSA2_LAUNCH("filter", k_filter, g, dim3(256), s, w.keys_e, w.se, q_nvis, 0, topk,
-                             w.hist_e, w.cnt_e, w.above_e, w.cand_e);
-            if (st) return st;
-        }
-        st = CSA2_LAUNCH("finalize", k_finalize, dim3(Q), dim3(kSelThreads), s, w.keys_e, w.se,
-                         q_nvis, 0, topk, w.cnt_e, w.above_e, w.cand_e, topk_idx);
+        st = select(false, w.keys_e, w.se, 0, max_nvis, topk, w.hist_e, w.cnt_e, w.above_e, w.cand_e,
+                    topk_idx);
         if (st) return st;
     }
     if (pool_blocks > 0) {
         const int nb = (max_nvis + block_size - 1) / block_size;
-        if (nb > 0) {
-            dim3 g((nb + kSelElems - 1) / kSelElems, Q);
-            st = CSA2_LAUNCH("filter", k_filter, g, dim3(256), s, w.keys_b, w.sb, q_nvis, bs_log2,
-                             pool_blocks, w.hist_b, w.cnt_b, w.above_b, w.cand_b);
-            if (st) return st;
-        }
-        st = CSA2_LAUNCH("finalize", k_finalize, dim3(Q), dim3(kSelThreads), s, w.keys_b, w.sb,
-                         q_nvis, bs_log2, pool_blocks, w.cnt_b, w.above_b, w.cand_b,
-                         pool_block_idx);
+        st = select(true, w.keys_b, w.sb, bs_log2, nb, pool_blocks, w.hist_b, w.cnt_b, w.above_b,
+                    w.cand_b, pool_block_idx);
         if (st) return st;
     }
     return CSA2_OK;

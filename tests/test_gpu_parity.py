@@ -275,3 +275,75 @@ def test_prefill_window_before_position_zero(csa2):
     ro, rl = C.oracle_prefill_rows(w, 0, ref, list(range(w.Qn)))
     C.assert_attn_close(out.cpu().numpy(), ro, "prefill near position 0")
     C.assert_lse_close(lse.cpu().numpy(), rl, "prefill near position 0")
+
+
+def test_index_long_rows_filter_paths(csa2):
+    # rows longer than one selecting workgroup reads: the multi-workgroup
+    # filter + finalize, with heavy ties (values in [-1, 1]) and with all-equal
+    # scores (the whole-row fallback)
+    w = _edge([150000, 140001], topk=512)
+    t = build_device(w, layers=0, with_kv=False)
+    n = sum(w.ctx) * w.row_width
+    kI = torch.from_numpy(host_ints(78, 1, 0, n, -1, 1).reshape(-1, w.Hk, w.Di)).cuda()
+    qI = torch.from_numpy(host_ints(78, 2, 0, w.B * w.Hi * w.Di, -1, 1).reshape(w.B, w.Hi, w.Di)).cuda()
+    t["kI"] = kI
+    idx, pool = C.gpu_index_full(w, t, qI=qI, pool_blocks=2048)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    kh, qh = kI.cpu().numpy(), qI.cpu().numpy()
+    for b in range(w.B):
+        off = int(w.seq_row_off[b])
+        r, p = oracle.index_full(qh[b:b + 1], kh[off:off + w.ctx[b]], [0], [0], [w.ctx[b]], w.Hi,
+                                 w.Hk, w.Di, 512, 2048, 8)
+        assert np.array_equal(idx[b], r[0]) and np.array_equal(pool[b], p[0]), f"query {b}"
+    zero = torch.zeros_like(qI)
+    idx, pool = C.gpu_index_full(w, t, qI=zero, pool_blocks=2048)
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(512), (2, 1)))
+    assert np.array_equal(pool.cpu().numpy(), np.tile(np.arange(2048), (2, 1)))
+
+
+def test_index_candidate_radix_paths(csa2):
+    # integer scores in a narrow range put several hundred to a thousand keys
+    # into the K-th key's histogram bin: the candidates are then picked by the
+    # radix select (from global memory after the multi-workgroup filter for
+    # the two long rows, from LDS in the one-workgroup select for the short
+    # row and the block rows), and Top-2048 lists are ordered by the bitonic
+    # sort
+    w = _edge([200000, 70000, 60000], topk=2048)
+    t = build_device(w, layers=0, with_kv=False)
+    n = sum(w.ctx) * w.row_width
+    kI = torch.from_numpy(host_ints(80, 1, 0, n, -2, 2).reshape(-1, w.Hk, w.Di)).cuda()
+    qI = torch.from_numpy(host_ints(80, 2, 0, w.B * w.Hi * w.Di, -2, 2).reshape(w.B, w.Hi, w.Di)).cuda()
+    t["kI"] = kI
+    idx, pool = C.gpu_index_full(w, t, qI=qI, pool_blocks=2048)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    kh, qh = kI.cpu().numpy(), qI.cpu().numpy()
+    for b in range(w.B):
+        off = int(w.seq_row_off[b])
+        r, p = oracle.index_full(qh[b:b + 1], kh[off:off + w.ctx[b]], [0], [0], [w.ctx[b]], w.Hi,
+                                 w.Hk, w.Di, 2048, 2048, 8)
+        assert np.array_equal(idx[b], r[0]), f"Top-K of query {b}"
+        assert np.array_equal(pool[b], p[0]), f"pool of query {b}"
+
+
+def test_prefill_indexer_general_fp32_inputs(csa2):
+    # inputs that are not exact in bf16 take the hi/lo split path; the
+    # selection must be the oracle's except for entries whose exact score is
+    # within the path's rounding of the K-th score
+    w = Workload("prefill_fp32", 11, "prefill", [3000], topk=64, layers=0, p0=4000, Qn=40, m=2)
+    t = build_device(w, with_kv=False, layers=0)
+    kI = (host_ints(79, 1, 0, w.rows * w.row_width) / 3.0).astype(np.float32).reshape(-1, w.Hk, w.Di)
+    qI = (host_ints(79, 2, 0, w.Qn * w.Hi * w.Di) / 7.0).astype(np.float32).reshape(w.Qn, w.Hi, w.Di)
+    t["kI"] = torch.from_numpy(kI).cuda()
+    idx, _ = C.gpu_index_full(w, t, qI=torch.from_numpy(qI).cuda())
+    idx = idx.cpu().numpy()
+    nv = w.q_nvis()
+    ref, _ = oracle.index_full(qI, kI, [0], np.zeros(w.Qn, np.int32), nv, w.Hi, w.Hk, w.Di, w.topk)
+    for i in range(w.Qn):
+        s = oracle.scores(qI, kI, [0], np.zeros(w.Qn, np.int32), nv, i, w.Hi, w.Hk, w.Di)
+        g = idx[i]
+        assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[:min(w.topk, nv[i])] >= 0)
+        kth = np.sort(s)[::-1][min(w.topk, nv[i]) - 1]
+        eps = 1e-3 * np.abs(s).max()
+        gsel, rsel = set(g[g >= 0].tolist()), set(ref[i][ref[i] >= 0].tolist())
+        assert all(s[j] >= kth - eps for j in gsel - rsel), f"query {i}"
+        assert all(s[j] <= kth + eps for j in rsel - gsel), f"query {i}"
