@@ -9,13 +9,17 @@
 //
 // Structure on the GPU.  64 heads share one 512-channel key set per query,
 // so S = Q K^T (over channels) and O = P V (over keys) are dense
-// contractions; they run on the bf16 matrix cores (V_MFMA_F32_32X32X16_BF16)
-// at fp32 accuracy:
-//   - dequantised K and V are exact in bf16 (an E2M1 value times an E4M3
-//     scale has at most 6 significant bits; E4M3 itself has 4);
-//   - the fp32 query and the fp32 probabilities are split into three bf16
-//     parts (x = x1 + x2 + x3 to 24 bits), each multiplied exactly and
-//     accumulated in fp32.
+// contractions; they run on the fp16 matrix cores (V_MFMA_F32_32X32X16_F16)
+// at close to fp32 accuracy:
+//   - dequantised K and V are exact in fp16 (an E2M1 value times an E4M3
+//     scale has at most 6 significant bits and lies in [2^-10, 2688]; E4M3
+//     itself has 4 bits and lies in [2^-9, 448]);
+//   - the fp32 query and the fp32 probabilities are split into two fp16
+//     parts (x = x1 + x2, relative residual about 2^-22), each multiplied
+//     exactly and accumulated in fp32.  The query slice of each head and
+//     channel quarter is first scaled by a power of two that puts its largest
+//     element in [2^13, 2^14), so both parts stay in fp16's normal range; the
+//     partial logits are scaled back exactly.
 // Work split: a workgroup (8 waves, 2 per SIMD) owns one query token, 64
 // heads and a range of 32-key tiles.  Wave w handles heads 32*(w&1).. and
 // channels 128*(w>>1)..; the four channel quarters add their partial logits
@@ -36,7 +40,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 512;
 constexpr int kTK = 32;             // keys per tile
@@ -58,148 +62,181 @@ struct AttnArgs {
     int64_t p0;                  // prefill: position of query 0
     int prefill;
     int ntiles_main, ntiles, tiles_per_split, nsplit;
+    int nsplit_main;             // splits [0, nsplit_main) cover main-KV tiles only
     float* out;                  // [rows_q, H, D]
     float* lse;                  // [rows_q, H] or nullptr
     float* part_o;               // [nsplit, rows_q, H, D] (nsplit > 1)
     float* part_ml;              // [nsplit, rows_q, H, 2]
 };
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 typedef float f32x2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 
-// Two fp32 values -> one dword of two bf16 (round to nearest even; one
-// v_cvt_pk_bf16_f32).  Element a lands in the low half.
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-    const bf16x2v r = __builtin_convertvector((f32x2v){a, b}, bf16x2v);
+// Two fp32 values -> one dword of two fp16 (element a in the low half).
+__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
+    const f16x2v r = __builtin_convertvector((f32x2v){a, b}, f16x2v);
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Pair (a, b) -> three packed bf16 pairs with a == p0.lo + p1.lo + p2.lo and
-// b == p0.hi + p1.hi + p2.hi to fp32 precision (each residual is exact).
-__device__ __forceinline__ void split3_pk(float a, float b, uint32_t& p0, uint32_t& p1,
-                                          uint32_t& p2) {
-    p0 = cvt_pk_bf16(a, b);
-    a -= __uint_as_float(p0 << 16);
-    b -= __uint_as_float(p0 & 0xFFFF0000u);
-    p1 = cvt_pk_bf16(a, b);
-    a -= __uint_as_float(p1 << 16);
-    b -= __uint_as_float(p1 & 0xFFFF0000u);
-    p2 = cvt_pk_bf16(a, b);
+__device__ __forceinline__ float2 f16pk_to_f32(uint32_t p) {
+    const f32x2v r = __builtin_convertvector(__builtin_bit_cast(f16x2v, p), f32x2v);
+    return make_float2(r[0], r[1]);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+// Pair (a, b) -> two packed fp16 pairs with a == p0.lo + p1.lo and
+// b == p0.hi + p1.hi up to the rounding of the (exact) residual to fp16.
+__device__ __forceinline__ void split2_pk(float a, float b, uint32_t& p0, uint32_t& p1) {
+    p0 = cvt_pk_f16(a, b);
+    const float2 h = f16pk_to_f32(p0);
+    p1 = cvt_pk_f16(a - h.x, b - h.y);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
     const uint32_t w[4] = {w0, w1, w2, w3};
-    return __builtin_bit_cast(bf16x8, w);
+    return __builtin_bit_cast(f16x8, w);
 }
 
 constexpr int kAttnThreads = 512;   // 8 waves
 
-// Raw bytes of one tile for one thread: 1 item of 4 keys x 8 channels.
-// Main keys: k.x = 4 code bytes (8 channels), k.y = scale byte.  Window
-// keys: k = 8 K bytes, v = 8 V bytes.
-struct TileRaw {
-    uint2 k[1][4];
-    uint2 v[1][4];
-    uint32_t ok[1];   // bit j: key 4*kq + j is real
+// Raw bytes of one tile for one thread: 4 keys x 8 channels (item mapping:
+// channels 8*(thread & 63) .. +8, keys 4*(thread >> 6) .. +4, so consecutive
+// threads write consecutive 16 B of a K row and V rows land 2 banks apart).
+// Main-KV tiles and window tiles keep their bytes in separate registers, so
+// that a gather in flight is never copied (and so never waited for) where the
+// two kinds of tile meet.
+struct RawMain {
+    uint32_t code[4];    // 8 E2M1 codes of key j
+    uint32_t scale[4];   // its E4M3 scale byte
+    uint32_t ok;         // bit j: key j is real
+};
+struct RawWin {
+    uint2 k[4], v[4];    // 8 E4M3 bytes of K and of V of key j
+    uint32_t ok;
 };
 
-// Item i of a tile: channels 8*(i & 63) .. +8, keys 4*(i >> 6) .. +4 (consecutive
-// threads write consecutive 16 B of a K row; V rows land 2 banks apart).
-// The main-KV indices of this thread's 4 keys of tile t: from `idxp` (the
-// tile's first slot; slots >= nslots are padding).
+// The main-KV indices of this thread's 4 keys of a tile: from `idxp` (the
+// tile's first slot; slots >= nslots >= 1 are padding).  The loads are
+// unconditional (clamped slot) so that they issue back to back.
 __device__ __forceinline__ void tile_idx(const int32_t* idxp, int nslots, int32_t (&idx)[4]) {
     const int kq = threadIdx.x >> 6;
+    int32_t v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) idx[j] = 4 * kq + j < nslots ? idxp[4 * kq + j] : -1;
+    for (int j = 0; j < 4; ++j) v[j] = idxp[min(4 * kq + j, nslots - 1)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) idx[j] = 4 * kq + j < nslots ? v[j] : -1;
 }
 
-// Global loads of tile t (issued early; consumed by store_tile).
-__device__ __forceinline__ void fetch_tile(const AttnArgs& a, const int32_t (&idx)[4], int64_t row0,
-                                           int wlo, int whi, int t, TileRaw& r) {
-    const bool main = t < a.ntiles_main;
-    const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
-    r.ok[0] = 0;
+// Byte range of the main-KV buffer resources: a sequence's rows are read at
+// offsets below 2^31 (fewer than 2^23 entries per sequence); a larger offset
+// is outside the resource and reads 0 without touching memory.
+constexpr uint32_t kKvRange = 0x80000000u;
+constexpr int kBufFlags = 0x00020000;   // raw 32-bit buffer (gfx9 family)
+
+// Gather of a main-KV tile (issued early; consumed by store_main) through
+// buffer resources based at the sequence's first row: a padding key's offset
+// is out of range, so every load issues back to back with no branch.
+__device__ __forceinline__ void fetch_main(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                           const int32_t (&idx)[4], RawMain& r) {
+    const int c8 = threadIdx.x & 63;
+    uint32_t ok = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int key = 4 * kq + j;
-        r.k[0][j] = make_uint2(0, 0);
-        r.v[0][j] = make_uint2(0, 0);
-        if (main) {
-            if (idx[j] >= 0) {
-                const int64_t row = row0 + idx[j];
-                r.k[0][j].x = *reinterpret_cast<const uint32_t*>(a.kv_codes + row * (kD / 2) + 4 * c8);
-                r.k[0][j].y = a.kv_scales[row * (kD / 16) + (c8 >> 1)];
-                r.ok[0] |= 1u << j;
-            }
-        } else {
-            const int w_ = kTK * (t - a.ntiles_main) + key;
-            if (w_ >= wlo && w_ < whi) {
-                const size_t off = (size_t)w_ * kD + 8 * c8;
-                r.k[0][j] = *reinterpret_cast<const uint2*>(a.swa_k + off);
-                r.v[0][j] = *reinterpret_cast<const uint2*>(a.swa_v + off);
-                r.ok[0] |= 1u << j;
-            }
-        }
+        const bool v = idx[j] >= 0;
+        ok |= (v ? 1u : 0u) << j;
+        const uint32_t oc = v ? (uint32_t)idx[j] * (kD / 2) + 4 * c8 : kKvRange;
+        const uint32_t os = v ? (uint32_t)idx[j] * (kD / 16) + (c8 >> 1) : kKvRange;
+        r.code[j] = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, 0);
+        r.scale[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
     }
+    r.ok = ok;
 }
 
-// Dequantises the fetched tile to bf16 (exactly) into sK (row-major K) and
-// sVt (transposed V); sValid[k] = 1 for a real key, 0 for padding.
-__device__ __forceinline__ void store_tile(bool main, const TileRaw& r, uint16_t* sK,
-                                           uint16_t* sVt, int* sValid) {
+// Gather of window tile tw (rows 32 tw ..): rows outside [wlo, whi) are
+// masked; rows past the window read its last row instead.
+__device__ __forceinline__ void fetch_win(const uint8_t* swk, const uint8_t* swv, int W, int wlo,
+                                          int whi, int tw, RawWin& r) {
+    const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
+    uint32_t ok = 0;
 #pragma unroll
-    for (int it = 0; it < 1; ++it) {
-        const int item = threadIdx.x + kAttnThreads * it;
-        const int c8 = item & 63, kq = item >> 6;
-        uint32_t vp[4][4];   // bf16 pairs of V, [key][channel pair]
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t kp[4];
-            if (main) {
-                const uint32_t w = r.k[it][j].x;
-                const float sc = e4m3_to_f32(r.k[it][j].y);
-                const float2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
-                const float2 p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
-                kp[0] = cvt_pk_bf16(p0.x * sc, p0.y * sc);
-                kp[1] = cvt_pk_bf16(p1.x * sc, p1.y * sc);
-                kp[2] = cvt_pk_bf16(p2.x * sc, p2.y * sc);
-                kp[3] = cvt_pk_bf16(p3.x * sc, p3.y * sc);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) vp[j][x] = kp[x];
-            } else {
-                const uint2 kw = r.k[it][j], vw = r.v[it][j];
-                const float2 k0 = fp8x2_to_f32<false>(kw.x), k1 = fp8x2_to_f32<true>(kw.x);
-                const float2 k2 = fp8x2_to_f32<false>(kw.y), k3 = fp8x2_to_f32<true>(kw.y);
-                const float2 v0 = fp8x2_to_f32<false>(vw.x), v1 = fp8x2_to_f32<true>(vw.x);
-                const float2 v2 = fp8x2_to_f32<false>(vw.y), v3 = fp8x2_to_f32<true>(vw.y);
-                kp[0] = cvt_pk_bf16(k0.x, k0.y); kp[1] = cvt_pk_bf16(k1.x, k1.y);
-                kp[2] = cvt_pk_bf16(k2.x, k2.y); kp[3] = cvt_pk_bf16(k3.x, k3.y);
-                vp[j][0] = cvt_pk_bf16(v0.x, v0.y); vp[j][1] = cvt_pk_bf16(v1.x, v1.y);
-                vp[j][2] = cvt_pk_bf16(v2.x, v2.y); vp[j][3] = cvt_pk_bf16(v3.x, v3.y);
-            }
-            *reinterpret_cast<uint4*>(sK + (4 * kq + j) * kKStr + 8 * c8) =
-                make_uint4(kp[0], kp[1], kp[2], kp[3]);
-        }
-        // transposed V: row = channel, 4 consecutive keys per 8-byte store
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            // channel pair x: low halves are channel 2x, high halves 2x + 1
-            const uint32_t lo01 = (vp[0][x] & 0xFFFFu) | (vp[1][x] << 16);
-            const uint32_t lo23 = (vp[2][x] & 0xFFFFu) | (vp[3][x] << 16);
-            const uint32_t hi01 = (vp[0][x] >> 16) | (vp[1][x] & 0xFFFF0000u);
-            const uint32_t hi23 = (vp[2][x] >> 16) | (vp[3][x] & 0xFFFF0000u);
-            *reinterpret_cast<uint2*>(sVt + (8 * c8 + 2 * x) * kVStr + 4 * kq) = make_uint2(lo01, lo23);
-            *reinterpret_cast<uint2*>(sVt + (8 * c8 + 2 * x + 1) * kVStr + 4 * kq) = make_uint2(hi01, hi23);
-        }
-        if (c8 == 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sValid[4 * kq + j] = (r.ok[it] >> j) & 1u;
-        }
+    for (int j = 0; j < 4; ++j) {
+        const int w_ = kTK * tw + 4 * kq + j;
+        ok |= (w_ >= wlo && w_ < whi ? 1u : 0u) << j;
+        const size_t off = (size_t)min(w_, W - 1) * kD + 8 * c8;
+        r.k[j] = *reinterpret_cast<const uint2*>(swk + off);
+        r.v[j] = *reinterpret_cast<const uint2*>(swv + off);
     }
+    r.ok = ok;
+}
+
+// Writes one thread's 4 keys (fp16 pairs kp[j][x] = channels 2x, 2x+1 of the
+// thread's 8) to sK (row-major K) and sVt (transposed V), and the keys'
+// validity to sValid (byte g holds keys 4g..4g+3 in bits 0..3).
+__device__ __forceinline__ void put_tile(const uint32_t (&kp)[4][4], const uint32_t (&vp)[4][4],
+                                         uint32_t ok, uint16_t* sK, uint16_t* sVt, uint8_t* sValid) {
+    const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(sK + (4 * kq + j) * kKStr + 8 * c8) =
+            make_uint4(kp[j][0], kp[j][1], kp[j][2], kp[j][3]);
+    // transposed V: row = channel, 4 consecutive keys per 8-byte store
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        // channel pair x: low halves are channel 2x, high halves 2x + 1
+        const uint32_t lo01 = (vp[0][x] & 0xFFFFu) | (vp[1][x] << 16);
+        const uint32_t lo23 = (vp[2][x] & 0xFFFFu) | (vp[3][x] << 16);
+        const uint32_t hi01 = (vp[0][x] >> 16) | (vp[1][x] & 0xFFFF0000u);
+        const uint32_t hi23 = (vp[2][x] >> 16) | (vp[3][x] & 0xFFFF0000u);
+        *reinterpret_cast<uint2*>(sVt + (8 * c8 + 2 * x) * kVStr + 4 * kq) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(sVt + (8 * c8 + 2 * x + 1) * kVStr + 4 * kq) = make_uint2(hi01, hi23);
+    }
+    if (c8 == 0) sValid[kq] = (uint8_t)(ok & 15u);
+}
+
+// Dequantises a main-KV tile to fp16 (exactly; K = V) into LDS.
+__device__ __forceinline__ void store_main(const RawMain& r, uint16_t* sK, uint16_t* sVt,
+                                           uint8_t* sValid) {
+    uint32_t kp[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool ok = (r.ok >> j) & 1u;
+        const uint32_t w = r.code[j];
+        const float sc = e4m3_to_f32(r.scale[j]);
+        const float2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
+        const float2 p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
+        kp[j][0] = ok ? cvt_pk_f16(p0.x * sc, p0.y * sc) : 0u;
+        kp[j][1] = ok ? cvt_pk_f16(p1.x * sc, p1.y * sc) : 0u;
+        kp[j][2] = ok ? cvt_pk_f16(p2.x * sc, p2.y * sc) : 0u;
+        kp[j][3] = ok ? cvt_pk_f16(p3.x * sc, p3.y * sc) : 0u;
+    }
+    put_tile(kp, kp, r.ok, sK, sVt, sValid);
+}
+
+// Converts a window tile (E4M3 K and V, exact in fp16) into LDS.
+__device__ __forceinline__ void store_win(const RawWin& r, uint16_t* sK, uint16_t* sVt,
+                                          uint8_t* sValid) {
+    uint32_t kp[4][4], vp[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool ok = (r.ok >> j) & 1u;
+        const uint2 kw = r.k[j], vw = r.v[j];
+        const float2 k0 = fp8x2_to_f32<false>(kw.x), k1 = fp8x2_to_f32<true>(kw.x);
+        const float2 k2 = fp8x2_to_f32<false>(kw.y), k3 = fp8x2_to_f32<true>(kw.y);
+        const float2 v0 = fp8x2_to_f32<false>(vw.x), v1 = fp8x2_to_f32<true>(vw.x);
+        const float2 v2 = fp8x2_to_f32<false>(vw.y), v3 = fp8x2_to_f32<true>(vw.y);
+        kp[j][0] = ok ? cvt_pk_f16(k0.x, k0.y) : 0u;
+        kp[j][1] = ok ? cvt_pk_f16(k1.x, k1.y) : 0u;
+        kp[j][2] = ok ? cvt_pk_f16(k2.x, k2.y) : 0u;
+        kp[j][3] = ok ? cvt_pk_f16(k3.x, k3.y) : 0u;
+        vp[j][0] = ok ? cvt_pk_f16(v0.x, v0.y) : 0u;
+        vp[j][1] = ok ? cvt_pk_f16(v1.x, v1.y) : 0u;
+        vp[j][2] = ok ? cvt_pk_f16(v2.x, v2.y) : 0u;
+        vp[j][3] = ok ? cvt_pk_f16(v3.x, v3.y) : 0u;
+    }
+    put_tile(kp, vp, r.ok, sK, sVt, sValid);
 }
 
 // Rescale threshold (log2 units): the running maximum used for the
@@ -211,7 +248,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[kTK * kKStr];
     __shared__ __attribute__((aligned(16))) uint16_t sVt[kD * kVStr];
     __shared__ __attribute__((aligned(16))) float4 sS[8][4][64];   // partial logits per wave
-    __shared__ int sValid[kTK];
+    __shared__ __attribute__((aligned(8))) uint8_t sValid[kTK / 4];
     __shared__ int32_t s_idx[CSA2_MAX_TOPK];
 
     const int split = blockIdx.x;
@@ -224,67 +261,110 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     const bool active = blockIdx.y * 64 + hg * 32 < a.H;   // wave-uniform
     const int cbase = 128 * cq;
 
-    int64_t row0 = 0;
+    int64_t row0 = 0;   // first main-KV row of this query's sequence
     int wlo = 0, whi = 0;
+    const uint8_t *swk, *swv;
     if (a.prefill) {
         const int64_t p = a.p0 + qi;
         wlo = (int)max((int64_t)0, (int64_t)(a.W - 1) - p);
         whi = a.W;
+        swk = a.swa_k + (size_t)qi * kD;
+        swv = a.swa_v + (size_t)qi * kD;
     } else {
         row0 = a.seq_row_off[qi];
         whi = min(a.swa_len[qi], a.W);
+        swk = a.swa_k + (size_t)qi * a.W * kD;
+        swv = a.swa_v + (size_t)qi * a.W * kD;
     }
-    AttnArgs aa = a;
-    if (a.prefill) {
-        aa.swa_k = a.swa_k + (size_t)qi * kD;
-        aa.swa_v = a.swa_v + (size_t)qi * kD;
+    // tile range: with several splits, each holds main-KV tiles only or
+    // window tiles only; a single split holds all tiles
+    int t0, t1;
+    if (a.nsplit == 1) {
+        t0 = 0;
+        t1 = a.ntiles;
+    } else if (split < a.nsplit_main) {
+        t0 = split * a.tiles_per_split;
+        t1 = min(a.ntiles_main, t0 + a.tiles_per_split);
     } else {
-        aa.swa_k = a.swa_k + (size_t)qi * a.W * kD;
-        aa.swa_v = a.swa_v + (size_t)qi * a.W * kD;
+        t0 = a.ntiles_main + (split - a.nsplit_main) * a.tiles_per_split;
+        t1 = min(a.ntiles, t0 + a.tiles_per_split);
     }
-    const int t0 = split * a.tiles_per_split;
-    const int t1 = min(a.ntiles, t0 + a.tiles_per_split);
+    const int tm = min(t1, a.ntiles_main);           // main tiles are [t0, tm)
     const int32_t* qidx = a.topk_idx + (size_t)qi * a.topk;
-    // Prologue: the first tile's indices (global), the split's index staging
-    // and the query slice are all requested before any of them is used.
-    TileRaw raw;
-    int32_t idx[4] = {-1, -1, -1, -1};
-    if (t0 < a.ntiles_main) tile_idx(qidx + kTK * t0, a.topk - kTK * t0, idx);
-    const int nslot = kTK * (min(t1, a.ntiles_main) - t0);
-    int32_t stage[CSA2_MAX_TOPK / kAttnThreads];
+    const __amdgpu_buffer_rsrc_t rcode = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.kv_codes + row0 * (kD / 2)), (short)0, (int)kKvRange, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rscale = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.kv_scales + row0 * (kD / 16)), (short)0, (int)kKvRange, kBufFlags);
+    // Prologue, in issue order: the first tile's indices, the query slice
+    // (16 loads per lane), the split's index staging; then the first gather
+    // once its indices are in.
+    RawMain rm;
+    RawWin rw;
+    const int nslot = kTK * (tm - t0);
+    // the query's Top-K row as a buffer resource: slots past topk read 0
+    // (and are masked), so no prologue load sits under a branch
+    const __amdgpu_buffer_rsrc_t ridx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)qidx, (short)0, a.topk * 4, kBufFlags);
+    const int kq = threadIdx.x >> 6;
+    int32_t idx0[4];
 #pragma unroll
-    for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i) {
-        const int k = threadIdx.x + kAttnThreads * i;
-        const int slot = kTK * t0 + k;
-        stage[i] = (k < nslot && slot < a.topk) ? qidx[slot] : -1;
-    }
-    if (t0 < t1) fetch_tile(aa, idx, row0, wlo, whi, t0, raw);
-#pragma unroll
-    for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i) {
-        const int k = threadIdx.x + kAttnThreads * i;
-        if (k < nslot) s_idx[k] = stage[i];
-    }
-
-    // query slice in three bf16 parts: step s (16 channels) of this lane is
-    // channels cbase + 16 s + 8 hh .. +8 of head h
-    bf16x8 q0[8], q1[8], q2[8];
+    for (int j = 0; j < 4; ++j)
+        idx0[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, (kTK * t0 + 4 * kq + j) * 4, 0, 0);
+    // query slice in two fp16 parts after a power-of-two scaling: step s (16
+    // channels) of this lane is channels cbase + 16 s + 8 hh .. +8 of head h
+    f16x8 q0[8], q1[8];
+    float qunscale;   // exact inverse of the scaling, applied to the partial logits
     {
         const float* qp = a.q + ((size_t)qi * a.H + (hvalid ? h : 0)) * kD + cbase + 8 * hh;
+        // head 0 stands in for a padding head (zeroed below)
+        float4 xq[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            xq[i] = *reinterpret_cast<const float4*>(qp + 16 * (i >> 1) + 4 * (i & 1));
+        // the index values are first used after every query load has issued
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (t0 >= tm || kTK * t0 + 4 * kq + j >= a.topk) idx0[j] = -1;
+        int32_t stage[CSA2_MAX_TOPK / kAttnThreads];
+#pragma unroll
+        for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i)
+            stage[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                ridx, (kTK * t0 + (int)threadIdx.x + kAttnThreads * i) * 4, 0, 0);
+        // a window-only split gathers nothing here: all its slots are padding
+        fetch_main(rcode, rscale, idx0, rm);
+
+        // largest magnitude of this head's 128 channels (both lane halves)
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xq[i].x), fabsf(xq[i].y)),
+                                 fmaxf(fabsf(xq[i].z), fabsf(xq[i].w))));
+        if (!hvalid) mx = 0.f;
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        int e = 0;
+        (void)frexpf(mx, &e);                          // mx in [2^(e-1), 2^e)
+        const int sh = mx > 0.f ? 14 - e : 0;          // mx * 2^sh in [2^13, 2^14)
+        const float qscale = ldexpf(1.f, sh);
+        qunscale = ldexpf(1.f, -sh);
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-            if (hvalid) {
-                x0 = *reinterpret_cast<const float4*>(qp + 16 * st);
-                x1 = *reinterpret_cast<const float4*>(qp + 16 * st + 4);
+            float4 x0 = xq[2 * st], x1 = xq[2 * st + 1];
+            if (!hvalid) x0 = x1 = make_float4(0.f, 0.f, 0.f, 0.f);
+            uint32_t a0[4], a1[4];
+            split2_pk(x0.x * qscale, x0.y * qscale, a0[0], a1[0]);
+            split2_pk(x0.z * qscale, x0.w * qscale, a0[1], a1[1]);
+            split2_pk(x1.x * qscale, x1.y * qscale, a0[2], a1[2]);
+            split2_pk(x1.z * qscale, x1.w * qscale, a0[3], a1[3]);
+            q0[st] = as_f16x8(a0[0], a0[1], a0[2], a0[3]);
+            q1[st] = as_f16x8(a1[0], a1[1], a1[2], a1[3]);
+        }
+        if (t0 < tm) {
+#pragma unroll
+            for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i) {
+                const int k = threadIdx.x + kAttnThreads * i;
+                if (k < nslot) s_idx[k] = kTK * t0 + k < a.topk ? stage[i] : -1;
             }
-            uint32_t a0[4], a1[4], a2[4];
-            split3_pk(x0.x, x0.y, a0[0], a1[0], a2[0]);
-            split3_pk(x0.z, x0.w, a0[1], a1[1], a2[1]);
-            split3_pk(x1.x, x1.y, a0[2], a1[2], a2[2]);
-            split3_pk(x1.z, x1.w, a0[3], a1[3], a2[3]);
-            q0[st] = as_bf16x8(a0[0], a0[1], a0[2], a0[3]);
-            q1[st] = as_bf16x8(a1[0], a1[1], a1[2], a1[3]);
-            q2[st] = as_bf16x8(a2[0], a2[1], a2[2], a2[3]);
         }
     }
     f32x16 o[4];
@@ -292,39 +372,34 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     for (int ct = 0; ct < 4; ++ct) o[ct] = f32x16{};
     float m = -INFINITY, l = 0.f;
 
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
-        __syncthreads();   // previous tile's LDS reads are done
-        store_tile(t < a.ntiles_main, raw, sK, sVt, sValid);
-        // next tile's global loads overlap the barrier and this tile's matrix work
-        if (t + 1 < t1) {
-            if (t + 1 < a.ntiles_main) tile_idx(s_idx + kTK * (t + 1 - t0), kTK, idx);
-            fetch_tile(aa, idx, row0, wlo, whi, t + 1, raw);
-        }
-        __syncthreads();
-
-        // partial S^T over this wave's 128 channels (the small query parts
-        // are folded into the same chain, after the main part of each step)
+    // The two matrix products and the softmax of the tile in LDS (entered
+    // after the barrier that publishes it).
+    auto compute = [&]() __attribute__((always_inline)) {
+        // partial S^T over this wave's 128 channels (the small query part is
+        // folded into the same chain, after the main part of each step)
         f32x16 s0 = f32x16{};
         if (active) {
             const uint16_t* kr = sK + l32 * kKStr + cbase + 8 * hh;
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr + 16 * st);
+                const f16x8 ka = *reinterpret_cast<const f16x8*>(kr + 16 * st);
                 s0 = mfma32(ka, q0[st], s0);
                 s0 = mfma32(ka, q1[st], s0);
-                s0 = mfma32(ka, q2[st], s0);
             }
+            s0 = s0 * qunscale;   // lane l32's column is head h: its own scaling
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4)
                 sS[wave][r4][lane] = make_float4(s0[4 * r4], s0[4 * r4 + 1], s0[4 * r4 + 2], s0[4 * r4 + 3]);
         }
         __syncthreads();
-        if (!active) continue;
+        if (!active) return;
         // full logits: the four channel quarters of this head group, added
         // in the same order in every wave
+        // (every read is unconditional; a padding key's zero logit gets -inf
+        // added, so no branch depends on LDS data)
         float z[16];
-        float tm = -INFINITY;
+        float tm_ = -INFINITY;
+        const uint64_t vmask = *reinterpret_cast<const uint64_t*>(sValid);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const float4 c0 = sS[hg][r4][lane], c1 = sS[hg + 2][r4][lane];
@@ -336,14 +411,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
                 const int r = 4 * r4 + i;
                 const int key = 8 * r4 + 4 * hh + i;
                 const float sv = (v0[i] + v1[i]) + (v2[i] + v3[i]);
-                z[r] = sValid[key] ? sv * a.scale_log2 : -INFINITY;
-                tm = fmaxf(tm, z[r]);
+                const uint32_t bit = 8 * (key >> 2) + (key & 3);
+                z[r] = fmaf(sv, a.scale_log2, ((vmask >> bit) & 1u) ? 0.f : -INFINITY);
+                tm_ = fmaxf(tm_, z[r]);
             }
+            // one group of partial-logit reads in flight at a time (registers)
+            __builtin_amdgcn_sched_barrier(0);
         }
-        tm = fmaxf(tm, __shfl_xor(tm, 32));
-        const bool bump = tm > m + kRescale;   // true for any finite tm while m = -inf
+        tm_ = fmaxf(tm_, __shfl_xor(tm_, 32));
+        const bool bump = tm_ > m + kRescale;   // true for any finite tm_ while m = -inf
         if (__ballot(bump)) {
-            const float mn = bump ? tm : m;
+            const float mn = bump ? tm_ : m;
             const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
             l *= alpha;
 #pragma unroll
@@ -351,9 +429,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             m = mn;
         }
         // P^T operands: MFMA u covers registers 8u..8u+7 (keys 16u + 8(j/4) + 4hh + j%4),
-        // each probability split into three bf16 parts
+        // each probability (<= 2^8) split into two fp16 parts
         float ps = 0.f;
-        bf16x8 pp[2][3];
+        f16x8 pp[2][2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             float pv[8];
@@ -363,12 +441,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
                 pv[j] = (zr == -INFINITY) ? 0.f : exp2f(zr - m);
                 ps += pv[j];
             }
-            uint32_t x0[4], x1[4], x2[4];
+            uint32_t x0[4], x1[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) split3_pk(pv[2 * j], pv[2 * j + 1], x0[j], x1[j], x2[j]);
-            pp[u][0] = as_bf16x8(x0[0], x0[1], x0[2], x0[3]);
-            pp[u][1] = as_bf16x8(x1[0], x1[1], x1[2], x1[3]);
-            pp[u][2] = as_bf16x8(x2[0], x2[1], x2[2], x2[3]);
+            for (int j = 0; j < 4; ++j) split2_pk(pv[2 * j], pv[2 * j + 1], x0[j], x1[j]);
+            pp[u][0] = as_f16x8(x0[0], x0[1], x0[2], x0[3]);
+            pp[u][1] = as_f16x8(x1[0], x1[1], x1[2], x1[3]);
         }
         l += ps;
         // O^T[channel cbase + 32 ct + m][head] += V^T P^T over the 32 keys
@@ -379,12 +456,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             for (int u = 0; u < 2; ++u) {
                 const uint2 va = *reinterpret_cast<const uint2*>(vr + 16 * u);
                 const uint2 vb = *reinterpret_cast<const uint2*>(vr + 16 * u + 8);
-                const bf16x8 vv = __builtin_bit_cast(bf16x8, make_uint4(va.x, va.y, vb.x, vb.y));
+                const f16x8 vv = __builtin_bit_cast(f16x8, make_uint4(va.x, va.y, vb.x, vb.y));
                 o[ct] = mfma32(vv, pp[u][0], o[ct]);
                 o[ct] = mfma32(vv, pp[u][1], o[ct]);
-                o[ct] = mfma32(vv, pp[u][2], o[ct]);
             }
         }
+    };
+
+    __syncthreads();   // s_idx staged
+    // main-KV tiles
+    for (int t = t0; t < tm; ++t) {
+        __syncthreads();   // previous tile's LDS reads are done
+        store_main(rm, sK, sVt, sValid);
+        if (t + 1 < tm) {
+            int32_t idx[4];
+            tile_idx(s_idx + kTK * (t + 1 - t0), kTK, idx);
+            fetch_main(rcode, rscale, idx, rm);
+        }
+        __syncthreads();
+        compute();
+    }
+    // window tiles (their first gather is issued here, so that the two raw
+    // buffers are never live together)
+    if (max(t0, a.ntiles_main) < t1)
+        fetch_win(swk, swv, a.W, wlo, whi, max(t0, a.ntiles_main) - a.ntiles_main, rw);
+    for (int t = max(t0, a.ntiles_main); t < t1; ++t) {
+        __syncthreads();
+        store_win(rw, sK, sVt, sValid);
+        if (t + 1 < t1) fetch_win(swk, swv, a.W, wlo, whi, t + 1 - a.ntiles_main, rw);
+        __syncthreads();
+        compute();
     }
     if (!active) return;
     const float lt = l + __shfl_xor(l, 32);
@@ -476,7 +577,7 @@ __global__ void k_decode_tables(float* fp4_hw, float* fp4_ref, float* fp8_hw, fl
 }
 
 struct AttnPlan {
-    int hgroups, ntiles_main, ntiles, nsplit, tps;
+    int hgroups, ntiles_main, ntiles, nsplit, tps, nsplit_main;
     size_t ws_bytes;
 };
 
@@ -496,7 +597,16 @@ int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnP
         if (nsplit > kMaxSplitRegs) nsplit = kMaxSplitRegs;
     }
     p->tps = p->ntiles > 0 ? (p->ntiles + nsplit - 1) / nsplit : 0;
-    if (p->tps > 0) nsplit = (p->ntiles + p->tps - 1) / p->tps;
+    p->nsplit_main = 0;
+    if (nsplit > 1) {
+        // no split straddles the main-KV and window tiles
+        const int nwin = p->ntiles - p->ntiles_main;
+        for (;; ++p->tps) {
+            p->nsplit_main = (p->ntiles_main + p->tps - 1) / p->tps;
+            nsplit = p->nsplit_main + (nwin + p->tps - 1) / p->tps;
+            if (nsplit <= kMaxSplitRegs) break;
+        }
+    }
     p->nsplit = nsplit;
     Carver c(nullptr);
     if (nsplit > 1) {
@@ -512,6 +622,7 @@ int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_q, void* ws, hipStream_
     a.ntiles = pl.ntiles;
     a.tiles_per_split = pl.tps;
     a.nsplit = pl.nsplit;
+    a.nsplit_main = pl.nsplit_main;
     if (pl.nsplit > 1) {
         Carver c(ws);
         a.part_o = c.take<float>((size_t)pl.nsplit * rows_q * a.H * kD);
