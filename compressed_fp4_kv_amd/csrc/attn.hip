@@ -24,12 +24,15 @@
 // heads and a range of 32-key tiles.  Wave w handles heads 32*(w&1).. and
 // channels 128*(w>>1)..; the four channel quarters add their partial logits
 // through LDS in a fixed order, then all run the same softmax and each
-// accumulates its quarter of the output.  Per
-// tile the workgroup dequantises 32 keys into LDS twice: row-major K (A
-// operand of S^T = K Q^T) and transposed V (A operand of O^T = V^T P^T).
-// S^T leaves each lane with 16 keys of one head, exactly the B-operand
-// layout the P V product needs, so P never leaves registers.  Key-range
-// splits across workgroups are merged by k_attn_combine.
+// accumulates its quarter of the output.  A tile is dequantised once into
+// LDS as row-major [key][channel]: it is the A operand of S^T = K Q^T as it
+// stands, and the gfx950 transposed LDS read (ds_read_b64_tr_b16) turns it
+// into the A operand of O^T = V^T P^T.  Main-KV tiles are double-buffered:
+// while the products of tile t read one buffer, tile t+1 is dequantised into
+// the other and tile t+2 is gathered into registers.  S^T leaves each lane
+// with 16 keys of one head, exactly the B-operand layout the P V product
+// needs, so P never leaves registers.  Key-range splits across workgroups
+// are merged by k_attn_combine.
 #include <math.h>
 
 #include "common.hpp"
@@ -44,8 +47,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 512;
 constexpr int kTK = 32;             // keys per tile
-constexpr int kKStr = kD + 8;       // LDS row stride of the K tile (bf16)
-constexpr int kVStr = kTK + 4;      // LDS row stride of the transposed V tile (bf16)
+constexpr int kKStr = kD + 8;       // LDS row stride of a tile (fp16 elements)
+constexpr int kTileElems = kTK * kKStr;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 struct AttnArgs {
@@ -173,38 +176,28 @@ __device__ __forceinline__ void fetch_win(const uint8_t* swk, const uint8_t* swv
 }
 
 // Writes one thread's 4 keys (fp16 pairs kp[j][x] = channels 2x, 2x+1 of the
-// thread's 8) to sK (row-major K) and sVt (transposed V), and the keys'
-// validity to sValid (byte g holds keys 4g..4g+3 in bits 0..3).
-__device__ __forceinline__ void put_tile(const uint32_t (&kp)[4][4], const uint32_t (&vp)[4][4],
-                                         uint32_t ok, uint16_t* sK, uint16_t* sVt, uint8_t* sValid) {
+// thread's 8) as rows of a tile buffer (row-major [key][channel]; the 64
+// lanes of a wave fill one 1 KB row per store).
+__device__ __forceinline__ void put_rows(const uint32_t (&kp)[4][4], uint16_t* buf) {
     const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(sK + (4 * kq + j) * kKStr + 8 * c8) =
+        *reinterpret_cast<uint4*>(buf + (4 * kq + j) * kKStr + 8 * c8) =
             make_uint4(kp[j][0], kp[j][1], kp[j][2], kp[j][3]);
-    // transposed V: row = channel, 4 consecutive keys per 8-byte store
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        // channel pair x: low halves are channel 2x, high halves 2x + 1
-        const uint32_t lo01 = (vp[0][x] & 0xFFFFu) | (vp[1][x] << 16);
-        const uint32_t lo23 = (vp[2][x] & 0xFFFFu) | (vp[3][x] << 16);
-        const uint32_t hi01 = (vp[0][x] >> 16) | (vp[1][x] & 0xFFFF0000u);
-        const uint32_t hi23 = (vp[2][x] >> 16) | (vp[3][x] & 0xFFFF0000u);
-        *reinterpret_cast<uint2*>(sVt + (8 * c8 + 2 * x) * kVStr + 4 * kq) = make_uint2(lo01, lo23);
-        *reinterpret_cast<uint2*>(sVt + (8 * c8 + 2 * x + 1) * kVStr + 4 * kq) = make_uint2(hi01, hi23);
-    }
-    if (c8 == 0) sValid[kq] = (uint8_t)(ok & 15u);
 }
 
-// Dequantises a main-KV tile to fp16 (exactly; K = V) into LDS.
-__device__ __forceinline__ void store_main(const RawMain& r, uint16_t* sK, uint16_t* sVt,
-                                           uint8_t* sValid) {
-    uint32_t kp[4][4];
+// The keys' validity: byte g holds keys 4g..4g+3 in bits 0..3.
+__device__ __forceinline__ void put_valid(uint32_t ok, uint8_t* sValid) {
+    if ((threadIdx.x & 63) == 0) sValid[threadIdx.x >> 6] = (uint8_t)(ok & 15u);
+}
+
+// Dequantises a main-KV tile to fp16 (exactly; K = V).
+__device__ __forceinline__ void dequant_main(const RawMain& r, uint32_t (&kp)[4][4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const bool ok = (r.ok >> j) & 1u;
         const uint32_t w = r.code[j];
-        const float sc = e4m3_to_f32(r.scale[j]);
+        const float sc = fp8x2_to_f32<false>(r.scale[j]).x;   // E4M3 scale byte
         const float2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
         const float2 p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
         kp[j][0] = ok ? cvt_pk_f16(p0.x * sc, p0.y * sc) : 0u;
@@ -212,13 +205,11 @@ __device__ __forceinline__ void store_main(const RawMain& r, uint16_t* sK, uint1
         kp[j][2] = ok ? cvt_pk_f16(p2.x * sc, p2.y * sc) : 0u;
         kp[j][3] = ok ? cvt_pk_f16(p3.x * sc, p3.y * sc) : 0u;
     }
-    put_tile(kp, kp, r.ok, sK, sVt, sValid);
 }
 
-// Converts a window tile (E4M3 K and V, exact in fp16) into LDS.
-__device__ __forceinline__ void store_win(const RawWin& r, uint16_t* sK, uint16_t* sVt,
-                                          uint8_t* sValid) {
-    uint32_t kp[4][4], vp[4][4];
+// Converts a window tile (E4M3 K and V, exact in fp16).
+__device__ __forceinline__ void dequant_win(const RawWin& r, uint32_t (&kp)[4][4],
+                                            uint32_t (&vp)[4][4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const bool ok = (r.ok >> j) & 1u;
@@ -236,7 +227,16 @@ __device__ __forceinline__ void store_win(const RawWin& r, uint16_t* sK, uint16_
         vp[j][2] = ok ? cvt_pk_f16(v2.x, v2.y) : 0u;
         vp[j][3] = ok ? cvt_pk_f16(v3.x, v3.y) : 0u;
     }
-    put_tile(kp, vp, r.ok, sK, sVt, sValid);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// gfx950 transposed LDS read: within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte chunks addressed by lanes i/4, i/4 + 4,
+// i/4 + 8 and i/4 + 12 of the group.
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (v4i16 __attribute__((address_space(3)))*)(p));
 }
 
 // Rescale threshold (log2 units): the running maximum used for the
@@ -245,10 +245,10 @@ __device__ __forceinline__ void store_win(const RawWin& r, uint16_t* sK, uint16_
 constexpr float kRescale = 8.f;
 
 __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kTK * kKStr];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[kD * kVStr];
+    // two tile buffers (main-KV: double buffering; window: K and V)
+    __shared__ __attribute__((aligned(16))) uint16_t sKV[2][kTileElems];
     __shared__ __attribute__((aligned(16))) float4 sS[8][4][64];   // partial logits per wave
-    __shared__ __attribute__((aligned(8))) uint8_t sValid[kTK / 4];
+    __shared__ __attribute__((aligned(8))) uint8_t sValid[2][kTK / 4];
     __shared__ int32_t s_idx[CSA2_MAX_TOPK];
 
     const int split = blockIdx.x;
@@ -306,10 +306,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     const __amdgpu_buffer_rsrc_t ridx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)qidx, (short)0, a.topk * 4, kBufFlags);
     const int kq = threadIdx.x >> 6;
-    int32_t idx0[4];
+    int32_t idx0[4], idx1[4];   // this thread's slots of the first two tiles
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
         idx0[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, (kTK * t0 + 4 * kq + j) * 4, 0, 0);
+        idx1[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, (kTK * (t0 + 1) + 4 * kq + j) * 4, 0, 0);
+    }
     // query slice in two fp16 parts after a power-of-two scaling: step s (16
     // channels) of this lane is channels cbase + 16 s + 8 hh .. +8 of head h
     f16x8 q0[8], q1[8];
@@ -324,8 +326,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         // the index values are first used after every query load has issued
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
             if (t0 >= tm || kTK * t0 + 4 * kq + j >= a.topk) idx0[j] = -1;
+            if (t0 + 1 >= tm || kTK * (t0 + 1) + 4 * kq + j >= a.topk) idx1[j] = -1;
+        }
         int32_t stage[CSA2_MAX_TOPK / kAttnThreads];
 #pragma unroll
         for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i)
@@ -372,34 +376,47 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     for (int ct = 0; ct < 4; ++ct) o[ct] = f32x16{};
     float m = -INFINITY, l = 0.f;
 
-    // The two matrix products and the softmax of the tile in LDS (entered
-    // after the barrier that publishes it).
-    auto compute = [&]() __attribute__((always_inline)) {
-        // partial S^T over this wave's 128 channels (the small query part is
-        // folded into the same chain, after the main part of each step)
+    // S^T of the tile in `kb` over this wave's 128 channels, to sS (the small
+    // query part is folded into the same chain, after the main part of each
+    // step).  Published by the caller's next barrier.
+    // (split in two so that independent work can run while the matrix core
+    // finishes the chain)
+    auto s_issue = [&](const uint16_t* kb) __attribute__((always_inline)) -> f32x16 {
         f32x16 s0 = f32x16{};
-        if (active) {
-            const uint16_t* kr = sK + l32 * kKStr + cbase + 8 * hh;
+        if (!active) return s0;
+        const uint16_t* kr = kb + l32 * kKStr + cbase + 8 * hh;
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const f16x8 ka = *reinterpret_cast<const f16x8*>(kr + 16 * st);
-                s0 = mfma32(ka, q0[st], s0);
-                s0 = mfma32(ka, q1[st], s0);
-            }
-            s0 = s0 * qunscale;   // lane l32's column is head h: its own scaling
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-                sS[wave][r4][lane] = make_float4(s0[4 * r4], s0[4 * r4 + 1], s0[4 * r4 + 2], s0[4 * r4 + 3]);
+        for (int st = 0; st < 8; ++st) {
+            const f16x8 ka = *reinterpret_cast<const f16x8*>(kr + 16 * st);
+            s0 = mfma32(ka, q0[st], s0);
+            s0 = mfma32(ka, q1[st], s0);
         }
-        __syncthreads();
+        return s0;
+    };
+    auto s_finish = [&](f32x16 s0) __attribute__((always_inline)) {
         if (!active) return;
-        // full logits: the four channel quarters of this head group, added
-        // in the same order in every wave
-        // (every read is unconditional; a padding key's zero logit gets -inf
-        // added, so no branch depends on LDS data)
+        s0 = s0 * qunscale;   // lane l32's column is head h: its own scaling
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            sS[wave][r4][lane] = make_float4(s0[4 * r4], s0[4 * r4 + 1], s0[4 * r4 + 2], s0[4 * r4 + 3]);
+    };
+
+    // Lane part of the transposed reads of V: lane l = 16 g + 4 b + c points
+    // at key row 4 (g >> 1) + b, channels cbase + 16 (g & 1) + 4 c .. +3, so
+    // that lane l receives channel cbase + (l & 31) of 4 consecutive keys.
+    const int trbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * kKStr + cbase +
+                       16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    // Softmax of the tile's logits (sS, published) and O^T += V^T P^T with V
+    // the row-major tile in `vb`.
+    auto pv_phase = [&](const uint16_t* vb, const uint8_t* valid) __attribute__((always_inline)) {
+        if (!active) return;
+        // full logits: the four channel quarters of this head group, added in
+        // the same order in every wave (every read is unconditional; a padding
+        // key's zero logit gets -inf added, so no branch depends on LDS data)
         float z[16];
         float tm_ = -INFINITY;
-        const uint64_t vmask = *reinterpret_cast<const uint64_t*>(sValid);
+        const uint64_t vmask = *reinterpret_cast<const uint64_t*>(valid);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const float4 c0 = sS[hg][r4][lane], c1 = sS[hg + 2][r4][lane];
@@ -422,7 +439,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         const bool bump = tm_ > m + kRescale;   // true for any finite tm_ while m = -inf
         if (__ballot(bump)) {
             const float mn = bump ? tm_ : m;
-            const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+            const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
             l *= alpha;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) o[ct] = o[ct] * alpha;
@@ -438,7 +455,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float zr = z[8 * u + j];
-                pv[j] = (zr == -INFINITY) ? 0.f : exp2f(zr - m);
+                // raw v_exp_f32: results below 2^-126 flush to 0 (negligible next
+                // to the tile maximum's 1)
+                pv[j] = (zr == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(zr - m);
                 ps += pv[j];
             }
             uint32_t x0[4], x1[4];
@@ -448,44 +467,70 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             pp[u][1] = as_f16x8(x1[0], x1[1], x1[2], x1[3]);
         }
         l += ps;
-        // O^T[channel cbase + 32 ct + m][head] += V^T P^T over the 32 keys
+        // O^T[channel cbase + 32 ct + m][head] += V^T P^T over the 32 keys;
+        // the A operand's 8 keys are 16u + 4hh + 0..3 and 16u + 8 + 4hh + 0..3
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            const uint16_t* vr = sVt + (cbase + 32 * ct + l32) * kVStr + 4 * hh;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const uint2 va = *reinterpret_cast<const uint2*>(vr + 16 * u);
-                const uint2 vb = *reinterpret_cast<const uint2*>(vr + 16 * u + 8);
-                const f16x8 vv = __builtin_bit_cast(f16x8, make_uint4(va.x, va.y, vb.x, vb.y));
+                const v4i16 lo = lds_read_tr16(vb + trbase + 16 * u * kKStr + 32 * ct);
+                const v4i16 hi = lds_read_tr16(vb + trbase + (16 * u + 8) * kKStr + 32 * ct);
+                const f16x8 vv = __builtin_bit_cast(
+                    f16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                        hi[0], hi[1], hi[2], hi[3]});
                 o[ct] = mfma32(vv, pp[u][0], o[ct]);
                 o[ct] = mfma32(vv, pp[u][1], o[ct]);
             }
         }
     };
 
-    __syncthreads();   // s_idx staged
-    // main-KV tiles
-    for (int t = t0; t < tm; ++t) {
-        __syncthreads();   // previous tile's LDS reads are done
-        store_main(rm, sK, sVt, sValid);
-        if (t + 1 < tm) {
-            int32_t idx[4];
-            tile_idx(s_idx + kTK * (t + 1 - t0), kTK, idx);
-            fetch_main(rcode, rscale, idx, rm);
-        }
-        __syncthreads();
-        compute();
+    // main-KV tiles, double-buffered: tile t lives in sKV[(t - t0) & 1]
+    if (t0 < tm) {
+        uint32_t kp[4][4];
+        dequant_main(rm, kp);
+        put_rows(kp, sKV[0]);
+        put_valid(rm.ok, sValid[0]);
+        if (t0 + 1 < tm) fetch_main(rcode, rscale, idx1, rm);
     }
-    // window tiles (their first gather is issued here, so that the two raw
-    // buffers are never live together)
-    if (max(t0, a.ntiles_main) < t1)
-        fetch_win(swk, swv, a.W, wlo, whi, max(t0, a.ntiles_main) - a.ntiles_main, rw);
-    for (int t = max(t0, a.ntiles_main); t < t1; ++t) {
+    for (int t = t0; t < tm; ++t) {
+        const int b = (t - t0) & 1;
+        // tile t published; every read of the other buffer (tile t-1) is
+        // done; the index staging is visible
         __syncthreads();
-        store_win(rw, sK, sVt, sValid);
+        const f32x16 s0 = s_issue(sKV[b]);
+        if (t + 1 < tm) {   // tile t+1 into the other buffer; gather of t+2
+            uint32_t kp[4][4];
+            dequant_main(rm, kp);
+            put_rows(kp, sKV[b ^ 1]);
+            put_valid(rm.ok, sValid[b ^ 1]);
+            if (t + 2 < tm) {
+                int32_t idx[4];
+                tile_idx(s_idx + kTK * (t + 2 - t0), kTK, idx);
+                fetch_main(rcode, rscale, idx, rm);
+            }
+        }
+        s_finish(s0);
+        __syncthreads();   // logits published
+        pv_phase(sKV[b], sValid[b]);
+    }
+    // window tiles: K in sKV[0], V in sKV[1] (their first gather is issued
+    // here, so that the two raw buffers are never live together)
+    const int w0 = max(t0, a.ntiles_main);
+    if (w0 < t1) fetch_win(swk, swv, a.W, wlo, whi, w0 - a.ntiles_main, rw);
+    for (int t = w0; t < t1; ++t) {
+        __syncthreads();   // previous tile's LDS reads are done
+        {
+            uint32_t kp[4][4], vp[4][4];
+            dequant_win(rw, kp, vp);
+            put_rows(kp, sKV[0]);
+            put_rows(vp, sKV[1]);
+            put_valid(rw.ok, sValid[0]);
+        }
         if (t + 1 < t1) fetch_win(swk, swv, a.W, wlo, whi, t + 1 - a.ntiles_main, rw);
         __syncthreads();
-        compute();
+        s_finish(s_issue(sKV[0]));
+        __syncthreads();
+        pv_phase(sKV[1], sValid[0]);
     }
     if (!active) return;
     const float lt = l + __shfl_xor(l, 32);
