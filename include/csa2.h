@@ -139,9 +139,11 @@ int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
  *   kv_scales [rows, D/16] u8        topk_idx [B, topk] int32 (-1 skipped)
  *   swa_k/swa_v [B, W, D] u8 (E4M3FN)  swa_len [B] int32
  *   out [B, H, D] fp32; lse [B, H] fp32 or NULL
- * Supported: D == 512, H a multiple of 16 up to 64... (any H % 16 == 0),
+ * Supported: D == 512, H a multiple of 16, B <= 65535,
  * 0 <= topk <= CSA2_MAX_TOPK, 0 <= W <= 1024.
- * Preconditions (device data): every valid index addresses a row of kv.
+ * Preconditions (device data): every valid index addresses a row of kv and
+ * is below 2^23 (the gathers address a sequence's rows with 32-bit byte
+ * offsets; a padding slot is read out of range and returns 0).
  * ---------------------------------------------------------------------- */
 size_t csa2_decode_workspace_bytes(int32_t B, int32_t H, int32_t D, int32_t topk, int32_t W);
 int csa2_sparse_attn_decode(const float* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
@@ -158,8 +160,10 @@ int csa2_sparse_attn_decode(const float* q, const uint8_t* kv_codes, const uint8
  *   q [Qn, H, D] fp32; kv_codes/kv_scales: this sequence's rows
  *   topk_idx [Qn, topk] int32 (-1 skipped)
  *   swa_k/swa_v [Qn + W - 1, D] u8: row r holds position p0 - W + 1 + r;
- *   rows of negative position are never read.
- *   out [Qn, H, D]; lse [Qn, H] or NULL.   Supported shapes as for decode.
+ *   rows of negative position may be read but never contribute (their bytes
+ *   need not be valid E4M3).
+ *   out [Qn, H, D]; lse [Qn, H] or NULL.   Supported shapes as for decode
+ *   (Qn <= 65535).
  * ---------------------------------------------------------------------- */
 size_t csa2_prefill_workspace_bytes(int32_t Qn, int32_t H, int32_t D, int32_t topk, int32_t W);
 int csa2_sparse_attn_prefill_chunk(const float* q, int64_t p0, const uint8_t* kv_codes,
