@@ -369,11 +369,12 @@ __device__ void select_global_row(const uint32_t* __restrict__ keys, int n, int 
     for (int i = (int)sel_run + threadIdx.x; i < K; i += NT) out[i] = -1;
 }
 
-// Writes the `count` distinct non-negative indices of s_list (unordered, room
-// for 4 pad slots after them) to o in ascending order and pads the K slots
-// with -1.  Lists of up to 512: each index is written at its rank.  Longer
-// ones: a counting sort into kSelThreads buckets spread evenly over [min, max]
-// of the list, then each index is placed by its rank inside its bucket.
+// Writes the `count` distinct non-negative indices of s_list (unordered,
+// 16-byte aligned, room for 4 pad slots after them) to o in ascending order
+// and pads the K slots with -1.  Lists of up to 512: each
+// index is written at its rank.  Longer ones: a counting sort into
+// kSelThreads buckets spread evenly over [min, max] of the list, then each
+// index is placed by its rank inside its bucket.
 __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __restrict__ o) {
     constexpr int NB = kSelThreads;
     __shared__ uint32_t s_start[NB + 1];
@@ -382,18 +383,31 @@ __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __res
     __shared__ int32_t s_mm[2 * (kSelThreads / kWave)];
     __shared__ uint32_t s_scan[kSelThreads / kWave + 1];
     if (count <= 512) {
-        if (threadIdx.x < 4) s_list[count + threadIdx.x] = INT_MAX;
+        // rank = #{smaller indices}, each element's comparisons split over
+        // kSelThreads / count threads whose partial counts add up in LDS
+        if (count == 0) {
+            for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
+            return;
+        }
+        for (int i = threadIdx.x; i < count; i += kSelThreads) s_cur[i] = 0u;
+        if (threadIdx.x < 4) s_list[count + threadIdx.x] = INT_MAX;   // never smaller
         __syncthreads();
-        const int4* l4 = reinterpret_cast<const int4*>(s_list);
-        for (int i = threadIdx.x; i < count; i += kSelThreads) {
+        const int P = kSelThreads / count, i = threadIdx.x % count, part = threadIdx.x / count;
+        if (part < P) {
+            const int n4 = (count + 3) / 4, chunk = (n4 + P - 1) / P;
+            const int j0 = part * chunk, j1 = min(n4, j0 + chunk);
+            const int4* l4 = reinterpret_cast<const int4*>(s_list);
             const int32_t e = s_list[i];
-            int r = 0;
-            for (int j = 0; j < (count + 3) / 4; ++j) {
+            uint32_t r = 0;
+#pragma unroll 4
+            for (int j = j0; j < j1; ++j) {
                 const int4 v = l4[j];
                 r += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
             }
-            o[r] = e;
+            if (r) atomicAdd(&s_cur[i], r);
         }
+        __syncthreads();
+        for (int i = threadIdx.x; i < count; i += kSelThreads) o[s_cur[i]] = s_list[i];
     } else {
         // range of the list
         int32_t mn = INT_MAX, mx = 0;
@@ -445,26 +459,39 @@ __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __res
 }
 
 // Appends to s_out[NA ..] the indices of the `need` best of the NC distinct
-// candidate keys in s_cand (1 <= need <= NC <= kRankMax; one spare slot after
-// them): direct ranking when NC <= kRankDirect, else a register-resident radix
-// select.  Ends with a barrier.
+// candidate keys in s_cand (1 <= need <= NC <= kRankMax, 16-byte aligned, one
+// pad slot after them): direct ranking when
+// NC <= kRankDirect, else a register-resident radix select.  Ends with a
+// barrier.
 __device__ void pick_lds_candidates(uint64_t* s_cand, uint32_t NC, uint32_t need, uint32_t NA,
                                     int32_t* s_out, uint32_t* s_hist, uint32_t* s_dig,
                                     uint32_t* s_count) {
     if (NC <= (uint32_t)kRankDirect) {
-        if (threadIdx.x == 0) s_cand[NC] = 0ull;  // pad for the paired reads
+        // candidate i has rank r = #{larger candidates}; the best `need` ranks
+        // win.  Each candidate's comparisons are split over kSelThreads / NC
+        // threads whose partial counts add up in LDS.
+        __shared__ uint32_t s_rank[kRankDirect];
+        for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) s_rank[i] = 0u;
+        if (threadIdx.x == 0) s_cand[NC] = 0ull;   // pad: never larger
         __syncthreads();
-        // candidate i has rank r = #{larger candidates}; the best `need` ranks win
-        const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s_cand);
-        for (int i = threadIdx.x; i < (int)NC; i += kSelThreads) {
+        const int n = (int)NC;
+        const int P = kSelThreads / n, i = threadIdx.x % n, part = threadIdx.x / n;
+        if (part < P) {
+            const int n2 = (n + 1) / 2, chunk = (n2 + P - 1) / P;
+            const int j0 = part * chunk, j1 = min(n2, j0 + chunk);
+            const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s_cand);
             const uint64_t ci = s_cand[i];
             uint32_t r = 0;
-            for (int j = 0; j < ((int)NC + 1) / 2; ++j) {
+#pragma unroll 4
+            for (int j = j0; j < j1; ++j) {
                 const ulonglong2 w = c2[j];
                 r += (w.x > ci) + (w.y > ci);
             }
-            if (r < need) s_out[NA + r] = (int32_t)comp_idx(ci);
+            if (r) atomicAdd(&s_rank[i], r);
         }
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += kSelThreads)
+            if (s_rank[i] < need) s_out[NA + s_rank[i]] = (int32_t)comp_idx(s_cand[i]);
     } else {
         uint64_t it[kLdsCandItems];
 #pragma unroll
@@ -627,7 +654,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_small(
     if (threadIdx.x == 0) { s_na = 0; s_nc = 0; }
     uint32_t b1, nabove;
     find_digit_4096<kSelThreads>(hist + (size_t)q * kHistBins, (uint32_t)K, s_tmp, b1, nabove);
-    // 32 keys per thread per pass (8 uint4 loads in flight)
+    // 32 keys per thread per pass (8 uint4 loads in flight); winners and
+    // candidates are appended with one LDS atomic per wave and list
     constexpr int kVec = 8;
     for (int base = 0; base < n; base += 4 * kVec * kSelThreads) {
         uint4 v[kVec];
@@ -847,24 +875,53 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
         for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
         return;
     }
-    const uint32_t* row = keys + (size_t)q * stride;
+    const uint32_t* row = keys + (size_t)q * stride;   // 16-byte aligned (stride % 64 == 0)
     for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
     if (threadIdx.x == 0) { s_na = 0; s_nc = 0; }
     __syncthreads();
-    for (int e = threadIdx.x; e < n; e += kSelThreads) atomicAdd(&s_h[row[e] >> kDigitShift], 1u);
+    // both passes read 32 keys per thread per round (8 uint4 loads in flight)
+    constexpr int kVec = 8;
+    for (int base = 0; base < n; base += 4 * kVec * kSelThreads) {
+        uint4 v[kVec];
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int e = base + 4 * (threadIdx.x + kSelThreads * j);
+            v[j] = e < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int e = base + 4 * (threadIdx.x + kSelThreads * j);
+            const uint32_t kk[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                if (e + x < n) atomicAdd(&s_h[kk[x] >> kDigitShift], 1u);
+        }
+    }
     __syncthreads();
     uint32_t b1, nabove;
     find_digit_4096<kSelThreads>(s_h, (uint32_t)K, s_tmp, b1, nabove);
-    for (int base = 0; base < n; base += kSelThreads) {
-        const int e = base + threadIdx.x;
-        const uint32_t k = e < n ? row[e] : 0u;
-        const uint32_t d = k >> kDigitShift;
-        if (e < n && d > b1) {
-            const uint32_t p = atomicAdd(&s_na, 1u);
-            if (p < (uint32_t)K) s_out[p] = e;
-        } else if (e < n && d == b1) {
-            const uint32_t p = atomicAdd(&s_nc, 1u);
-            if (p < (uint32_t)kRankMax) s_cand[p] = comp_key(k, (uint32_t)e);
+    for (int base = 0; base < n; base += 4 * kVec * kSelThreads) {
+        uint4 v[kVec];
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int e = base + 4 * (threadIdx.x + kSelThreads * j);
+            v[j] = e < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int e = base + 4 * (threadIdx.x + kSelThreads * j);
+            const uint32_t kk[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t d = kk[x] >> kDigitShift;
+                if (e + x < n && d > b1) {
+                    const uint32_t p = atomicAdd(&s_na, 1u);
+                    if (p < (uint32_t)K) s_out[p] = e + x;
+                } else if (e + x < n && d == b1) {
+                    const uint32_t p = atomicAdd(&s_nc, 1u);
+                    if (p < (uint32_t)kRankMax) s_cand[p] = comp_key(kk[x], (uint32_t)(e + x));
+                }
+            }
         }
     }
     __syncthreads();
