@@ -104,6 +104,7 @@ __device__ __forceinline__ f16x8 as_f16x8(uint32_t w0, uint32_t w1, uint32_t w2,
 }
 
 constexpr int kAttnThreads = 512;   // 8 waves
+constexpr int kXcds = 8;            // XCDs of an MI355X (L2 domains)
 
 // Raw bytes of one tile for one thread: 4 keys x 8 channels (item mapping:
 // channels 8*(thread & 63) .. +8, keys 4*(thread >> 6) .. +4, so consecutive
@@ -251,14 +252,30 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     __shared__ __attribute__((aligned(8))) uint8_t sValid[2][kTK / 4];
     __shared__ int32_t s_idx[CSA2_MAX_TOPK];
 
-    const int split = blockIdx.x;
-    const int qi = blockIdx.z;
+    // Work item.  Workgroups are dealt to the XCDs round-robin by linear
+    // id; when the (query, 64-head group) units divide evenly among them, all
+    // key-range splits of a unit go to one XCD, so that they share its L2
+    // (each reads the unit's 128 KB query slice).  Any other count keeps the
+    // plain order; the mapping is a bijection either way.
+    const int nsp = gridDim.x, nhg = gridDim.y;
+    const int units = nhg * gridDim.z;
+    int split, unit;
+    if (nsp > 1 && units % kXcds == 0) {
+        const int L = blockIdx.x + nsp * (blockIdx.y + nhg * blockIdx.z);
+        const int slot = L / kXcds;
+        split = slot % nsp;
+        unit = L % kXcds + kXcds * (slot / nsp);
+    } else {
+        split = blockIdx.x;
+        unit = blockIdx.y + nhg * blockIdx.z;
+    }
+    const int hgrp = unit % nhg, qi = unit / nhg;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hh = lane >> 5, l32 = lane & 31;      // lane half, lane in half
     const int hg = wave & 1, cq = wave >> 1;         // head group, channel quarter
-    const int h = blockIdx.y * 64 + hg * 32 + l32;   // this lane's head
+    const int h = hgrp * 64 + hg * 32 + l32;         // this lane's head
     const bool hvalid = h < a.H;
-    const bool active = blockIdx.y * 64 + hg * 32 < a.H;   // wave-uniform
+    const bool active = hgrp * 64 + hg * 32 < a.H;   // wave-uniform
     const int cbase = 128 * cq;
 
     int64_t row0 = 0;   // first main-KV row of this query's sequence
@@ -295,10 +312,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         (void*)(a.kv_codes + row0 * (kD / 2)), (short)0, (int)kKvRange, kBufFlags);
     const __amdgpu_buffer_rsrc_t rscale = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.kv_scales + row0 * (kD / 16)), (short)0, (int)kKvRange, kBufFlags);
-    // Prologue, in issue order: the first tile's indices, the query slice
-    // (16 loads per lane), the split's index staging; then the first gather
-    // once its indices are in.
-    RawMain rm;
+    // Prologue, in issue order: the first two tiles' indices, the query slice
+    // (16 loads per lane), the split's index staging; then the first two
+    // gathers once their indices are in.
+    RawMain rm0, rm;   // first tile (prologue only); the tile after the current one
     RawWin rw;
     const int nslot = kTK * (tm - t0);
     // the query's Top-K row as a buffer resource: slots past topk read 0
@@ -335,8 +352,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i)
             stage[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
                 ridx, (kTK * t0 + (int)threadIdx.x + kAttnThreads * i) * 4, 0, 0);
-        // a window-only split gathers nothing here: all its slots are padding
-        fetch_main(rcode, rscale, idx0, rm);
+        // the first two tiles' gathers go out together (a window-only split's
+        // slots are all padding: nothing is read)
+        fetch_main(rcode, rscale, idx0, rm0);
+        fetch_main(rcode, rscale, idx1, rm);
 
         // largest magnitude of this head's 128 channels (both lane halves)
         float mx = 0.f;
@@ -487,10 +506,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     // main-KV tiles, double-buffered: tile t lives in sKV[(t - t0) & 1]
     if (t0 < tm) {
         uint32_t kp[4][4];
-        dequant_main(rm, kp);
+        dequant_main(rm0, kp);
         put_rows(kp, sKV[0]);
-        put_valid(rm.ok, sValid[0]);
-        if (t0 + 1 < tm) fetch_main(rcode, rscale, idx1, rm);
+        put_valid(rm0.ok, sValid[0]);
     }
     for (int t = t0; t < tm; ++t) {
         const int b = (t - t0) & 1;
@@ -575,7 +593,15 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
                                                       int nsplit, int rows_q, int H,
                                                       float* __restrict__ out,
                                                       float* __restrict__ lse) {
-    const int qh = blockIdx.x;  // qi * H + h
+    // (query, head) of this workgroup: when the attention kernel gave all
+    // splits of a (query, 64-head group) unit to one XCD, the merge of the
+    // unit's heads runs on that XCD too (its partials are in that L2)
+    int qh = blockIdx.x;  // qi * H + h
+    if (H % 64 == 0 && (rows_q * (H / 64)) % kXcds == 0) {
+        const int L = blockIdx.x, slot = L / kXcds;
+        const int unit = L % kXcds + kXcds * (slot / 64);   // unit = qi * (H / 64) + group
+        qh = unit * 64 + slot % 64;
+    }
     const size_t stride_o = (size_t)rows_q * H * kD;
     const size_t stride_ml = (size_t)rows_q * H * 2;
     float2 ml[kMaxSplitRegs];
