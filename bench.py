@@ -67,9 +67,11 @@ def make_step(csa2, w, t, torch):
     if w.kind == "decode_hier":
         pool = torch.empty((Q, w.pool_blocks), dtype=torch.int32, device=dev)
     P = w.pool_blocks if w.kind == "decode_hier" else 0
-    ws_i = torch.empty(max(256, csa2.csa2_index_full_workspace_bytes(Q, max_nvis, w.topk, P,
-                                                                       w.block_size)),
-                       dtype=torch.uint8, device=dev)
+    if w.kind == "prefill":
+        nb_i = csa2.csa2_index_prefill_workspace_bytes(Q, max_nvis, w.topk, w.Hk, w.Di)
+    else:
+        nb_i = csa2.csa2_index_full_workspace_bytes(Q, max_nvis, w.topk, P, w.block_size)
+    ws_i = torch.empty(max(256, nb_i), dtype=torch.uint8, device=dev)
     ws_r = torch.empty(max(256, csa2.csa2_reindex_workspace_bytes(Q, w.pool_blocks, w.block_size)),
                        dtype=torch.uint8, device=dev)
     if w.kind == "prefill":

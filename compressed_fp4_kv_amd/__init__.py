@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 EXPORTED_SYMBOLS = [
     "csa2_status_str", "csa2_last_hip_error",
-    "csa2_index_full_workspace_bytes", "csa2_index_full",
+    "csa2_index_full_workspace_bytes", "csa2_index_prefill_workspace_bytes", "csa2_index_full",
     "csa2_reindex_workspace_bytes", "csa2_reindex",
     "csa2_decode_workspace_bytes", "csa2_sparse_attn_decode",
     "csa2_prefill_workspace_bytes", "csa2_sparse_attn_prefill_chunk",
@@ -118,6 +118,10 @@ def _dt():
 
 def csa2_index_full_workspace_bytes(Q, max_nvis, topk, pool_blocks=0, block_size=8):
     return int(lib.csa2_index_full_workspace_bytes(Q, max_nvis, topk, pool_blocks, block_size))
+
+
+def csa2_index_prefill_workspace_bytes(Q, max_nvis, topk, Hk, Di):
+    return int(lib.csa2_index_prefill_workspace_bytes(Q, max_nvis, topk, Hk, Di))
 
 
 def csa2_index_full(qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,

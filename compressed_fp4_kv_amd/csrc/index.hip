@@ -695,22 +695,24 @@ __global__ __launch_bounds__(kSelThreads) void k_select_small(
 
 // A prefill chunk of Q queries of one sequence scores the same key rows for
 // every query, so it is a dense contraction S = Qi K^T ([Q x RW] x [RW x N])
-// on the bf16 matrix cores.  Integer-valued inputs of magnitude <= 256 are
-// exact in bf16 and every partial sum of the fp32 accumulation is an integer
-// below 2^24, so the scores equal the definition bit for bit.  Other fp32
-// inputs are split x = hi + lo (two bf16); a K-chunk whose lo parts are not
-// all zero adds the hi*lo and lo*hi products (about 16 significand bits).
-// Workgroup tile: 128 queries x 128 keys, 4 waves of 64 x 64, K in chunks of
-// 64 staged through LDS (rows padded to 144 B so 16 lanes hit 16 bank groups).
+// on the bf16 matrix cores, in two kernels:
+//   k_prefill_convert: one bf16 copy of the chunk's query rows (heads summed
+//     when the key row is shared, Hk == 1) and of the sequence's key rows,
+//     each value split x = hi + lo (lo = x - hi rounded to bf16), rows padded
+//     to tiles with zeros, and one flag per 64 rows: some lo part is non-zero;
+//   k_prefill_gemm: 128 x 128 score tiles; hi*hi always, hi*lo + lo*hi only
+//     for tiles whose flags are set.
+// Integer-valued inputs of magnitude <= 256 are exact in bf16 (no lo part)
+// and, while every partial sum stays below 2^24 in magnitude, the fp32
+// accumulation is exact in any order: the scores equal the definition bit
+// for bit.  Other fp32 inputs get about 16 significand bits.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPM = 128, kPN = 128, kPK = 64, kPStr = kPK + 8;
-
-__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
-    hi = (__bf16)x;
-    lo = (__bf16)(x - (float)hi);
-}
+constexpr int kGM = 128, kGN = 128, kGK = 128;  // score tile and K chunk
+constexpr int kGStr = kGK + 8;                  // LDS row stride (bf16): 272 B
+constexpr int kGVec = kGM * kGK / 8 / 256;      // 16-byte pieces per thread and operand
+constexpr int kCvtRows = 64;                    // rows per conversion workgroup (and flag)
 
 __device__ __forceinline__ float4 load_qrow4(const float* __restrict__ qI, int q, int Hi, int Hk,
                                              int Di, int c) {
@@ -723,130 +725,150 @@ __device__ __forceinline__ float4 load_qrow4(const float* __restrict__ qI, int q
     return s;
 }
 
-__global__ __launch_bounds__(256) void k_prefill_scores(
-    const float* __restrict__ qI, const float* __restrict__ kI, const int64_t* __restrict__ seq_row_off,
-    const int32_t* __restrict__ q_nvis, int Q, int Hi, int Hk, int Di, int max_nvis,
-    uint32_t* __restrict__ keys, int64_t kstride) {
-    __shared__ __attribute__((aligned(16))) __bf16 sA[2][kPM * kPStr];
-    __shared__ __attribute__((aligned(16))) __bf16 sB[2][kPN * kPStr];
-    const int RW = Hk * Di;
-    const int n0 = blockIdx.x * kPN, m0 = blockIdx.y * kPM;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, l16 = lane & 15;
-    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
-    const float* kb = kI + seq_row_off[0] * (int64_t)RW;
-
-    f32x4 acc[4][4];
+// Four fp32 -> packed bf16 hi and lo parts (round to nearest even); returns
+// whether a lo part is non-zero.
+__device__ __forceinline__ bool split4_bf16(float4 x, uint2& hi, uint2& lo) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    uint32_t h[4], l[4];
+    bool any = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // register stage of one K-chunk: 8 float4 of the query tile, 8 of the key tile
-    float4 ra[8], rb[8];
-    auto fetch = [&](int kc) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int f = threadIdx.x + 256 * j;       // float4 id in the 128 x 16 chunk
-            const int r = f >> 4, c = kc + 4 * (f & 15);
-            const int q = m0 + r, t = n0 + r;
-            ra[j] = q < Q ? load_qrow4(qI, q, Hi, Hk, Di, c) : make_float4(0.f, 0.f, 0.f, 0.f);
-            rb[j] = t < max_nvis ? *reinterpret_cast<const float4*>(kb + (int64_t)t * RW + c)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    };
-    fetch(0);
-    for (int kc = 0; kc < RW; kc += kPK) {
-        // split into bf16 hi/lo in registers; lo tiles are only staged (and
-        // only multiplied) when some value of this chunk is not exact in bf16
-        uint2 ah[8], bh[8], al[8], bl[8];
-        int any_lo = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float av[4] = {ra[j].x, ra[j].y, ra[j].z, ra[j].w};
-            const float bv[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
-            uint32_t hw[4], lw[4], hb[4], lb[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                __bf16 h, lo;
-                split_bf16(av[x], h, lo);
-                hw[x] = __builtin_bit_cast(uint16_t, h);
-                lw[x] = __builtin_bit_cast(uint16_t, lo);
-                any_lo |= (lw[x] & 0x7FFFu) != 0;
-                split_bf16(bv[x], h, lo);
-                hb[x] = __builtin_bit_cast(uint16_t, h);
-                lb[x] = __builtin_bit_cast(uint16_t, lo);
-                any_lo |= (lb[x] & 0x7FFFu) != 0;
-            }
-            ah[j] = make_uint2(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16));
-            al[j] = make_uint2(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16));
-            bh[j] = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-            bl[j] = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
-        }
-        __syncthreads();   // previous chunk's LDS reads are done
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int f = threadIdx.x + 256 * j;
-            const int r = f >> 4, c = 4 * (f & 15);
-            *reinterpret_cast<uint2*>(&sA[0][r * kPStr + c]) = ah[j];
-            *reinterpret_cast<uint2*>(&sB[0][r * kPStr + c]) = bh[j];
-        }
-        const int need_lo = __syncthreads_or(any_lo);
-        if (need_lo) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int f = threadIdx.x + 256 * j;
-                const int r = f >> 4, c = 4 * (f & 15);
-                *reinterpret_cast<uint2*>(&sA[1][r * kPStr + c]) = al[j];
-                *reinterpret_cast<uint2*>(&sB[1][r * kPStr + c]) = bl[j];
-            }
-            __syncthreads();
-        }
-        if (kc + kPK < RW) fetch(kc + kPK);
-#pragma unroll
-        for (int ks = 0; ks < kPK; ks += 32) {
-            bf16x8 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(&sA[0][(wm + 16 * i + l16) * kPStr + ks + 8 * g]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const bf16x8*>(&sB[0][(wn + 16 * j + l16) * kPStr + ks + 8 * g]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            if (need_lo) {
-                bf16x8 al[4], bl[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    al[i] = *reinterpret_cast<const bf16x8*>(&sA[1][(wm + 16 * i + l16) * kPStr + ks + 8 * g]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    bl[j] = *reinterpret_cast<const bf16x8*>(&sB[1][(wn + 16 * j + l16) * kPStr + ks + 8 * g]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
-                    }
-            }
-        }
+    for (int i = 0; i < 4; ++i) {
+        const __bf16 hb = (__bf16)v[i];
+        const __bf16 lb = (__bf16)(v[i] - (float)hb);
+        h[i] = __builtin_bit_cast(uint16_t, hb);
+        l[i] = __builtin_bit_cast(uint16_t, lb);
+        any |= (l[i] & 0x7FFFu) != 0;
     }
-    // lane (g, l16) of tile (i, j) holds S[row wm + 16i + 4g + r][key wn + 16j + l16]
+    hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    lo = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+    return any;
+}
+
+// Workgroups [0, Qp/64) convert query rows, the rest key rows (64 each).
+__global__ __launch_bounds__(256) void k_prefill_convert(
+    const float* __restrict__ qI, const float* __restrict__ kI,
+    const int64_t* __restrict__ seq_row_off, int Q, int Qp, int Hi, int Hk,
+    int Di, int N, uint16_t* __restrict__ qh, uint16_t* __restrict__ ql,
+    uint16_t* __restrict__ kh, uint16_t* __restrict__ kl, uint32_t* __restrict__ qflag,
+    uint32_t* __restrict__ kflag) {
+    const int RW = Hk * Di, f4 = RW / 4;
+    const float* kb = kI + seq_row_off[0] * (int64_t)RW;
+    const int nqb = Qp / kCvtRows;
+    const bool isq = (int)blockIdx.x < nqb;
+    const int blk = isq ? blockIdx.x : blockIdx.x - nqb;
+    const int r0 = blk * kCvtRows, nrow = isq ? Q : N;
+    uint16_t* dh = isq ? qh : kh;
+    uint16_t* dl = isq ? ql : kl;
+    int any = 0;
+    for (int f = threadIdx.x; f < kCvtRows * f4; f += 256) {
+        const int r = r0 + f / f4, c = 4 * (f % f4);
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < nrow)
+            x = isq ? load_qrow4(qI, r, Hi, Hk, Di, c)
+                    : *reinterpret_cast<const float4*>(kb + (size_t)r * RW + c);
+        uint2 h, l;
+        any |= split4_bf16(x, h, l) ? 1 : 0;
+        *reinterpret_cast<uint2*>(dh + (size_t)r * RW + c) = h;
+        *reinterpret_cast<uint2*>(dl + (size_t)r * RW + c) = l;
+    }
+    any = __syncthreads_or(any);
+    if (threadIdx.x == 0) (isq ? qflag : kflag)[blk] = any ? 1u : 0u;
+}
+
+// A thread's share of one K chunk: kGVec x 16 B of the query tile and of the
+// key tile (row f / (kGK/8), 8 bf16 at column 8 (f % (kGK/8)), f = thread + 256 j).
+// Chunk c of the (pass, K chunk) sequence: pass 0 = hi*hi, 1 = hi*lo,
+// 2 = lo*hi.  (Native vector types keep the staging in registers.)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define CSA2_GEMM_LOAD(RA, RB, c)                                                          \
+    do {                                                                                   \
+        const int pass_ = (c) / nch, kc_ = ((c) - pass_ * nch) * kGK;                      \
+        const uint16_t* A_ = pass_ == 2 ? ql : qh;                                         \
+        const uint16_t* B_ = pass_ == 1 ? kl : kh;                                         \
+        _Pragma("unroll") for (int j_ = 0; j_ < kGVec; ++j_) {                             \
+            const int f_ = threadIdx.x + 256 * j_, r_ = f_ / (kGK / 8), c8_ = f_ % (kGK / 8); \
+            RA[j_] = *reinterpret_cast<const u32x4*>(A_ + (size_t)(m0 + r_) * RW + kc_ + 8 * c8_); \
+            RB[j_] = *reinterpret_cast<const u32x4*>(B_ + (size_t)(n0 + r_) * RW + kc_ + 8 * c8_); \
+        }                                                                                  \
+    } while (0)
+#define CSA2_GEMM_STORE(RA, RB)                                                            \
+    do {                                                                                   \
+        _Pragma("unroll") for (int j_ = 0; j_ < kGVec; ++j_) {                             \
+            const int f_ = threadIdx.x + 256 * j_, r_ = f_ / (kGK / 8), c8_ = f_ % (kGK / 8); \
+            *reinterpret_cast<u32x4*>(sA + r_ * kGStr + 8 * c8_) = RA[j_];                 \
+            *reinterpret_cast<u32x4*>(sB + r_ * kGStr + 8 * c8_) = RB[j_];                 \
+        }                                                                                  \
+    } while (0)
+
+// The products of the chunk in LDS for this wave's 64 x 64 sub-tile.
+__device__ __forceinline__ void gemm_mma(const uint16_t* sA, const uint16_t* sB, int wm, int wn,
+                                         int l32, int hh, f32x16 (&acc)[2][2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ks = 0; ks < kGK; ks += 16) {
+        bf16x8 av[2], bv[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int q = m0 + wm + 16 * i + 4 * g + r;
+        for (int i = 0; i < 2; ++i)
+            av[i] = *reinterpret_cast<const bf16x8*>(sA + (wm + 32 * i + l32) * kGStr + ks + 8 * hh);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bv[j] = *reinterpret_cast<const bf16x8*>(sB + (wn + 32 * j + l32) * kGStr + ks + 8 * hh);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// One 128 x 128 tile of scores per workgroup (4 waves of 64 x 64 on the
+// 32x32x16 bf16 MFMA).  The chunk sequence is (pass, K chunk) with pass 0 =
+// hi*hi, 1 = hi*lo, 2 = lo*hi; a chunk is loaded into registers during the
+// previous chunk's products and stored to LDS right before its own, so one
+// LDS buffer serves and two workgroups fit a CU.
+__global__ __launch_bounds__(256) void k_prefill_gemm(
+    const uint16_t* __restrict__ qh, const uint16_t* __restrict__ ql,
+    const uint16_t* __restrict__ kh, const uint16_t* __restrict__ kl,
+    const uint32_t* __restrict__ qflag, const uint32_t* __restrict__ kflag, int RW, int Q,
+    const int32_t* __restrict__ q_nvis, int max_nvis, uint32_t* __restrict__ keys,
+    int64_t kstride) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[kGM * kGStr];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[kGN * kGStr];
+    const int n0 = blockIdx.x * kGN, m0 = blockIdx.y * kGM;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hh = lane >> 5, l32 = lane & 31;
+    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+    const int mb = m0 / kCvtRows, nb = n0 / kCvtRows;
+    const bool need_lo = (qflag[mb] | qflag[mb + 1] | kflag[nb] | kflag[nb + 1]) != 0u;
+    const int nch = RW / kGK, total = (need_lo ? 3 : 1) * nch;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    u32x4 ra[kGVec], rb[kGVec];
+    CSA2_GEMM_LOAD(ra, rb, 0);
+    for (int c = 0; c < total; ++c) {
+        __syncthreads();   // the previous chunk's operand reads are done
+        CSA2_GEMM_STORE(ra, rb);
+        __syncthreads();
+        CSA2_GEMM_LOAD(ra, rb, min(c + 1, total - 1));   // next chunk, during these products
+        gemm_mma(sA, sB, wm, wn, l32, hh, acc);
+    }
+#undef CSA2_GEMM_LOAD
+#undef CSA2_GEMM_STORE
+    // lane (hh, l32) of tile (i, j), register r holds
+    // S[query m0 + wm + 32i + 8(r/4) + 4hh + r%4][key n0 + wn + 32j + l32]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int q = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
             if (q >= Q) continue;
             const int nv = min(q_nvis[q], max_nvis);
             uint32_t* krow = keys + (size_t)q * kstride;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = n0 + wn + 16 * j + l16;
+            for (int j = 0; j < 2; ++j) {
+                const int t = n0 + wn + 32 * j + l32;
                 if (t < nv) krow[t] = ord_key(acc[i][j][r]);
             }
         }
@@ -1078,6 +1100,36 @@ int check_indexer_shape(int Q, int Hi, int Hk, int Di, int* vpr) {
 
 using namespace csa2;
 
+// The prefill form's bf16 copies, carved after the index region (at `at`,
+// a multiple of 256) of the same workspace; returns the total bytes.
+struct PrefillWs {
+    uint16_t *qh, *ql, *kh, *kl;
+    uint32_t *qflag, *kflag;
+    int Qp, Np;   // rows padded to whole score tiles
+};
+
+size_t carve_prefill(void* ws, size_t at, int Q, int max_nvis, int RW, PrefillWs* p) {
+    Carver c(ws);
+    (void)c.take<uint8_t>(at);
+    p->Qp = (Q + kGM - 1) / kGM * kGM;
+    p->Np = (max_nvis + kGN - 1) / kGN * kGN;
+    p->qh = c.take<uint16_t>((size_t)p->Qp * RW);
+    p->ql = c.take<uint16_t>((size_t)p->Qp * RW);
+    p->kh = c.take<uint16_t>((size_t)p->Np * RW);
+    p->kl = c.take<uint16_t>((size_t)p->Np * RW);
+    p->qflag = c.take<uint32_t>(p->Qp / kCvtRows);
+    p->kflag = c.take<uint32_t>(p->Np / kCvtRows);
+    return c.bytes();
+}
+
+extern "C" size_t csa2_index_prefill_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
+                                                     int32_t Hk, int32_t Di) {
+    if (Q < 0 || max_nvis < 0 || topk < 0 || Hk <= 0 || Di <= 0) return 0;
+    PrefillWs p;
+    const size_t at = carve_index(nullptr, Q, max_nvis, topk, 0, 1).bytes;
+    return carve_prefill(nullptr, at, Q, max_nvis, Hk * Di, &p);
+}
+
 extern "C" size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
                                                   int32_t pool_blocks, int32_t block_size) {
     if (Q < 0 || max_nvis < 0 || topk < 0 || pool_blocks < 0) return 0;
@@ -1108,13 +1160,21 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
     const int bs_log2 = pool_blocks > 0 ? ilog2(block_size) : 0;
 
     if (!q_seq) {
-        // prefill chunk of one sequence: bf16-MFMA score tiles, then one
-        // selecting workgroup per query
+        // prefill chunk of one sequence: bf16 copies of the query and key
+        // rows, bf16-MFMA score tiles, then one selecting workgroup per query
         if (pool_blocks > 0) return CSA2_ERR_UNSUPPORTED;
+        PrefillWs pw;
+        if (ws_bytes < carve_prefill(ws, w.bytes, Q, max_nvis, Hk * Di, &pw))
+            return CSA2_ERR_WORKSPACE;
         if (max_nvis > 0) {
-            dim3 grid((max_nvis + kPN - 1) / kPN, (Q + kPM - 1) / kPM);
-            st = CSA2_LAUNCH("prefill_scores", k_prefill_scores, grid, dim3(256), s, qI, kI,
-                             seq_row_off, q_nvis, Q, Hi, Hk, Di, max_nvis, w.keys_e, w.se);
+            st = CSA2_LAUNCH("prefill_convert", k_prefill_convert,
+                             dim3((pw.Qp + pw.Np) / kCvtRows), dim3(256), s, qI, kI, seq_row_off,
+                             Q, pw.Qp, Hi, Hk, Di, max_nvis, pw.qh, pw.ql, pw.kh, pw.kl,
+                             pw.qflag, pw.kflag);
+            if (st) return st;
+            st = CSA2_LAUNCH("prefill_scores", k_prefill_gemm, dim3(pw.Np / kGN, pw.Qp / kGM),
+                             dim3(256), s, pw.qh, pw.ql, pw.kh, pw.kl, pw.qflag, pw.kflag, Hk * Di,
+                             Q, q_nvis, max_nvis, w.keys_e, w.se);
             if (st) return st;
         }
         return CSA2_LAUNCH("row_select", k_row_select, dim3(Q), dim3(kSelThreads), s, w.keys_e,

@@ -95,10 +95,15 @@ int csa2_last_hip_error(void);
  *   topk           0..CSA2_MAX_TOPK; topk_idx [Q, topk] int32 (may be NULL iff 0)
  *   pool_blocks    0..CSA2_MAX_TOPK; block_size in {1,2,4,8};
  *                  pool_block_idx [Q, pool_blocks] int32 (NULL iff pool_blocks 0)
+ * Workspace: csa2_index_full_workspace_bytes for q_seq != NULL;
+ * csa2_index_prefill_workspace_bytes (which also holds bf16 copies of the
+ * chunk's query rows and the sequence's key rows) for q_seq == NULL.
  * Preconditions (device data): rows read stay inside kI.
  * ---------------------------------------------------------------------- */
 size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
                                        int32_t pool_blocks, int32_t block_size);
+size_t csa2_index_prefill_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
+                                          int32_t Hk, int32_t Di);
 int csa2_index_full(const float* qI, const float* kI, const int64_t* seq_row_off,
                     const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
                     int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk, int32_t* topk_idx,

@@ -35,7 +35,10 @@ def gpu_index_full(w, t, qI=None, topk=None, pool_blocks=0, prefill=None):
     max_nvis = int(w.q_nvis().max()) if Q else 0
     idx = poison_i32((Q, topk))
     pool = poison_i32((Q, pool_blocks)) if pool_blocks else None
-    buf = ws(csa2.csa2_index_full_workspace_bytes(Q, max_nvis, topk, pool_blocks, w.block_size))
+    if prefill:
+        buf = ws(csa2.csa2_index_prefill_workspace_bytes(Q, max_nvis, topk, w.Hk, w.Di))
+    else:
+        buf = ws(csa2.csa2_index_full_workspace_bytes(Q, max_nvis, topk, pool_blocks, w.block_size))
     csa2.csa2_index_full(qI, t["kI"], t["seq_row_off"], None if prefill else t["q_seq"],
                          t["q_nvis"], max_nvis, topk, idx, pool_blocks, w.block_size, pool, buf)
     torch.cuda.synchronize()

@@ -64,6 +64,14 @@ def test_index_full_argument_checks(pkg):
     assert _idx(pkg, Q=0) == 0             # nothing to do, nothing launched
     need = pkg.csa2_index_full_workspace_bytes(1, 100, 8, 0, 8)
     assert need > 0 and _idx(pkg, wsb=need - 1) == 4
+    # the prefill form (q_seq NULL) also holds the bf16 row copies: a
+    # workspace sized for the decode form is refused before any launch
+    pre = pkg.csa2_index_prefill_workspace_bytes(1, 100, 8, 4, 128)
+    assert pre > need
+    assert _idx(pkg, qseq=NULL, wsb=need) == 4
+    assert _idx(pkg, qseq=NULL, wsb=pre - 1) == 4
+    assert _idx(pkg, qseq=NULL, P=16, pool=1) == 3     # no pool in the prefill form
+    assert pkg.csa2_index_prefill_workspace_bytes(-1, 100, 8, 4, 128) == 0
 
 
 def test_reindex_argument_checks(pkg):
