@@ -28,6 +28,7 @@ EXPORTED_SYMBOLS = [
     "csa2_prefill_workspace_bytes", "csa2_sparse_attn_prefill_chunk",
     "csa2_profile_enable", "csa2_profile_read", "csa2_profile_reset",
     "csa2_debug_decode_tables",
+    "csa2_debug_dequant_tables",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -64,6 +65,7 @@ lib.csa2_profile_enable.argtypes = [ctypes.c_int]
 lib.csa2_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
 lib.csa2_debug_decode_tables.argtypes = [_P, _P, _P, _P, _P]
+lib.csa2_debug_dequant_tables.argtypes = [_P, _P, _P]
 
 
 class CSA2Error(RuntimeError):
@@ -234,3 +236,16 @@ def debug_decode_tables(stream=None):
     _check(lib.csa2_debug_decode_tables(_ptr(fp4_hw), _ptr(fp4_ref), _ptr(fp8_hw), _ptr(fp8_ref),
                                         _stream(stream)), "csa2_debug_decode_tables")
     return fp4_hw, fp4_ref, fp8_hw, fp8_ref
+
+
+def debug_dequant_tables(stream=None):
+    """The attention kernels' fp16 dequantisation of every (E2M1 code, E4M3
+    scale byte) pair, [256, 16, 8] (scale byte, code, nibble position), and of
+    every E4M3 byte, [256, 8] (byte, position in a window chunk)."""
+    import torch
+    dev = torch.device("cuda")
+    main = torch.empty((256, 16, 8), dtype=torch.float32, device=dev)
+    win = torch.empty((256, 8), dtype=torch.float32, device=dev)
+    _check(lib.csa2_debug_dequant_tables(_ptr(main), _ptr(win), _stream(stream)),
+           "csa2_debug_dequant_tables")
+    return main, win

@@ -187,46 +187,55 @@ __device__ __forceinline__ void put_rows(const uint32_t (&kp)[4][4], uint16_t* b
             make_uint4(kp[j][0], kp[j][1], kp[j][2], kp[j][3]);
 }
 
-// The keys' validity: byte g holds keys 4g..4g+3 in bits 0..3.
-__device__ __forceinline__ void put_valid(uint32_t ok, uint8_t* sValid) {
-    if ((threadIdx.x & 63) == 0) sValid[threadIdx.x >> 6] = (uint8_t)(ok & 15u);
-}
-
-// Dequantises a main-KV tile to fp16 (exactly; K = V).
-__device__ __forceinline__ void dequant_main(const RawMain& r, uint32_t (&kp)[4][4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const bool ok = (r.ok >> j) & 1u;
-        const uint32_t w = r.code[j];
-        const float sc = fp8x2_to_f32<false>(r.scale[j]).x;   // E4M3 scale byte
-        const float2 p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
-        const float2 p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
-        kp[j][0] = ok ? cvt_pk_f16(p0.x * sc, p0.y * sc) : 0u;
-        kp[j][1] = ok ? cvt_pk_f16(p1.x * sc, p1.y * sc) : 0u;
-        kp[j][2] = ok ? cvt_pk_f16(p2.x * sc, p2.y * sc) : 0u;
-        kp[j][3] = ok ? cvt_pk_f16(p3.x * sc, p3.y * sc) : 0u;
+// The keys' logit bias: 0 for a real key, -inf for padding (entry g holds
+// keys 4g..4g+3).
+__device__ __forceinline__ void put_valid(uint32_t ok, float4* sBias) {
+    if ((threadIdx.x & 63) == 0) {
+        const float ninf = -INFINITY;
+        sBias[threadIdx.x >> 6] = make_float4((ok & 1u) ? 0.f : ninf, (ok & 2u) ? 0.f : ninf,
+                                              (ok & 4u) ? 0.f : ninf, (ok & 8u) ? 0.f : ninf);
     }
 }
 
-// Converts a window tile (E4M3 K and V, exact in fp16).
+// Eight E2M1 codes (dword w; byte x holds channels 2x, 2x+1, low nibble
+// first) times their E4M3 group scale (byte sb), as four fp16 pairs.  Exact:
+// the gfx950 FP4 -> fp16 conversion is exact, the scale is exact in fp16
+// (4 significant bits, |s| in [2^-9, 448]) and so is each product (at most 6
+// significant bits, magnitude in [2^-10, 2688]).
+__device__ __forceinline__ void dequant_fp4x8(uint32_t w, uint32_t sb, uint32_t (&o)[4]) {
+    const _Float16 s = (_Float16)fp8x2_to_f32<false>(sb).x;
+    const f16x2v sc = {s, s};
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc);
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc);
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc);
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc);
+}
+
+// Eight E4M3 bytes as four fp16 pairs (exact), ANDed with `keep` (all ones
+// or zero).
+__device__ __forceinline__ void dequant_fp8x8(uint2 w, uint32_t keep, uint32_t (&o)[4]) {
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false)) & keep;
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true)) & keep;
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false)) & keep;
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true)) & keep;
+}
+
+// Dequantises a main-KV tile to fp16 (K = V).  A padding key's bytes were
+// read as 0 (outside the buffer range), so its row is 0.
+__device__ __forceinline__ void dequant_main(const RawMain& r, uint32_t (&kp)[4][4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dequant_fp4x8(r.code[j], r.scale[j], kp[j]);
+}
+
+// Converts a window tile (E4M3 K and V); rows outside the window become 0
+// (they are real memory that may hold anything).
 __device__ __forceinline__ void dequant_win(const RawWin& r, uint32_t (&kp)[4][4],
                                             uint32_t (&vp)[4][4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const bool ok = (r.ok >> j) & 1u;
-        const uint2 kw = r.k[j], vw = r.v[j];
-        const float2 k0 = fp8x2_to_f32<false>(kw.x), k1 = fp8x2_to_f32<true>(kw.x);
-        const float2 k2 = fp8x2_to_f32<false>(kw.y), k3 = fp8x2_to_f32<true>(kw.y);
-        const float2 v0 = fp8x2_to_f32<false>(vw.x), v1 = fp8x2_to_f32<true>(vw.x);
-        const float2 v2 = fp8x2_to_f32<false>(vw.y), v3 = fp8x2_to_f32<true>(vw.y);
-        kp[j][0] = ok ? cvt_pk_f16(k0.x, k0.y) : 0u;
-        kp[j][1] = ok ? cvt_pk_f16(k1.x, k1.y) : 0u;
-        kp[j][2] = ok ? cvt_pk_f16(k2.x, k2.y) : 0u;
-        kp[j][3] = ok ? cvt_pk_f16(k3.x, k3.y) : 0u;
-        vp[j][0] = ok ? cvt_pk_f16(v0.x, v0.y) : 0u;
-        vp[j][1] = ok ? cvt_pk_f16(v1.x, v1.y) : 0u;
-        vp[j][2] = ok ? cvt_pk_f16(v2.x, v2.y) : 0u;
-        vp[j][3] = ok ? cvt_pk_f16(v3.x, v3.y) : 0u;
+        const uint32_t keep = 0u - ((r.ok >> j) & 1u);
+        dequant_fp8x8(r.k[j], keep, kp[j]);
+        dequant_fp8x8(r.v[j], keep, vp[j]);
     }
 }
 
@@ -249,14 +258,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     // two tile buffers (main-KV: double buffering; window: K and V)
     __shared__ __attribute__((aligned(16))) uint16_t sKV[2][kTileElems];
     __shared__ __attribute__((aligned(16))) float4 sS[8][4][64];   // partial logits per wave
-    __shared__ __attribute__((aligned(8))) uint8_t sValid[2][kTK / 4];
+    __shared__ float4 sValid[2][kTK / 4];   // logit bias per key
     __shared__ int32_t s_idx[CSA2_MAX_TOPK];
 
     // Work item.  Workgroups are dealt to the XCDs round-robin by linear
     // id; when the (query, 64-head group) units divide evenly among them, all
     // key-range splits of a unit go to one XCD, so that they share its L2
-    // (each reads the unit's 128 KB query slice).  Any other count keeps the
-    // plain order; the mapping is a bijection either way.
+    // (each reads the unit's 128 KB query slice); without splits, each XCD
+    // takes a contiguous run of units, so that neighbouring prefill queries
+    // (whose windows overlap in all but one row) share its L2.  Any other
+    // count keeps the plain order; the mapping is a bijection either way.
     const int nsp = gridDim.x, nhg = gridDim.y;
     const int units = nhg * gridDim.z;
     int split, unit;
@@ -265,6 +276,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         const int slot = L / kXcds;
         split = slot % nsp;
         unit = L % kXcds + kXcds * (slot / nsp);
+    } else if (nsp == 1 && units % kXcds == 0) {
+        const int L = blockIdx.y + nhg * blockIdx.z;
+        split = 0;
+        unit = (L % kXcds) * (units / kXcds) + L / kXcds;
     } else {
         split = blockIdx.x;
         unit = blockIdx.y + nhg * blockIdx.z;
@@ -404,11 +419,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         f32x16 s0 = f32x16{};
         if (!active) return s0;
         const uint16_t* kr = kb + l32 * kKStr + cbase + 8 * hh;
+        // every K fragment is requested before the first product (one LDS
+        // round trip per tile)
+        f16x8 ka[8];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) ka[st] = *reinterpret_cast<const f16x8*>(kr + 16 * st);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            const f16x8 ka = *reinterpret_cast<const f16x8*>(kr + 16 * st);
-            s0 = mfma32(ka, q0[st], s0);
-            s0 = mfma32(ka, q1[st], s0);
+            s0 = mfma32(ka[st], q0[st], s0);
+            s0 = mfma32(ka[st], q1[st], s0);
         }
         return s0;
     };
@@ -428,27 +448,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 
     // Softmax of the tile's logits (sS, published) and O^T += V^T P^T with V
     // the row-major tile in `vb`.
-    auto pv_phase = [&](const uint16_t* vb, const uint8_t* valid) __attribute__((always_inline)) {
+    // Softmax of the tile's logits (sS, published) -> the P^T operands.
+    auto softmax = [&](const float4* bias, f16x8 (&pp)[2][2]) __attribute__((always_inline)) {
         if (!active) return;
         // full logits: the four channel quarters of this head group, added in
         // the same order in every wave (every read is unconditional; a padding
-        // key's zero logit gets -inf added, so no branch depends on LDS data)
+        // key's zero logit gets its -inf bias added, so no branch depends on
+        // LDS data)
         float z[16];
         float tm_ = -INFINITY;
-        const uint64_t vmask = *reinterpret_cast<const uint64_t*>(valid);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const float4 c0 = sS[hg][r4][lane], c1 = sS[hg + 2][r4][lane];
             const float4 c2 = sS[hg + 4][r4][lane], c3 = sS[hg + 6][r4][lane];
+            const float4 bb = bias[2 * r4 + hh];   // keys 8 r4 + 4 hh + 0..3
             const float v0[4] = {c0.x, c0.y, c0.z, c0.w}, v1[4] = {c1.x, c1.y, c1.z, c1.w};
             const float v2[4] = {c2.x, c2.y, c2.z, c2.w}, v3[4] = {c3.x, c3.y, c3.z, c3.w};
+            const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * r4 + i;
-                const int key = 8 * r4 + 4 * hh + i;
                 const float sv = (v0[i] + v1[i]) + (v2[i] + v3[i]);
-                const uint32_t bit = 8 * (key >> 2) + (key & 3);
-                z[r] = fmaf(sv, a.scale_log2, ((vmask >> bit) & 1u) ? 0.f : -INFINITY);
+                z[r] = fmaf(sv, a.scale_log2, bv[i]);
                 tm_ = fmaxf(tm_, z[r]);
             }
             // one group of partial-logit reads in flight at a time (registers)
@@ -457,17 +478,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         tm_ = fmaxf(tm_, __shfl_xor(tm_, 32));
         const bool bump = tm_ > m + kRescale;   // true for any finite tm_ while m = -inf
         if (__ballot(bump)) {
-            const float mn = bump ? tm_ : m;
-            const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+            const float mn = bump ? tm_ : m;   // finite where bump
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 from m = -inf
             l *= alpha;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) o[ct] = o[ct] * alpha;
             m = mn;
         }
         // P^T operands: MFMA u covers registers 8u..8u+7 (keys 16u + 8(j/4) + 4hh + j%4),
-        // each probability (<= 2^8) split into two fp16 parts
+        // each probability (<= 2^8) split into two fp16 parts.  m = -inf only
+        // while every logit so far is -inf: those give exp2(-inf) = 0.
+        const float ms = m == -INFINITY ? 0.f : m;
         float ps = 0.f;
-        f16x8 pp[2][2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             float pv[8];
@@ -475,8 +497,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             for (int j = 0; j < 8; ++j) {
                 const float zr = z[8 * u + j];
                 // raw v_exp_f32: results below 2^-126 flush to 0 (negligible next
-                // to the tile maximum's 1)
-                pv[j] = (zr == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(zr - m);
+                // to the running maximum's 1)
+                pv[j] = __builtin_amdgcn_exp2f(zr - ms);
                 ps += pv[j];
             }
             uint32_t x0[4], x1[4];
@@ -486,50 +508,88 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             pp[u][1] = as_f16x8(x1[0], x1[1], x1[2], x1[3]);
         }
         l += ps;
+    };
+    // O^T += V^T P^T with V the row-major tile in `vb`.
+    auto pv_mma = [&](const uint16_t* vb, const f16x8 (&pp)[2][2]) __attribute__((always_inline)) {
+        if (!active) return;
         // O^T[channel cbase + 32 ct + m][head] += V^T P^T over the 32 keys;
-        // the A operand's 8 keys are 16u + 4hh + 0..3 and 16u + 8 + 4hh + 0..3
+        // the A operand's 8 keys are 16u + 4hh + 0..3 and 16u + 8 + 4hh + 0..3.
+        // Every V^T fragment is requested before the first product.
+        f16x8 vv[4][2];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const v4i16 lo = lds_read_tr16(vb + trbase + 16 * u * kKStr + 32 * ct);
                 const v4i16 hi = lds_read_tr16(vb + trbase + (16 * u + 8) * kKStr + 32 * ct);
-                const f16x8 vv = __builtin_bit_cast(
+                vv[ct][u] = __builtin_bit_cast(
                     f16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
                                                                         hi[0], hi[1], hi[2], hi[3]});
-                o[ct] = mfma32(vv, pp[u][0], o[ct]);
-                o[ct] = mfma32(vv, pp[u][1], o[ct]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // consecutive products go to different accumulators
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) o[ct] = mfma32(vv[ct][u], pp[u][part], o[ct]);
             }
         }
     };
+    auto pv_phase = [&](const uint16_t* vb, const float4* bias) __attribute__((always_inline)) {
+        f16x8 pp[2][2];
+        softmax(bias, pp);
+        pv_mma(vb, pp);
+    };
 
-    // main-KV tiles, double-buffered: tile t lives in sKV[(t - t0) & 1]
+    // main-KV tiles, double-buffered: tile t lives in sKV[(t - t0) & 1].
+    // Entering step t, the logits of tile t are in sS and tile t+1 is in the
+    // other buffer; step t computes the logits of tile t+1 and the softmax and
+    // P V of tile t, then dequantises tile t+2 while the products finish.
     if (t0 < tm) {
         uint32_t kp[4][4];
         dequant_main(rm0, kp);
         put_rows(kp, sKV[0]);
         put_valid(rm0.ok, sValid[0]);
-    }
-    for (int t = t0; t < tm; ++t) {
-        const int b = (t - t0) & 1;
-        // tile t published; every read of the other buffer (tile t-1) is
-        // done; the index staging is visible
-        __syncthreads();
-        const f32x16 s0 = s_issue(sKV[b]);
-        if (t + 1 < tm) {   // tile t+1 into the other buffer; gather of t+2
-            uint32_t kp[4][4];
+        __syncthreads();   // tile t0 and the index staging visible
+        const f32x16 s0 = s_issue(sKV[0]);
+        if (t0 + 1 < tm) {   // tile t0+1 into the other buffer; gather of t0+2
             dequant_main(rm, kp);
-            put_rows(kp, sKV[b ^ 1]);
-            put_valid(rm.ok, sValid[b ^ 1]);
-            if (t + 2 < tm) {
+            put_rows(kp, sKV[1]);
+            put_valid(rm.ok, sValid[1]);
+            if (t0 + 2 < tm) {
                 int32_t idx[4];
-                tile_idx(s_idx + kTK * (t + 2 - t0), kTK, idx);
+                tile_idx(s_idx + 2 * kTK, kTK, idx);
                 fetch_main(rcode, rscale, idx, rm);
             }
         }
         s_finish(s0);
-        __syncthreads();   // logits published
-        pv_phase(sKV[b], sValid[b]);
+        __syncthreads();   // logits of t0 and tile t0+1 published
+    }
+    for (int t = t0; t < tm; ++t) {
+        const int b = (t - t0) & 1;
+        const bool next = t + 1 < tm, deq = t + 2 < tm;   // uniform
+        f32x16 sn = f32x16{};
+        f16x8 pp[2][2];
+        if (next) sn = s_issue(sKV[b ^ 1]);
+        softmax(sValid[b], pp);
+        pv_mma(sKV[b], pp);
+        __syncthreads();   // every read of sS and of tile t is done
+        if (next) s_finish(sn);
+        if (deq) {   // tile t+2 into this buffer (while the P V products run); gather of t+3
+            uint32_t kp[4][4];
+            dequant_main(rm, kp);
+            put_rows(kp, sKV[b]);
+            put_valid(rm.ok, sValid[b]);
+            if (t + 3 < tm) {
+                int32_t idx[4];
+                tile_idx(s_idx + kTK * (t + 3 - t0), kTK, idx);
+                fetch_main(rcode, rscale, idx, rm);
+            }
+        }
+        __syncthreads();   // logits of t+1 and tile t+2 published
     }
     // window tiles: K in sKV[0], V in sKV[1] (their first gather is issued
     // here, so that the two raw buffers are never live together)
@@ -645,6 +705,29 @@ __global__ void k_decode_tables(float* fp4_hw, float* fp4_ref, float* fp8_hw, fl
     const float2 f = fp8x2_to_f32<true>(w);
     fp8_hw[b] = f.y;
     fp8_ref[b] = e4m3_to_f32(b);
+}
+
+// Test hook: the attention's own dequantisation, converted back to fp32, of
+// every (E2M1 code, E4M3 scale byte) pair at each of the 8 nibble positions
+// of a code dword, and of every E4M3 byte at each of the 8 byte positions of
+// a window chunk (the other positions hold other values).
+// main_out [256 scale bytes][16 codes][8 positions], win_out [256][8].
+__global__ void k_dequant_tables(float* main_out, float* win_out) {
+    const uint32_t sb = blockIdx.x, c = threadIdx.x & 15u, pos = threadIdx.x >> 4;
+    uint32_t w = 0;
+    for (uint32_t x = 0; x < 8; ++x) w |= (x == pos ? c : (c + 3 * x + 1) & 15u) << (4 * x);
+    uint32_t o[4];
+    dequant_fp4x8(w, sb, o);
+    main_out[(sb * 16 + c) * 8 + pos] = (float)__builtin_bit_cast(f16x2v, o[pos >> 1])[pos & 1];
+    if (threadIdx.x < 8) {
+        uint32_t wb[2] = {0u, 0u};
+        for (uint32_t x = 0; x < 8; ++x)
+            wb[x >> 2] |= (x == threadIdx.x ? sb : (sb + 37 * x + 11) & 255u) << (8 * (x & 3));
+        uint32_t o8[4];
+        dequant_fp8x8(make_uint2(wb[0], wb[1]), ~0u, o8);
+        win_out[sb * 8 + threadIdx.x] =
+            (float)__builtin_bit_cast(f16x2v, o8[threadIdx.x >> 1])[threadIdx.x & 1];
+    }
 }
 
 struct AttnPlan {
@@ -786,4 +869,10 @@ extern "C" int csa2_debug_decode_tables(float* fp4_hw, float* fp4_ref, float* fp
     if (!fp4_hw || !fp4_ref || !fp8_hw || !fp8_ref) return CSA2_ERR_NULL;
     return CSA2_LAUNCH("decode_tables", k_decode_tables, dim3(1), dim3(256),
                        (hipStream_t)stream, fp4_hw, fp4_ref, fp8_hw, fp8_ref);
+}
+
+extern "C" int csa2_debug_dequant_tables(float* main_out, float* win_out, void* stream) {
+    if (!main_out || !win_out) return CSA2_ERR_NULL;
+    return CSA2_LAUNCH("dequant_tables", k_dequant_tables, dim3(256), dim3(128),
+                       (hipStream_t)stream, main_out, win_out);
 }

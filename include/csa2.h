@@ -197,6 +197,15 @@ int csa2_profile_reset(void);
 int csa2_debug_decode_tables(float* fp4_hw, float* fp4_ref, float* fp8_hw, float* fp8_ref,
                              void* stream);
 
+/* Test hook: the attention kernels' own dequantisation to fp16, read back as
+ * fp32.  main_out [256 * 16 * 8]: entry (s * 16 + c) * 8 + p = E2M1 code c at
+ * nibble position p of a code dword, times E4M3 scale byte s (every E2M1 x
+ * E4M3 product is exact in fp16).  win_out [256 * 8]: entry b * 8 + p =
+ * E4M3 byte b at byte position p of an 8-byte window chunk.  The other
+ * positions hold other values, so a wrong byte or nibble selection shows.
+ * Device pointers; CSA2_ERR_NULL on a null pointer. */
+int csa2_debug_dequant_tables(float* main_out, float* win_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

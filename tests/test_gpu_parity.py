@@ -46,6 +46,24 @@ def test_device_codecs_match_oracle_tables(csa2):
     assert np.array_equal(fp8_hw[~nan], exp8[~nan]), "gfx950 FP8 conversion differs from E4M3FN"
 
 
+def test_attention_dequant_is_exact(csa2):
+    """Every E2M1 code times every E4M3 scale byte, at every nibble position,
+    and every E4M3 byte at every byte position, as the attention kernels
+    dequantise them, against the oracle's codec tables."""
+    main, win = [x.cpu().numpy() for x in csa2.debug_dequant_tables()]
+    torch.cuda.synchronize()
+    e2 = np.array([oracle.e2m1(c) for c in range(16)])
+    e8 = np.array([oracle.e4m3(b) for b in range(256)])
+    exp_main = np.broadcast_to((e8[:, None] * e2[None, :])[:, :, None], main.shape)
+    nan = np.isnan(exp_main)
+    assert np.array_equal(np.isnan(main), nan)
+    assert np.array_equal(main[~nan], exp_main[~nan]), "FP4 x E4M3 dequantisation is not exact"
+    exp_win = np.broadcast_to(e8[:, None], win.shape)
+    nan = np.isnan(exp_win)
+    assert np.array_equal(np.isnan(win), nan)
+    assert np.array_equal(win[~nan], exp_win[~nan]), "E4M3 window conversion is not exact"
+
+
 # ----------------------------------------------------------- decode groups
 
 def _check_decode_group(csa2, w, t, idx_gpu, idx_ref_rows, layers, queries):
