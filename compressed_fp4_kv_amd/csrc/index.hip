@@ -461,11 +461,13 @@ __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __res
 // Appends to s_out[NA ..] the indices of the `need` best of the NC distinct
 // candidate keys in s_cand (1 <= need <= NC <= kRankMax, 16-byte aligned, one
 // pad slot after them): direct ranking when
-// NC <= kRankDirect, else a register-resident radix select.  Ends with a
+// NC <= kRankDirect, else a register-resident radix select whose digits
+// start at bit top_shift (48 when the candidates share their top 8 bits, as
+// keys of one first-level bin do; 56 for any candidates).  Ends with a
 // barrier.
 __device__ void pick_lds_candidates(uint64_t* s_cand, uint32_t NC, uint32_t need, uint32_t NA,
                                     int32_t* s_out, uint32_t* s_hist, uint32_t* s_dig,
-                                    uint32_t* s_count) {
+                                    uint32_t* s_count, int top_shift = 48) {
     if (NC <= (uint32_t)kRankDirect) {
         // candidate i has rank r = #{larger candidates}; the best `need` ranks
         // win.  Each candidate's comparisons are split over kSelThreads / NC
@@ -499,7 +501,8 @@ __device__ void pick_lds_candidates(uint64_t* s_cand, uint32_t NC, uint32_t need
             const uint32_t i = threadIdx.x + j * kSelThreads;
             it[j] = i < NC ? s_cand[i] : 0ull;
         }
-        const uint64_t T = block_select_kth<kSelThreads, kLdsCandItems>(it, need, s_hist, s_dig, 48);
+        const uint64_t T =
+            block_select_kth<kSelThreads, kLdsCandItems>(it, need, s_hist, s_dig, top_shift);
         if (threadIdx.x == 0) *s_count = NA;
         __syncthreads();
 #pragma unroll
@@ -874,11 +877,18 @@ __global__ __launch_bounds__(256) void k_prefill_gemm(
         }
 }
 
-// Exact Top-K of one row of score keys (prefill: one workgroup per query):
-// a 4096-bin LDS histogram of the top 12 bits finds the bin b1 of the K-th
+// Exact Top-K of one row of score keys (prefill: one workgroup per query).
+// Rows of up to kSmallRow keys are read once, into registers: the keys at
+// 1024 spread-out positions give a threshold T (a few times more sampled keys
+// lie above T than the K-th key is expected to leave); when the row then
+// holds between K and kRankMax keys >= T, those are the candidates and the
+// best K of them are picked in LDS.  Otherwise (and for longer rows): a
+// 4096-bin LDS histogram of the top 12 bits finds the bin b1 of the K-th
 // key; a second pass over the row keeps the keys above b1 and collects the
 // keys in b1, of which the best are picked in LDS.  More than kRankMax keys
 // in b1 falls back to the exact whole-row select.
+constexpr int kRowRegs = kSmallRow / (4 * kSelThreads);   // uint4 per thread for a whole row
+
 __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __restrict__ keys,
                                                             int64_t stride,
                                                             const int32_t* __restrict__ q_nvis,
@@ -898,6 +908,63 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
         return;
     }
     const uint32_t* row = keys + (size_t)q * stride;   // 16-byte aligned (stride % 64 == 0)
+    if (n <= kSmallRow) {
+        // thread t holds keys 4 (t + 1024 j) .. +3 in v[j]; 0 past the row
+        // (no real key is 0)
+        uint4 v[kRowRegs];
+#pragma unroll
+        for (int j = 0; j < kRowRegs; ++j) {
+            const int e = 4 * ((int)threadIdx.x + kSelThreads * j);
+            uint4 x = e + 3 < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
+            if (e + 3 >= n && e < n) {
+                x.x = row[e];
+                x.y = e + 1 < n ? row[e + 1] : 0u;
+                x.z = e + 2 < n ? row[e + 2] : 0u;
+            }
+            v[j] = x;
+        }
+        uint32_t tord = 1u;   // every key is a candidate for rows of up to kRankMax keys
+        if (n > kRankMax) {
+            // sample: this thread's key in slot t % kRowRegs (first lane of
+            // it); T = the lower bound of the first-level bin holding the m-th
+            // largest sample, m about twice the number of samples expected
+            // above the K-th key
+            uint32_t smp = 0;
+#pragma unroll
+            for (int j = 0; j < kRowRegs; ++j)
+                if (j == (int)threadIdx.x % kRowRegs) smp = v[j].x;
+            for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
+            __syncthreads();
+            if (smp) atomicAdd(&s_h[smp >> kDigitShift], 1u);
+            const uint32_t ns = __syncthreads_count(smp != 0u);
+            const uint32_t expect = (uint32_t)(((int64_t)K * ns + n - 1) / n);
+            const uint32_t m = min(ns, 2u * expect + 4u);
+            uint32_t bin, above;
+            find_digit_4096<kSelThreads>(s_h, m, s_tmp, bin, above);
+            tord = max(1u, bin << kDigitShift);
+        }
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < kRowRegs; ++j)
+            mine += (v[j].x >= tord) + (v[j].y >= tord) + (v[j].z >= tord) + (v[j].w >= tord);
+        uint32_t total;
+        uint32_t at = block_exclusive_sum<kSelThreads>(mine, s_tmp, total);
+        if (total >= (uint32_t)K && total <= (uint32_t)kRankMax) {
+#pragma unroll
+            for (int j = 0; j < kRowRegs; ++j) {
+                const uint32_t e = 4u * (threadIdx.x + kSelThreads * j);
+                const uint32_t kk[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    if (kk[x] >= tord) s_cand[at++] = comp_key(kk[x], e + x);
+            }
+            __syncthreads();
+            pick_lds_candidates(s_cand, total, (uint32_t)K, 0u, s_out, s_hist, s_dig, &s_count,
+                                56);
+            rank_and_write(s_out, K, K, o);
+            return;
+        }
+    }
     for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
     if (threadIdx.x == 0) { s_na = 0; s_nc = 0; }
     __syncthreads();

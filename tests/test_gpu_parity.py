@@ -365,3 +365,31 @@ def test_prefill_indexer_general_fp32_inputs(csa2):
         gsel, rsel = set(g[g >= 0].tolist()), set(ref[i][ref[i] >= 0].tolist())
         assert all(s[j] >= kth - eps for j in gsel - rsel), f"query {i}"
         assert all(s[j] <= kth + eps for j in rsel - gsel), f"query {i}"
+
+
+def test_prefill_row_select_paths(csa2):
+    # prefill rows are selected one workgroup per query: rows of up to 65,536
+    # keys are read once and filtered against a sampled threshold, longer
+    # rows (and rows whose threshold keeps too many keys) take the histogram
+    # passes; integer scores with heavy ties and all-equal scores take the
+    # fallbacks
+    w = Workload("prefill_rows", 12, "prefill", [65600], topk=512, layers=0, p0=131059, Qn=34, m=2)
+    nv = w.q_nvis()
+    assert nv.min() < 65536 < nv.max()
+    t = build_device(w, with_kv=False, layers=0)
+    kI = t["kI"].cpu().numpy()
+    for label, lo, hi in (("uniform [-8, 8]", -8, 8), ("ties [-1, 1]", -1, 1)):
+        if lo == -8:
+            qI = host_qI(w, T_QI_FULL)
+        else:
+            kI = host_ints(81, 1, 0, w.rows * w.row_width, lo, hi).reshape(-1, w.Hk, w.Di)
+            qI = host_ints(81, 2, 0, w.Qn * w.Hi * w.Di, lo, hi).reshape(w.Qn, w.Hi, w.Di)
+            t["kI"] = torch.from_numpy(kI).cuda()
+        _say(f"[{w.name}] {label}")
+        idx, _ = C.gpu_index_full(w, t, qI=torch.from_numpy(qI).cuda())
+        ref, _ = oracle.index_full(qI, kI, [0], np.zeros(w.Qn, np.int32), nv, w.Hi, w.Hk, w.Di,
+                                   w.topk)
+        assert np.array_equal(idx.cpu().numpy(), ref), label
+    zero = torch.zeros((w.Qn, w.Hi, w.Di), dtype=torch.float32, device="cuda")
+    idx, _ = C.gpu_index_full(w, t, qI=zero)
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(512), (w.Qn, 1)))
