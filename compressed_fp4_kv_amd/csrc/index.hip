@@ -877,12 +877,61 @@ __global__ __launch_bounds__(256) void k_prefill_gemm(
         }
 }
 
+// The K-th largest of the non-zero 32-bit values held IPT per thread (ties
+// allowed; 1 <= K <= their number), by 8-bit radix passes from the top:
+// returns thr and sets `need` so that the K largest are every value > thr and
+// the first `need` values == thr (in any fixed order).  A pass whose chosen
+// bucket holds exactly the values still wanted ends the search: then every
+// value >= the bucket's lower bound is taken (thr = bound - 1, need = 0).
+template <int NT, int IPT>
+__device__ int64_t block_kth_u32(const uint32_t (&it)[IPT], uint32_t K, uint32_t* s_hist,
+                                 uint32_t* s_dig, uint32_t& need) {
+    uint32_t prefix = 0, mask = 0, want = K;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += NT) s_hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+            const uint32_t v = it[j];
+            const bool m = v != 0u && (v & mask) == prefix;
+            const uint32_t d = (v >> shift) & 255u;
+            // one atomic per wave when all matching lanes share the digit
+            const uint64_t mm = __ballot(m);
+            if (mm) {
+                const int lead = __builtin_ctzll(mm);
+                const uint32_t d0 = (uint32_t)__shfl((int)d, lead);
+                const uint64_t same = __ballot(m && d == d0);
+                if (same == mm) {
+                    if (lane_id() == lead) atomicAdd(&s_hist[d0], (uint32_t)__popcll(mm));
+                } else if (m) {
+                    atomicAdd(&s_hist[d], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        find_digit_256(s_hist, want, s_dig);
+        const uint32_t d = s_dig[0], above = s_dig[1];
+        const uint32_t bucket = s_hist[d];
+        __syncthreads();
+        prefix |= d << shift;
+        mask |= 0xFFu << shift;
+        want -= above;
+        if (bucket == want) {
+            need = 0u;
+            return (int64_t)prefix - 1;
+        }
+    }
+    need = want;
+    return (int64_t)prefix;
+}
+
 // Exact Top-K of one row of score keys (prefill: one workgroup per query).
 // Rows of up to kSmallRow keys are read once, into registers: the keys at
 // 1024 spread-out positions give a threshold T (a few times more sampled keys
 // lie above T than the K-th key is expected to leave); when the row then
-// holds between K and kRankMax keys >= T, those are the candidates and the
-// best K of them are picked in LDS.  Otherwise (and for longer rows): a
+// holds between K and kRankMax keys >= T, those are the candidates, written
+// to LDS in index order; a radix select finds the K-th key value among them
+// and one ordered pass writes the winners.  Otherwise (and for longer rows): a
 // 4096-bin LDS histogram of the top 12 bits finds the bin b1 of the K-th
 // key; a second pass over the row keeps the keys above b1 and collects the
 // keys in b1, of which the best are picked in LDS.  More than kRankMax keys
@@ -893,13 +942,15 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
                                                             int64_t stride,
                                                             const int32_t* __restrict__ q_nvis,
                                                             int K, int32_t* __restrict__ out) {
-    __shared__ uint32_t s_h[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_h[kHistBins];
     __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
     __shared__ uint32_t s_na, s_nc, s_count;
+    __shared__ __attribute__((aligned(16))) uint32_t s_rtop[kWave];      // 4 per wave
+    __shared__ uint32_t s_wbase[kRowRegs * (kSelThreads / kWave)];       // per (slot, wave)
     const int q = blockIdx.x;
     const int n = min(q_nvis[q], (int)stride);
     int32_t* o = out + (size_t)q * K;
@@ -923,35 +974,78 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
             }
             v[j] = x;
         }
+        const int wv = threadIdx.x / kWave, ln = lane_id();
         uint32_t tord = 1u;   // every key is a candidate for rows of up to kRankMax keys
         if (n > kRankMax) {
-            // sample: this thread's key in slot t % kRowRegs (first lane of
-            // it); T = the lower bound of the first-level bin holding the m-th
-            // largest sample, m about twice the number of samples expected
-            // above the K-th key
+            // threshold T: each wave publishes its 4 largest samples (the key
+            // in slot t % kRowRegs of each thread); T is the m-th largest of
+            // those 64, m about twice the number of samples expected above the
+            // K-th key (at most the m-th largest sample, so a too-low T only
+            // costs candidates)
             uint32_t smp = 0;
 #pragma unroll
             for (int j = 0; j < kRowRegs; ++j)
                 if (j == (int)threadIdx.x % kRowRegs) smp = v[j].x;
-            for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
-            __syncthreads();
-            if (smp) atomicAdd(&s_h[smp >> kDigitShift], 1u);
+            uint32_t rest = smp;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t mx = rest;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+                const uint64_t hv = __ballot(rest == mx);
+                if (ln == __builtin_ctzll(hv)) rest = 0u;
+                if (ln == 0) s_rtop[wv * 4 + r] = mx;
+            }
             const uint32_t ns = __syncthreads_count(smp != 0u);
             const uint32_t expect = (uint32_t)(((int64_t)K * ns + n - 1) / n);
-            const uint32_t m = min(ns, 2u * expect + 4u);
-            uint32_t bin, above;
-            find_digit_4096<kSelThreads>(s_h, m, s_tmp, bin, above);
-            tord = max(1u, bin << kDigitShift);
+            const uint32_t m = min(64u, 2u * expect + 4u);
+            if (wv == 0) {   // rank among the 64: larger ones, and equal ones at lower lanes
+                const uint32_t x = s_rtop[ln];
+                uint32_t rank = 0;
+                for (int i = 0; i < kWave; ++i) {
+                    const uint32_t y = (uint32_t)__shfl((int)x, i);
+                    rank += (y > x || (y == x && i < ln)) ? 1u : 0u;
+                }
+                if (rank == m - 1) s_dig[0] = x;
+            }
+            __syncthreads();
+            tord = max(1u, s_dig[0]);
         }
-        uint32_t mine = 0;
+        // candidates (keys >= T) in index order: slot j of lane l of wave w
+        // holds indices 4 (64 w + l + 1024 j) + x, so (j, w, l, x) order is
+        // index order; in-wave offsets from ballots, wave offsets from one
+        // scan over (j, w)
+        uint32_t inwave[kRowRegs];
 #pragma unroll
-        for (int j = 0; j < kRowRegs; ++j)
-            mine += (v[j].x >= tord) + (v[j].y >= tord) + (v[j].z >= tord) + (v[j].w >= tord);
-        uint32_t total;
-        uint32_t at = block_exclusive_sum<kSelThreads>(mine, s_tmp, total);
+        for (int j = 0; j < kRowRegs; ++j) {
+            const uint64_t b0 = __ballot(v[j].x >= tord), b1 = __ballot(v[j].y >= tord);
+            const uint64_t b2 = __ballot(v[j].z >= tord), b3 = __ballot(v[j].w >= tord);
+            inwave[j] = (uint32_t)(lanes_below(b0) + lanes_below(b1) + lanes_below(b2) + lanes_below(b3));
+            if (ln == 0) s_wbase[j * (kSelThreads / kWave) + wv] =
+                (uint32_t)(__popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3));
+        }
+        __syncthreads();
+        if (wv == 0) {   // exclusive scan of the 256 (slot, wave) counts, 4 per lane
+            uint32_t c[4], sum = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { c[k] = s_wbase[4 * ln + k]; sum += c[k]; }
+            uint32_t incl = sum;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const uint32_t y = (uint32_t)__shfl_up((int)incl, off);
+                if (ln >= off) incl += y;
+            }
+            uint32_t run = incl - sum;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { s_wbase[4 * ln + k] = run; run += c[k]; }
+            if (ln == kWave - 1) s_dig[1] = incl;
+        }
+        __syncthreads();
+        const uint32_t total = s_dig[1];
         if (total >= (uint32_t)K && total <= (uint32_t)kRankMax) {
 #pragma unroll
             for (int j = 0; j < kRowRegs; ++j) {
+                uint32_t at = s_wbase[j * (kSelThreads / kWave) + wv] + inwave[j];
                 const uint32_t e = 4u * (threadIdx.x + kSelThreads * j);
                 const uint32_t kk[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
@@ -959,9 +1053,36 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
                     if (kk[x] >= tord) s_cand[at++] = comp_key(kk[x], e + x);
             }
             __syncthreads();
-            pick_lds_candidates(s_cand, total, (uint32_t)K, 0u, s_out, s_hist, s_dig, &s_count,
-                                56);
-            rank_and_write(s_out, K, K, o);
+            // the K-th largest key value among the candidates (ties allowed),
+            // then one ordered pass: keys above it, and its ties in index
+            // order up to K
+            uint32_t it[kLdsCandItems];
+#pragma unroll
+            for (int k = 0; k < kLdsCandItems; ++k) {
+                const uint32_t c = kLdsCandItems * threadIdx.x + k;
+                it[k] = c < total ? (uint32_t)(s_cand[c] >> 32) : 0u;
+            }
+            uint32_t need;
+            const int64_t thr = block_kth_u32<kSelThreads, kLdsCandItems>(it, (uint32_t)K, s_hist, s_dig,
+                                                                          need);
+            uint32_t na = 0, nt = 0;
+#pragma unroll
+            for (int k = 0; k < kLdsCandItems; ++k) {
+                na += (it[k] != 0u && (int64_t)it[k] > thr) ? 1u : 0u;
+                nt += (it[k] != 0u && (int64_t)it[k] == thr) ? 1u : 0u;
+            }
+            uint32_t tot2;
+            const uint32_t pre = block_exclusive_sum<kSelThreads>((na << 16) | nt, s_tmp, tot2);
+            uint32_t ab = pre >> 16, ti = pre & 0xFFFFu;
+#pragma unroll
+            for (int k = 0; k < kLdsCandItems; ++k) {
+                const uint32_t c = kLdsCandItems * threadIdx.x + k;
+                const bool above = it[k] != 0u && (int64_t)it[k] > thr;
+                const bool tie = it[k] != 0u && (int64_t)it[k] == thr;
+                if (above || (tie && ti < need)) o[ab + min(ti, need)] = (int32_t)comp_idx(s_cand[c]);
+                ab += above ? 1u : 0u;
+                ti += tie ? 1u : 0u;
+            }
             return;
         }
     }
