@@ -41,15 +41,17 @@ def log(*a):
 def measured_traffic():
     """HBM bytes per score-stream launch from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration),
-    or None if the kernel source changed since the counters were taken."""
+    or None if the kernel's sources changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "score_stream_c1_traffic.md")
     try:
         for line in open(path):
             if line.startswith("traffic_record:"):
                 rec = json.loads(line.split(":", 1)[1])
-                src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-                if hashlib.sha256(src).hexdigest()[:16] == rec["source_sha256_16"]:
+                h = hashlib.sha256()
+                for src in rec["sources"]:
+                    h.update(open(os.path.join(ROOT, src), "rb").read())
+                if h.hexdigest()[:16] == rec["sources_sha256_16"]:
                     return rec["traffic_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         pass

@@ -8,7 +8,7 @@
 // Reindex layer rescores only the pool with its own indexer query.
 //
 // Structure on the GPU
-//   1. k_score_stream: one pass over the key rows at HBM speed.  A wave
+//   1. k_score_stream (stream.hip): one pass over the key rows at HBM speed.  A wave
 //      takes 8 rows at a time (each lane holds 2 float4 of every 2 KB row,
 //      fully coalesced), dots them with the query held in registers and
 //      reduces the 8 sums across the wave with a transpose-reduction.  The
@@ -33,17 +33,14 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "rowdot.hpp"
 
 namespace csa2 {
 namespace {
 
-constexpr int kHistBins = 4096;      // first-level digit: top 12 bits of the key
-constexpr int kDigitShift = 20;
 constexpr int kCandCap = 16384;      // candidates a selecting workgroup holds
 constexpr int kSelThreads = 1024;
 constexpr int kSelItems = kCandCap / kSelThreads;
-constexpr int kStreamThreads = 512;
-constexpr int kRowsPerWG = 2048;     // score stream: rows per workgroup
 constexpr int kSelElems = 16384;    // filter: keys per workgroup (64 per thread)
 constexpr int kFilterLoads = kSelElems / (4 * 256);   // uint4 loads per thread
 constexpr int kRankMax = 4096;      // candidates held in LDS by the one-workgroup selects
@@ -52,202 +49,6 @@ constexpr int kLdsCandItems = kRankMax / kSelThreads;  // per thread, radix path
 constexpr int kSmallRow = 65536;    // rows up to this length are selected by one workgroup
 constexpr int kReindexPerWG = 256;   // reindex: candidates per workgroup
 constexpr int kReindexThreads = 256;
-
-// ------------------------------------------------------------ row dots
-
-// Lane-resident slice of the query vector: chunk j of lane l holds floats
-// [4(l + 64 j), 4(l + 64 j) + 4) of the RW = 256*VPR-float query row.  With
-// one shared key head (Hk == 1) the query heads are summed first.
-template <int VPR>
-__device__ __forceinline__ void load_qvec(const float* __restrict__ qI, int q, int Hi, int Hk,
-                                          int Di, float4 (&qv)[VPR]) {
-    const int lane = lane_id();
-    if (Hk == Hi) {
-        const float4* p = reinterpret_cast<const float4*>(qI + (size_t)q * Hi * Di);
-#pragma unroll
-        for (int j = 0; j < VPR; ++j) qv[j] = p[lane + 64 * j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < VPR; ++j) {
-            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int h = 0; h < Hi; ++h) {
-                float4 v = reinterpret_cast<const float4*>(qI + ((size_t)q * Hi + h) * Di)[lane + 64 * j];
-                s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-            }
-            qv[j] = s;
-        }
-    }
-}
-
-typedef float f32x4v __attribute__((ext_vector_type(4)));
-
-// Streaming load of one float4 of a key row: each key byte is read once, so
-// the load is marked nontemporal (no reuse expected in the caches).
-__device__ __forceinline__ float4 load_stream(const float* p) {
-    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-
-// Sums 8 per-lane partials across the wave (transpose-reduction): returns in
-// every lane the full sum of partial (lane >> 3) & 7.  After the xor-32/16/8
-// steps lane l holds a partial of row (l>>3)&7 summed over 8 lanes; xor-4/2/1
-// completes it.
-__device__ __forceinline__ float reduce8(float (&a)[8]) {
-    const int lane = lane_id();
-    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float send = b5 ? a[i] : a[i + 4];
-        float keep = b5 ? a[i + 4] : a[i];
-        a[i] = keep + __shfl_xor(send, 32);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        float send = b4 ? a[i] : a[i + 2];
-        float keep = b4 ? a[i + 2] : a[i];
-        a[i] = keep + __shfl_xor(send, 16);
-    }
-    {
-        float send = b3 ? a[0] : a[1];
-        float keep = b3 ? a[1] : a[0];
-        a[0] = keep + __shfl_xor(send, 8);
-    }
-    a[0] += __shfl_xor(a[0], 4);
-    a[0] += __shfl_xor(a[0], 2);
-    a[0] += __shfl_xor(a[0], 1);
-    return a[0];
-}
-
-// Dot products of the query with ROWS key rows (all loads issued first).
-// Returns in out[h] the full sum of row 8h + ((lane >> 3) & 7).  Invalid
-// rows (ok[i] false) read nothing.
-template <int VPR, int ROWS>
-__device__ __forceinline__ void dot_rows(const float* const (&rows)[ROWS], const bool (&ok)[ROWS],
-                                         const float4 (&qv)[VPR], float (&out)[ROWS / 8]) {
-    const int lane = lane_id();
-    float4 k[ROWS][VPR];
-#pragma unroll
-    for (int i = 0; i < ROWS; ++i)
-#pragma unroll
-        for (int j = 0; j < VPR; ++j)
-            k[i][j] = ok[i] ? load_stream(rows[i] + 4 * (lane + 64 * j))
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int h = 0; h < ROWS / 8; ++h) {
-        float a[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float s = 0.f;
-#pragma unroll
-            for (int j = 0; j < VPR; ++j) {
-                const float4 x = k[8 * h + i][j];
-                s += qv[j].x * x.x + qv[j].y * x.y + qv[j].z * x.z + qv[j].w * x.w;
-            }
-            a[i] = s;
-        }
-        out[h] = reduce8(a);
-    }
-}
-
-// ------------------------------------------------------- score stream
-
-template <int VPR>
-__global__ __launch_bounds__(kStreamThreads) void k_score_stream(
-    const float* __restrict__ qI, const float* __restrict__ kI,
-    const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
-    int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
-    int64_t bstride, int bs_log2, uint32_t* __restrict__ hist_b) {
-    // 16-bit bin counters, two per word (a workgroup sees at most
-    // kRowsPerWG keys), so that four workgroups fit a CU's LDS
-    __shared__ uint32_t s_he[kHistBins / 2];
-    __shared__ uint32_t s_hb[kHistBins / 2];
-    // this workgroup's keys, written out as whole lines at the end
-    __shared__ __attribute__((aligned(16))) uint32_t s_ke[kRowsPerWG];
-    __shared__ __attribute__((aligned(16))) uint32_t s_kb[kRowsPerWG];
-    constexpr int RW = 256 * VPR;
-    constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (64 KB in flight per 4 waves)
-    const int q = blockIdx.y;
-    const int nvis = min(q_nvis[q], (int)kstride);   // q_nvis <= max_nvis <= kstride
-    const int r0 = blockIdx.x * kRowsPerWG;
-    if (r0 >= nvis) return;
-    const int r1 = min(nvis, r0 + kRowsPerWG);
-    const bool pool = bkeys != nullptr;
-    for (int i = threadIdx.x; i < kHistBins / 2; i += kStreamThreads) { s_he[i] = 0; s_hb[i] = 0; }
-    __syncthreads();
-
-    float4 qv[VPR];
-    load_qvec<VPR>(qI, q, Hi, Hk, Di, qv);
-    const int64_t row0 = seq_row_off[q_seq ? q_seq[q] : 0];
-    const float* kb = kI + row0 * RW;
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int myrow = (lane >> 3) & 7;
-    const uint32_t bmask = (1u << bs_log2) - 1u;
-    uint32_t* krow = keys + (size_t)q * kstride;
-
-    for (int g0 = r0 + kStreamRows * wave; g0 < r1; g0 += kStreamRows * (kStreamThreads / kWave)) {
-        const float* rows[kStreamRows];
-        bool ok[kStreamRows];
-#pragma unroll
-        for (int i = 0; i < kStreamRows; ++i) {
-            ok[i] = g0 + i < r1;
-            rows[i] = kb + (int64_t)(g0 + i) * RW;
-        }
-        float sc[kStreamRows / 8];
-        dot_rows<VPR, kStreamRows>(rows, ok, qv, sc);
-#pragma unroll
-        for (int hh = 0; hh < kStreamRows / 8; ++hh) {
-            const int row = g0 + 8 * hh + myrow;
-            const bool valid = row < r1;
-            const uint32_t k = ord_key(sc[hh]);
-            if ((lane & 7) == 0 && valid) {
-                s_ke[row - r0] = k;
-                const uint32_t d = k >> kDigitShift;
-                atomicAdd(&s_he[d >> 1], 1u << ((d & 1u) << 4));
-            }
-            if (pool) {
-                uint32_t bk = valid ? k : 0u;
-                if (bs_log2 >= 1) bk = max(bk, (uint32_t)__shfl_xor(bk, 8));
-                if (bs_log2 >= 2) bk = max(bk, (uint32_t)__shfl_xor(bk, 16));
-                if (bs_log2 >= 3) bk = max(bk, (uint32_t)__shfl_xor(bk, 32));
-                if ((lane & 7) == 0 && valid && ((uint32_t)myrow & bmask) == 0) {
-                    s_kb[(row - r0) >> bs_log2] = bk;
-                    const uint32_t d = bk >> kDigitShift;
-                    atomicAdd(&s_hb[d >> 1], 1u << ((d & 1u) << 4));
-                }
-            }
-        }
-    }
-    __syncthreads();
-    // r0 and the key strides are multiples of 4 (64): whole uint4 stores,
-    // a scalar tail for the last workgroup of a row
-    const int nk = r1 - r0;
-    for (int i = 4 * threadIdx.x; i < nk; i += 4 * kStreamThreads) {
-        if (i + 4 <= nk)
-            *reinterpret_cast<uint4*>(krow + r0 + i) = *reinterpret_cast<const uint4*>(s_ke + i);
-        else
-            for (int x = i; x < nk; ++x) krow[r0 + x] = s_ke[x];
-    }
-    if (pool) {
-        const int b0 = r0 >> bs_log2, nb = ((r1 - 1) >> bs_log2) - b0 + 1;
-        uint32_t* brow = bkeys + (size_t)q * bstride + b0;
-        for (int i = 4 * threadIdx.x; i < nb; i += 4 * kStreamThreads) {
-            if (i + 4 <= nb)
-                *reinterpret_cast<uint4*>(brow + i) = *reinterpret_cast<const uint4*>(s_kb + i);
-            else
-                for (int x = i; x < nb; ++x) brow[x] = s_kb[x];
-        }
-    }
-    for (int i = threadIdx.x; i < kHistBins; i += kStreamThreads) {
-        const uint32_t sh = (i & 1) << 4;
-        const uint32_t ce = (s_he[i >> 1] >> sh) & 0xFFFFu;
-        if (ce) atomicAdd(&hist_e[(size_t)q * kHistBins + i], ce);
-        if (pool) {
-            const uint32_t cb = (s_hb[i >> 1] >> sh) & 0xFFFFu;
-            if (cb) atomicAdd(&hist_b[(size_t)q * kHistBins + i], cb);
-        }
-    }
-}
 
 __global__ void k_zero_u32(uint32_t* __restrict__ p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -1375,12 +1176,8 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
     } else {
         dim3 grid((max_nvis + kRowsPerWG - 1) / kRowsPerWG, Q);
         uint32_t* bk = pool_blocks > 0 ? w.keys_b : nullptr;
-#define CSA2_STREAM(V)                                                                        \
-    CSA2_LAUNCH("score_stream", k_score_stream<V>, grid, dim3(kStreamThreads), s, qI, kI,     \
-                seq_row_off, q_seq, q_nvis, Hi, Hk, Di, w.keys_e, w.se, w.hist_e, bk, w.sb,   \
-                bs_log2, w.hist_b)
-        st = vpr == 1 ? CSA2_STREAM(1) : vpr == 2 ? CSA2_STREAM(2) : CSA2_STREAM(4);
-#undef CSA2_STREAM
+        st = launch_score_stream(vpr, grid, s, qI, kI, seq_row_off, q_seq, q_nvis, Hi, Hk, Di,
+                                 w.keys_e, w.se, w.hist_e, bk, w.sb, bs_log2, w.hist_b);
         if (st) return st;
     }
     // selection of one row per query: a single workgroup for short rows,
