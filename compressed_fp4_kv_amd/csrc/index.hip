@@ -513,8 +513,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_small(
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGM = 128, kGN = 128, kGK = 128;  // score tile and K chunk
-constexpr int kGStr = kGK + 8;                  // LDS row stride (bf16): 272 B
+constexpr int kGM = 128, kGN = 128, kGK = 64;   // score tile and K chunk
+constexpr int kGStr = kGK + 8;                  // LDS row stride (bf16): 144 B
 constexpr int kGVec = kGM * kGK / 8 / 256;      // 16-byte pieces per thread and operand
 constexpr int kCvtRows = 64;                    // rows per conversion workgroup (and flag)
 
@@ -628,8 +628,11 @@ __device__ __forceinline__ void gemm_mma(const uint16_t* sA, const uint16_t* sB,
 // 32x32x16 bf16 MFMA).  The chunk sequence is (pass, K chunk) with pass 0 =
 // hi*hi, 1 = hi*lo, 2 = lo*hi; a chunk is loaded into registers during the
 // previous chunk's products and stored to LDS right before its own, so one
-// LDS buffer serves and two workgroups fit a CU.
-__global__ __launch_bounds__(256) void k_prefill_gemm(
+// 36 KB LDS buffer serves.  Four workgroups per CU (the register budget is
+// capped to fit them) hide the operand loads' latency better than deeper
+// staging in fewer workgroups: 128-wide chunks with two workgroups per CU
+// took 25 % longer.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_prefill_gemm(
     const uint16_t* __restrict__ qh, const uint16_t* __restrict__ ql,
     const uint16_t* __restrict__ kh, const uint16_t* __restrict__ kl,
     const uint32_t* __restrict__ qflag, const uint32_t* __restrict__ kflag, int RW, int Q,
