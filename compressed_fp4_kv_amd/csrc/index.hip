@@ -47,6 +47,7 @@ constexpr int kRankMax = 4096;      // candidates held in LDS by the one-workgro
 constexpr int kRankDirect = 512;    // up to this many candidates are ranked directly
 constexpr int kLdsCandItems = kRankMax / kSelThreads;  // per thread, radix path
 constexpr int kSmallRow = 65536;    // rows up to this length are selected by one workgroup
+constexpr int kRowRegs = kSmallRow / (4 * kSelThreads);   // uint4 per thread for a whole row
 constexpr int kReindexPerWG = 256;   // reindex: candidates per workgroup
 constexpr int kReindexThreads = 256;
 
@@ -432,20 +433,167 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
     rank_and_write(s_out, K, K, o);
 }
 
+// The K-th largest of the non-zero 32-bit values held IPT per thread (ties
+// allowed; 1 <= K <= their number), by 8-bit radix passes from the top:
+// returns thr and sets `need` so that the K largest are every value > thr and
+// the first `need` values == thr (in any fixed order).  A pass whose chosen
+// bucket holds exactly the values still wanted ends the search: then every
+// value >= the bucket's lower bound is taken (thr = bound - 1, need = 0).
+template <int NT, int IPT>
+__device__ int64_t block_kth_u32(const uint32_t (&it)[IPT], uint32_t K, uint32_t* s_hist,
+                                 uint32_t* s_dig, uint32_t& need) {
+    uint32_t prefix = 0, mask = 0, want = K;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += NT) s_hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+            const uint32_t v = it[j];
+            const bool m = v != 0u && (v & mask) == prefix;
+            const uint32_t d = (v >> shift) & 255u;
+            // one atomic per wave when all matching lanes share the digit
+            const uint64_t mm = __ballot(m);
+            if (mm) {
+                const int lead = __builtin_ctzll(mm);
+                const uint32_t d0 = (uint32_t)__shfl((int)d, lead);
+                const uint64_t same = __ballot(m && d == d0);
+                if (same == mm) {
+                    if (lane_id() == lead) atomicAdd(&s_hist[d0], (uint32_t)__popcll(mm));
+                } else if (m) {
+                    atomicAdd(&s_hist[d], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        find_digit_256(s_hist, want, s_dig);
+        const uint32_t d = s_dig[0], above = s_dig[1];
+        const uint32_t bucket = s_hist[d];
+        __syncthreads();
+        prefix |= d << shift;
+        mask |= 0xFFu << shift;
+        want -= above;
+        if (bucket == want) {
+            need = 0u;
+            return (int64_t)prefix - 1;
+        }
+    }
+    need = want;
+    return (int64_t)prefix;
+}
+
+// A whole row of n <= kSmallRow keys in registers: thread t holds keys
+// 4 (t + 1024 j) .. +3 in v[j], 0 past the row (no real key is 0).
+__device__ __forceinline__ void load_row_regs(const uint32_t* __restrict__ row, int n,
+                                              uint4 (&v)[kRowRegs]) {
+#pragma unroll
+    for (int j = 0; j < kRowRegs; ++j) {
+        const int e = 4 * ((int)threadIdx.x + kSelThreads * j);
+        uint4 x = e + 3 < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
+        if (e + 3 >= n && e < n) {
+            x.x = row[e];
+            x.y = e + 1 < n ? row[e + 1] : 0u;
+            x.z = e + 2 < n ? row[e + 2] : 0u;
+        }
+        v[j] = x;
+    }
+}
+
+// Exact Top-K of a row held as load_row_regs leaves it, given a threshold
+// T >= 1: when between K and kRankMax keys are >= T, writes the K best
+// indices to o in ascending order and returns true; otherwise writes nothing
+// and returns false (uniformly).  The keys >= T go to LDS in index order
+// (slot j of lane l of wave w holds indices 4 (64 w + l + 1024 j) + x, so
+// (j, w, l, x) order is index order: offsets within a wave from ballots,
+// wave offsets from one scan over (slot, wave) counts); a radix select over
+// their 32-bit values finds the K-th value and how many of its ties to take;
+// one block scan then puts every key above it, and the first such ties in
+// index order, at its output slot.  s_wbase holds kRowRegs * 16 words.
+__device__ __forceinline__ bool select_row_regs(const uint4 (&v)[kRowRegs], uint32_t tord, int K,
+                                int32_t* __restrict__ o, uint64_t* s_cand, uint32_t* s_wbase,
+                                uint32_t* s_hist, uint32_t* s_dig, uint32_t* s_tmp) {
+    const int wv = threadIdx.x / kWave, ln = lane_id();
+    uint32_t inwave[kRowRegs];
+#pragma unroll
+    for (int j = 0; j < kRowRegs; ++j) {
+        const uint64_t b0 = __ballot(v[j].x >= tord), b1 = __ballot(v[j].y >= tord);
+        const uint64_t b2 = __ballot(v[j].z >= tord), b3 = __ballot(v[j].w >= tord);
+        inwave[j] = (uint32_t)(lanes_below(b0) + lanes_below(b1) + lanes_below(b2) + lanes_below(b3));
+        if (ln == 0) s_wbase[j * (kSelThreads / kWave) + wv] =
+            (uint32_t)(__popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3));
+    }
+    __syncthreads();
+    if (wv == 0) {   // exclusive scan of the 256 (slot, wave) counts, 4 per lane
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { c[k] = s_wbase[4 * ln + k]; sum += c[k]; }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t y = (uint32_t)__shfl_up((int)incl, off);
+            if (ln >= off) incl += y;
+        }
+        uint32_t run = incl - sum;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { s_wbase[4 * ln + k] = run; run += c[k]; }
+        if (ln == kWave - 1) s_dig[1] = incl;
+    }
+    __syncthreads();
+    const uint32_t total = s_dig[1];
+    if (total < (uint32_t)K || total > (uint32_t)kRankMax) return false;
+#pragma unroll
+    for (int j = 0; j < kRowRegs; ++j) {
+        uint32_t at = s_wbase[j * (kSelThreads / kWave) + wv] + inwave[j];
+        const uint32_t e = 4u * (threadIdx.x + kSelThreads * j);
+        const uint32_t kk[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            if (kk[x] >= tord) s_cand[at++] = comp_key(kk[x], e + x);
+    }
+    __syncthreads();
+    uint32_t it[kLdsCandItems];
+#pragma unroll
+    for (int k = 0; k < kLdsCandItems; ++k) {
+        const uint32_t c = kLdsCandItems * threadIdx.x + k;
+        it[k] = c < total ? (uint32_t)(s_cand[c] >> 32) : 0u;
+    }
+    uint32_t need;
+    const int64_t thr = block_kth_u32<kSelThreads, kLdsCandItems>(it, (uint32_t)K, s_hist, s_dig, need);
+    uint32_t na = 0, nt = 0;
+#pragma unroll
+    for (int k = 0; k < kLdsCandItems; ++k) {
+        na += (it[k] != 0u && (int64_t)it[k] > thr) ? 1u : 0u;
+        nt += (it[k] != 0u && (int64_t)it[k] == thr) ? 1u : 0u;
+    }
+    uint32_t tot2;
+    const uint32_t pre = block_exclusive_sum<kSelThreads>((na << 16) | nt, s_tmp, tot2);
+    uint32_t ab = pre >> 16, ti = pre & 0xFFFFu;
+#pragma unroll
+    for (int k = 0; k < kLdsCandItems; ++k) {
+        const uint32_t c = kLdsCandItems * threadIdx.x + k;
+        const bool above = it[k] != 0u && (int64_t)it[k] > thr;
+        const bool tie = it[k] != 0u && (int64_t)it[k] == thr;
+        if (above || (tie && ti < need)) o[ab + min(ti, need)] = (int32_t)comp_idx(s_cand[c]);
+        ab += above ? 1u : 0u;
+        ti += tie ? 1u : 0u;
+    }
+    return true;
+}
+
 // Top-K of one key row per query by a single workgroup (rows of at most
 // kSmallRow keys: the c1 entry rows, the pool's block rows): the bin b1 of
-// the K-th key comes from the first-level histogram; one pass over the row
-// puts winners and candidates into LDS, where the best candidates are picked.
+// the K-th key comes from the first-level histogram, so the keys at or above
+// b1's lower bound are the candidates; the row is read once into registers
+// and select_row_regs picks the K best of them.  More than kRankMax such keys
+// (degenerate score distributions) falls back to the exact whole-row select.
 // Replaces the filter + finalize pair where one workgroup can read the row.
 __global__ __launch_bounds__(kSelThreads) void k_select_small(
     const uint32_t* __restrict__ keys, int64_t stride, const int32_t* __restrict__ q_nvis,
     int bs_log2, int K, const uint32_t* __restrict__ hist, int32_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
+    __shared__ uint32_t s_wbase[kRowRegs * (kSelThreads / kWave)];
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
-    __shared__ uint32_t s_na, s_nc, s_count;
     const int q = blockIdx.x;
     const int nvis = q_nvis[q];
     const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, (int)stride);
@@ -455,44 +603,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_small(
         return;
     }
     const uint32_t* row = keys + (size_t)q * stride;
-    if (threadIdx.x == 0) { s_na = 0; s_nc = 0; }
+    uint4 v[kRowRegs];
+    load_row_regs(row, n, v);
     uint32_t b1, nabove;
     find_digit_4096<kSelThreads>(hist + (size_t)q * kHistBins, (uint32_t)K, s_tmp, b1, nabove);
-    // 32 keys per thread per pass (8 uint4 loads in flight); winners and
-    // candidates are appended with one LDS atomic per wave and list
-    constexpr int kVec = 8;
-    for (int base = 0; base < n; base += 4 * kVec * kSelThreads) {
-        uint4 v[kVec];
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            const int e = base + 4 * (threadIdx.x + kSelThreads * j);
-            v[j] = e < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            const int e = base + 4 * (threadIdx.x + kSelThreads * j);
-            const uint32_t kk[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const uint32_t d = kk[x] >> kDigitShift;
-                if (e + x < n && d > b1) {
-                    const uint32_t p = atomicAdd(&s_na, 1u);
-                    if (p < (uint32_t)K) s_out[p] = e + x;
-                } else if (e + x < n && d == b1) {
-                    const uint32_t p = atomicAdd(&s_nc, 1u);
-                    if (p < (uint32_t)kRankMax) s_cand[p] = comp_key(kk[x], (uint32_t)(e + x));
-                }
-            }
-        }
-    }
-    __syncthreads();
-    const uint32_t NA = min(s_na, (uint32_t)K - 1u), NC = s_nc;
-    if (NC > (uint32_t)kRankMax) {
-        select_global_row<kSelThreads>(row, n, K, o, s_hist, s_dig, s_tmp);
+    if (select_row_regs(v, max(1u, b1 << kDigitShift), K, o, s_cand, s_wbase, s_hist, s_dig, s_tmp))
         return;
-    }
-    pick_lds_candidates(s_cand, NC, (uint32_t)K - NA, NA, s_out, s_hist, s_dig, &s_count);
-    rank_and_write(s_out, K, K, o);
+    select_global_row<kSelThreads>(row, n, K, o, s_hist, s_dig, s_tmp);
 }
 
 // -------------------------------------------------- prefill indexer
@@ -681,54 +798,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         }
 }
 
-// The K-th largest of the non-zero 32-bit values held IPT per thread (ties
-// allowed; 1 <= K <= their number), by 8-bit radix passes from the top:
-// returns thr and sets `need` so that the K largest are every value > thr and
-// the first `need` values == thr (in any fixed order).  A pass whose chosen
-// bucket holds exactly the values still wanted ends the search: then every
-// value >= the bucket's lower bound is taken (thr = bound - 1, need = 0).
-template <int NT, int IPT>
-__device__ int64_t block_kth_u32(const uint32_t (&it)[IPT], uint32_t K, uint32_t* s_hist,
-                                 uint32_t* s_dig, uint32_t& need) {
-    uint32_t prefix = 0, mask = 0, want = K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = threadIdx.x; i < 256; i += NT) s_hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < IPT; ++j) {
-            const uint32_t v = it[j];
-            const bool m = v != 0u && (v & mask) == prefix;
-            const uint32_t d = (v >> shift) & 255u;
-            // one atomic per wave when all matching lanes share the digit
-            const uint64_t mm = __ballot(m);
-            if (mm) {
-                const int lead = __builtin_ctzll(mm);
-                const uint32_t d0 = (uint32_t)__shfl((int)d, lead);
-                const uint64_t same = __ballot(m && d == d0);
-                if (same == mm) {
-                    if (lane_id() == lead) atomicAdd(&s_hist[d0], (uint32_t)__popcll(mm));
-                } else if (m) {
-                    atomicAdd(&s_hist[d], 1u);
-                }
-            }
-        }
-        __syncthreads();
-        find_digit_256(s_hist, want, s_dig);
-        const uint32_t d = s_dig[0], above = s_dig[1];
-        const uint32_t bucket = s_hist[d];
-        __syncthreads();
-        prefix |= d << shift;
-        mask |= 0xFFu << shift;
-        want -= above;
-        if (bucket == want) {
-            need = 0u;
-            return (int64_t)prefix - 1;
-        }
-    }
-    need = want;
-    return (int64_t)prefix;
-}
-
 // Exact Top-K of one row of score keys (prefill: one workgroup per query).
 // Rows of up to kSmallRow keys are read once, into registers: the keys at
 // 1024 spread-out positions give a threshold T (a few times more sampled keys
@@ -740,7 +809,6 @@ __device__ int64_t block_kth_u32(const uint32_t (&it)[IPT], uint32_t K, uint32_t
 // key; a second pass over the row keeps the keys above b1 and collects the
 // keys in b1, of which the best are picked in LDS.  More than kRankMax keys
 // in b1 falls back to the exact whole-row select.
-constexpr int kRowRegs = kSmallRow / (4 * kSelThreads);   // uint4 per thread for a whole row
 
 __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __restrict__ keys,
                                                             int64_t stride,
@@ -764,20 +832,8 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
     }
     const uint32_t* row = keys + (size_t)q * stride;   // 16-byte aligned (stride % 64 == 0)
     if (n <= kSmallRow) {
-        // thread t holds keys 4 (t + 1024 j) .. +3 in v[j]; 0 past the row
-        // (no real key is 0)
         uint4 v[kRowRegs];
-#pragma unroll
-        for (int j = 0; j < kRowRegs; ++j) {
-            const int e = 4 * ((int)threadIdx.x + kSelThreads * j);
-            uint4 x = e + 3 < n ? *reinterpret_cast<const uint4*>(row + e) : make_uint4(0, 0, 0, 0);
-            if (e + 3 >= n && e < n) {
-                x.x = row[e];
-                x.y = e + 1 < n ? row[e + 1] : 0u;
-                x.z = e + 2 < n ? row[e + 2] : 0u;
-            }
-            v[j] = x;
-        }
+        load_row_regs(row, n, v);
         const int wv = threadIdx.x / kWave, ln = lane_id();
         uint32_t tord = 1u;   // every key is a candidate for rows of up to kRankMax keys
         if (n > kRankMax) {
@@ -815,80 +871,7 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
             __syncthreads();
             tord = max(1u, s_dig[0]);
         }
-        // candidates (keys >= T) in index order: slot j of lane l of wave w
-        // holds indices 4 (64 w + l + 1024 j) + x, so (j, w, l, x) order is
-        // index order; in-wave offsets from ballots, wave offsets from one
-        // scan over (j, w)
-        uint32_t inwave[kRowRegs];
-#pragma unroll
-        for (int j = 0; j < kRowRegs; ++j) {
-            const uint64_t b0 = __ballot(v[j].x >= tord), b1 = __ballot(v[j].y >= tord);
-            const uint64_t b2 = __ballot(v[j].z >= tord), b3 = __ballot(v[j].w >= tord);
-            inwave[j] = (uint32_t)(lanes_below(b0) + lanes_below(b1) + lanes_below(b2) + lanes_below(b3));
-            if (ln == 0) s_wbase[j * (kSelThreads / kWave) + wv] =
-                (uint32_t)(__popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3));
-        }
-        __syncthreads();
-        if (wv == 0) {   // exclusive scan of the 256 (slot, wave) counts, 4 per lane
-            uint32_t c[4], sum = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) { c[k] = s_wbase[4 * ln + k]; sum += c[k]; }
-            uint32_t incl = sum;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const uint32_t y = (uint32_t)__shfl_up((int)incl, off);
-                if (ln >= off) incl += y;
-            }
-            uint32_t run = incl - sum;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) { s_wbase[4 * ln + k] = run; run += c[k]; }
-            if (ln == kWave - 1) s_dig[1] = incl;
-        }
-        __syncthreads();
-        const uint32_t total = s_dig[1];
-        if (total >= (uint32_t)K && total <= (uint32_t)kRankMax) {
-#pragma unroll
-            for (int j = 0; j < kRowRegs; ++j) {
-                uint32_t at = s_wbase[j * (kSelThreads / kWave) + wv] + inwave[j];
-                const uint32_t e = 4u * (threadIdx.x + kSelThreads * j);
-                const uint32_t kk[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    if (kk[x] >= tord) s_cand[at++] = comp_key(kk[x], e + x);
-            }
-            __syncthreads();
-            // the K-th largest key value among the candidates (ties allowed),
-            // then one ordered pass: keys above it, and its ties in index
-            // order up to K
-            uint32_t it[kLdsCandItems];
-#pragma unroll
-            for (int k = 0; k < kLdsCandItems; ++k) {
-                const uint32_t c = kLdsCandItems * threadIdx.x + k;
-                it[k] = c < total ? (uint32_t)(s_cand[c] >> 32) : 0u;
-            }
-            uint32_t need;
-            const int64_t thr = block_kth_u32<kSelThreads, kLdsCandItems>(it, (uint32_t)K, s_hist, s_dig,
-                                                                          need);
-            uint32_t na = 0, nt = 0;
-#pragma unroll
-            for (int k = 0; k < kLdsCandItems; ++k) {
-                na += (it[k] != 0u && (int64_t)it[k] > thr) ? 1u : 0u;
-                nt += (it[k] != 0u && (int64_t)it[k] == thr) ? 1u : 0u;
-            }
-            uint32_t tot2;
-            const uint32_t pre = block_exclusive_sum<kSelThreads>((na << 16) | nt, s_tmp, tot2);
-            uint32_t ab = pre >> 16, ti = pre & 0xFFFFu;
-#pragma unroll
-            for (int k = 0; k < kLdsCandItems; ++k) {
-                const uint32_t c = kLdsCandItems * threadIdx.x + k;
-                const bool above = it[k] != 0u && (int64_t)it[k] > thr;
-                const bool tie = it[k] != 0u && (int64_t)it[k] == thr;
-                if (above || (tie && ti < need)) o[ab + min(ti, need)] = (int32_t)comp_idx(s_cand[c]);
-                ab += above ? 1u : 0u;
-                ti += tie ? 1u : 0u;
-            }
-            return;
-        }
+        if (select_row_regs(v, tord, K, o, s_cand, s_wbase, s_hist, s_dig, s_tmp)) return;
     }
     for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
     if (threadIdx.x == 0) { s_na = 0; s_nc = 0; }
