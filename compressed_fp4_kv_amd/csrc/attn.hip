@@ -47,8 +47,19 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 512;
 constexpr int kTK = 32;             // keys per tile
-constexpr int kKStr = kD + 8;       // LDS row stride of a tile (fp16 elements)
+constexpr int kKStr = kD;           // LDS row stride of a tile (fp16 elements): 1 KB
 constexpr int kTileElems = kTK * kKStr;
+
+// Tile rows are not padded; instead 16-byte chunk ch of row `row` is stored
+// at chunk ch ^ tile_swz(row) of that row.  The 16 rows one K-operand read
+// instruction takes (one column chunk each) then cover all 64 banks, and the
+// 4 rows each 32-lane half of a transposed V read touches fall in 4 distinct
+// 16-bank windows: both reads are free of bank conflicts (a 16-element pad
+// served the first but gave the second 2-way conflicts).
+__device__ __forceinline__ int tile_swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+__device__ __forceinline__ int tile_off(int row, int ch) {
+    return row * kKStr + 8 * (ch ^ tile_swz(row));
+}
 constexpr float kLn2 = 0.69314718055994530942f;
 
 struct AttnArgs {
@@ -183,7 +194,7 @@ __device__ __forceinline__ void put_rows(const uint32_t (&kp)[4][4], uint16_t* b
     const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(buf + (4 * kq + j) * kKStr + 8 * c8) =
+        *reinterpret_cast<uint4*>(buf + tile_off(4 * kq + j, c8)) =
             make_uint4(kp[j][0], kp[j][1], kp[j][2], kp[j][3]);
 }
 
@@ -415,15 +426,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     // step).  Published by the caller's next barrier.
     // (split in two so that independent work can run while the matrix core
     // finishes the chain)
+    const int kr0 = l32 * kKStr + 8 * ((cbase >> 3) + (hh ^ ((l32 >> 2) & 3)));
+    const int kr1 = l32 * kKStr + 8 * ((cbase >> 3) + ((2 + hh) ^ ((l32 >> 2) & 3)));
     auto s_issue = [&](const uint16_t* kb) __attribute__((always_inline)) -> f32x16 {
         f32x16 s0 = f32x16{};
         if (!active) return s0;
-        const uint16_t* kr = kb + l32 * kKStr + cbase + 8 * hh;
         // every K fragment is requested before the first product (one LDS
-        // round trip per tile)
+        // round trip per tile): row l32, chunk (cbase >> 3) + 2 st + hh, whose
+        // swizzle splits like the transposed reads' (kr0/kr1 by st & 1)
         f16x8 ka[8];
 #pragma unroll
-        for (int st = 0; st < 8; ++st) ka[st] = *reinterpret_cast<const f16x8*>(kr + 16 * st);
+        for (int st = 0; st < 8; ++st)
+            ka[st] = *reinterpret_cast<const f16x8*>(kb + ((st & 1) ? kr1 : kr0) +
+                                                     32 * ((st >> 1) ^ (l32 & 3)));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
@@ -442,9 +457,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 
     // Lane part of the transposed reads of V: lane l = 16 g + 4 b + c points
     // at key row 4 (g >> 1) + b, channels cbase + 16 (g & 1) + 4 c .. +3, so
-    // that lane l receives channel cbase + (l & 31) of 4 consecutive keys.
-    const int trbase = (4 * (lane >> 5) + ((lane >> 2) & 3)) * kKStr + cbase +
-                       16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // that lane l receives channel cbase + (l & 31) of 4 consecutive keys
+    // (row, 16-byte chunk and the half of it).
+    // In tile_off terms: row 16 u + 8 hi + trrow, chunk (cbase >> 3) + 4 ct +
+    // tsub; since tile_swz(row) = 4 (row & 3) + ((row >> 2) & 3), the chunk's
+    // swizzle splits into tsub ^ ((row >> 2) & 3), which depends on hi only,
+    // and ct ^ (row & 3), which depends on the lane only.
+    const int trrow = 4 * (lane >> 5) + ((lane >> 2) & 3);
+    const int tsub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int trhi = (lane >> 2) & 3;   // row & 3
+    const int trb0 = trrow * kKStr + 8 * ((cbase >> 3) + (tsub ^ ((trrow >> 2) & 3))) + 4 * (lane & 1);
+    const int trb1 = (trrow + 8) * kKStr + 8 * ((cbase >> 3) + (tsub ^ (((trrow >> 2) + 2) & 3))) +
+                     4 * (lane & 1);
 
     // Softmax of the tile's logits (sS, published) and O^T += V^T P^T with V
     // the row-major tile in `vb`.
@@ -520,8 +544,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const v4i16 lo = lds_read_tr16(vb + trbase + 16 * u * kKStr + 32 * ct);
-                const v4i16 hi = lds_read_tr16(vb + trbase + (16 * u + 8) * kKStr + 32 * ct);
+                const int cto = 32 * (ct ^ trhi);
+                const v4i16 lo = lds_read_tr16(vb + trb0 + 16 * u * kKStr + cto);
+                const v4i16 hi = lds_read_tr16(vb + trb1 + 16 * u * kKStr + cto);
                 vv[ct][u] = __builtin_bit_cast(
                     f16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
                                                                         hi[0], hi[1], hi[2], hi[3]});
