@@ -953,29 +953,44 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
     const int32_t* prow = pool + (size_t)q * P;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int myrow = (lane >> 3) & 7;
-    for (int g0 = c0 + 8 * wave; g0 < c1; g0 += 8 * (kReindexThreads / kWave)) {
-        const float* rows[8];
-        bool ok[8];
+    // wave w scores candidates c0 + 64 w .. +63: lane l first resolves
+    // candidate c0 + 64 w + l to its entry row (-1: none), so that every row
+    // address of the gathers below is a lane read away, not a load away
+    constexpr int kRows = VPR >= 4 ? 8 : 16;   // rows per gather round
+    const int cw = c0 + kWave * wave;
+    int64_t tl = -1;
+    {
+        const int c = cw + lane;
+        if (c < c1) {
+            const int b = prow[c / bs];
+            tl = b >= 0 ? (int64_t)b * bs + c % bs : -1;
+            if (tl >= nvis) tl = -1;
+        }
+    }
+    const uint32_t tlo = (uint32_t)tl, thi = (uint32_t)(tl >> 32);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = g0 + i;
-            int64_t t = -1;
-            if (c < c1) {
-                const int b = prow[c / bs];
-                t = b >= 0 ? (int64_t)b * bs + c % bs : -1;
-            }
-            ok[i] = t >= 0 && t < nvis;
+    for (int it = 0; it < kWave / kRows; ++it) {
+        if (cw + kRows * it >= c1) break;   // wave-uniform
+        const float* rows[kRows];
+        bool ok[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const int src = kRows * it + i;
+            const int64_t t = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(thi, src) << 32) |
+                                        __builtin_amdgcn_readlane(tlo, src));
+            ok[i] = t >= 0;
             rows[i] = kb + (ok[i] ? t : 0) * RW;
         }
-        float sv[1];
-        dot_rows<VPR, 8>(rows, ok, qv, sv);
-        const float s = sv[0];
-        const int c = g0 + myrow;
-        if ((lane & 7) == 0 && c < c1) {
-            const int b = prow[c / bs];
-            const int64_t t = b >= 0 ? (int64_t)b * bs + c % bs : -1;
-            const bool v = t >= 0 && t < nvis;
-            ckeys[(size_t)q * ncand + c] = v ? comp_key(ord_key(s), (uint32_t)t) : 0ull;
+        float sv[kRows / 8];
+        dot_rows<VPR, kRows>(rows, ok, qv, sv);
+#pragma unroll
+        for (int hh = 0; hh < kRows / 8; ++hh) {
+            const int r = kRows * it + 8 * hh + myrow;   // this lane's candidate within the wave
+            const int64_t t = (int64_t)(((uint64_t)(uint32_t)__shfl((int)thi, r) << 32) |
+                                        (uint32_t)__shfl((int)tlo, r));
+            const int c = cw + r;
+            if ((lane & 7) == 0 && c < c1)
+                ckeys[(size_t)q * ncand + c] = t >= 0 ? comp_key(ord_key(sv[hh]), (uint32_t)t) : 0ull;
         }
     }
 }

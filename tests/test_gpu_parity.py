@@ -232,7 +232,7 @@ def test_index_is_deterministic(csa2):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("H", [16, 32, 48, 64])
+@pytest.mark.parametrize("H", [16, 32, 48, 64, 80, 128])
 def test_attention_heads_padding_and_short_windows(csa2, H):
     w = _edge([300, 50, 1000], H=H, topk=96, W=128)
     t = build_device(w, layers=1, with_kI=False)
