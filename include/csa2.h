@@ -97,7 +97,9 @@ int csa2_last_hip_error(void);
  *                  pool_block_idx [Q, pool_blocks] int32 (NULL iff pool_blocks 0)
  * Workspace: csa2_index_full_workspace_bytes for q_seq != NULL;
  * csa2_index_prefill_workspace_bytes (which also holds bf16 copies of the
- * chunk's query rows and the sequence's key rows) for q_seq == NULL.
+ * chunk's query rows and the sequence's key rows) for q_seq == NULL.  The
+ * prefill form (q_seq == NULL) builds no pool: pool_blocks must be 0, else
+ * CSA2_ERR_UNSUPPORTED.  Too small a workspace: CSA2_ERR_WORKSPACE.
  * Preconditions (device data): rows read stay inside kI.
  * ---------------------------------------------------------------------- */
 size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
