@@ -393,3 +393,36 @@ def test_prefill_row_select_paths(csa2):
     zero = torch.zeros((w.Qn, w.Hi, w.Di), dtype=torch.float32, device="cuda")
     idx, _ = C.gpu_index_full(w, t, qI=zero)
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(512), (w.Qn, 1)))
+
+
+def test_attention_largest_topk_and_window(csa2):
+    # the largest Top-K list (2,048 entries, 64 main-KV tiles split across
+    # workgroups) and the largest window (1,024 tokens), with a ragged tail
+    w = _edge([5000, 2100], H=32, topk=2048, W=1024)
+    t = build_device(w, layers=1, with_kI=False)
+    rng = np.random.default_rng(11)
+    idx = np.full((w.B, w.topk), -1, np.int32)
+    idx[0] = np.sort(rng.choice(5000, 2048, replace=False))
+    idx[1, :2000] = np.sort(rng.choice(2100, 2000, replace=False))
+    sl = torch.tensor([1024, 700], dtype=torch.int32, device="cuda")
+    out, lse = C.gpu_attn(w, t, 0, torch.from_numpy(idx).cuda(), swa_len=sl)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b, s in zip(range(2), [1024, 700]):
+        ro, rl = C.oracle_attn_query(w, b, 0, idx[b], swa_len=s)
+        C.assert_attn_close(out[b], ro[0], f"query {b}")
+        C.assert_lse_close(lse[b], rl[0], f"query {b}")
+
+
+def test_prefill_chunk_two_head_groups(csa2):
+    # 128 heads (two 64-head groups per query) in the prefill form
+    w = Workload("prefill_h128", 13, "prefill", [600], H=128, topk=64, W=128, layers=1, p0=1000,
+                 Qn=24, m=2)
+    t = build_device(w)
+    idx, _ = C.gpu_index_full(w, t)
+    ref, _ = oracle.index_full(host_qI(w, T_QI_FULL), host_kI_rows(w, 0, w.ctx[0]), [0],
+                               np.zeros(w.Qn, np.int32), w.q_nvis(), w.Hi, w.Hk, w.Di, w.topk)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+    out, lse = C.gpu_attn(w, t, 0, idx)
+    ro, rl = C.oracle_prefill_rows(w, 0, ref, list(range(w.Qn)))
+    C.assert_attn_close(out.cpu().numpy(), ro, "prefill, 128 heads")
+    C.assert_lse_close(lse.cpu().numpy(), rl, "prefill, 128 heads")
