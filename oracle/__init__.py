@@ -39,6 +39,7 @@ def lib():
         _lib.oracle_e4m3.restype = ctypes.c_double
         _lib.oracle_e4m3.argtypes = [i32]
         _lib.oracle_dequant_row.argtypes = [P, P, i32, P]
+        _lib.oracle_fp4_quantize_row.argtypes = [P, i32, P, P]
         _lib.oracle_index_full.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, P, i32, i32, P]
         _lib.oracle_reindex.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P]
         _lib.oracle_attn_decode.argtypes = [P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32,
@@ -73,6 +74,17 @@ def dequant_row(codes, scales, D):
     out = np.empty(D, np.float64)
     lib().oracle_dequant_row(_p(codes), _p(scales), D, _p(out))
     return out
+
+
+def fp4_quantize_rows(x):
+    """fp32 rows [R, D] -> (codes [R, D/2] u8, scales [R, D/16] u8)."""
+    x = _c(x, np.float32)
+    R, D = x.shape
+    codes = np.zeros((R, D // 2), np.uint8)
+    scales = np.zeros((R, D // 16), np.uint8)
+    for r in range(R):
+        lib().oracle_fp4_quantize_row(_p(x[r]), D, _p(codes[r]), _p(scales[r]))
+    return codes, scales
 
 
 def set_threads(n):

@@ -72,6 +72,48 @@ void oracle_dequant_row(const uint8_t* codes, const uint8_t* scales, int D, doub
     }
 }
 
+/* ------------------------------------------------------ FP4 main-KV writer */
+
+/* Quantises one fp32 row of D channels (D % 16 == 0) into the main-KV
+ * format [J-FP4], [A-NEWS]: E2M1 codes (channel c in the low nibble of byte
+ * c/2 when even, the high nibble when odd) with one E4M3 scale per 16
+ * channels.  READING (the pages fix the format, not the rounding): a group's
+ * scale is the smallest positive finite E4M3 value s with 6 s >= amax, the
+ * group's largest magnitude (so nothing clips; above 6 x 448 the scale stays
+ * 448 and magnitudes saturate at 6); amax = 0 gives scale byte 0.  Each value
+ * takes the E2M1 magnitude nearest to |x| / s, ties to the even code, the
+ * sign of x, and no negative zero.  The comparisons |x| against a midpoint
+ * times s are exact in double (and in fp32: the products have at most 7
+ * significant bits). */
+void oracle_fp4_quantize_row(const float* x, int D, uint8_t* codes, uint8_t* scales) {
+    /* midpoints between E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 */
+    static const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+    for (int g = 0; g < D / 16; ++g) {
+        double amax = 0.0;
+        for (int c = 16 * g; c < 16 * g + 16; ++c) amax = fmax(amax, fabs((double)x[c]));
+        int sb = 0;
+        if (amax > 0.0) {
+            sb = 0x7E;   /* 448, the largest finite E4M3 value */
+            for (int b = 1; b <= 0x7E; ++b)
+                if (6.0 * oracle_e4m3(b) >= amax) { sb = b; break; }
+        }
+        scales[g] = (uint8_t)sb;
+        const double sc = oracle_e4m3(sb);
+        for (int c = 16 * g; c < 16 * g + 16; ++c) {
+            const double a = fabs((double)x[c]);
+            int mag = 0;
+            if (sc > 0.0)
+                for (int k = 0; k < 7; ++k) {
+                    const double t = mid[k] * sc;   /* between magnitude codes k and k+1 */
+                    if (a > t || (a == t && (k + 1) % 2 == 0)) mag = k + 1;
+                }
+            const int code = mag == 0 ? 0 : ((x[c] < 0.0f ? 8 : 0) | mag);
+            if (c % 2 == 0) codes[c / 2] = (uint8_t)code;
+            else codes[c / 2] = (uint8_t)(codes[c / 2] | (code << 4));
+        }
+    }
+}
+
 /* ----------------------------------------------------------------- scores */
 
 /* Indexer score of one query against one key row.

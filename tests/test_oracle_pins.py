@@ -428,3 +428,88 @@ def test_prefill_visibility_rule_m2():
     p = w.p0 + np.arange(w.Qn)
     for pi, n in zip(p, nv):
         assert 2 * (n - 1) + 1 <= pi and not (2 * n + 1 <= pi)
+
+
+# ------------------------------------------------------ FP4 main-KV writer
+
+E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _dequant_rows(codes, scales):
+    return np.stack([oracle.dequant_row(codes[r], scales[r], codes.shape[1] * 2)
+                     for r in range(codes.shape[0])])
+
+
+def test_fp4_writer_round_trips_every_grid_row():
+    # rows that are exactly representable (each group holds a +-6 value, so
+    # its scale is recovered) come back with the same codes and scales
+    rng = np.random.default_rng(31)
+    R, D = 64, 512
+    nonneg0 = np.array([c for c in range(16) if c != 8], np.uint8)
+    nib = rng.choice(nonneg0, size=(R, D))
+    nib[:, ::16] = rng.choice([7, 15], size=(R, D // 16))   # one +-6 per group
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(1, 127, size=(R, D // 16)).astype(np.uint8)
+    x = _dequant_rows(codes, scales).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), _dequant_rows(codes, scales))   # exact in fp32
+    c2, s2 = oracle.fp4_quantize_rows(x)
+    assert np.array_equal(s2, scales)
+    assert np.array_equal(c2, codes)
+
+
+def test_fp4_writer_scale_is_the_smallest_that_covers_the_group():
+    rng = np.random.default_rng(32)
+    R, D = 96, 256
+    mags = 10.0 ** rng.uniform(-4, 4, size=(R, 1))
+    x = (rng.standard_normal((R, D)) * mags).astype(np.float32)
+    x[0] = 0.0                    # all-zero row
+    x[1, :16] = 1e5               # saturating group
+    _, s = oracle.fp4_quantize_rows(x)
+    e4 = np.array([oracle.e4m3(b) for b in range(127)])
+    for r in range(R):
+        for g in range(D // 16):
+            amax = np.abs(x[r, 16 * g:16 * g + 16].astype(np.float64)).max()
+            b = int(s[r, g])
+            if amax == 0.0:
+                assert b == 0
+            elif amax > 6 * 448:
+                assert b == 0x7E
+            else:
+                assert 1 <= b <= 0x7E and 6 * e4[b] >= amax and (b == 1 or 6 * e4[b - 1] < amax)
+
+
+def test_fp4_writer_picks_the_nearest_grid_value():
+    # brute force: the decoded value is a nearest point of the group's grid
+    # {+-m * s}; a tie goes to the even magnitude code
+    rng = np.random.default_rng(33)
+    R, D = 128, 256
+    x = (rng.standard_normal((R, D)) * 10.0 ** rng.uniform(-3, 3, size=(R, 1))).astype(np.float32)
+    codes, scales = oracle.fp4_quantize_rows(x)
+    y = _dequant_rows(codes, scales)
+    for r in range(R):
+        for g in range(D // 16):
+            s = oracle.e4m3(int(scales[r, g]))
+            xs = x[r, 16 * g:16 * g + 16].astype(np.float64)
+            d = np.abs(np.abs(xs)[:, None] - E2M1_MAG[None, :] * s)
+            best = d.min(axis=1)
+            got = np.abs(np.abs(y[r, 16 * g:16 * g + 16]) - np.abs(xs))
+            assert np.array_equal(got, best)
+            assert np.all(np.sign(y[r, 16 * g:16 * g + 16]) * np.sign(xs) >= 0)
+
+
+def test_fp4_writer_ties_go_to_the_even_code_and_no_negative_zero():
+    # a group with scale 1 (one value 6): the other 15 sit on midpoints
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    even_choice = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]   # the even neighbour of each midpoint
+    row = np.zeros(16, np.float32)
+    row[0] = 6.0
+    for i, m in enumerate(mids):
+        row[1 + 2 * i] = m
+        row[2 + 2 * i] = -m
+    row[15] = -1e-9                                    # rounds to 0: code 0, not -0
+    codes, scales = oracle.fp4_quantize_rows(row[None])
+    assert oracle.e4m3(int(scales[0, 0])) == 1.0
+    y = _dequant_rows(codes, scales)[0]
+    for i, m in enumerate(mids):
+        assert y[1 + 2 * i] == even_choice[i] and y[2 + 2 * i] == -even_choice[i]
+    assert (codes[0, 7] >> 4) == 0
