@@ -8,7 +8,8 @@ channels over the 512 selected FP4 rows + a 128-token FP8 window, each layer
 with its own query and window).  Inputs are seeded synthetic tensors already
 resident in HBM.  Prints one JSON line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+       python bench.py --kv-writer   (the FP4 main-KV writer alone, its own line)
 """
 import argparse
 import json
@@ -38,12 +39,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic():
-    """HBM bytes per score-stream launch from the committed rocprofv3 counter
+def measured_traffic(profile="score_stream_c1_traffic.md"):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration),
     or None if the kernel's sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "score_stream_c1_traffic.md")
+    path = os.path.join(ROOT, "profiles", profile)
     try:
         for line in open(path):
             if line.startswith("traffic_record:"):
@@ -184,6 +185,83 @@ def cpu_baseline(w, max_threads):
                       f"{dt:.2f} s"}
 
 
+def kv_writer_bench(args, torch, csa2):
+    """FP4 main-KV writer alone: fp32 rows -> E2M1 codes + E4M3 scale per 16
+    channels, on a 1M-entry context's main KV (1,048,576 entries x 512
+    channels: 65,536 generated rows tiled 16 times, 2 GiB of fp32, more than
+    the last-level cache holds), on the 65,536-entry prefill context and on
+    one prefill chunk's append (4,096 queries, m = 2: 2,048 entries).  One
+    step = one writer launch over all rows."""
+    import oracle
+    from gen import kv_rows_f32
+
+    D = 512
+    res_sizes = {}
+    base = torch.from_numpy(kv_rows_f32(2, 9001, 65536, D)).cuda()
+    for name, rows in (("context_1m", 1 << 20), ("context_64k", 65536), ("chunk_append", 2048)):
+        x = base.repeat(rows // 65536, 1) if rows > 65536 else base[:rows].contiguous()
+        codes = torch.empty((rows, D // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((rows, D // 16), dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            csa2.csa2_kv_quantize_fp4(x, codes, scales)
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            csa2.csa2_kv_quantize_fp4(x, codes, scales)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        csa2.profile_reset()
+        csa2.profile_enable(True)
+        for _ in range(args.steps):
+            csa2.csa2_kv_quantize_fp4(x, codes, scales)
+        torch.cuda.synchronize()
+        n, kms = csa2.profile_read()["kv_quantize_fp4"]
+        csa2.profile_enable(False)
+        avg_us = 1000.0 * kms / n
+        alg = rows * (4 * D + D // 2 + D // 16)     # fp32 read, codes + scale bytes written
+        ach = alg / (avg_us * 1e-6) / 1e9
+        res_sizes[name] = {"rows": rows, "ms_per_step": ms, "avg_us": avg_us,
+                           "achieved_gbs": ach, "frac": ach / HBM_PEAK_GBS}
+        log(f"kv writer {name}: rows={rows} {ms * 1e3:.1f} us/step, kernel {avg_us:.1f} us, "
+            f"{ach:.0f} GB/s")
+        del x, codes, scales
+    del base
+    big = res_sizes["context_1m"]
+    res = {
+        "metric": "FP4 main-KV writer rows/s (fp32 -> E2M1 + E4M3 per 16 channels) at 1 MI355X",
+        "value": big["rows"] / (big["ms_per_step"] * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": big["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (N(0,1) rows, each 16-channel group scaled by 2^U[-30,14))",
+        "config": {"workload": "FP4 main-KV writer: 1,048,576 entries x 512 channels",
+                   "rows": big["rows"], "D": D, "parallelism": "single GPU"},
+        "sizes": res_sizes,
+        "roofline": {"bound": "hbm", "kernel": "kv_quantize_fp4", "achieved": big["achieved_gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": big["frac"],
+                     "traffic": measured_traffic("kv_writer_1m_rows.md")},
+    }
+    if not args.no_cpu_baseline:
+        rows = 16384
+        xs = kv_rows_f32(2, 9001, rows, D)
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.fp4_quantize_rows(xs)
+            reps += 1
+            if time.perf_counter() - t0 > 5.0:
+                break
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": reps * rows / dt, "unit": "rows/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} x {rows} rows x {D} channels, {dt:.2f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +271,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1,
                     help="workload number (1 = the decode workload the metric is quoted on)")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--kv-writer", action="store_true",
+                    help="measure the FP4 main-KV writer alone (its own JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (reference "
                          "kernel of known traffic for the hardware byte counters)")
@@ -214,6 +294,9 @@ def main():
         return
     import compressed_fp4_kv_amd as csa2
     from gen.workloads import build_device, workload
+    if args.kv_writer:
+        kv_writer_bench(args, torch, csa2)
+        return
 
     w = workload(args.workload)
     log(f"building inputs: {w.name} B={w.B} ctx={w.ctx[0]} H={w.H} topk={w.topk}")

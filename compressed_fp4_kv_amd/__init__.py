@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = [
     "csa2_profile_enable", "csa2_profile_read", "csa2_profile_reset",
     "csa2_debug_decode_tables",
     "csa2_debug_dequant_tables",
+    "csa2_kv_quantize_fp4",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -66,6 +67,7 @@ lib.csa2_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
 lib.csa2_debug_decode_tables.argtypes = [_P, _P, _P, _P, _P]
 lib.csa2_debug_dequant_tables.argtypes = [_P, _P, _P]
+lib.csa2_kv_quantize_fp4.argtypes = [_P, _I64, _I32, _P, _P, _P]
 
 
 class CSA2Error(RuntimeError):
@@ -199,6 +201,21 @@ def csa2_sparse_attn_prefill_chunk(q, p0, kv_codes, kv_scales, topk_idx, swa_k, 
         _ptr(swa_k, u8, "swa_k"), _ptr(swa_v, u8, "swa_v"), W, Qn, H, D, float(softmax_scale),
         _ptr(out, f32, "out"), _ptr(lse, f32, "lse"), wp, wn, _stream(stream)),
         "csa2_sparse_attn_prefill_chunk")
+
+
+# ---------------------------------------------------------------- KV writer
+
+def csa2_kv_quantize_fp4(x, codes, scales, stream=None):
+    """x [rows, D] f32 (D % 16 == 0) -> codes [rows, D/2] u8 (even channel in
+    the low nibble), scales [rows, D/16] u8 (E4M3)."""
+    f32, _, _, u8 = _dt()
+    rows, D = x.shape
+    if tuple(codes.shape) != (rows, D // 2) or tuple(scales.shape) != (rows, D // 16):
+        raise ValueError(f"codes {tuple(codes.shape)} / scales {tuple(scales.shape)} do not "
+                         f"match x {tuple(x.shape)}")
+    _check(lib.csa2_kv_quantize_fp4(_ptr(x, f32, "x"), rows, D, _ptr(codes, u8, "codes"),
+                                    _ptr(scales, u8, "scales"), _stream(stream)),
+           "csa2_kv_quantize_fp4")
 
 
 # ----------------------------------------------------------------- profiling

@@ -91,6 +91,18 @@ def normal_f32(seed, tensor, shape):
     return np.random.default_rng([seed, tensor]).standard_normal(shape, dtype=np.float32)
 
 
+def kv_rows_f32(seed, tensor, rows, D, log2_lo=-30.0, log2_hi=14.0):
+    """fp32 main-KV rows [rows, D] before quantisation: N(0,1) values, each run
+    of 16 channels multiplied by its own 2^u with u uniform in
+    [log2_lo, log2_hi), so that the groups span tiny, ordinary and huge
+    magnitudes."""
+    rng = np.random.default_rng([seed, tensor])
+    g = rows * D // 16
+    mag = np.exp2(rng.uniform(log2_lo, log2_hi, size=(g, 1))).astype(np.float32)
+    x = rng.standard_normal((g, 16), dtype=np.float32) * mag
+    return x.reshape(rows, D)
+
+
 def e4m3_bytes(x):
     """Round fp32 values to E4M3FN bytes (torch CPU cast, nearest-even)."""
     import torch

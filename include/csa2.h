@@ -181,6 +181,25 @@ int csa2_sparse_attn_prefill_chunk(const float* q, int64_t p0, const uint8_t* kv
                                    size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * FP4 main-KV writer: quantises fp32 rows into the main-KV format the
+ * attention calls read (jaehun.me review, section "3) FP4 main KV"; the
+ * ainewsway.com article: E2M1 values with one scale per 16 channels).  The
+ * pages fix the format, not the rounding; this writer's rule: a group's
+ * scale is the smallest positive finite E4M3 value s with 6 s >= its
+ * largest magnitude (448 and saturation at 6 beyond 6 x 448; scale byte 0
+ * and all-zero codes for an all-zero group); each value takes the E2M1
+ * magnitude nearest to |x| / s, ties to the even code, the sign of x and no
+ * negative zero.
+ *   x      [rows, D] fp32, 16-byte aligned, finite
+ *   codes  [rows, D/2] u8: channel c in the low nibble of byte c/2 when c is
+ *          even, the high nibble when odd; 2-byte aligned
+ *   scales [rows, D/16] u8 (E4M3FN)
+ * D must be a multiple of 16 (else CSA2_ERR_UNSUPPORTED).  No workspace.
+ * ---------------------------------------------------------------------- */
+int csa2_kv_quantize_fp4(const float* x, int64_t rows, int32_t D, uint8_t* codes,
+                         uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------
  * Optional per-kernel timing (for measurement tools).  While enabled, every
  * kernel the library launches is bracketed by hipEvents recorded on the
  * launch stream; csa2_profile_read synchronises on the last event and
