@@ -38,6 +38,9 @@ def lib():
         _lib.oracle_e2m1.argtypes = [i32]
         _lib.oracle_e4m3.restype = ctypes.c_double
         _lib.oracle_e4m3.argtypes = [i32]
+        _lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        _lib.oracle_e4m3_encode.argtypes = [f32]
+        _lib.oracle_swa_append.argtypes = [P, P, P, i32, i32, i32, P, P]
         _lib.oracle_dequant_row.argtypes = [P, P, i32, P]
         _lib.oracle_fp4_quantize_row.argtypes = [P, i32, P, P]
         _lib.oracle_index_full.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, P, i32, i32, P]
@@ -85,6 +88,23 @@ def fp4_quantize_rows(x):
     for r in range(R):
         lib().oracle_fp4_quantize_row(_p(x[r]), D, _p(codes[r]), _p(scales[r]))
     return codes, scales
+
+
+def e4m3_encode(x):
+    """fp32 values (any shape) -> E4M3FN bytes, element by element."""
+    x = np.asarray(x, np.float32)
+    f = lib().oracle_e4m3_encode
+    return np.array([f(float(v)) for v in x.reshape(-1)], np.uint8).reshape(x.shape)
+
+
+def swa_append(k_new, v_new, pos, swa_k, swa_v):
+    """In place: token b's K/V rows [B, D] go to slot pos[b] mod W of the
+    rings swa_k / swa_v [B, W, D] (u8, modified)."""
+    k_new, v_new = _c(k_new, np.float32), _c(v_new, np.float32)
+    pos = _c(pos, np.int64)
+    assert swa_k.flags["C_CONTIGUOUS"] and swa_v.flags["C_CONTIGUOUS"]
+    B, W, D = swa_k.shape
+    lib().oracle_swa_append(_p(k_new), _p(v_new), _p(pos), B, D, W, _p(swa_k), _p(swa_v))
 
 
 def set_threads(n):

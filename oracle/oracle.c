@@ -31,7 +31,9 @@
  * Parity status: every function here is pinned by the CPU tests (codec
  * tables against the OCP formulas and torch's FP8 decoder, integer
  * recomputation of scores, selection invariants and brute force, dense
- * attention special cases and a float64 textbook softmax attention).
+ * attention special cases and a float64 textbook softmax attention; the
+ * writers by round trips, brute-force nearest values, torch's FP8 cast within
+ * its finite range and the ring's contents after many appends).
  */
 #include <math.h>
 #include <stdint.h>
@@ -110,6 +112,46 @@ void oracle_fp4_quantize_row(const float* x, int D, uint8_t* codes, uint8_t* sca
             const int code = mag == 0 ? 0 : ((x[c] < 0.0f ? 8 : 0) | mag);
             if (c % 2 == 0) codes[c / 2] = (uint8_t)code;
             else codes[c / 2] = (uint8_t)(codes[c / 2] | (code << 4));
+        }
+    }
+}
+
+/* E4M3FN encoding of one fp32 value for the FP8 window (jaehun.me review,
+ * section "3) FP4 main KV + SWA Bounded Replay": the 128-token window is kept
+ * in FP8).  READING (the pages give no rounding rule): the nearest E4M3FN
+ * value, ties to the code with an even mantissa (round to nearest even), the
+ * sign of x kept (a negative value that rounds to zero gives 0x80), and
+ * magnitudes beyond 448, the largest finite value, saturate to 448 instead of
+ * becoming NaN.  Brute force over the 127 non-negative finite codes, in
+ * double (every E4M3 value and every fp32 input are exact there). */
+uint8_t oracle_e4m3_encode(float x) {
+    const double a = fabs((double)x);
+    const int sign = signbit(x) ? 0x80 : 0;
+    if (a >= 448.0) return (uint8_t)(0x7E | sign);   /* 448 is the nearest finite value */
+    int best = 0;
+    double bd = a;                           /* distance to code 0 */
+    /* below 448 the distances to the two neighbours of a are exact in double,
+     * and every other value is farther by at least an E4M3 step */
+    for (int b = 1; b <= 0x7E; ++b) {
+        const double d = fabs(a - oracle_e4m3(b));
+        if (d < bd || (d == bd && (b & 1) == 0 && (best & 1) == 1)) { best = b; bd = d; }
+    }
+    return (uint8_t)(best | sign);
+}
+
+/* Window ring update (same section: the window holds the W most recent
+ * tokens).  READING: sequence b keeps W slots [W, D]; the token at position
+ * pos[b] goes to slot pos[b] mod W, so after position p the ring holds
+ * exactly the tokens max(0, p - W + 1) .. p, in slot order rather than
+ * position order (attention over the window does not depend on the order).
+ * k_new, v_new [B, D] fp32; swa_k, swa_v [B, W, D] E4M3 bytes. */
+void oracle_swa_append(const float* k_new, const float* v_new, const int64_t* pos, int B, int D,
+                       int W, uint8_t* swa_k, uint8_t* swa_v) {
+    for (int b = 0; b < B; ++b) {
+        const size_t row = ((size_t)b * W + (size_t)(pos[b] % W)) * D;
+        for (int c = 0; c < D; ++c) {
+            swa_k[row + c] = oracle_e4m3_encode(k_new[(size_t)b * D + c]);
+            swa_v[row + c] = oracle_e4m3_encode(v_new[(size_t)b * D + c]);
         }
     }
 }

@@ -513,3 +513,91 @@ def test_fp4_writer_ties_go_to_the_even_code_and_no_negative_zero():
     for i, m in enumerate(mids):
         assert y[1 + 2 * i] == even_choice[i] and y[2 + 2 * i] == -even_choice[i]
     assert (codes[0, 7] >> 4) == 0
+
+
+# ------------------------------------------------- FP8 window ring writer
+
+def _e4m3_values():
+    return _fp8(np.arange(256, dtype=np.uint8))
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    # torch's CPU cast to float8_e4m3fn rounds to nearest even; within the
+    # finite rounding range (|x| < 464) the oracle must agree with it exactly
+    rng = np.random.default_rng(61)
+    x = (rng.standard_normal(6000) * np.exp2(rng.uniform(-14, 9, 6000))).astype(np.float32)
+    vals = _e4m3_values()[:127]
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)     # exact in fp32
+    edges = np.concatenate([mids, np.nextafter(mids, np.float32(0)),
+                            np.nextafter(mids, np.float32(1e9)), vals.astype(np.float32)])
+    x = np.concatenate([x, edges, -edges, [0.0, -0.0, 1e-30, -1e-30, 463.99, -463.99]])
+    x = x[np.abs(x) < 464].astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(x), want)
+
+
+def test_e4m3_encode_saturates_and_keeps_sign():
+    x = np.array([464, 480, 1e6, 3.4e38, -464, -1e30, 448, -448], np.float32)
+    assert oracle.e4m3_encode(x).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7E, 0xFE]
+    # a negative value that rounds to zero keeps its sign; ties between 0 and
+    # the smallest subnormal 2^-9 go to 0 (even)
+    x = np.array([-1e-6, 1e-6, 2 ** -10, -(2 ** -10), 3 * 2 ** -11], np.float32)
+    assert oracle.e4m3_encode(x).tolist() == [0x80, 0x00, 0x00, 0x80, 0x01]
+
+
+def test_e4m3_encode_is_a_nearest_value():
+    # brute force independent of the oracle's loop: the decoded byte is at a
+    # minimal distance from x among all finite E4M3 values
+    rng = np.random.default_rng(62)
+    x = (rng.standard_normal(3000) * np.exp2(rng.uniform(-12, 8, 3000))).astype(np.float32)
+    got = _fp8(oracle.e4m3_encode(x))
+    vals = _e4m3_values()
+    fin = vals[np.isfinite(vals)]
+    dist = np.abs(np.abs(x.astype(np.float64))[:, None] - np.abs(fin)[None, :]).min(axis=1)
+    assert np.array_equal(np.abs(np.abs(got) - np.abs(x.astype(np.float64))), dist)
+    assert np.all((got == 0) | (np.sign(got) == np.sign(x)))
+
+
+def test_swa_ring_holds_the_last_w_tokens():
+    B, W, D, T = 2, 5, 32, 13
+    rng = np.random.default_rng(63)
+    k = rng.standard_normal((T, B, D)).astype(np.float32)
+    v = rng.standard_normal((T, B, D)).astype(np.float32)
+    sk = np.zeros((B, W, D), np.uint8)
+    sv = np.zeros((B, W, D), np.uint8)
+    start = np.array([0, 3], np.int64)            # sequence 1 starts at position 3
+    for t in range(T):
+        oracle.swa_append(k[t], v[t], start + t, sk, sv)
+        for b in range(B):
+            n = min(W, t + 1)
+            held = sorted(sk[b, (start[b] + t - j) % W].tobytes() for j in range(n))
+            want = sorted(oracle.e4m3_encode(k[t - j, b]).tobytes() for j in range(n))
+            assert held == want
+            assert np.array_equal(sv[b, (start[b] + t) % W], oracle.e4m3_encode(v[t, b]))
+
+
+def test_attention_over_the_ring_equals_the_window_in_position_order():
+    # a window-only (K = 0) layer over the ring after 11 appends with W = 4
+    # equals the same layer with the last 4 tokens laid out in position order
+    B, H, W, D, T = 1, 3, 4, 32, 11
+    rng = np.random.default_rng(64)
+    k = rng.standard_normal((T, 1, D)).astype(np.float32)
+    v = rng.standard_normal((T, 1, D)).astype(np.float32)
+    sk = np.zeros((B, W, D), np.uint8)
+    sv = np.zeros((B, W, D), np.uint8)
+    for t in range(T):
+        oracle.swa_append(k[t], v[t], np.array([t], np.int64), sk, sv)
+    lin_k = np.stack([oracle.e4m3_encode(k[t, 0]) for t in range(T - W, T)])[None]
+    lin_v = np.stack([oracle.e4m3_encode(v[t, 0]) for t in range(T - W, T)])[None]
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    codes = np.zeros((1, D // 2), np.uint8)
+    scales = np.zeros((1, D // 16), np.uint8)
+    none = np.zeros((B, 0), np.int32)
+    off = np.zeros(1, np.int64)
+    sl = np.array([W], np.int32)
+    o1, l1 = oracle.attn_decode(q, codes, scales, off, none, sk, sv, sl, 0.2)
+    o2, l2 = oracle.attn_decode(q, codes, scales, off, none, lin_k, lin_v, sl, 0.2)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+    ref, rl = _textbook(q[0], _fp8(lin_k[0]), _fp8(lin_v[0]), 0.2)
+    np.testing.assert_allclose(o1[0], ref, rtol=0, atol=1e-5)
