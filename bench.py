@@ -186,12 +186,14 @@ def cpu_baseline(w, max_threads):
 
 
 def kv_writer_bench(args, torch, csa2):
-    """FP4 main-KV writer alone: fp32 rows -> E2M1 codes + E4M3 scale per 16
+    """The KV writers.  FP4 main-KV writer: fp32 rows -> E2M1 codes + E4M3 scale per 16
     channels, on a 1M-entry context's main KV (1,048,576 entries x 512
     channels: 65,536 generated rows tiled 16 times, 2 GiB of fp32, more than
     the last-level cache holds), on the 65,536-entry prefill context and on
     one prefill chunk's append (4,096 queries, m = 2: 2,048 entries).  One
-    step = one writer launch over all rows."""
+    step = one writer launch over all rows.  Also the FP8 window ring append
+    (one token per sequence, W = 128) for 32, 4,096 and 65,536 sequences, in
+    "swa_append"."""
     import oracle
     from gen import kv_rows_f32
 
@@ -229,6 +231,31 @@ def kv_writer_bench(args, torch, csa2):
             f"{ach:.0f} GB/s")
         del x, codes, scales
     del base
+    # FP8 window ring append: one token per sequence, 512 channels of K and V
+    swa = {}
+    for B in (32, 4096, 65536):
+        W = 128
+        k = torch.randn((B, D), device="cuda")
+        v = torch.randn((B, D), device="cuda")
+        pos = torch.arange(B, dtype=torch.int64, device="cuda") * 7 + 1000
+        rk = torch.zeros((B, W, D), dtype=torch.uint8, device="cuda")
+        rv = torch.zeros_like(rk)
+        for _ in range(args.warmup):
+            csa2.csa2_swa_append(k, v, pos, rk, rv)
+        csa2.profile_reset()
+        csa2.profile_enable(True)
+        for _ in range(args.steps):
+            csa2.csa2_swa_append(k, v, pos, rk, rv)
+        torch.cuda.synchronize()
+        n, kms = csa2.profile_read()["swa_append"]
+        csa2.profile_enable(False)
+        avg_us = 1000.0 * kms / n
+        alg = B * (2 * 4 * D + 2 * D)      # K and V: fp32 read, E4M3 bytes written
+        ach = alg / (avg_us * 1e-6) / 1e9
+        swa[f"B{B}"] = {"sequences": B, "avg_us": avg_us, "achieved_gbs": ach,
+                        "frac": ach / HBM_PEAK_GBS}
+        log(f"swa append B={B}: kernel {avg_us:.2f} us, {ach:.0f} GB/s")
+        del k, v, pos, rk, rv
     big = res_sizes["context_1m"]
     res = {
         "metric": "FP4 main-KV writer rows/s (fp32 -> E2M1 + E4M3 per 16 channels) at 1 MI355X",
@@ -241,6 +268,7 @@ def kv_writer_bench(args, torch, csa2):
         "config": {"workload": "FP4 main-KV writer: 1,048,576 entries x 512 channels",
                    "rows": big["rows"], "D": D, "parallelism": "single GPU"},
         "sizes": res_sizes,
+        "swa_append": swa,
         "roofline": {"bound": "hbm", "kernel": "kv_quantize_fp4", "achieved": big["achieved_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": big["frac"],
                      "traffic": measured_traffic("kv_writer_1m_rows.md")},

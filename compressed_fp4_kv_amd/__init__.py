@@ -13,7 +13,8 @@ import os
 __all__ = [
     "CSA2Error", "lib", "csa2_index_full", "csa2_index_full_workspace_bytes", "csa2_reindex",
     "csa2_reindex_workspace_bytes", "csa2_sparse_attn_decode", "csa2_decode_workspace_bytes",
-    "csa2_sparse_attn_prefill_chunk", "csa2_prefill_workspace_bytes", "profile_enable",
+    "csa2_sparse_attn_prefill_chunk", "csa2_prefill_workspace_bytes", "csa2_kv_quantize_fp4",
+    "csa2_swa_append", "profile_enable",
     "profile_read", "profile_reset", "EXPORTED_SYMBOLS",
 ]
 
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = [
     "csa2_debug_decode_tables",
     "csa2_debug_dequant_tables",
     "csa2_kv_quantize_fp4",
+    "csa2_swa_append",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -68,6 +70,7 @@ lib.csa2_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
 lib.csa2_debug_decode_tables.argtypes = [_P, _P, _P, _P, _P]
 lib.csa2_debug_dequant_tables.argtypes = [_P, _P, _P]
 lib.csa2_kv_quantize_fp4.argtypes = [_P, _I64, _I32, _P, _P, _P]
+lib.csa2_swa_append.argtypes = [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P]
 
 
 class CSA2Error(RuntimeError):
@@ -216,6 +219,20 @@ def csa2_kv_quantize_fp4(x, codes, scales, stream=None):
     _check(lib.csa2_kv_quantize_fp4(_ptr(x, f32, "x"), rows, D, _ptr(codes, u8, "codes"),
                                     _ptr(scales, u8, "scales"), _stream(stream)),
            "csa2_kv_quantize_fp4")
+
+
+def csa2_swa_append(k_new, v_new, pos, swa_k, swa_v, stream=None):
+    """k_new, v_new [B, D] f32; pos [B] i64; swa_k, swa_v [B, W, D] u8 rings:
+    token b goes to slot pos[b] mod W as E4M3FN bytes."""
+    f32, _, i64, u8 = _dt()
+    B, D = k_new.shape
+    W = swa_k.shape[1]
+    if (tuple(v_new.shape) != (B, D) or tuple(pos.shape) != (B,)
+            or tuple(swa_k.shape) != (B, W, D) or tuple(swa_v.shape) != (B, W, D)):
+        raise ValueError("csa2_swa_append: shapes of k_new, v_new, pos, swa_k, swa_v disagree")
+    _check(lib.csa2_swa_append(_ptr(k_new, f32, "k_new"), _ptr(v_new, f32, "v_new"),
+                               _ptr(pos, i64, "pos"), B, D, W, _ptr(swa_k, u8, "swa_k"),
+                               _ptr(swa_v, u8, "swa_v"), _stream(stream)), "csa2_swa_append")
 
 
 # ----------------------------------------------------------------- profiling

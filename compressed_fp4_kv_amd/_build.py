@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["abi.cpp", "stream.hip", "index.hip", "attn.hip", "kvwrite.hip"]
+SOURCES = ["abi.cpp", "stream.hip", "index.hip", "attn.hip", "kvwrite.hip", "swa.hip"]
 HIPCC = "/opt/rocm/bin/hipcc"
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # keep packed-fp32 instructions out of the generated code

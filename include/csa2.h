@@ -200,6 +200,26 @@ int csa2_kv_quantize_fp4(const float* x, int64_t rows, int32_t D, uint8_t* codes
                          uint8_t* scales, void* stream);
 
 /* ------------------------------------------------------------------------
+ * FP8 window ring append (jaehun.me review, section "3) FP4 main KV + SWA
+ * Bounded Replay": the last 128 tokens are kept in FP8 beside the sparse main
+ * KV; ainewsway.com article: a 128-token sliding window).  Reading of the
+ * ring: sequence b keeps W slots; its token at position pos[b] goes to slot
+ * pos[b] mod W, so after position p the ring holds tokens max(0, p-W+1) .. p
+ * and csa2_sparse_attn_decode reads it as the window with
+ * swa_len = min(W, p + 1) (the attention does not depend on the order of the
+ * window's tokens).  A window-only layer is csa2_sparse_attn_decode with
+ * topk = 0.  Encoding: E4M3FN, round to nearest even, the sign of zero kept,
+ * magnitudes beyond 448 saturated to 448 (never NaN for finite input).
+ *   k_new, v_new [B, D] fp32, 16-byte aligned, finite
+ *   pos          [B] int64, device; a negative position appends nothing
+ *   swa_k, swa_v [B, W, D] u8 (E4M3FN), 8-byte aligned; only slot
+ *                pos[b] mod W of each sequence is written
+ * D must be a multiple of 8 (else CSA2_ERR_UNSUPPORTED).  No workspace.
+ * ---------------------------------------------------------------------- */
+int csa2_swa_append(const float* k_new, const float* v_new, const int64_t* pos, int32_t B,
+                    int32_t D, int32_t W, uint8_t* swa_k, uint8_t* swa_v, void* stream);
+
+/* ------------------------------------------------------------------------
  * Optional per-kernel timing (for measurement tools).  While enabled, every
  * kernel the library launches is bracketed by hipEvents recorded on the
  * launch stream; csa2_profile_read synchronises on the last event and

@@ -1,7 +1,10 @@
-"""GPU parity of the FP4 main-KV writer (csa2_kv_quantize_fp4) with the
-oracle's quantiser: E2M1 codes and E4M3 scale bytes bit-exact, on random rows
-spanning every scale byte, on rows built around the rounding boundaries, at
-the prefill context's size, and on the argument checks."""
+"""GPU parity of the KV writers with the oracle.
+
+FP4 main-KV writer (csa2_kv_quantize_fp4): E2M1 codes and E4M3 scale bytes
+bit-exact, on random rows spanning every scale byte, on rows built around the
+rounding boundaries, at the prefill context's size and at 1M rows (sampled).
+FP8 window ring (csa2_swa_append): ring bytes bit-exact, and a window-only
+layer over the ring within the attention tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -171,3 +174,106 @@ def test_kv_writer_million_rows_sampled(csa2):
     ec, es = oracle.fp4_quantize_rows(xs)
     assert np.array_equal(scales[sel].cpu().numpy(), es)
     assert np.array_equal(codes[sel].cpu().numpy(), ec)
+
+
+# ------------------------------------------------------------ window ring
+
+def _fp8_edges():
+    """E4M3 values, midpoints between neighbours and one ulp either side,
+    saturation, tiny values and signed zeros, all as fp32."""
+    vals = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    e = np.concatenate([vals.astype(np.float32), mids, np.nextafter(mids, np.float32(0)),
+                        np.nextafter(mids, np.float32(1e9)),
+                        np.array([448, 460, 464, 465, 480, 1e6, 3.4e38, 1e-30, 2 ** -10,
+                                  2 ** -149, 0.0], np.float32)])
+    return np.concatenate([e, -e]).astype(np.float32)
+
+
+def test_swa_append_matches_oracle(csa2):
+    """One token per sequence into rings that already hold bytes: only slot
+    pos mod W changes, with the oracle's E4M3 bytes; a negative position
+    changes nothing."""
+    B, W, D = 37, 128, 512
+    rng = np.random.default_rng([7, 1])
+    k = (rng.standard_normal((B, D)) * np.exp2(rng.uniform(-14, 10, (B, 1)))).astype(np.float32)
+    v = (rng.standard_normal((B, D)) * np.exp2(rng.uniform(-14, 10, (B, 1)))).astype(np.float32)
+    edges = _fp8_edges()
+    k[:3].reshape(-1)[:edges.size] = edges
+    v[3:6].reshape(-1)[:edges.size] = edges[::-1]
+    pos = rng.integers(0, 5000, size=B).astype(np.int64)
+    pos[4], pos[5], pos[6] = 0, W - 1, -3
+    sk = rng.integers(0, 256, size=(B, W, D), dtype=np.uint8)
+    sv = rng.integers(0, 256, size=(B, W, D), dtype=np.uint8)
+    gk, gv = torch.from_numpy(sk.copy()).cuda(), torch.from_numpy(sv.copy()).cuda()
+    _say(f"swa append B={B} W={W} D={D}")
+    csa2.csa2_swa_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                         torch.from_numpy(pos).cuda(), gk, gv)
+    torch.cuda.synchronize()
+    keep = pos >= 0
+    ek, ev = sk.copy(), sv.copy()
+    for b in range(B):
+        if pos[b] >= 0:
+            ek[b, pos[b] % W] = oracle.e4m3_encode(k[b])
+            ev[b, pos[b] % W] = oracle.e4m3_encode(v[b])
+    # the same through the oracle's own ring update
+    rk, rv = sk[keep].copy(), sv[keep].copy()
+    oracle.swa_append(k[keep], v[keep], pos[keep], rk, rv)
+    assert np.array_equal(rk, ek[keep]) and np.array_equal(rv, ev[keep])
+    assert np.array_equal(gk.cpu().numpy(), ek), "window K ring differs"
+    assert np.array_equal(gv.cpu().numpy(), ev), "window V ring differs"
+
+
+def test_swa_ring_feeds_a_window_only_layer(csa2):
+    """300 appends per sequence (W = 128) through the ring, sequences
+    starting at different positions, then a window-only layer (K = 0) on
+    each sequence's ring at several points: rings bit-exact against the
+    oracle's, attention within max-abs 2e-3 / rel-L2 1e-3 of the oracle's."""
+    import _cases as C
+    B, W, D, H, T = 4, 128, 512, 64, 300
+    start = np.array([0, 5, 127, 1000], np.int64)
+    rng = np.random.default_rng([7, 2])
+    ks = rng.standard_normal((T, B, D)).astype(np.float32)
+    vs = rng.standard_normal((T, B, D)).astype(np.float32)
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    gk = torch.zeros((B, W, D), dtype=torch.uint8, device="cuda")
+    gv = torch.zeros((B, W, D), dtype=torch.uint8, device="cuda")
+    ok_, ov_ = np.zeros((B, W, D), np.uint8), np.zeros((B, W, D), np.uint8)
+    dk, dv = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    qd = torch.from_numpy(q).cuda()
+    codes = torch.zeros((1, D // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((1, D // 16), dtype=torch.uint8, device="cuda")
+    off = torch.zeros(B, dtype=torch.int64, device="cuda")
+    scale = 1.0 / np.sqrt(D)
+    _say(f"swa ring B={B} W={W} T={T}")
+    for t in range(T):
+        p = start + t
+        csa2.csa2_swa_append(dk[t], dv[t], torch.from_numpy(p).cuda(), gk, gv)
+        oracle.swa_append(ks[t], vs[t], p, ok_, ov_)
+        if t in (0, 60, 127, 128, 299):
+            n = np.minimum(W, start + t + 1).astype(np.int32)
+            out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+            lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+            nb = csa2.csa2_decode_workspace_bytes(B, H, D, 0, W)
+            ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+            csa2.csa2_sparse_attn_decode(qd, codes, scales, off, None, gk, gv,
+                                         torch.from_numpy(n).cuda(), scale, out, lse, ws=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(gk.cpu().numpy(), ok_) and np.array_equal(gv.cpu().numpy(), ov_)
+            ro, rl = oracle.attn_decode(q, codes.cpu().numpy(), scales.cpu().numpy(),
+                                        np.zeros(B, np.int64), np.zeros((B, 0), np.int32),
+                                        ok_, ov_, n, scale)
+            C.assert_attn_close(out.cpu().numpy(), ro, f"window-only layer after {t + 1} appends")
+            C.assert_lse_close(lse.cpu().numpy(), rl, f"window-only lse after {t + 1} appends")
+
+
+def test_swa_append_argument_checks(csa2):
+    dev = "cuda"
+    k = torch.zeros((2, 12), device=dev)
+    pos = torch.zeros(2, dtype=torch.int64, device=dev)
+    ring = torch.zeros((2, 4, 12), dtype=torch.uint8, device=dev)
+    with pytest.raises(csa2.CSA2Error):        # D not a multiple of 8
+        csa2.csa2_swa_append(k, k, pos, ring, ring.clone())
+    with pytest.raises(ValueError):            # ring shape disagrees
+        csa2.csa2_swa_append(torch.zeros((2, 16), device=dev), torch.zeros((2, 16), device=dev),
+                             pos, ring, ring.clone())
