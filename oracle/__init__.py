@@ -45,6 +45,9 @@ def lib():
         _lib.oracle_fp4_quantize_row.argtypes = [P, i32, P, P]
         _lib.oracle_index_full.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, P, i32, i32, P]
         _lib.oracle_reindex.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P]
+        _lib.oracle_index_full_e4m3.argtypes = _lib.oracle_index_full.argtypes
+        _lib.oracle_reindex_e4m3.argtypes = _lib.oracle_reindex.argtypes
+        _lib.oracle_scores_e4m3.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P]
         _lib.oracle_attn_decode.argtypes = [P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32,
                                             P, P]
         _lib.oracle_attn_prefill.argtypes = [P, i64, P, P, P, i32, P, P, i32, i32, i32, i32, f32,
@@ -116,37 +119,52 @@ def max_threads():
 
 
 def scores(qI, kI, seq_row_off, q_seq, q_nvis, q, Hi, Hk, Di):
-    qI, kI = _c(qI, np.float32), _c(kI, np.float32)
+    """Scores of query q; kI is an fp32 key cache or (uint8) E4M3FN key bytes."""
+    qI = _c(qI, np.float32)
+    kI, e4m3 = _keys(kI)
     seq_row_off, q_seq, q_nvis = _c(seq_row_off, np.int64), _c(q_seq, np.int32), _c(q_nvis, np.int32)
     out = np.empty(int(q_nvis[q]), np.float64)
-    lib().oracle_scores(_p(qI), _p(kI), _p(seq_row_off), _p(q_seq), _p(q_nvis), q, Hi, Hk, Di,
-                        _p(out))
+    f = lib().oracle_scores_e4m3 if e4m3 else lib().oracle_scores
+    f(_p(qI), _p(kI), _p(seq_row_off), _p(q_seq), _p(q_nvis), q, Hi, Hk, Di, _p(out))
     return out
+
+
+def _keys(kI):
+    """(pointer-ready array, e4m3?) for an fp32 key cache or a uint8 E4M3FN one."""
+    if np.asarray(kI).dtype == np.uint8:
+        return _c(kI, np.uint8), True
+    return _c(kI, np.float32), False
 
 
 def index_full(qI, kI, seq_row_off, q_seq, q_nvis, Hi, Hk, Di, topk, pool_blocks=0,
                block_size=8):
-    """Returns (topk_idx [Q,topk] int32, pool [Q,pool_blocks] int32 or None)."""
-    qI, kI = _c(qI, np.float32), _c(kI, np.float32)
+    """Returns (topk_idx [Q,topk] int32, pool [Q,pool_blocks] int32 or None).
+    kI is an fp32 key cache or, as uint8, the compact E4M3FN key cache."""
+    qI = _c(qI, np.float32)
+    kI, e4m3 = _keys(kI)
     seq_row_off, q_seq, q_nvis = _c(seq_row_off, np.int64), _c(q_seq, np.int32), _c(q_nvis, np.int32)
     Q = int(q_nvis.shape[0])
     idx = np.empty((Q, topk), np.int32)
     pool = np.empty((Q, pool_blocks), np.int32) if pool_blocks > 0 else None
-    rc = lib().oracle_index_full(_p(qI), _p(kI), _p(seq_row_off), _p(q_seq), _p(q_nvis), Q, Hi,
-                                 Hk, Di, topk, _p(idx), pool_blocks, block_size, _p(pool))
+    f = lib().oracle_index_full_e4m3 if e4m3 else lib().oracle_index_full
+    rc = f(_p(qI), _p(kI), _p(seq_row_off), _p(q_seq), _p(q_nvis), Q, Hi, Hk, Di, topk, _p(idx),
+           pool_blocks, block_size, _p(pool))
     if rc != 0:
         raise ValueError("oracle_index_full: bad argument")
     return idx, pool
 
 
 def reindex(qI, kI, seq_row_off, q_seq, q_nvis, pool, block_size, Hi, Hk, Di, topk):
-    qI, kI = _c(qI, np.float32), _c(kI, np.float32)
+    """kI is an fp32 key cache or, as uint8, the compact E4M3FN key cache."""
+    qI = _c(qI, np.float32)
+    kI, e4m3 = _keys(kI)
     seq_row_off, q_seq, q_nvis = _c(seq_row_off, np.int64), _c(q_seq, np.int32), _c(q_nvis, np.int32)
     pool = _c(pool, np.int32)
     Q, P = pool.shape
     idx = np.empty((Q, topk), np.int32)
-    rc = lib().oracle_reindex(_p(qI), _p(kI), _p(seq_row_off), _p(q_seq), _p(q_nvis), _p(pool), P,
-                              block_size, Q, Hi, Hk, Di, topk, _p(idx))
+    f = lib().oracle_reindex_e4m3 if e4m3 else lib().oracle_reindex
+    rc = f(_p(qI), _p(kI), _p(seq_row_off), _p(q_seq), _p(q_nvis), _p(pool), P, block_size, Q, Hi,
+           Hk, Di, topk, _p(idx))
     if rc != 0:
         raise ValueError("oracle_reindex: bad argument")
     return idx

@@ -30,7 +30,8 @@
  *
  * Parity status: every function here is pinned by the CPU tests (codec
  * tables against the OCP formulas and torch's FP8 decoder, integer
- * recomputation of scores, selection invariants and brute force, dense
+ * recomputation of scores over fp32 and over E4M3 key caches, a float64 sum
+ * over every finite E4M3 key value, selection invariants and brute force, dense
  * attention special cases and a float64 textbook softmax attention; the
  * writers by round trips, brute-force nearest values, torch's FP8 cast within
  * its finite range and the ring's contents after many appends).
@@ -207,6 +208,25 @@ static void select_topk(cand_t* c, int64_t n, int k, int32_t* out) {
     for (int i = take; i < k; ++i) out[i] = -1;
 }
 
+/* An indexer-key cache: rows of Hk*Di values, stored either as fp32 or, in
+ * the compact form, as one E4M3FN byte per value; exactly one of the two
+ * pointers is set.  READING: the pages give no storage format for indexer
+ * keys; a compact cache holds plain E4M3FN values with no scale (integers of
+ * magnitude up to 16 are exact in it). */
+typedef struct {
+    const float* f32;
+    const uint8_t* e4m3;
+} keys_t;
+
+/* Key row r (absolute row number) as fp32 values: the fp32 cache is read in
+ * place, E4M3 bytes are decoded into buf (every E4M3FN value is exact in
+ * fp32). */
+static const float* key_row(keys_t k, int64_t r, int RW, float* buf) {
+    if (k.f32) return k.f32 + (size_t)r * RW;
+    for (int i = 0; i < RW; ++i) buf[i] = (float)oracle_e4m3(k.e4m3[(size_t)r * RW + i]);
+    return buf;
+}
+
 /* Full mode [J-CSA2], [J-EX]: score every visible entry t < q_nvis[q] of the
  * query's sequence and keep the Top-K.  With pool_blocks > 0 it also builds
  * the candidate pool [J-CSA2]: entries are grouped into aligned blocks
@@ -215,23 +235,27 @@ static void select_topk(cand_t* c, int64_t n, int k, int32_t* out) {
  * id) form the pool, written ascending and padded with -1.
  * Index arrays are local to the sequence.  Returns 0, or -1 on a bad
  * argument. */
-int oracle_index_full(const float* qI, const float* kI, const int64_t* seq_row_off,
+static int index_full(const float* qI, keys_t kI, const int64_t* seq_row_off,
                       const int32_t* q_seq, const int32_t* q_nvis, int Q, int Hi, int Hk, int Di,
                       int topk, int32_t* topk_idx, int pool_blocks, int block_size,
                       int32_t* pool_idx) {
     if (Q < 0 || Hi <= 0 || Hk <= 0 || Di <= 0 || topk < 0 || pool_blocks < 0) return -1;
     if (pool_blocks > 0 && block_size <= 0) return -1;
+    const int RW = Hk * Di;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int q = 0; q < Q; ++q) {
         int64_t n = q_nvis[q];
-        const float* base = kI + (size_t)seq_row_off[q_seq[q]] * Hk * Di;
+        const int64_t row0 = seq_row_off[q_seq[q]];
         cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
-        if (!c) { bad = 1; continue; }
+        float* buf = (float*)malloc(sizeof(float) * (size_t)RW);
+        if (!c || !buf) { free(c); free(buf); bad = 1; continue; }
         for (int64_t t = 0; t < n; ++t) {
-            c[t].s = oracle_score(qI + (size_t)q * Hi * Di, base + (size_t)t * Hk * Di, Hi, Hk, Di);
+            c[t].s = oracle_score(qI + (size_t)q * Hi * Di, key_row(kI, row0 + t, RW, buf), Hi, Hk,
+                                  Di);
             c[t].id = t;
         }
+        free(buf);
         if (pool_blocks > 0) {
             int64_t nb = (n + block_size - 1) / block_size;
             cand_t* b = (cand_t*)malloc(sizeof(cand_t) * (size_t)(nb > 0 ? nb : 1));
@@ -252,24 +276,44 @@ int oracle_index_full(const float* qI, const float* kI, const int64_t* seq_row_o
     return bad ? -1 : 0;
 }
 
+int oracle_index_full(const float* qI, const float* kI, const int64_t* seq_row_off,
+                      const int32_t* q_seq, const int32_t* q_nvis, int Q, int Hi, int Hk, int Di,
+                      int topk, int32_t* topk_idx, int pool_blocks, int block_size,
+                      int32_t* pool_idx) {
+    keys_t k = {kI, NULL};
+    return index_full(qI, k, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, topk, topk_idx,
+                      pool_blocks, block_size, pool_idx);
+}
+
+/* The same Full mode over a compact key cache of E4M3FN bytes [rows, Hk, Di]. */
+int oracle_index_full_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row_off,
+                           const int32_t* q_seq, const int32_t* q_nvis, int Q, int Hi, int Hk,
+                           int Di, int topk, int32_t* topk_idx, int pool_blocks, int block_size,
+                           int32_t* pool_idx) {
+    keys_t k = {NULL, kI};
+    return index_full(qI, k, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, topk, topk_idx,
+                      pool_blocks, block_size, pool_idx);
+}
+
 /* Reindex mode [J-CSA2], [J-EX]: the candidates are the visible positions of
  * the pool's blocks, {b*bs + j : b in the pool row (b >= 0), j < bs,
  * b*bs + j < q_nvis[q]}; they are rescored with this layer's own indexer
  * query against the shared key cache and the Top-K taken, ties to the lower
  * entry index.  READING: the keys are the Full layer's indexer-key cache. */
-int oracle_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
-                   const int32_t* q_seq, const int32_t* q_nvis, const int32_t* pool_idx,
-                   int pool_blocks, int block_size, int Q, int Hi, int Hk, int Di, int topk,
-                   int32_t* topk_idx) {
+static int reindex(const float* qI, keys_t kI, const int64_t* seq_row_off, const int32_t* q_seq,
+                   const int32_t* q_nvis, const int32_t* pool_idx, int pool_blocks,
+                   int block_size, int Q, int Hi, int Hk, int Di, int topk, int32_t* topk_idx) {
     if (Q < 0 || Hi <= 0 || Hk <= 0 || Di <= 0 || topk < 0 || pool_blocks < 0 || block_size <= 0)
         return -1;
+    const int RW = Hk * Di;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int q = 0; q < Q; ++q) {
         int64_t n = q_nvis[q];
-        const float* base = kI + (size_t)seq_row_off[q_seq[q]] * Hk * Di;
+        const int64_t row0 = seq_row_off[q_seq[q]];
         cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)pool_blocks * block_size + 1);
-        if (!c) { bad = 1; continue; }
+        float* buf = (float*)malloc(sizeof(float) * (size_t)RW);
+        if (!c || !buf) { free(c); free(buf); bad = 1; continue; }
         int64_t m = 0;
         for (int j = 0; j < pool_blocks; ++j) {
             int64_t b = pool_idx[(size_t)q * pool_blocks + j];
@@ -277,15 +321,36 @@ int oracle_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
             for (int i = 0; i < block_size; ++i) {
                 int64_t t = b * block_size + i;
                 if (t >= n) break;
-                c[m].s = oracle_score(qI + (size_t)q * Hi * Di, base + (size_t)t * Hk * Di, Hi, Hk, Di);
+                c[m].s = oracle_score(qI + (size_t)q * Hi * Di, key_row(kI, row0 + t, RW, buf), Hi,
+                                      Hk, Di);
                 c[m].id = t;
                 ++m;
             }
         }
+        free(buf);
         if (topk > 0) select_topk(c, m, topk, topk_idx + (size_t)q * topk);
         free(c);
     }
     return bad ? -1 : 0;
+}
+
+int oracle_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
+                   const int32_t* q_seq, const int32_t* q_nvis, const int32_t* pool_idx,
+                   int pool_blocks, int block_size, int Q, int Hi, int Hk, int Di, int topk,
+                   int32_t* topk_idx) {
+    keys_t k = {kI, NULL};
+    return reindex(qI, k, seq_row_off, q_seq, q_nvis, pool_idx, pool_blocks, block_size, Q, Hi,
+                   Hk, Di, topk, topk_idx);
+}
+
+/* The same Reindex mode over a compact key cache of E4M3FN bytes. */
+int oracle_reindex_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row_off,
+                        const int32_t* q_seq, const int32_t* q_nvis, const int32_t* pool_idx,
+                        int pool_blocks, int block_size, int Q, int Hi, int Hk, int Di, int topk,
+                        int32_t* topk_idx) {
+    keys_t k = {NULL, kI};
+    return reindex(qI, k, seq_row_off, q_seq, q_nvis, pool_idx, pool_blocks, block_size, Q, Hi,
+                   Hk, Di, topk, topk_idx);
 }
 
 /* -------------------------------------------------------------- attention */
@@ -422,6 +487,20 @@ int oracle_scores(const float* qI, const float* kI, const int64_t* seq_row_off,
     const float* base = kI + (size_t)seq_row_off[q_seq[q]] * Hk * Di;
     for (int64_t t = 0; t < q_nvis[q]; ++t)
         out[t] = oracle_score(qI + (size_t)q * Hi * Di, base + (size_t)t * Hk * Di, Hi, Hk, Di);
+    return 0;
+}
+
+int oracle_scores_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row_off,
+                       const int32_t* q_seq, const int32_t* q_nvis, int q, int Hi, int Hk, int Di,
+                       double* out) {
+    keys_t k = {NULL, kI};
+    const int RW = Hk * Di;
+    float* buf = (float*)malloc(sizeof(float) * (size_t)RW);
+    if (!buf) return -1;
+    for (int64_t t = 0; t < q_nvis[q]; ++t)
+        out[t] = oracle_score(qI + (size_t)q * Hi * Di,
+                              key_row(k, seq_row_off[q_seq[q]] + t, RW, buf), Hi, Hk, Di);
+    free(buf);
     return 0;
 }
 

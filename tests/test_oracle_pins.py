@@ -601,3 +601,88 @@ def test_attention_over_the_ring_equals_the_window_in_position_order():
     np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
     ref, rl = _textbook(q[0], _fp8(lin_k[0]), _fp8(lin_v[0]), 0.2)
     np.testing.assert_allclose(o1[0], ref, rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------- compact (E4M3) indexer keys
+
+def _e4m3_bytes_of(x):
+    """fp32 values -> E4M3FN bytes with torch's cast (exact for the integers used here)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_decode_torch(b):
+    return torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_integer_keys_are_exact_in_e4m3():
+    v = np.arange(-16, 17, dtype=np.float32)
+    assert np.array_equal(_e4m3_decode_torch(_e4m3_bytes_of(v)), v.astype(np.float64))
+
+
+@pytest.mark.parametrize("Hk", [4, 1])
+def test_e4m3_key_scores_equal_int64_recomputation(Hk):
+    Hi, Di, n = 4, 64, 300
+    kI = host_ints(12, 1, 0, n * Hk * Di).reshape(n, Hk, Di)
+    qI = host_ints(12, 2, 0, Hi * Di).reshape(1, Hi, Di)
+    k8 = _e4m3_bytes_of(kI)
+    assert k8.dtype == np.uint8 and k8.shape == (n, Hk, Di)
+    s = oracle.scores(qI, k8, [0], [0], [n], 0, Hi, Hk, Di)
+    ki, qi = kI.astype(np.int64), qI[0].astype(np.int64)
+    ref = np.zeros(n, np.int64)
+    for h in range(Hi):
+        ref += ki[:, h % Hk, :] @ qi[h]
+    assert np.array_equal(s, ref.astype(np.float64))
+
+
+def test_e4m3_key_scores_over_every_finite_value():
+    # random bytes over all 254 finite E4M3FN values (subnormals, 448, both
+    # zeros) against general fp32 queries: a float64 sum of torch's decodes
+    rng = np.random.default_rng(5)
+    Hi, Hk, Di, n = 2, 2, 128, 64
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    k8 = rng.choice(finite, size=(n, Hk, Di)).astype(np.uint8)
+    k8[0, 0, :] = finite[:128]
+    k8[0, 1, :] = finite[126:]
+    qI = rng.standard_normal((1, Hi, Di)).astype(np.float32)
+    s = oracle.scores(qI, k8, [0], [0], [n], 0, Hi, Hk, Di)
+    kd = _e4m3_decode_torch(k8)
+    ref = np.einsum("nhd,hd->n", kd, qI[0].astype(np.float64))
+    assert np.allclose(s, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+
+
+def test_e4m3_keys_select_as_the_fp32_keys_they_encode():
+    # packed sequences, partial visibility, Top-K, pool and Reindex
+    Hi, Hk, Di = 4, 4, 64
+    ctx = [3000, 1500, 777]
+    off = np.concatenate([[0], np.cumsum(ctx)[:-1]]).astype(np.int64)
+    rows = int(np.sum(ctx))
+    kI = host_ints(13, 1, 0, rows * Hk * Di).reshape(rows, Hk, Di)
+    qI = host_ints(13, 2, 0, 3 * Hi * Di).reshape(3, Hi, Di)
+    k8 = _e4m3_bytes_of(kI)
+    nvis = [3000, 1200, 777]
+    a = oracle.index_full(qI, kI, off, [0, 1, 2], nvis, Hi, Hk, Di, 64, pool_blocks=40,
+                          block_size=8)
+    b = oracle.index_full(qI, k8, off, [0, 1, 2], nvis, Hi, Hk, Di, 64, pool_blocks=40,
+                          block_size=8)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    q2 = host_ints(13, 3, 0, 3 * Hi * Di).reshape(3, Hi, Di)
+    ra = oracle.reindex(q2, kI, off, [0, 1, 2], nvis, a[1], 8, Hi, Hk, Di, 64)
+    rb = oracle.reindex(q2, k8, off, [0, 1, 2], nvis, a[1], 8, Hi, Hk, Di, 64)
+    assert np.array_equal(ra, rb)
+    for q in range(3):
+        s = oracle.scores(qI, k8, off, [0, 1, 2], nvis, q, Hi, Hk, Di)
+        _check_topk_invariants(s, b[0][q], 64)
+
+
+def test_e4m3_key_topk_invariants_on_general_values():
+    rng = np.random.default_rng(6)
+    Hi, Hk, Di, n, k = 4, 1, 64, 2000, 100
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    k8 = rng.choice(finite, size=(n, Hk, Di)).astype(np.uint8)
+    qI = rng.standard_normal((1, Hi, Di)).astype(np.float32)
+    idx, _ = oracle.index_full(qI, k8, [0], [0], [n], Hi, Hk, Di, k)
+    kd = _e4m3_decode_torch(k8)[:, 0, :]
+    s = kd @ qI[0].astype(np.float64).sum(axis=0)
+    _check_topk_invariants(s, idx[0], k)
