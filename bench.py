@@ -8,8 +8,12 @@ channels over the 512 selected FP4 rows + a 128-token FP8 window, each layer
 with its own query and window).  Inputs are seeded synthetic tensors already
 resident in HBM.  Prints one JSON line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--keys f32|e4m3]
        python bench.py --kv-writer   (the FP4 main-KV writer alone, its own line)
+
+--keys e4m3 runs the same step over the compact indexer-key cache (one
+E4M3FN byte per key value instead of fp32), through csa2_index_full_e4m3 and
+csa2_reindex_e4m3.
 """
 import argparse
 import json
@@ -59,8 +63,12 @@ def measured_traffic(profile="score_stream_c1_traffic.md"):
     return None
 
 
-def make_step(csa2, w, t, torch):
+def make_step(csa2, w, t, torch, keys="f32"):
     """One pass of the workload's call sequence (all of its layers)."""
+    e4m3 = keys == "e4m3"
+    kI = t["kI8"] if e4m3 else t["kI"]
+    index_full = csa2.csa2_index_full_e4m3 if e4m3 else csa2.csa2_index_full
+    reindex = csa2.csa2_reindex_e4m3 if e4m3 else csa2.csa2_reindex
     Q = w.Q
     max_nvis = int(w.q_nvis().max())
     dev = "cuda"
@@ -99,39 +107,45 @@ def make_step(csa2, w, t, torch):
     def step():
         if w.kind in ("decode_full", "prefill"):
             # Full layer: indexer, then Full + Reuse layers on the same indices and KV
-            csa2.csa2_index_full(t["qI_full"], t["kI"], t["seq_row_off"],
-                                 None if w.kind == "prefill" else t["q_seq"], t["q_nvis"],
-                                 max_nvis, w.topk, idx, ws=ws_i)
+            index_full(t["qI_full"], kI, t["seq_row_off"],
+                       None if w.kind == "prefill" else t["q_seq"], t["q_nvis"], max_nvis, w.topk,
+                       idx, ws=ws_i)
             for layer in range(w.layers):
                 attn(layer, idx)
             return
         if w.kind == "decode_hier":
             # the Full layer's indexer builds Top-K and the candidate pool
-            csa2.csa2_index_full(t["qI_full"], t["kI"], t["seq_row_off"], t["q_seq"], t["q_nvis"],
-                                 max_nvis, w.topk, idx, P, w.block_size, pool, ws=ws_i)
+            index_full(t["qI_full"], kI, t["seq_row_off"], t["q_seq"], t["q_nvis"], max_nvis,
+                       w.topk, idx, P, w.block_size, pool, ws=ws_i)
         # Reindex layer over the pool, then Reindex + Reuse layers' attention
-        csa2.csa2_reindex(t["qI_reindex"], t["kI"], t["seq_row_off"], t["q_seq"], t["q_nvis"],
-                          pool, w.block_size, w.topk, ridx, ws=ws_r)
+        reindex(t["qI_reindex"], kI, t["seq_row_off"], t["q_seq"], t["q_nvis"], pool,
+                w.block_size, w.topk, ridx, ws=ws_r)
         for layer in range(w.layers):
             attn(layer, ridx)
     return step, idx
 
 
-def dominant_roofline(w, kern):
+def dominant_roofline(w, kern, keys="f32"):
     """Roofline record of the workload's dominant kernel (algorithmic work per
-    launch / measured average launch time)."""
-    if w.kind in ("decode_full", "decode_hier") and "score_stream" in kern:
-        alg = float(w.rows) * w.row_width * 4 + float(w.Q) * w.Hi * w.Di * 4
-        ach = alg / (kern["score_stream"]["avg_us"] * 1e-6) / 1e9
-        return {"bound": "hbm", "kernel": "score_stream", "achieved": ach, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                "traffic": measured_traffic() if w.name.startswith("c1") else None}
-    if w.kind == "decode_reindex" and "reindex_score" in kern:
+    launch / measured average launch time).  Key bytes per value: 4 (fp32) or
+    1 (E4M3 key cache)."""
+    sfx, vb = ("_e4m3", 1) if keys == "e4m3" else ("", 4)
+    stream, rscore = "score_stream" + sfx, "reindex_score" + sfx
+    if w.kind in ("decode_full", "decode_hier") and stream in kern:
+        alg = float(w.rows) * w.row_width * vb + float(w.Q) * w.Hi * w.Di * 4
+        ach = alg / (kern[stream]["avg_us"] * 1e-6) / 1e9
+        traffic = None
+        if w.name.startswith("c1"):
+            traffic = measured_traffic("score_stream_e4m3_c1_traffic.md" if sfx
+                                       else "score_stream_c1_traffic.md")
+        return {"bound": "hbm", "kernel": stream, "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic}
+    if w.kind == "decode_reindex" and rscore in kern:
         import numpy as np
         rows = sum(min(int(np.sum(w.pool[b] >= 0)) * w.block_size, w.ctx[b]) for b in range(w.B))
-        alg = float(rows) * w.row_width * 4
-        ach = alg / (kern["reindex_score"]["avg_us"] * 1e-6) / 1e9
-        return {"bound": "hbm", "kernel": "reindex_score", "achieved": ach, "peak": HBM_PEAK_GBS,
+        alg = float(rows) * w.row_width * vb
+        ach = alg / (kern[rscore]["avg_us"] * 1e-6) / 1e9
+        return {"bound": "hbm", "kernel": rscore, "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
     if "attn" in kern:
         return mfma_utilisation(w, kern)["attn"] | {"traffic": None}
@@ -159,15 +173,15 @@ def mfma_utilisation(w, kern):
     return res
 
 
-def cpu_baseline(w, max_threads):
+def cpu_baseline(w, max_threads, keys="f32"):
     """The oracle on the host cores, on the same workload (whole batch)."""
-    import numpy as np
     import oracle
-    from gen.workloads import T_QI_FULL, host_kI_rows, host_kv_rows, host_q, host_qI, host_swa
+    from gen.workloads import (T_QI_FULL, host_kI_rows, host_kI_rows_e4m3, host_kv_rows, host_q,
+                               host_qI, host_swa)
 
     threads = max(1, min(max_threads, w.B))
     oracle.set_threads(threads)
-    kI = host_kI_rows(w, 0, w.rows)
+    kI = (host_kI_rows_e4m3 if keys == "e4m3" else host_kI_rows)(w, 0, w.rows)
     qI = host_qI(w, T_QI_FULL)
     codes, scales = host_kv_rows(w, 0, w.rows)
     qs = [host_q(w, l) for l in range(w.layers)]
@@ -299,6 +313,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1,
                     help="workload number (1 = the decode workload the metric is quoted on)")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--keys", choices=("f32", "e4m3"), default="f32",
+                    help="indexer-key cache: fp32 (the workloads as stated) or E4M3 bytes")
     ap.add_argument("--kv-writer", action="store_true",
                     help="measure the FP4 main-KV writer alone (its own JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -328,8 +344,8 @@ def main():
 
     w = workload(args.workload)
     log(f"building inputs: {w.name} B={w.B} ctx={w.ctx[0]} H={w.H} topk={w.topk}")
-    t = build_device(w)
-    step, idx = make_step(csa2, w, t, torch)
+    t = build_device(w, keys=args.keys)
+    step, idx = make_step(csa2, w, t, torch, args.keys)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -371,10 +387,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded integer indexer inputs, FP4 E2M1/E4M3 KV, N(0,1) queries, "
                 "FP8 window)",
-        "config": {"workload": WORKLOAD_NAMES.get(w.name, w.name),
+        "config": {"workload": WORKLOAD_NAMES.get(w.name, w.name) + (
+                       "; indexer keys stored as E4M3FN bytes" if args.keys == "e4m3" else ""),
                    "global_batch": w.Q, "seq_len": int(max(w.ctx)), "parallelism": "single GPU"},
         "kernels": kern,
-        "roofline": dominant_roofline(w, kern),
+        "roofline": dominant_roofline(w, kern, args.keys),
     }
     if w.kind == "prefill":
         res["mfma_utilisation"] = mfma_utilisation(w, kern)
@@ -382,7 +399,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.workload == 1:
         log("cpu baseline (oracle) ...")
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_threads)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_threads, args.keys)
     print(json.dumps(res), flush=True)
 
 

@@ -12,6 +12,7 @@ import os
 
 __all__ = [
     "CSA2Error", "lib", "csa2_index_full", "csa2_index_full_workspace_bytes", "csa2_reindex",
+    "csa2_index_full_e4m3", "csa2_reindex_e4m3",
     "csa2_reindex_workspace_bytes", "csa2_sparse_attn_decode", "csa2_decode_workspace_bytes",
     "csa2_sparse_attn_prefill_chunk", "csa2_prefill_workspace_bytes", "csa2_kv_quantize_fp4",
     "csa2_swa_append", "profile_enable",
@@ -32,6 +33,7 @@ EXPORTED_SYMBOLS = [
     "csa2_debug_dequant_tables",
     "csa2_kv_quantize_fp4",
     "csa2_swa_append",
+    "csa2_index_full_e4m3", "csa2_reindex_e4m3",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -52,10 +54,12 @@ lib.csa2_index_full_workspace_bytes.restype = _SZ
 lib.csa2_index_full_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
 lib.csa2_index_full.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32,
                                 _I32, _P, _P, _SZ, _P]
+lib.csa2_index_full_e4m3.argtypes = lib.csa2_index_full.argtypes
 lib.csa2_reindex_workspace_bytes.restype = _SZ
 lib.csa2_reindex_workspace_bytes.argtypes = [_I32, _I32, _I32]
 lib.csa2_reindex.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                              _P, _SZ, _P]
+lib.csa2_reindex_e4m3.argtypes = lib.csa2_reindex.argtypes
 lib.csa2_decode_workspace_bytes.restype = _SZ
 lib.csa2_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
 lib.csa2_sparse_attn_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
@@ -131,37 +135,64 @@ def csa2_index_prefill_workspace_bytes(Q, max_nvis, topk, Hk, Di):
     return int(lib.csa2_index_prefill_workspace_bytes(Q, max_nvis, topk, Hk, Di))
 
 
-def csa2_index_full(qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,
-                    pool_blocks=0, block_size=8, pool_block_idx=None, ws=None, stream=None):
-    """qI [Q,Hi,Di] f32; kI [rows,Hk,Di] f32; seq_row_off [S] i64; q_seq [Q] i32 or None;
-    q_nvis [Q] i32; topk_idx [Q,topk] i32 out; pool_block_idx [Q,pool_blocks] i32 out."""
+def _index_full(fn, kdt, qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,
+                pool_blocks, block_size, pool_block_idx, ws, stream):
     f32, i32, i64, _ = _dt()
     Q, Hi, Di = qI.shape
     Hk = kI.shape[1]
     wp, wn = _ws(ws)
-    _check(lib.csa2_index_full(
-        _ptr(qI, f32, "qI"), _ptr(kI, f32, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
+    name = fn.__name__
+    _check(fn(
+        _ptr(qI, f32, "qI"), _ptr(kI, kdt, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
         _ptr(q_seq, i32, "q_seq"), _ptr(q_nvis, i32, "q_nvis"), Q, Hi, Hk, Di, max_nvis, topk,
         _ptr(topk_idx, i32, "topk_idx"), pool_blocks, block_size,
-        _ptr(pool_block_idx, i32, "pool_block_idx"), wp, wn, _stream(stream)), "csa2_index_full")
+        _ptr(pool_block_idx, i32, "pool_block_idx"), wp, wn, _stream(stream)), name)
+
+
+def csa2_index_full(qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,
+                    pool_blocks=0, block_size=8, pool_block_idx=None, ws=None, stream=None):
+    """qI [Q,Hi,Di] f32; kI [rows,Hk,Di] f32; seq_row_off [S] i64; q_seq [Q] i32 or None;
+    q_nvis [Q] i32; topk_idx [Q,topk] i32 out; pool_block_idx [Q,pool_blocks] i32 out."""
+    _index_full(lib.csa2_index_full, _dt()[0], qI, kI, seq_row_off, q_seq, q_nvis, max_nvis,
+                topk, topk_idx, pool_blocks, block_size, pool_block_idx, ws, stream)
+
+
+def csa2_index_full_e4m3(qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,
+                         pool_blocks=0, block_size=8, pool_block_idx=None, ws=None, stream=None):
+    """As csa2_index_full with kI [rows,Hk,Di] u8 holding E4M3FN key bytes."""
+    _index_full(lib.csa2_index_full_e4m3, _dt()[3], qI, kI, seq_row_off, q_seq, q_nvis,
+                max_nvis, topk, topk_idx, pool_blocks, block_size, pool_block_idx, ws, stream)
 
 
 def csa2_reindex_workspace_bytes(Q, pool_blocks, block_size):
     return int(lib.csa2_reindex_workspace_bytes(Q, pool_blocks, block_size))
 
 
-def csa2_reindex(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, block_size, topk, topk_idx,
-                 ws=None, stream=None):
+def _reindex(fn, kdt, qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, block_size, topk,
+             topk_idx, ws, stream):
     f32, i32, i64, _ = _dt()
     Q, Hi, Di = qI.shape
     Hk = kI.shape[1]
     P = pool_block_idx.shape[1]
     wp, wn = _ws(ws)
-    _check(lib.csa2_reindex(
-        _ptr(qI, f32, "qI"), _ptr(kI, f32, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
+    _check(fn(
+        _ptr(qI, f32, "qI"), _ptr(kI, kdt, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
         _ptr(q_seq, i32, "q_seq"), _ptr(q_nvis, i32, "q_nvis"),
         _ptr(pool_block_idx, i32, "pool_block_idx"), P, block_size, Q, Hi, Hk, Di, topk,
-        _ptr(topk_idx, i32, "topk_idx"), wp, wn, _stream(stream)), "csa2_reindex")
+        _ptr(topk_idx, i32, "topk_idx"), wp, wn, _stream(stream)), fn.__name__)
+
+
+def csa2_reindex(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, block_size, topk, topk_idx,
+                 ws=None, stream=None):
+    _reindex(lib.csa2_reindex, _dt()[0], qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx,
+             block_size, topk, topk_idx, ws, stream)
+
+
+def csa2_reindex_e4m3(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, block_size, topk,
+                      topk_idx, ws=None, stream=None):
+    """As csa2_reindex with kI [rows,Hk,Di] u8 holding E4M3FN key bytes."""
+    _reindex(lib.csa2_reindex_e4m3, _dt()[3], qI, kI, seq_row_off, q_seq, q_nvis,
+             pool_block_idx, block_size, topk, topk_idx, ws, stream)
 
 
 # ---------------------------------------------------------------- attention

@@ -665,15 +665,27 @@ __device__ __forceinline__ bool split4_bf16(float4 x, uint2& hi, uint2& lo) {
     return any;
 }
 
+// Four consecutive key values as fp32: an fp32 key row is read as is, E4M3
+// key bytes are decoded exactly (gfx950 OCP FP8 conversion).
+__device__ __forceinline__ float4 load_key4(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ float4 load_key4(const uint8_t* p) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    const float2 lo = fp8x2_to_f32<false>(w), hi = fp8x2_to_f32<true>(w);
+    return make_float4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // Workgroups [0, Qp/64) convert query rows, the rest key rows (64 each).
+template <typename KT>
 __global__ __launch_bounds__(256) void k_prefill_convert(
-    const float* __restrict__ qI, const float* __restrict__ kI,
+    const float* __restrict__ qI, const KT* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, int Q, int Qp, int Hi, int Hk,
     int Di, int N, uint16_t* __restrict__ qh, uint16_t* __restrict__ ql,
     uint16_t* __restrict__ kh, uint16_t* __restrict__ kl, uint32_t* __restrict__ qflag,
     uint32_t* __restrict__ kflag) {
     const int RW = Hk * Di, f4 = RW / 4;
-    const float* kb = kI + seq_row_off[0] * (int64_t)RW;
+    const KT* kb = kI + seq_row_off[0] * (int64_t)RW;
     const int nqb = Qp / kCvtRows;
     const bool isq = (int)blockIdx.x < nqb;
     const int blk = isq ? blockIdx.x : blockIdx.x - nqb;
@@ -685,8 +697,7 @@ __global__ __launch_bounds__(256) void k_prefill_convert(
         const int r = r0 + f / f4, c = 4 * (f % f4);
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
         if (r < nrow)
-            x = isq ? load_qrow4(qI, r, Hi, Hk, Di, c)
-                    : *reinterpret_cast<const float4*>(kb + (size_t)r * RW + c);
+            x = isq ? load_qrow4(qI, r, Hi, Hk, Di, c) : load_key4(kb + (size_t)r * RW + c);
         uint2 h, l;
         any |= split4_bf16(x, h, l) ? 1 : 0;
         *reinterpret_cast<uint2*>(dh + (size_t)r * RW + c) = h;
@@ -933,9 +944,9 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
 
 // ------------------------------------------------------------- reindex
 
-template <int VPR>
+template <int VPR, typename KT>
 __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
-    const float* __restrict__ qI, const float* __restrict__ kI,
+    const float* __restrict__ qI, const KT* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, const int32_t* __restrict__ pool,
     int P, int bs, uint64_t* __restrict__ ckeys) {
@@ -946,17 +957,17 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
     if (c0 >= ncand) return;
     const int c1 = min(ncand, c0 + kReindexPerWG);
     float4 qv[VPR];
-    load_qvec<VPR>(qI, q, Hi, Hk, Di, qv);
+    load_qvec<VPR, sizeof(KT) == 1>(qI, q, Hi, Hk, Di, qv);
     const int nvis = q_nvis[q];
     const int64_t row0 = seq_row_off[q_seq ? q_seq[q] : 0];
-    const float* kb = kI + row0 * RW;
+    const KT* kb = kI + row0 * RW;
     const int32_t* prow = pool + (size_t)q * P;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int myrow = (lane >> 3) & 7;
     // wave w scores candidates c0 + 64 w .. +63: lane l first resolves
     // candidate c0 + 64 w + l to its entry row (-1: none), so that every row
     // address of the gathers below is a lane read away, not a load away
-    constexpr int kRows = VPR >= 4 ? 8 : 16;   // rows per gather round
+    constexpr int kRows = stream_rows<VPR, KT>();   // rows per gather round
     const int cw = c0 + kWave * wave;
     int64_t tl = -1;
     {
@@ -971,7 +982,7 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
 #pragma unroll
     for (int it = 0; it < kWave / kRows; ++it) {
         if (cw + kRows * it >= c1) break;   // wave-uniform
-        const float* rows[kRows];
+        const KT* rows[kRows];
         bool ok[kRows];
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
@@ -1127,12 +1138,13 @@ extern "C" size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, i
     return carve_index(nullptr, Q, max_nvis, topk, pool_blocks, block_size).bytes;
 }
 
-extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* seq_row_off,
-                               const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
-                               int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk,
-                               int32_t* topk_idx, int32_t pool_blocks, int32_t block_size,
-                               int32_t* pool_block_idx, void* ws, size_t ws_bytes,
-                               void* stream_) {
+// Full-mode indexer over a key cache of KT values (float or E4M3 bytes).
+template <typename KT>
+static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row_off,
+                    const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
+                    int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk, int32_t* topk_idx,
+                    int32_t pool_blocks, int32_t block_size, int32_t* pool_block_idx, void* ws,
+                    size_t ws_bytes, void* stream_) {
     int vpr = 0;
     int st = check_indexer_shape(Q, Hi, Hk, Di, &vpr);
     if (st != CSA2_OK) return st;
@@ -1157,7 +1169,7 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
         if (ws_bytes < carve_prefill(ws, w.bytes, Q, max_nvis, Hk * Di, &pw))
             return CSA2_ERR_WORKSPACE;
         if (max_nvis > 0) {
-            st = CSA2_LAUNCH("prefill_convert", k_prefill_convert,
+            st = CSA2_LAUNCH("prefill_convert", k_prefill_convert<KT>,
                              dim3((pw.Qp + pw.Np) / kCvtRows), dim3(256), s, qI, kI, seq_row_off,
                              Q, pw.Qp, Hi, Hk, Di, max_nvis, pw.qh, pw.ql, pw.kh, pw.kl,
                              pw.qflag, pw.kflag);
@@ -1177,8 +1189,9 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
     } else {
         dim3 grid((max_nvis + kRowsPerWG - 1) / kRowsPerWG, Q);
         uint32_t* bk = pool_blocks > 0 ? w.keys_b : nullptr;
-        st = launch_score_stream(vpr, grid, s, qI, kI, seq_row_off, q_seq, q_nvis, Hi, Hk, Di,
-                                 w.keys_e, w.se, w.hist_e, bk, w.sb, bs_log2, w.hist_b);
+        st = launch_score_stream(vpr, sizeof(KT) == 1, grid, s, qI, kI, seq_row_off, q_seq,
+                                 q_nvis, Hi, Hk, Di, w.keys_e, w.se, w.hist_e, bk, w.sb, bs_log2,
+                                 w.hist_b);
         if (st) return st;
     }
     // selection of one row per query: a single workgroup for short rows,
@@ -1212,6 +1225,29 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
     return CSA2_OK;
 }
 
+extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* seq_row_off,
+                               const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
+                               int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk,
+                               int32_t* topk_idx, int32_t pool_blocks, int32_t block_size,
+                               int32_t* pool_block_idx, void* ws, size_t ws_bytes,
+                               void* stream) {
+    return index_full_impl<float>(qI, kI, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, max_nvis,
+                                  topk, topk_idx, pool_blocks, block_size, pool_block_idx, ws,
+                                  ws_bytes, stream);
+}
+
+extern "C" int csa2_index_full_e4m3(const float* qI, const uint8_t* kI,
+                                    const int64_t* seq_row_off, const int32_t* q_seq,
+                                    const int32_t* q_nvis, int32_t Q, int32_t Hi, int32_t Hk,
+                                    int32_t Di, int32_t max_nvis, int32_t topk,
+                                    int32_t* topk_idx, int32_t pool_blocks, int32_t block_size,
+                                    int32_t* pool_block_idx, void* ws, size_t ws_bytes,
+                                    void* stream) {
+    return index_full_impl<uint8_t>(qI, kI, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, max_nvis,
+                                    topk, topk_idx, pool_blocks, block_size, pool_block_idx, ws,
+                                    ws_bytes, stream);
+}
+
 extern "C" size_t csa2_reindex_workspace_bytes(int32_t Q, int32_t pool_blocks, int32_t block_size) {
     if (Q < 0 || pool_blocks < 0 || block_size <= 0) return 0;
     Carver c(nullptr);
@@ -1219,11 +1255,13 @@ extern "C" size_t csa2_reindex_workspace_bytes(int32_t Q, int32_t pool_blocks, i
     return c.bytes();
 }
 
-extern "C" int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
-                            const int32_t* q_seq, const int32_t* q_nvis,
-                            const int32_t* pool_block_idx, int32_t pool_blocks, int32_t block_size,
-                            int32_t Q, int32_t Hi, int32_t Hk, int32_t Di, int32_t topk,
-                            int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream_) {
+// Reindex over a key cache of KT values (float or E4M3 bytes).
+template <typename KT>
+static int reindex_impl(const float* qI, const KT* kI, const int64_t* seq_row_off,
+                 const int32_t* q_seq, const int32_t* q_nvis, const int32_t* pool_block_idx,
+                 int32_t pool_blocks, int32_t block_size, int32_t Q, int32_t Hi, int32_t Hk,
+                 int32_t Di, int32_t topk, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                 void* stream_) {
     int vpr = 0;
     int st = check_indexer_shape(Q, Hi, Hk, Di, &vpr);
     if (st != CSA2_OK) return st;
@@ -1242,13 +1280,32 @@ extern "C" int csa2_reindex(const float* qI, const float* kI, const int64_t* seq
     if (ncand > 0) {
         dim3 g((ncand + kReindexPerWG - 1) / kReindexPerWG, Q);
 #define CSA2_RS(V)                                                                             \
-    CSA2_LAUNCH("reindex_score", k_reindex_score<V>, g, dim3(kReindexThreads), s, qI, kI,       \
-                seq_row_off, q_seq, q_nvis, Hi, Hk, Di, pool_block_idx, pool_blocks,           \
-                block_size, ck)
+    CSA2_LAUNCH(sizeof(KT) == 1 ? "reindex_score_e4m3" : "reindex_score",                     \
+                (k_reindex_score<V, KT>), g, dim3(kReindexThreads), s, qI, kI, seq_row_off,    \
+                q_seq, q_nvis, Hi, Hk, Di, pool_block_idx, pool_blocks, block_size, ck)
         st = vpr == 1 ? CSA2_RS(1) : vpr == 2 ? CSA2_RS(2) : CSA2_RS(4);
 #undef CSA2_RS
         if (st) return st;
     }
     return CSA2_LAUNCH("reindex_select", k_reindex_select, dim3(Q), dim3(kSelThreads), s, ck,
                        ncand, topk, topk_idx);
+}
+
+extern "C" int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
+                            const int32_t* q_seq, const int32_t* q_nvis,
+                            const int32_t* pool_block_idx, int32_t pool_blocks, int32_t block_size,
+                            int32_t Q, int32_t Hi, int32_t Hk, int32_t Di, int32_t topk,
+                            int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+    return reindex_impl<float>(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, pool_blocks,
+                               block_size, Q, Hi, Hk, Di, topk, topk_idx, ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_reindex_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row_off,
+                                 const int32_t* q_seq, const int32_t* q_nvis,
+                                 const int32_t* pool_block_idx, int32_t pool_blocks,
+                                 int32_t block_size, int32_t Q, int32_t Hi, int32_t Hk,
+                                 int32_t Di, int32_t topk, int32_t* topk_idx, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    return reindex_impl<uint8_t>(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, pool_blocks,
+                                 block_size, Q, Hi, Hk, Di, topk, topk_idx, ws, ws_bytes, stream);
 }

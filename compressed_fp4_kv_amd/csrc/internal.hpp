@@ -35,11 +35,13 @@ struct Carver {
     size_t bytes() const { return (off + 255) & ~size_t(255); }
 };
 
-// Score stream launcher (stream.hip): vpr = 1, 2 or 4 float4 per lane and key row.
-int launch_score_stream(int vpr, dim3 grid, hipStream_t s, const float* qI, const float* kI,
-                        const int64_t* seq_row_off, const int32_t* q_seq, const int32_t* q_nvis,
-                        int Hi, int Hk, int Di, uint32_t* keys, int64_t kstride, uint32_t* hist_e,
-                        uint32_t* bkeys, int64_t bstride, int bs_log2, uint32_t* hist_b);
+// Score stream launcher (stream.hip): key rows of 256 * vpr values (vpr = 1,
+// 2 or 4), fp32 (kI a const float*) or E4M3FN bytes (e4m3, kI a const uint8_t*).
+int launch_score_stream(int vpr, bool e4m3, dim3 grid, hipStream_t s, const float* qI,
+                        const void* kI, const int64_t* seq_row_off, const int32_t* q_seq,
+                        const int32_t* q_nvis, int Hi, int Hk, int Di, uint32_t* keys,
+                        int64_t kstride, uint32_t* hist_e, uint32_t* bkeys, int64_t bstride,
+                        int bs_log2, uint32_t* hist_b);
 
 }  // namespace csa2
 

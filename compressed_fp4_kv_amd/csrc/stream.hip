@@ -4,7 +4,8 @@
 //
 // Method (jaehun.me review of arXiv 2609.19969, section "2) CSA2"): a Full
 // layer scores every visible compressed entry with its indexer; the score is
-// the sum over indexer heads of the query head dotted with the key row.
+// the sum over indexer heads of the query head dotted with the key row.  Key
+// rows are fp32 or, in the compact cache, one E4M3FN byte per value.
 #include "common.hpp"
 #include "internal.hpp"
 #include "rowdot.hpp"
@@ -12,9 +13,9 @@
 namespace csa2 {
 namespace {
 
-template <int VPR>
+template <int VPR, typename KT>
 __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
-    const float* __restrict__ qI, const float* __restrict__ kI,
+    const float* __restrict__ qI, const KT* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     __shared__ __attribute__((aligned(16))) uint32_t s_ke[kRowsPerWG];
     __shared__ __attribute__((aligned(16))) uint32_t s_kb[kRowsPerWG];
     constexpr int RW = 256 * VPR;
-    constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (64 KB in flight per 4 waves)
+    constexpr int kStreamRows = stream_rows<VPR, KT>();   // rows per wave iteration
     const int q = blockIdx.y;
     const int nvis = min(q_nvis[q], (int)kstride);   // q_nvis <= max_nvis <= kstride
     const int r0 = blockIdx.x * kRowsPerWG;
@@ -38,16 +39,16 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     __syncthreads();
 
     float4 qv[VPR];
-    load_qvec<VPR>(qI, q, Hi, Hk, Di, qv);
+    load_qvec<VPR, sizeof(KT) == 1>(qI, q, Hi, Hk, Di, qv);
     const int64_t row0 = seq_row_off[q_seq ? q_seq[q] : 0];
-    const float* kb = kI + row0 * RW;
+    const KT* kb = kI + row0 * RW;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int myrow = (lane >> 3) & 7;
     const uint32_t bmask = (1u << bs_log2) - 1u;
     uint32_t* krow = keys + (size_t)q * kstride;
 
     for (int g0 = r0 + kStreamRows * wave; g0 < r1; g0 += kStreamRows * (kStreamThreads / kWave)) {
-        const float* rows[kStreamRows];
+        const KT* rows[kStreamRows];
         bool ok[kStreamRows];
 #pragma unroll
         for (int i = 0; i < kStreamRows; ++i) {
@@ -112,15 +113,22 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
 
 }  // namespace
 
-int launch_score_stream(int vpr, dim3 grid, hipStream_t s, const float* qI, const float* kI,
-                        const int64_t* seq_row_off, const int32_t* q_seq, const int32_t* q_nvis,
-                        int Hi, int Hk, int Di, uint32_t* keys, int64_t kstride, uint32_t* hist_e,
-                        uint32_t* bkeys, int64_t bstride, int bs_log2, uint32_t* hist_b) {
-#define CSA2_STREAM(V)                                                                        \
-    CSA2_LAUNCH("score_stream", k_score_stream<V>, grid, dim3(kStreamThreads), s, qI, kI,     \
-                seq_row_off, q_seq, q_nvis, Hi, Hk, Di, keys, kstride, hist_e, bkeys, bstride,\
-                bs_log2, hist_b)
-    return vpr == 1 ? CSA2_STREAM(1) : vpr == 2 ? CSA2_STREAM(2) : CSA2_STREAM(4);
+int launch_score_stream(int vpr, bool e4m3, dim3 grid, hipStream_t s, const float* qI,
+                        const void* kI, const int64_t* seq_row_off, const int32_t* q_seq,
+                        const int32_t* q_nvis, int Hi, int Hk, int Di, uint32_t* keys,
+                        int64_t kstride, uint32_t* hist_e, uint32_t* bkeys, int64_t bstride,
+                        int bs_log2, uint32_t* hist_b) {
+#define CSA2_STREAM(V, KT, NAME)                                                              \
+    CSA2_LAUNCH(NAME, (k_score_stream<V, KT>), grid, dim3(kStreamThreads), s, qI,             \
+                static_cast<const KT*>(kI), seq_row_off, q_seq, q_nvis, Hi, Hk, Di, keys,     \
+                kstride, hist_e, bkeys, bstride, bs_log2, hist_b)
+    if (e4m3)
+        return vpr == 1   ? CSA2_STREAM(1, uint8_t, "score_stream_e4m3")
+               : vpr == 2 ? CSA2_STREAM(2, uint8_t, "score_stream_e4m3")
+                          : CSA2_STREAM(4, uint8_t, "score_stream_e4m3");
+    return vpr == 1   ? CSA2_STREAM(1, float, "score_stream")
+           : vpr == 2 ? CSA2_STREAM(2, float, "score_stream")
+                      : CSA2_STREAM(4, float, "score_stream");
 #undef CSA2_STREAM
 }
 

@@ -151,6 +151,12 @@ def host_kI_rows(w, row0, nrows):
     return host_ints(w.seed, T_KI, row0 * rw, nrows * rw).reshape(nrows, w.Hk, w.Di)
 
 
+def host_kI_rows_e4m3(w, row0, nrows):
+    """The same key rows as E4M3FN bytes (torch's cast; the integers drawn
+    are exact in E4M3), the compact key cache's input."""
+    return e4m3_bytes(host_kI_rows(w, row0, nrows))
+
+
 def host_qI(w, tensor):
     return host_ints(w.seed, tensor, 0, w.Q * w.Hi * w.Di).reshape(w.Q, w.Hi, w.Di)
 
@@ -177,15 +183,36 @@ def host_swa(w, layer):
 
 # ----------------------------------------------------------- device build
 
-def build_device(w, device="cuda", layers=None, with_kI=True, with_kv=True):
-    """All inputs of workload w as device tensors (dict of torch tensors)."""
+def dev_kI_e4m3(w, device="cuda", chunk_rows=1 << 18):
+    """The key cache of workload w as E4M3FN bytes [rows, Hk, Di] on the
+    device: generated as fp32 integers chunk by chunk and cast by torch (the
+    values are exact in E4M3), so the fp32 copy never exists whole."""
+    import torch
+    dev = torch.device(device)
+    out = torch.empty((w.rows, w.Hk, w.Di), dtype=torch.uint8, device=dev)
+    rw = w.row_width
+    tmp = torch.empty((min(chunk_rows, max(w.rows, 1)), w.Hk, w.Di), dtype=torch.float32,
+                      device=dev)
+    for r0 in range(0, w.rows, chunk_rows):
+        n = min(chunk_rows, w.rows - r0)
+        dev_ints(tmp[:n], w.seed, T_KI, start=r0 * rw)
+        out[r0:r0 + n] = tmp[:n].to(torch.float8_e4m3fn).view(torch.uint8)
+    torch.cuda.synchronize(dev)
+    return out
+
+
+def build_device(w, device="cuda", layers=None, with_kI=True, with_kv=True, keys="f32"):
+    """All inputs of workload w as device tensors (dict of torch tensors).
+    keys: "f32" (t["kI"] fp32), "e4m3" (t["kI8"] E4M3 bytes) or "both"."""
     import torch
     dev = torch.device(device)
     L = w.layers if layers is None else layers
     t = {}
-    if with_kI:
+    if with_kI and keys in ("f32", "both"):
         t["kI"] = torch.empty((w.rows, w.Hk, w.Di), dtype=torch.float32, device=dev)
         dev_ints(t["kI"], w.seed, T_KI)
+    if with_kI and keys in ("e4m3", "both"):
+        t["kI8"] = dev_kI_e4m3(w, device)
     if with_kv:
         t["kv_codes"] = torch.empty((w.rows, w.D // 2), dtype=torch.uint8, device=dev)
         t["kv_scales"] = torch.empty((w.rows, w.D // 16), dtype=torch.uint8, device=dev)

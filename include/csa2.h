@@ -131,6 +131,34 @@ int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
                  void* stream);
 
 /* ------------------------------------------------------------------------
+ * Compact indexer-key cache: the same Full-mode and Reindex calls over keys
+ * stored as one E4M3FN byte per value (a quarter of the fp32 cache's bytes).
+ * The pages (jaehun.me review, TL;DR and section "2) CSA2": the global KV
+ * cache, indexer keys included, takes 890 bytes per token; indexer K is a
+ * projection of main KV) give no storage format for indexer keys.  Reading
+ * used: plain OCP E4M3FN values with no scale, decoded exactly to fp32 before
+ * the dot product; a scale common to all keys can be folded into qI.  With
+ * integer-valued keys of magnitude <= 16 (exact in E4M3) and integer queries
+ * whose dot products stay below 2^24 the selection is exactly the one of the
+ * fp32 cache holding the same values.
+ *   kI  [rows, Hk, Di] u8 (E4M3FN; S.1111.111 = NaN must not occur), 16-byte
+ *       aligned; every other argument, the workspace sizes
+ *       (csa2_index_full_workspace_bytes, csa2_index_prefill_workspace_bytes,
+ *       csa2_reindex_workspace_bytes), the shapes supported and the errors
+ *       are those of csa2_index_full and csa2_reindex.
+ * ---------------------------------------------------------------------- */
+int csa2_index_full_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row_off,
+                         const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
+                         int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk,
+                         int32_t* topk_idx, int32_t pool_blocks, int32_t block_size,
+                         int32_t* pool_block_idx, void* ws, size_t ws_bytes, void* stream);
+int csa2_reindex_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row_off,
+                      const int32_t* q_seq, const int32_t* q_nvis, const int32_t* pool_block_idx,
+                      int32_t pool_blocks, int32_t block_size, int32_t Q, int32_t Hi, int32_t Hk,
+                      int32_t Di, int32_t topk, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
  * Sparse attention, decode (one query token per sequence; any layer mode).
  * (jaehun.me review, sections "2) CSA2" and "3) FP4 main KV"; ainewsway.com
  * article: window and global sparse retrieval form one attention.)

@@ -216,14 +216,30 @@ static void select_topk(cand_t* c, int64_t n, int k, int32_t* out) {
 typedef struct {
     const float* f32;
     const uint8_t* e4m3;
+    float dec[256];   /* oracle_e4m3 of every byte, filled by keys_e4m3() */
 } keys_t;
+
+static keys_t keys_f32(const float* kI) {
+    keys_t k;
+    k.f32 = kI;
+    k.e4m3 = NULL;
+    return k;
+}
+
+static keys_t keys_e4m3(const uint8_t* kI) {
+    keys_t k;
+    k.f32 = NULL;
+    k.e4m3 = kI;
+    for (int b = 0; b < 256; ++b) k.dec[b] = (float)oracle_e4m3(b);
+    return k;
+}
 
 /* Key row r (absolute row number) as fp32 values: the fp32 cache is read in
  * place, E4M3 bytes are decoded into buf (every E4M3FN value is exact in
  * fp32). */
-static const float* key_row(keys_t k, int64_t r, int RW, float* buf) {
-    if (k.f32) return k.f32 + (size_t)r * RW;
-    for (int i = 0; i < RW; ++i) buf[i] = (float)oracle_e4m3(k.e4m3[(size_t)r * RW + i]);
+static const float* key_row(const keys_t* k, int64_t r, int RW, float* buf) {
+    if (k->f32) return k->f32 + (size_t)r * RW;
+    for (int i = 0; i < RW; ++i) buf[i] = k->dec[k->e4m3[(size_t)r * RW + i]];
     return buf;
 }
 
@@ -235,7 +251,7 @@ static const float* key_row(keys_t k, int64_t r, int RW, float* buf) {
  * id) form the pool, written ascending and padded with -1.
  * Index arrays are local to the sequence.  Returns 0, or -1 on a bad
  * argument. */
-static int index_full(const float* qI, keys_t kI, const int64_t* seq_row_off,
+static int index_full(const float* qI, const keys_t* kI, const int64_t* seq_row_off,
                       const int32_t* q_seq, const int32_t* q_nvis, int Q, int Hi, int Hk, int Di,
                       int topk, int32_t* topk_idx, int pool_blocks, int block_size,
                       int32_t* pool_idx) {
@@ -280,8 +296,8 @@ int oracle_index_full(const float* qI, const float* kI, const int64_t* seq_row_o
                       const int32_t* q_seq, const int32_t* q_nvis, int Q, int Hi, int Hk, int Di,
                       int topk, int32_t* topk_idx, int pool_blocks, int block_size,
                       int32_t* pool_idx) {
-    keys_t k = {kI, NULL};
-    return index_full(qI, k, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, topk, topk_idx,
+    keys_t k = keys_f32(kI);
+    return index_full(qI, &k, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, topk, topk_idx,
                       pool_blocks, block_size, pool_idx);
 }
 
@@ -290,8 +306,8 @@ int oracle_index_full_e4m3(const float* qI, const uint8_t* kI, const int64_t* se
                            const int32_t* q_seq, const int32_t* q_nvis, int Q, int Hi, int Hk,
                            int Di, int topk, int32_t* topk_idx, int pool_blocks, int block_size,
                            int32_t* pool_idx) {
-    keys_t k = {NULL, kI};
-    return index_full(qI, k, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, topk, topk_idx,
+    keys_t k = keys_e4m3(kI);
+    return index_full(qI, &k, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, topk, topk_idx,
                       pool_blocks, block_size, pool_idx);
 }
 
@@ -300,7 +316,7 @@ int oracle_index_full_e4m3(const float* qI, const uint8_t* kI, const int64_t* se
  * b*bs + j < q_nvis[q]}; they are rescored with this layer's own indexer
  * query against the shared key cache and the Top-K taken, ties to the lower
  * entry index.  READING: the keys are the Full layer's indexer-key cache. */
-static int reindex(const float* qI, keys_t kI, const int64_t* seq_row_off, const int32_t* q_seq,
+static int reindex(const float* qI, const keys_t* kI, const int64_t* seq_row_off, const int32_t* q_seq,
                    const int32_t* q_nvis, const int32_t* pool_idx, int pool_blocks,
                    int block_size, int Q, int Hi, int Hk, int Di, int topk, int32_t* topk_idx) {
     if (Q < 0 || Hi <= 0 || Hk <= 0 || Di <= 0 || topk < 0 || pool_blocks < 0 || block_size <= 0)
@@ -338,8 +354,8 @@ int oracle_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
                    const int32_t* q_seq, const int32_t* q_nvis, const int32_t* pool_idx,
                    int pool_blocks, int block_size, int Q, int Hi, int Hk, int Di, int topk,
                    int32_t* topk_idx) {
-    keys_t k = {kI, NULL};
-    return reindex(qI, k, seq_row_off, q_seq, q_nvis, pool_idx, pool_blocks, block_size, Q, Hi,
+    keys_t k = keys_f32(kI);
+    return reindex(qI, &k, seq_row_off, q_seq, q_nvis, pool_idx, pool_blocks, block_size, Q, Hi,
                    Hk, Di, topk, topk_idx);
 }
 
@@ -348,8 +364,8 @@ int oracle_reindex_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_r
                         const int32_t* q_seq, const int32_t* q_nvis, const int32_t* pool_idx,
                         int pool_blocks, int block_size, int Q, int Hi, int Hk, int Di, int topk,
                         int32_t* topk_idx) {
-    keys_t k = {NULL, kI};
-    return reindex(qI, k, seq_row_off, q_seq, q_nvis, pool_idx, pool_blocks, block_size, Q, Hi,
+    keys_t k = keys_e4m3(kI);
+    return reindex(qI, &k, seq_row_off, q_seq, q_nvis, pool_idx, pool_blocks, block_size, Q, Hi,
                    Hk, Di, topk, topk_idx);
 }
 
@@ -493,13 +509,13 @@ int oracle_scores(const float* qI, const float* kI, const int64_t* seq_row_off,
 int oracle_scores_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row_off,
                        const int32_t* q_seq, const int32_t* q_nvis, int q, int Hi, int Hk, int Di,
                        double* out) {
-    keys_t k = {NULL, kI};
+    keys_t k = keys_e4m3(kI);
     const int RW = Hk * Di;
     float* buf = (float*)malloc(sizeof(float) * (size_t)RW);
     if (!buf) return -1;
     for (int64_t t = 0; t < q_nvis[q]; ++t)
         out[t] = oracle_score(qI + (size_t)q * Hi * Di,
-                              key_row(k, seq_row_off[q_seq[q]] + t, RW, buf), Hi, Hk, Di);
+                              key_row(&k, seq_row_off[q_seq[q]] + t, RW, buf), Hi, Hk, Di);
     free(buf);
     return 0;
 }
