@@ -944,9 +944,9 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
 
 // ------------------------------------------------------------- reindex
 
-template <int VPR, typename KT>
+template <int VPR>
 __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
-    const float* __restrict__ qI, const KT* __restrict__ kI,
+    const float* __restrict__ qI, const float* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, const int32_t* __restrict__ pool,
     int P, int bs, uint64_t* __restrict__ ckeys) {
@@ -957,17 +957,17 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
     if (c0 >= ncand) return;
     const int c1 = min(ncand, c0 + kReindexPerWG);
     float4 qv[VPR];
-    load_qvec<VPR, sizeof(KT) == 1>(qI, q, Hi, Hk, Di, qv);
+    load_qvec<VPR>(qI, q, Hi, Hk, Di, qv);
     const int nvis = q_nvis[q];
     const int64_t row0 = seq_row_off[q_seq ? q_seq[q] : 0];
-    const KT* kb = kI + row0 * RW;
+    const float* kb = kI + row0 * RW;
     const int32_t* prow = pool + (size_t)q * P;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int myrow = (lane >> 3) & 7;
     // wave w scores candidates c0 + 64 w .. +63: lane l first resolves
     // candidate c0 + 64 w + l to its entry row (-1: none), so that every row
     // address of the gathers below is a lane read away, not a load away
-    constexpr int kRows = stream_rows<VPR, KT>();   // rows per gather round
+    constexpr int kRows = VPR >= 4 ? 8 : 16;   // rows per gather round
     const int cw = c0 + kWave * wave;
     int64_t tl = -1;
     {
@@ -982,7 +982,7 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
 #pragma unroll
     for (int it = 0; it < kWave / kRows; ++it) {
         if (cw + kRows * it >= c1) break;   // wave-uniform
-        const KT* rows[kRows];
+        const float* rows[kRows];
         bool ok[kRows];
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
@@ -1002,6 +1002,78 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
             const int c = cw + r;
             if ((lane & 7) == 0 && c < c1)
                 ckeys[(size_t)q * ncand + c] = t >= 0 ? comp_key(ord_key(sv[hh]), (uint32_t)t) : 0ull;
+        }
+    }
+}
+
+// Reindex scorer over E4M3 key rows (RB = 256 * VPR bytes), in the 16-lanes-
+// per-row layout of dot_rows16: wave w scores candidates c0 + 64 w .. +63 in
+// rounds of G groups of four rows (16 KB; issuing all 64 rows at once needs
+// registers that cost more occupancy than the deeper gather gains); each lane
+// first resolves one candidate to its entry (-1: none),
+// and the rows of a round are read with entries taken from those lanes.  A
+// lane whose candidate is empty reads its 16-byte columns of this query's
+// indexer row instead (always valid memory, at least RB bytes) and the result
+// is discarded.
+template <int VPR>
+__global__ __launch_bounds__(kReindexThreads) void k_reindex_score_e4m3(
+    const float* __restrict__ qI, const uint8_t* __restrict__ kI,
+    const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, const int32_t* __restrict__ pool,
+    int P, int bs, uint64_t* __restrict__ ckeys) {
+    constexpr int RB = 256 * VPR;
+    constexpr int G = 16 / VPR;
+    constexpr int RPB = 4 * G;                        // rows per sub-block
+    constexpr int NB = 1;                             // sub-blocks per round
+    constexpr int RPI = NB * RPB;                     // rows per round
+    constexpr int GSH = 4 - log2_groups<G>();
+    const int q = blockIdx.y;
+    const int ncand = P * bs;
+    const int c0 = blockIdx.x * kReindexPerWG;
+    if (c0 >= ncand) return;
+    const int c1 = min(ncand, c0 + kReindexPerWG);
+    float4 qv[VPR][4];
+    load_qvec16<VPR>(qI, q, Hi, Hk, Di, qv);
+    const int nvis = q_nvis[q];
+    const int64_t row0 = seq_row_off[q_seq ? q_seq[q] : 0];
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int u16 = 16 * (lane & 15), rq = lane >> 4;
+    const int myrow = 4 * ((lane & 15) >> GSH) + rq;
+    const bool writer = (lane & ((1 << GSH) - 1)) == 0;
+    const uint8_t* kl = kI + row0 * RB + u16;
+    const uint8_t* dummy = reinterpret_cast<const uint8_t*>(qI + (size_t)q * Hi * Di) + u16;
+    const int32_t* prow = pool + (size_t)q * P;
+    const int cw = c0 + kWave * wave;
+    int tl = -1;
+    {
+        const int c = cw + lane;
+        if (c < c1) {
+            const int b = prow[c / bs];
+            tl = b >= 0 ? b * bs + c % bs : -1;
+            if (tl >= nvis) tl = -1;
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < kWave / RPI; ++it) {
+        if (cw + RPI * it >= c1) break;   // wave-uniform
+        const uint8_t* grow[NB][G];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int t = __shfl(tl, RPI * it + RPB * b + 4 * g + rq);
+                grow[b][g] = t >= 0 ? kl + (int64_t)t * RB : dummy;
+            }
+        float sv[NB];
+        dot_rows16<VPR, G, NB>(grow, qv, sv);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int r = RPI * it + RPB * b + myrow;   // this lane's candidate within the wave
+            const int t = __shfl(tl, r);
+            const int c = cw + r;
+            if (writer && c < c1)
+                ckeys[(size_t)q * ncand + c] =
+                    t >= 0 ? comp_key(ord_key(sv[b]), (uint32_t)t) : 0ull;
         }
     }
 }
@@ -1187,11 +1259,10 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
     if (max_nvis == 0) {
         // no visible entries anywhere: the finalize kernels write -1 rows
     } else {
-        dim3 grid((max_nvis + kRowsPerWG - 1) / kRowsPerWG, Q);
         uint32_t* bk = pool_blocks > 0 ? w.keys_b : nullptr;
-        st = launch_score_stream(vpr, sizeof(KT) == 1, grid, s, qI, kI, seq_row_off, q_seq,
-                                 q_nvis, Hi, Hk, Di, w.keys_e, w.se, w.hist_e, bk, w.sb, bs_log2,
-                                 w.hist_b);
+        st = launch_score_stream(vpr, sizeof(KT) == 1, max_nvis, Q, s, qI, kI, seq_row_off,
+                                 q_seq, q_nvis, Hi, Hk, Di, w.keys_e, w.se, w.hist_e, bk, w.sb,
+                                 bs_log2, w.hist_b);
         if (st) return st;
     }
     // selection of one row per query: a single workgroup for short rows,
@@ -1279,11 +1350,17 @@ static int reindex_impl(const float* qI, const KT* kI, const int64_t* seq_row_of
     const int ncand = pool_blocks * block_size;
     if (ncand > 0) {
         dim3 g((ncand + kReindexPerWG - 1) / kReindexPerWG, Q);
-#define CSA2_RS(V)                                                                             \
-    CSA2_LAUNCH(sizeof(KT) == 1 ? "reindex_score_e4m3" : "reindex_score",                     \
-                (k_reindex_score<V, KT>), g, dim3(kReindexThreads), s, qI, kI, seq_row_off,    \
-                q_seq, q_nvis, Hi, Hk, Di, pool_block_idx, pool_blocks, block_size, ck)
-        st = vpr == 1 ? CSA2_RS(1) : vpr == 2 ? CSA2_RS(2) : CSA2_RS(4);
+#define CSA2_RS(K, NAME)                                                                      \
+    CSA2_LAUNCH(NAME, K, g, dim3(kReindexThreads), s, qI, kI, seq_row_off, q_seq, q_nvis, Hi,  \
+                Hk, Di, pool_block_idx, pool_blocks, block_size, ck)
+        if constexpr (sizeof(KT) == 1)
+            st = vpr == 1   ? CSA2_RS(k_reindex_score_e4m3<1>, "reindex_score_e4m3")
+                 : vpr == 2 ? CSA2_RS(k_reindex_score_e4m3<2>, "reindex_score_e4m3")
+                            : CSA2_RS(k_reindex_score_e4m3<4>, "reindex_score_e4m3");
+        else
+            st = vpr == 1   ? CSA2_RS(k_reindex_score<1>, "reindex_score")
+                 : vpr == 2 ? CSA2_RS(k_reindex_score<2>, "reindex_score")
+                            : CSA2_RS(k_reindex_score<4>, "reindex_score");
 #undef CSA2_RS
         if (st) return st;
     }
