@@ -38,12 +38,12 @@ def test_status_strings(pkg):
 NULL = None
 
 
-def _idx(pkg, **kw):
+def _idx(pkg, fn="csa2_index_full", **kw):
     a = dict(qI=1, kI=1, off=1, qseq=1, nvis=1, Q=1, Hi=4, Hk=4, Di=128, maxn=100, topk=8,
              out=1, P=0, bs=8, pool=NULL, ws=1, wsb=1 << 30)
     a.update(kw)
     v = lambda x: None if x is None else ctypes.c_void_p(16 * x)
-    return pkg.lib.csa2_index_full(v(a["qI"]), v(a["kI"]), v(a["off"]), v(a["qseq"]), v(a["nvis"]),
+    return getattr(pkg.lib, fn)(v(a["qI"]), v(a["kI"]), v(a["off"]), v(a["qseq"]), v(a["nvis"]),
                                    a["Q"], a["Hi"], a["Hk"], a["Di"], a["maxn"], a["topk"],
                                    v(a["out"]), a["P"], a["bs"], v(a["pool"]), v(a["ws"]), a["wsb"],
                                    None)
@@ -74,9 +74,24 @@ def test_index_full_argument_checks(pkg):
     assert pkg.csa2_index_prefill_workspace_bytes(-1, 100, 8, 4, 128) == 0
 
 
-def test_reindex_argument_checks(pkg):
+def test_index_full_e4m3_argument_checks(pkg):
+    # the E4M3-key form shares the checks of csa2_index_full
+    f = "csa2_index_full_e4m3"
+    assert _idx(pkg, f, kI=NULL) == 1
+    assert _idx(pkg, f, Q=-1) == 2
+    assert _idx(pkg, f, Hk=2) == 3
+    assert _idx(pkg, f, Di=100) == 3
+    assert _idx(pkg, f, wsb=10) == 4
+    assert _idx(pkg, f, Q=0) == 0
+    assert _idx(pkg, f, qseq=NULL, P=16, pool=1) == 3
+    pre = pkg.csa2_index_prefill_workspace_bytes(1, 100, 8, 4, 128)
+    assert _idx(pkg, f, qseq=NULL, wsb=pre - 1) == 4
+
+
+@pytest.mark.parametrize("fn", ["csa2_reindex", "csa2_reindex_e4m3"])
+def test_reindex_argument_checks(pkg, fn):
     v = lambda x: None if x is None else ctypes.c_void_p(16 * x)
-    f = pkg.lib.csa2_reindex
+    f = getattr(pkg.lib, fn)
     base = [v(1), v(1), v(1), v(1), v(1), v(1), 2048, 8, 4, 4, 4, 128, 512, v(1), v(1), 1 << 30, None]
     assert f(*base[:5], None, *base[6:]) == 1
     b = list(base); b[6] = 4096
@@ -85,6 +100,8 @@ def test_reindex_argument_checks(pkg):
     assert f(*b) == 2
     b = list(base); b[15] = 8
     assert f(*b) == 4
+    b = list(base); b[1] = None
+    assert f(*b) == 1                       # no key cache
 
 
 def test_attention_argument_checks(pkg):
