@@ -45,9 +45,10 @@ def lib():
         _lib.oracle_fp4_quantize_row.argtypes = [P, i32, P, P]
         _lib.oracle_index_full.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, P, i32, i32, P]
         _lib.oracle_reindex.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P]
-        _lib.oracle_index_full_e4m3.argtypes = _lib.oracle_index_full.argtypes
         _lib.oracle_reindex_e4m3.argtypes = _lib.oracle_reindex.argtypes
         _lib.oracle_scores_e4m3.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P]
+        _lib.oracle_index_full_ex.argtypes = [P, P, i32, P, P, P, i32, i32, i32, i32, i32, P, i32,
+                                              i32, P, i32]
         _lib.oracle_attn_decode.argtypes = [P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32,
                                             P, P]
         _lib.oracle_attn_prefill.argtypes = [P, i64, P, P, P, i32, P, P, i32, i32, i32, i32, f32,
@@ -137,18 +138,20 @@ def _keys(kI):
 
 
 def index_full(qI, kI, seq_row_off, q_seq, q_nvis, Hi, Hk, Di, topk, pool_blocks=0,
-               block_size=8):
+               block_size=8, block_rule="max"):
     """Returns (topk_idx [Q,topk] int32, pool [Q,pool_blocks] int32 or None).
-    kI is an fp32 key cache or, as uint8, the compact E4M3FN key cache."""
+    kI is an fp32 key cache or, as uint8, the compact E4M3FN key cache;
+    block_rule "max" (the reading used) or "sum" (a variant) scores blocks."""
     qI = _c(qI, np.float32)
     kI, e4m3 = _keys(kI)
     seq_row_off, q_seq, q_nvis = _c(seq_row_off, np.int64), _c(q_seq, np.int32), _c(q_nvis, np.int32)
     Q = int(q_nvis.shape[0])
     idx = np.empty((Q, topk), np.int32)
     pool = np.empty((Q, pool_blocks), np.int32) if pool_blocks > 0 else None
-    f = lib().oracle_index_full_e4m3 if e4m3 else lib().oracle_index_full
-    rc = f(_p(qI), _p(kI), _p(seq_row_off), _p(q_seq), _p(q_nvis), Q, Hi, Hk, Di, topk, _p(idx),
-           pool_blocks, block_size, _p(pool))
+    rule = {"max": 0, "sum": 1}[block_rule]
+    rc = lib().oracle_index_full_ex(_p(qI), _p(kI), 1 if e4m3 else 0, _p(seq_row_off), _p(q_seq),
+                                    _p(q_nvis), Q, Hi, Hk, Di, topk, _p(idx), pool_blocks,
+                                    block_size, _p(pool), rule)
     if rc != 0:
         raise ValueError("oracle_index_full: bad argument")
     return idx, pool

@@ -247,16 +247,18 @@ static const float* key_row(const keys_t* k, int64_t r, int RW, float* buf) {
  * query's sequence and keep the Top-K.  With pool_blocks > 0 it also builds
  * the candidate pool [J-CSA2]: entries are grouped into aligned blocks
  * [b*bs, b*bs + bs); READING: a block scores the maximum of its visible
- * entries' scores, and the top pool_blocks blocks (ties to the lower block
- * id) form the pool, written ascending and padded with -1.
+ * entries' scores (block_rule 0; block_rule 1, a variant: their sum), and the
+ * top pool_blocks blocks (ties to the lower block id) form the pool, written
+ * ascending and padded with -1.
  * Index arrays are local to the sequence.  Returns 0, or -1 on a bad
  * argument. */
 static int index_full(const float* qI, const keys_t* kI, const int64_t* seq_row_off,
                       const int32_t* q_seq, const int32_t* q_nvis, int Q, int Hi, int Hk, int Di,
                       int topk, int32_t* topk_idx, int pool_blocks, int block_size,
-                      int32_t* pool_idx) {
+                      int32_t* pool_idx, int block_rule) {
     if (Q < 0 || Hi <= 0 || Hk <= 0 || Di <= 0 || topk < 0 || pool_blocks < 0) return -1;
     if (pool_blocks > 0 && block_size <= 0) return -1;
+    if (block_rule != 0 && block_rule != 1) return -1;
     const int RW = Hk * Di;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -277,9 +279,14 @@ static int index_full(const float* qI, const keys_t* kI, const int64_t* seq_row_
             cand_t* b = (cand_t*)malloc(sizeof(cand_t) * (size_t)(nb > 0 ? nb : 1));
             if (!b) { free(c); bad = 1; continue; }
             for (int64_t j = 0; j < nb; ++j) {
-                double m = -INFINITY;
-                for (int64_t t = j * block_size; t < (j + 1) * block_size && t < n; ++t)
-                    if (c[t].s > m) m = c[t].s;
+                double m = block_rule == 0 ? -INFINITY : 0.0;
+                for (int64_t t = j * block_size; t < (j + 1) * block_size && t < n; ++t) {
+                    if (block_rule == 0) {
+                        if (c[t].s > m) m = c[t].s;
+                    } else {
+                        m += c[t].s;
+                    }
+                }
                 b[j].s = m;
                 b[j].id = j;
             }
@@ -298,17 +305,20 @@ int oracle_index_full(const float* qI, const float* kI, const int64_t* seq_row_o
                       int32_t* pool_idx) {
     keys_t k = keys_f32(kI);
     return index_full(qI, &k, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, topk, topk_idx,
-                      pool_blocks, block_size, pool_idx);
+                      pool_blocks, block_size, pool_idx, 0);
 }
 
-/* The same Full mode over a compact key cache of E4M3FN bytes [rows, Hk, Di]. */
-int oracle_index_full_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row_off,
-                           const int32_t* q_seq, const int32_t* q_nvis, int Q, int Hi, int Hk,
-                           int Di, int topk, int32_t* topk_idx, int pool_blocks, int block_size,
-                           int32_t* pool_idx) {
-    keys_t k = keys_e4m3(kI);
+/* The Full mode with a choice of key cache (key_format 0: fp32 rows at kI,
+ * 1: E4M3FN bytes) and of block score (block_rule 0: maximum, 1: sum of the
+ * block's visible entries' scores). */
+int oracle_index_full_ex(const float* qI, const void* kI, int key_format,
+                         const int64_t* seq_row_off, const int32_t* q_seq, const int32_t* q_nvis,
+                         int Q, int Hi, int Hk, int Di, int topk, int32_t* topk_idx,
+                         int pool_blocks, int block_size, int32_t* pool_idx, int block_rule) {
+    if (key_format != 0 && key_format != 1) return -1;
+    keys_t k = key_format == 0 ? keys_f32((const float*)kI) : keys_e4m3((const uint8_t*)kI);
     return index_full(qI, &k, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, topk, topk_idx,
-                      pool_blocks, block_size, pool_idx);
+                      pool_blocks, block_size, pool_idx, block_rule);
 }
 
 /* Reindex mode [J-CSA2], [J-EX]: the candidates are the visible positions of

@@ -686,3 +686,48 @@ def test_e4m3_key_topk_invariants_on_general_values():
     kd = _e4m3_decode_torch(k8)[:, 0, :]
     s = kd @ qI[0].astype(np.float64).sum(axis=0)
     _check_topk_invariants(s, idx[0], k)
+
+
+# ------------------------------------------------------------ pool variants
+
+def test_pool_sum_rule_is_exact_block_selection():
+    # variant block score: the sum of the block's visible entries (ragged
+    # last block sums fewer entries)
+    n, bs, P = 1003, 8, 20
+    qI, kI = _rand_full(24, n)
+    _, pool = oracle.index_full(qI, kI, [0], [0], [n], 2, 2, 8, 16, pool_blocks=P, block_size=bs,
+                                block_rule="sum")
+    s = oracle.scores(qI, kI, [0], [0], [n], 0, 2, 2, 8)
+    bsum = np.add.reduceat(s, np.arange(0, n, bs))
+    _check_topk_invariants(bsum, pool[0], P)
+    _, pmax = oracle.index_full(qI, kI, [0], [0], [n], 2, 2, 8, 16, pool_blocks=P, block_size=bs)
+    assert not np.array_equal(pool, pmax)          # the two rules differ on these inputs
+
+
+def test_pool_sum_rule_with_unit_blocks_equals_topk():
+    n = 500
+    qI, kI = _rand_full(25, n)
+    idx, pool = oracle.index_full(qI, kI, [0], [0], [n], 2, 2, 8, 37, pool_blocks=37,
+                                  block_size=1, block_rule="sum")
+    assert np.array_equal(idx, pool)
+
+
+@pytest.mark.parametrize("bs,lo,hi", [(8, -1, 1), (8, -8, 8), (4, -2, 2), (2, -1, 1)])
+def test_pool_of_widened_top_entries_equals_max_rule(bs, lo, hi):
+    # the other reading of "blocks x positions": walk the entries in rank
+    # order (score desc, index asc) and take the block of each until P
+    # distinct blocks are held.  A block enters at its best entry, so this is
+    # the max rule with ties to the lower block id, heavy ties included
+    n, P = 777, 40
+    qI, kI = _rand_full(26 + bs, n, lo=lo, hi=hi)
+    s = oracle.scores(qI, kI, [0], [0], [n], 0, 2, 2, 8)
+    order = np.lexsort((np.arange(n), -s))
+    held = []
+    for t in order:
+        b = t // bs
+        if b not in held:
+            held.append(b)
+        if len(held) == P:
+            break
+    _, pool = oracle.index_full(qI, kI, [0], [0], [n], 2, 2, 8, 1, pool_blocks=P, block_size=bs)
+    assert pool[0].tolist() == sorted(held)
