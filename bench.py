@@ -13,7 +13,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--key
 
 --keys e4m3 runs the same step over the compact indexer-key cache (one
 E4M3FN byte per key value instead of fp32), through csa2_index_full_e4m3 and
-csa2_reindex_e4m3.
+csa2_reindex_e4m3.  For the hierarchical workload (--workload 3) the
+candidate pool is a parameter: --pool-blocks P --block-size S (P x S <=
+16,384) and --block-rule max|sum (the block score; max is the reading used).
 """
 import argparse
 import json
@@ -63,7 +65,7 @@ def measured_traffic(profile="score_stream_c1_traffic.md"):
     return None
 
 
-def make_step(csa2, w, t, torch, keys="f32"):
+def make_step(csa2, w, t, torch, keys="f32", block_rule="max"):
     """One pass of the workload's call sequence (all of its layers)."""
     e4m3 = keys == "e4m3"
     kI = t["kI8"] if e4m3 else t["kI"]
@@ -115,8 +117,9 @@ def make_step(csa2, w, t, torch, keys="f32"):
             return
         if w.kind == "decode_hier":
             # the Full layer's indexer builds Top-K and the candidate pool
-            index_full(t["qI_full"], kI, t["seq_row_off"], t["q_seq"], t["q_nvis"], max_nvis,
-                       w.topk, idx, P, w.block_size, pool, ws=ws_i)
+            csa2.csa2_index_full_ex(t["qI_full"], kI, t["seq_row_off"], t["q_seq"], t["q_nvis"],
+                                    max_nvis, w.topk, idx, P, w.block_size, pool,
+                                    block_rule=block_rule, ws=ws_i)
         # Reindex layer over the pool, then Reindex + Reuse layers' attention
         reindex(t["qI_reindex"], kI, t["seq_row_off"], t["q_seq"], t["q_nvis"], pool,
                 w.block_size, w.topk, ridx, ws=ws_r)
@@ -315,6 +318,12 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--keys", choices=("f32", "e4m3"), default="f32",
                     help="indexer-key cache: fp32 (the workloads as stated) or E4M3 bytes")
+    ap.add_argument("--pool-blocks", type=int, default=None,
+                    help="hierarchical workload: blocks in the candidate pool (default 2,048)")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="hierarchical workload: positions per block (default 8)")
+    ap.add_argument("--block-rule", choices=("max", "sum"), default="max",
+                    help="hierarchical workload: block score of the candidate pool")
     ap.add_argument("--kv-writer", action="store_true",
                     help="measure the FP4 main-KV writer alone (its own JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -343,9 +352,17 @@ def main():
         return
 
     w = workload(args.workload)
+    pool_variant = (args.pool_blocks, args.block_size, args.block_rule) != (None, None, "max")
+    if pool_variant:
+        if w.kind != "decode_hier":
+            print("--pool-blocks / --block-size / --block-rule apply to --workload 3 only",
+                  file=sys.stderr)
+            sys.exit(2)
+        w.pool_blocks = args.pool_blocks or w.pool_blocks
+        w.block_size = args.block_size or w.block_size
     log(f"building inputs: {w.name} B={w.B} ctx={w.ctx[0]} H={w.H} topk={w.topk}")
     t = build_device(w, keys=args.keys)
-    step, idx = make_step(csa2, w, t, torch, args.keys)
+    step, idx = make_step(csa2, w, t, torch, args.keys, args.block_rule)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -388,7 +405,9 @@ def main():
         "data": "synthetic (seeded integer indexer inputs, FP4 E2M1/E4M3 KV, N(0,1) queries, "
                 "FP8 window)",
         "config": {"workload": WORKLOAD_NAMES.get(w.name, w.name) + (
-                       "; indexer keys stored as E4M3FN bytes" if args.keys == "e4m3" else ""),
+                       "; indexer keys stored as E4M3FN bytes" if args.keys == "e4m3" else "") + (
+                       f"; pool {w.pool_blocks} blocks x {w.block_size}, block score "
+                       f"{args.block_rule}" if pool_variant else ""),
                    "global_batch": w.Q, "seq_len": int(max(w.ctx)), "parallelism": "single GPU"},
         "kernels": kern,
         "roofline": dominant_roofline(w, kern, args.keys),

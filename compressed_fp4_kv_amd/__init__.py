@@ -12,7 +12,7 @@ import os
 
 __all__ = [
     "CSA2Error", "lib", "csa2_index_full", "csa2_index_full_workspace_bytes", "csa2_reindex",
-    "csa2_index_full_e4m3", "csa2_reindex_e4m3",
+    "csa2_index_full_e4m3", "csa2_reindex_e4m3", "csa2_index_full_ex",
     "csa2_reindex_workspace_bytes", "csa2_sparse_attn_decode", "csa2_decode_workspace_bytes",
     "csa2_sparse_attn_prefill_chunk", "csa2_prefill_workspace_bytes", "csa2_kv_quantize_fp4",
     "csa2_swa_append", "profile_enable",
@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = [
     "csa2_debug_dequant_tables",
     "csa2_kv_quantize_fp4",
     "csa2_swa_append",
-    "csa2_index_full_e4m3", "csa2_reindex_e4m3",
+    "csa2_index_full_e4m3", "csa2_reindex_e4m3", "csa2_index_full_ex",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -55,6 +55,8 @@ lib.csa2_index_full_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
 lib.csa2_index_full.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32,
                                 _I32, _P, _P, _SZ, _P]
 lib.csa2_index_full_e4m3.argtypes = lib.csa2_index_full.argtypes
+lib.csa2_index_full_ex.argtypes = [_P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                   _P, _I32, _I32, _P, _I32, _P, _SZ, _P]
 lib.csa2_reindex_workspace_bytes.restype = _SZ
 lib.csa2_reindex_workspace_bytes.argtypes = [_I32, _I32, _I32]
 lib.csa2_reindex.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
@@ -162,6 +164,34 @@ def csa2_index_full_e4m3(qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, top
     """As csa2_index_full with kI [rows,Hk,Di] u8 holding E4M3FN key bytes."""
     _index_full(lib.csa2_index_full_e4m3, _dt()[3], qI, kI, seq_row_off, q_seq, q_nvis,
                 max_nvis, topk, topk_idx, pool_blocks, block_size, pool_block_idx, ws, stream)
+
+
+BLOCK_RULES = {"max": 0, "sum": 1}
+
+
+def csa2_index_full_ex(qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,
+                       pool_blocks=0, block_size=8, pool_block_idx=None, block_rule="max",
+                       ws=None, stream=None):
+    """General Full-mode indexer: kI [rows,Hk,Di] f32 (CSA2_KEYS_F32) or u8 E4M3FN bytes
+    (CSA2_KEYS_E4M3), the key format following kI's dtype; block_rule "max" or "sum"."""
+    f32, i32, i64, u8 = _dt()
+    if kI.dtype == f32:
+        fmt = 0
+    elif kI.dtype == u8:
+        fmt = 1
+    else:
+        raise TypeError(f"kI: expected {f32} or {u8}, got {kI.dtype}")
+    if block_rule not in BLOCK_RULES:
+        raise ValueError(f"block_rule: {block_rule!r} is not one of {sorted(BLOCK_RULES)}")
+    Q, Hi, Di = qI.shape
+    Hk = kI.shape[1]
+    wp, wn = _ws(ws)
+    _check(lib.csa2_index_full_ex(
+        _ptr(qI, f32, "qI"), _ptr(kI, kI.dtype, "kI"), fmt, _ptr(seq_row_off, i64, "seq_row_off"),
+        _ptr(q_seq, i32, "q_seq"), _ptr(q_nvis, i32, "q_nvis"), Q, Hi, Hk, Di, max_nvis, topk,
+        _ptr(topk_idx, i32, "topk_idx"), pool_blocks, block_size,
+        _ptr(pool_block_idx, i32, "pool_block_idx"), BLOCK_RULES[block_rule], wp, wn,
+        _stream(stream)), "csa2_index_full_ex")
 
 
 def csa2_reindex_workspace_bytes(Q, pool_blocks, block_size):

@@ -15,6 +15,11 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of ord_key (a key of an fp32 score back to the score).
+__device__ __forceinline__ float ord_key_to_f32(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Composite selection key: score first, then the LOWER index.  Distinct
 // indices make every key distinct, so "the k largest keys" is a unique set.
 // 0 is reserved for "no candidate" (no real key is 0: ord_key >= 0x007FFFFF).

@@ -1215,8 +1215,8 @@ template <typename KT>
 static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row_off,
                     const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
                     int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk, int32_t* topk_idx,
-                    int32_t pool_blocks, int32_t block_size, int32_t* pool_block_idx, void* ws,
-                    size_t ws_bytes, void* stream_) {
+                    int32_t pool_blocks, int32_t block_size, int32_t* pool_block_idx,
+                    int32_t block_rule, void* ws, size_t ws_bytes, void* stream_) {
     int vpr = 0;
     int st = check_indexer_shape(Q, Hi, Hk, Di, &vpr);
     if (st != CSA2_OK) return st;
@@ -1224,6 +1224,7 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
     if (topk > CSA2_MAX_TOPK || pool_blocks > CSA2_MAX_TOPK) return CSA2_ERR_UNSUPPORTED;
     if (pool_blocks > 0 && block_size != 1 && block_size != 2 && block_size != 4 && block_size != 8)
         return block_size <= 0 ? CSA2_ERR_SHAPE : CSA2_ERR_UNSUPPORTED;
+    if (block_rule != CSA2_BLOCK_MAX && block_rule != CSA2_BLOCK_SUM) return CSA2_ERR_UNSUPPORTED;
     if (Q == 0 || (topk == 0 && pool_blocks == 0)) return CSA2_OK;
     if (!qI || !kI || !seq_row_off || !q_nvis || !ws) return CSA2_ERR_NULL;
     if ((topk > 0 && !topk_idx) || (pool_blocks > 0 && !pool_block_idx)) return CSA2_ERR_NULL;
@@ -1262,7 +1263,7 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
         uint32_t* bk = pool_blocks > 0 ? w.keys_b : nullptr;
         st = launch_score_stream(vpr, sizeof(KT) == 1, max_nvis, Q, s, qI, kI, seq_row_off,
                                  q_seq, q_nvis, Hi, Hk, Di, w.keys_e, w.se, w.hist_e, bk, w.sb,
-                                 bs_log2, w.hist_b);
+                                 bs_log2, block_rule == CSA2_BLOCK_SUM, w.hist_b);
         if (st) return st;
     }
     // selection of one row per query: a single workgroup for short rows,
@@ -1303,8 +1304,8 @@ extern "C" int csa2_index_full(const float* qI, const float* kI, const int64_t* 
                                int32_t* pool_block_idx, void* ws, size_t ws_bytes,
                                void* stream) {
     return index_full_impl<float>(qI, kI, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, max_nvis,
-                                  topk, topk_idx, pool_blocks, block_size, pool_block_idx, ws,
-                                  ws_bytes, stream);
+                                  topk, topk_idx, pool_blocks, block_size, pool_block_idx,
+                                  CSA2_BLOCK_MAX, ws, ws_bytes, stream);
 }
 
 extern "C" int csa2_index_full_e4m3(const float* qI, const uint8_t* kI,
@@ -1315,8 +1316,28 @@ extern "C" int csa2_index_full_e4m3(const float* qI, const uint8_t* kI,
                                     int32_t* pool_block_idx, void* ws, size_t ws_bytes,
                                     void* stream) {
     return index_full_impl<uint8_t>(qI, kI, seq_row_off, q_seq, q_nvis, Q, Hi, Hk, Di, max_nvis,
-                                    topk, topk_idx, pool_blocks, block_size, pool_block_idx, ws,
-                                    ws_bytes, stream);
+                                    topk, topk_idx, pool_blocks, block_size, pool_block_idx,
+                                    CSA2_BLOCK_MAX, ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_index_full_ex(const float* qI, const void* kI, int32_t key_format,
+                                  const int64_t* seq_row_off, const int32_t* q_seq,
+                                  const int32_t* q_nvis, int32_t Q, int32_t Hi, int32_t Hk,
+                                  int32_t Di, int32_t max_nvis, int32_t topk, int32_t* topk_idx,
+                                  int32_t pool_blocks, int32_t block_size,
+                                  int32_t* pool_block_idx, int32_t block_rule, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    if (key_format == CSA2_KEYS_F32)
+        return index_full_impl<float>(qI, static_cast<const float*>(kI), seq_row_off, q_seq,
+                                      q_nvis, Q, Hi, Hk, Di, max_nvis, topk, topk_idx,
+                                      pool_blocks, block_size, pool_block_idx, block_rule, ws,
+                                      ws_bytes, stream);
+    if (key_format == CSA2_KEYS_E4M3)
+        return index_full_impl<uint8_t>(qI, static_cast<const uint8_t*>(kI), seq_row_off, q_seq,
+                                        q_nvis, Q, Hi, Hk, Di, max_nvis, topk, topk_idx,
+                                        pool_blocks, block_size, pool_block_idx, block_rule, ws,
+                                        ws_bytes, stream);
+    return CSA2_ERR_UNSUPPORTED;
 }
 
 extern "C" size_t csa2_reindex_workspace_bytes(int32_t Q, int32_t pool_blocks, int32_t block_size) {

@@ -38,11 +38,13 @@ struct Carver {
 // Score stream launcher (stream.hip): key rows of 256 * vpr values (vpr = 1,
 // 2 or 4), fp32 (kI a const float*) or E4M3FN bytes (e4m3, kI a const
 // uint8_t*); one grid row per query, enough workgroups for max_nvis rows.
+// With bkeys set, blocks of 2^bs_log2 rows are scored by the maximum of their
+// rows' scores, or by their sum when block_sum is non-zero.
 int launch_score_stream(int vpr, bool e4m3, int max_nvis, int Q, hipStream_t s,
                         const float* qI, const void* kI, const int64_t* seq_row_off,
                         const int32_t* q_seq, const int32_t* q_nvis, int Hi, int Hk, int Di,
                         uint32_t* keys, int64_t kstride, uint32_t* hist_e, uint32_t* bkeys,
-                        int64_t bstride, int bs_log2, uint32_t* hist_b);
+                        int64_t bstride, int bs_log2, int block_sum, uint32_t* hist_b);
 
 }  // namespace csa2
 

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
-    int64_t bstride, int bs_log2, uint32_t* __restrict__ hist_b) {
+    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b) {
     // 16-bit bin counters, two per word (a workgroup sees at most
     // kRowsPerWG keys), so that four workgroups fit a CU's LDS
     __shared__ uint32_t s_he[kHistBins / 2];
@@ -110,10 +110,20 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
                 atomicAdd(&s_he[d >> 1], 1u << ((d & 1u) << 4));
             }
             if (pool) {
-                uint32_t bk = valid ? k : 0u;
-                if (bs_log2 >= 1) bk = max(bk, (uint32_t)__shfl_xor(bk, 8));
-                if (bs_log2 >= 2) bk = max(bk, (uint32_t)__shfl_xor(bk, 16));
-                if (bs_log2 >= 3) bk = max(bk, (uint32_t)__shfl_xor(bk, 32));
+                // rows 8 hh + 0..7 sit in lanes that differ in bits 3..5
+                uint32_t bk;
+                if (block_sum) {
+                    float bsum = valid ? sc[hh] : 0.f;
+                    if (bs_log2 >= 1) bsum += __shfl_xor(bsum, 8);
+                    if (bs_log2 >= 2) bsum += __shfl_xor(bsum, 16);
+                    if (bs_log2 >= 3) bsum += __shfl_xor(bsum, 32);
+                    bk = ord_key(bsum);
+                } else {
+                    bk = valid ? k : 0u;
+                    if (bs_log2 >= 1) bk = max(bk, (uint32_t)__shfl_xor(bk, 8));
+                    if (bs_log2 >= 2) bk = max(bk, (uint32_t)__shfl_xor(bk, 16));
+                    if (bs_log2 >= 3) bk = max(bk, (uint32_t)__shfl_xor(bk, 32));
+                }
                 if ((lane & 7) == 0 && valid && ((uint32_t)myrow & bmask) == 0) {
                     s_kb[(row - r0) >> bs_log2] = bk;
                     const uint32_t d = bk >> kDigitShift;
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream_e4m3(
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
-    int64_t bstride, int bs_log2, uint32_t* __restrict__ hist_b) {
+    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b) {
     __shared__ uint32_t s_he[kHistBins / 2];
     __shared__ uint32_t s_hb[kHistBins / 2];
     __shared__ __attribute__((aligned(16))) uint32_t s_ke[kRowsPerWG8];
@@ -192,15 +202,23 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream_e4m3(
     if (pool) {
         // block keys from the row keys staged in LDS: block bi covers rows
         // [bi << bs_log2, (bi + 1) << bs_log2) of this workgroup's range
-        // (ranges start on whole blocks: kRowsPerWG8 is a multiple of 8); the
-        // rows past the last valid one read as 0, below every real key
+        // (ranges start on whole blocks: kRowsPerWG8 is a multiple of 8); for
+        // the maximum, the rows past the last valid one read as 0, below
+        // every real key
         const int nk = r1 - r0, nb = (nk + (int)bmask) >> bs_log2;
         if (threadIdx.x < 8 && nk + (int)threadIdx.x < ((nk + 7) & ~7)) s_ke[nk + threadIdx.x] = 0u;
         __syncthreads();
         for (int bi = threadIdx.x; bi < nb; bi += kStreamThreads) {
             const int i0 = bi << bs_log2;
             uint32_t bk = 0u;
-            if (bs_log2 >= 2) {
+            if (block_sum) {
+                // the scores back from their keys, summed in row order over
+                // the block's valid rows
+                float bsum = 0.f;
+                for (int i = i0; i < min(nk, i0 + (1 << bs_log2)); ++i)
+                    bsum += ord_key_to_f32(s_ke[i]);
+                bk = ord_key(bsum);
+            } else if (bs_log2 >= 2) {
                 for (int i = i0; i < i0 + (1 << bs_log2); i += 4) {
                     const uint4 v = *reinterpret_cast<const uint4*>(s_ke + i);
                     bk = max(bk, max(max(v.x, v.y), max(v.z, v.w)));
@@ -223,13 +241,13 @@ int launch_score_stream(int vpr, bool e4m3, int max_nvis, int Q, hipStream_t s,
                         const float* qI, const void* kI, const int64_t* seq_row_off,
                         const int32_t* q_seq, const int32_t* q_nvis, int Hi, int Hk, int Di,
                         uint32_t* keys, int64_t kstride, uint32_t* hist_e, uint32_t* bkeys,
-                        int64_t bstride, int bs_log2, uint32_t* hist_b) {
+                        int64_t bstride, int bs_log2, int block_sum, uint32_t* hist_b) {
     const int rpw = e4m3 ? kRowsPerWG8 : kRowsPerWG;
     const dim3 grid((max_nvis + rpw - 1) / rpw, Q);
 #define CSA2_STREAM(KERNEL, KT, NAME)                                                         \
     CSA2_LAUNCH(NAME, KERNEL, grid, dim3(kStreamThreads), s, qI, static_cast<const KT*>(kI), \
                 seq_row_off, q_seq, q_nvis, Hi, Hk, Di, keys, kstride, hist_e, bkeys, bstride,\
-                bs_log2, hist_b)
+                bs_log2, block_sum, hist_b)
     if (e4m3)
         return vpr == 1 ? CSA2_STREAM((k_score_stream_e4m3<1, kStreamNB8>), uint8_t,
                                       "score_stream_e4m3")

@@ -159,6 +159,35 @@ int csa2_reindex_e4m3(const float* qI, const uint8_t* kI, const int64_t* seq_row
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * General form of the Full-mode indexer: the key cache's format and the
+ * candidate pool's block score are parameters.  The pages (jaehun.me review,
+ * section "2) CSA2") give the pool as 2,048 blocks x 8 positions and no block
+ * score; the reading used everywhere else is the block's maximum entry score
+ * (CSA2_BLOCK_MAX), which also equals taking the blocks of the top entries in
+ * rank order until pool_blocks distinct blocks are held.  CSA2_BLOCK_SUM, a
+ * variant, scores a block by the sum of its visible entries' scores (exact
+ * for integer-valued inputs while the sums stay below 2^24 in magnitude;
+ * otherwise fp32 sums).
+ *   kI          key_format CSA2_KEYS_F32: const float* [rows, Hk, Di];
+ *               CSA2_KEYS_E4M3: const uint8_t* [rows, Hk, Di] (E4M3FN)
+ *   block_rule  CSA2_BLOCK_MAX or CSA2_BLOCK_SUM (used when pool_blocks > 0)
+ * Every other argument, the workspace sizes and the errors are those of
+ * csa2_index_full; an unknown key_format or block_rule gives
+ * CSA2_ERR_UNSUPPORTED.  csa2_index_full = (CSA2_KEYS_F32, CSA2_BLOCK_MAX),
+ * csa2_index_full_e4m3 = (CSA2_KEYS_E4M3, CSA2_BLOCK_MAX).
+ * ---------------------------------------------------------------------- */
+#define CSA2_KEYS_F32 0
+#define CSA2_KEYS_E4M3 1
+#define CSA2_BLOCK_MAX 0
+#define CSA2_BLOCK_SUM 1
+int csa2_index_full_ex(const float* qI, const void* kI, int32_t key_format,
+                       const int64_t* seq_row_off, const int32_t* q_seq, const int32_t* q_nvis,
+                       int32_t Q, int32_t Hi, int32_t Hk, int32_t Di, int32_t max_nvis,
+                       int32_t topk, int32_t* topk_idx, int32_t pool_blocks, int32_t block_size,
+                       int32_t* pool_block_idx, int32_t block_rule, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Sparse attention, decode (one query token per sequence; any layer mode).
  * (jaehun.me review, sections "2) CSA2" and "3) FP4 main KV"; ainewsway.com
  * article: window and global sparse retrieval form one attention.)

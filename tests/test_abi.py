@@ -123,3 +123,18 @@ def test_attention_argument_checks(pkg):
     pb = [v(1), -5, v(1), v(1), v(1), 512, v(1), v(1), 128, 64, 64, 512, 0.04, v(1), None, v(1),
           1 << 30, None]
     assert g(*pb) == 2                      # negative position
+
+
+def test_index_full_ex_refuses_unknown_rule_and_key_format(pkg):
+    v = lambda x: ctypes.c_void_p(16 * x)
+    f = pkg.lib.csa2_index_full_ex
+    base = [v(1), v(1), 0, v(1), v(1), v(1), 1, 4, 4, 128, 100, 8, v(1), 16, 8, v(1), 0, v(1),
+            1 << 30, None]
+    b = list(base); b[16] = 2
+    assert f(*b) == 3                       # unknown block rule
+    b = list(base); b[2] = 7
+    assert f(*b) == 3                       # unknown key format
+    b = list(base); b[1] = None
+    assert f(*b) == 1
+    b = list(base); b[18] = 10
+    assert f(*b) == 4
