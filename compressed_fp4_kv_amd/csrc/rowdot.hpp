@@ -13,8 +13,9 @@ namespace {
 
 constexpr int kHistBins = 4096;      // first-level digit: top 12 bits of the key
 constexpr int kDigitShift = 20;
-constexpr int kStreamThreads = 512;
-constexpr int kRowsPerWG = 2048;     // score stream: rows per workgroup (fp32 keys)
+constexpr int kStreamThreads32 = 256;   // score stream workgroup (fp32 keys)
+constexpr int kStreamThreads8 = 512;    // score stream workgroup (E4M3 keys)
+constexpr int kRowsPerWG = 4096;     // score stream: rows per workgroup (fp32 keys)
 constexpr int kRowsPerWG8 = 8192;    // score stream: rows per workgroup (E4M3 keys)
 constexpr int kStreamNB8 = 2;        // E4M3 stream: 16 KB sub-blocks per wave iteration
 

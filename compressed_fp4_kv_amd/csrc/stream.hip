@@ -17,6 +17,7 @@ namespace {
 // End of a score-stream workgroup: its keys (staged in LDS) are written out
 // as whole lines and its 16-bit LDS bin counts added to the query's
 // histograms.
+template <int NT>
 __device__ __forceinline__ void stream_flush(int q, int r0, int r1, bool pool, int bs_log2,
                                              const uint32_t* s_ke, const uint32_t* s_kb,
                                              const uint32_t* s_he, const uint32_t* s_hb,
@@ -28,7 +29,7 @@ __device__ __forceinline__ void stream_flush(int q, int r0, int r1, bool pool, i
     // r0 and the key strides are multiples of 4 (64): whole uint4 stores,
     // a scalar tail for the last workgroup of a row
     const int nk = r1 - r0;
-    for (int i = 4 * threadIdx.x; i < nk; i += 4 * kStreamThreads) {
+    for (int i = 4 * threadIdx.x; i < nk; i += 4 * NT) {
         if (i + 4 <= nk)
             *reinterpret_cast<uint4*>(krow + r0 + i) = *reinterpret_cast<const uint4*>(s_ke + i);
         else
@@ -37,14 +38,14 @@ __device__ __forceinline__ void stream_flush(int q, int r0, int r1, bool pool, i
     if (pool) {
         const int b0 = r0 >> bs_log2, nb = ((r1 - 1) >> bs_log2) - b0 + 1;
         uint32_t* brow = bkeys + (size_t)q * bstride + b0;
-        for (int i = 4 * threadIdx.x; i < nb; i += 4 * kStreamThreads) {
+        for (int i = 4 * threadIdx.x; i < nb; i += 4 * NT) {
             if (i + 4 <= nb)
                 *reinterpret_cast<uint4*>(brow + i) = *reinterpret_cast<const uint4*>(s_kb + i);
             else
                 for (int x = i; x < nb; ++x) brow[x] = s_kb[x];
         }
     }
-    for (int i = threadIdx.x; i < kHistBins; i += kStreamThreads) {
+    for (int i = threadIdx.x; i < kHistBins; i += NT) {
         const uint32_t sh = (i & 1) << 4;
         const uint32_t ce = (s_he[i >> 1] >> sh) & 0xFFFFu;
         if (ce) atomicAdd(&hist_e[(size_t)q * kHistBins + i], ce);
@@ -56,28 +57,30 @@ __device__ __forceinline__ void stream_flush(int q, int r0, int r1, bool pool, i
 }
 
 template <int VPR>
-__global__ __launch_bounds__(kStreamThreads) void k_score_stream(
+__global__ __launch_bounds__(kStreamThreads32) void k_score_stream(
     const float* __restrict__ qI, const float* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
     int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b) {
     // 16-bit bin counters, two per word (a workgroup sees at most
-    // kRowsPerWG keys), so that four workgroups fit a CU's LDS
+    // kRowsPerWG keys).  Three 4-wave workgroups of 4,096 rows (48 KB of LDS
+    // each) fill the twelve wave slots the registers allow per CU; a sweep
+    // over 256/512 threads and 1,024-4,096 rows per workgroup chose this
     __shared__ uint32_t s_he[kHistBins / 2];
     __shared__ uint32_t s_hb[kHistBins / 2];
     // this workgroup's keys, written out as whole lines at the end
     __shared__ __attribute__((aligned(16))) uint32_t s_ke[kRowsPerWG];
     __shared__ __attribute__((aligned(16))) uint32_t s_kb[kRowsPerWG];
     constexpr int RW = 256 * VPR;
-    constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (64 KB in flight per 4 waves)
+    constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (32 KB of 2 KB rows)
     const int q = blockIdx.y;
     const int nvis = min(q_nvis[q], (int)kstride);   // q_nvis <= max_nvis <= kstride
     const int r0 = blockIdx.x * kRowsPerWG;
     if (r0 >= nvis) return;
     const int r1 = min(nvis, r0 + kRowsPerWG);
     const bool pool = bkeys != nullptr;
-    for (int i = threadIdx.x; i < kHistBins / 2; i += kStreamThreads) { s_he[i] = 0; s_hb[i] = 0; }
+    for (int i = threadIdx.x; i < kHistBins / 2; i += kStreamThreads32) { s_he[i] = 0; s_hb[i] = 0; }
     __syncthreads();
 
     float4 qv[VPR];
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
     const uint32_t bmask = (1u << bs_log2) - 1u;
     uint32_t* krow = keys + (size_t)q * kstride;
 
-    for (int g0 = r0 + kStreamRows * wave; g0 < r1; g0 += kStreamRows * (kStreamThreads / kWave)) {
+    for (int g0 = r0 + kStreamRows * wave; g0 < r1; g0 += kStreamRows * (kStreamThreads32 / kWave)) {
         const float* rows[kStreamRows];
         bool ok[kStreamRows];
 #pragma unroll
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
             }
         }
     }
-    stream_flush(q, r0, r1, pool, bs_log2, s_ke, s_kb, s_he, s_hb, krow, bkeys, bstride, hist_e,
+    stream_flush<kStreamThreads32>(q, r0, r1, pool, bs_log2, s_ke, s_kb, s_he, s_hb, krow, bkeys, bstride, hist_e,
                  hist_b);
 }
 
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream(
 // the workgroup's last one are read as that last row again and discarded, so
 // no load is predicated.
 template <int VPR, int NB>
-__global__ __launch_bounds__(kStreamThreads) void k_score_stream_e4m3(
+__global__ __launch_bounds__(kStreamThreads8) void k_score_stream_e4m3(
     const float* __restrict__ qI, const uint8_t* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream_e4m3(
     if (r0 >= nvis) return;
     const int r1 = min(nvis, r0 + kRowsPerWG8);
     const bool pool = bkeys != nullptr;
-    for (int i = threadIdx.x; i < kHistBins / 2; i += kStreamThreads) { s_he[i] = 0; s_hb[i] = 0; }
+    for (int i = threadIdx.x; i < kHistBins / 2; i += kStreamThreads8) { s_he[i] = 0; s_hb[i] = 0; }
     __syncthreads();
 
     float4 qv[VPR][4];
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream_e4m3(
     const uint32_t bmask = (1u << bs_log2) - 1u;
     uint32_t* krow = keys + (size_t)q * kstride;
 
-    for (int g0 = r0 + RPI * wave; g0 < r1; g0 += RPI * (kStreamThreads / kWave)) {
+    for (int g0 = r0 + RPI * wave; g0 < r1; g0 += RPI * (kStreamThreads8 / kWave)) {
         const uint8_t* grow[NB][G];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream_e4m3(
         const int nk = r1 - r0, nb = (nk + (int)bmask) >> bs_log2;
         if (threadIdx.x < 8 && nk + (int)threadIdx.x < ((nk + 7) & ~7)) s_ke[nk + threadIdx.x] = 0u;
         __syncthreads();
-        for (int bi = threadIdx.x; bi < nb; bi += kStreamThreads) {
+        for (int bi = threadIdx.x; bi < nb; bi += kStreamThreads8) {
             const int i0 = bi << bs_log2;
             uint32_t bk = 0u;
             if (block_sum) {
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_score_stream_e4m3(
             atomicAdd(&s_hb[d >> 1], 1u << ((d & 1u) << 4));
         }
     }
-    stream_flush(q, r0, r1, pool, bs_log2, s_ke, s_kb, s_he, s_hb, krow, bkeys, bstride, hist_e,
+    stream_flush<kStreamThreads8>(q, r0, r1, pool, bs_log2, s_ke, s_kb, s_he, s_hb, krow, bkeys, bstride, hist_e,
                  hist_b);
 }
 
@@ -244,8 +247,9 @@ int launch_score_stream(int vpr, bool e4m3, int max_nvis, int Q, hipStream_t s,
                         int64_t bstride, int bs_log2, int block_sum, uint32_t* hist_b) {
     const int rpw = e4m3 ? kRowsPerWG8 : kRowsPerWG;
     const dim3 grid((max_nvis + rpw - 1) / rpw, Q);
+    const dim3 block(e4m3 ? kStreamThreads8 : kStreamThreads32);
 #define CSA2_STREAM(KERNEL, KT, NAME)                                                         \
-    CSA2_LAUNCH(NAME, KERNEL, grid, dim3(kStreamThreads), s, qI, static_cast<const KT*>(kI), \
+    CSA2_LAUNCH(NAME, KERNEL, grid, block, s, qI, static_cast<const KT*>(kI),                \
                 seq_row_off, q_seq, q_nvis, Hi, Hk, Di, keys, kstride, hist_e, bkeys, bstride,\
                 bs_log2, block_sum, hist_b)
     if (e4m3)
