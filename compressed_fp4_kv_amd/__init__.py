@@ -13,6 +13,7 @@ import os
 __all__ = [
     "CSA2Error", "lib", "csa2_index_full", "csa2_index_full_workspace_bytes", "csa2_reindex",
     "csa2_index_full_e4m3", "csa2_reindex_e4m3", "csa2_index_full_ex",
+    "csa2_index_prefill_workspace_bytes", "csa2_index_prefill_workspace_bytes_ex",
     "csa2_reindex_workspace_bytes", "csa2_sparse_attn_decode", "csa2_decode_workspace_bytes",
     "csa2_sparse_attn_prefill_chunk", "csa2_prefill_workspace_bytes", "csa2_kv_quantize_fp4",
     "csa2_swa_append", "profile_enable",
@@ -34,6 +35,7 @@ EXPORTED_SYMBOLS = [
     "csa2_kv_quantize_fp4",
     "csa2_swa_append",
     "csa2_index_full_e4m3", "csa2_reindex_e4m3", "csa2_index_full_ex",
+    "csa2_index_prefill_workspace_bytes_ex",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -55,6 +57,10 @@ lib.csa2_index_full_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
 lib.csa2_index_full.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32,
                                 _I32, _P, _P, _SZ, _P]
 lib.csa2_index_full_e4m3.argtypes = lib.csa2_index_full.argtypes
+lib.csa2_index_prefill_workspace_bytes.restype = _SZ
+lib.csa2_index_prefill_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
+lib.csa2_index_prefill_workspace_bytes_ex.restype = _SZ
+lib.csa2_index_prefill_workspace_bytes_ex.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32, _I32]
 lib.csa2_index_full_ex.argtypes = [_P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                    _P, _I32, _I32, _P, _I32, _P, _SZ, _P]
 lib.csa2_reindex_workspace_bytes.restype = _SZ
@@ -135,6 +141,11 @@ def csa2_index_full_workspace_bytes(Q, max_nvis, topk, pool_blocks=0, block_size
 
 def csa2_index_prefill_workspace_bytes(Q, max_nvis, topk, Hk, Di):
     return int(lib.csa2_index_prefill_workspace_bytes(Q, max_nvis, topk, Hk, Di))
+
+
+def csa2_index_prefill_workspace_bytes_ex(Q, max_nvis, topk, pool_blocks, block_size, Hk, Di):
+    return int(lib.csa2_index_prefill_workspace_bytes_ex(Q, max_nvis, topk, pool_blocks,
+                                                         block_size, Hk, Di))
 
 
 def _index_full(fn, kdt, qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,

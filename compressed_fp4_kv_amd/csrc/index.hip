@@ -942,6 +942,37 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
     rank_and_write(s_out, K, K, o);
 }
 
+// Candidate pool of a prefill chunk (the encoder-side form of the
+// hierarchical indexer): each query's row of score keys becomes a row of
+// block keys, blocks of 2^bs_log2 entries clipped to the query's visible
+// entries, scored by their largest key (= the key of the largest score) or by
+// the key of the sum of their scores; nblk[q] receives the query's block
+// count.  One thread per block; the rows then go through k_row_select.
+__global__ __launch_bounds__(256) void k_block_keys(const uint32_t* __restrict__ keys,
+                                                    int64_t stride,
+                                                    const int32_t* __restrict__ q_nvis,
+                                                    int bs_log2, int block_sum,
+                                                    uint32_t* __restrict__ bkeys, int64_t bstride,
+                                                    int32_t* __restrict__ nblk) {
+    const int q = blockIdx.y;
+    const int n = min(q_nvis[q], (int)stride);
+    const int nb = (n + (1 << bs_log2) - 1) >> bs_log2;
+    if (blockIdx.x == 0 && threadIdx.x == 0) nblk[q] = nb;
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b >= nb) return;
+    const uint32_t* row = keys + (size_t)q * stride;
+    const int i0 = b << bs_log2, i1 = min(n, i0 + (1 << bs_log2));
+    uint32_t bk = 0u;
+    if (block_sum) {
+        float sum = 0.f;
+        for (int i = i0; i < i1; ++i) sum += ord_key_to_f32(row[i]);
+        bk = ord_key(sum);
+    } else {
+        for (int i = i0; i < i1; ++i) bk = max(bk, row[i]);
+    }
+    bkeys[(size_t)q * bstride + b] = bk;
+}
+
 // ------------------------------------------------------------- reindex
 
 template <int VPR>
@@ -1122,6 +1153,7 @@ struct IndexWs {
     uint32_t *keys_e, *keys_b, *hist_e, *hist_b, *cnt_e, *cnt_b;
     int32_t *above_e, *above_b;
     uint64_t *cand_e, *cand_b;
+    int32_t* nblk;   // prefill pool: blocks per query
     int64_t se, sb;
     size_t zero_words;
     size_t bytes;
@@ -1151,6 +1183,7 @@ IndexWs carve_index(void* ws, int Q, int max_nvis, int topk, int pool_blocks, in
     w.above_b = c.take<int32_t>((size_t)Q * pool_blocks);
     w.cand_e = c.take<uint64_t>(topk > 0 ? (size_t)Q * kCandCap : 0);
     w.cand_b = c.take<uint64_t>(pool_blocks > 0 ? (size_t)Q * kCandCap : 0);
+    w.nblk = c.take<int32_t>(pool_blocks > 0 ? (size_t)Q : 0);
     w.bytes = c.bytes();
     return w;
 }
@@ -1195,12 +1228,20 @@ size_t carve_prefill(void* ws, size_t at, int Q, int max_nvis, int RW, PrefillWs
     return c.bytes();
 }
 
+extern "C" size_t csa2_index_prefill_workspace_bytes_ex(int32_t Q, int32_t max_nvis,
+                                                        int32_t topk, int32_t pool_blocks,
+                                                        int32_t block_size, int32_t Hk,
+                                                        int32_t Di) {
+    if (Q < 0 || max_nvis < 0 || topk < 0 || pool_blocks < 0 || Hk <= 0 || Di <= 0) return 0;
+    if (pool_blocks > 0 && block_size <= 0) return 0;
+    PrefillWs p;
+    const size_t at = carve_index(nullptr, Q, max_nvis, topk, pool_blocks, block_size).bytes;
+    return carve_prefill(nullptr, at, Q, max_nvis, Hk * Di, &p);
+}
+
 extern "C" size_t csa2_index_prefill_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
                                                      int32_t Hk, int32_t Di) {
-    if (Q < 0 || max_nvis < 0 || topk < 0 || Hk <= 0 || Di <= 0) return 0;
-    PrefillWs p;
-    const size_t at = carve_index(nullptr, Q, max_nvis, topk, 0, 1).bytes;
-    return carve_prefill(nullptr, at, Q, max_nvis, Hk * Di, &p);
+    return csa2_index_prefill_workspace_bytes_ex(Q, max_nvis, topk, 0, 1, Hk, Di);
 }
 
 extern "C" size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
@@ -1237,7 +1278,7 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
     if (!q_seq) {
         // prefill chunk of one sequence: bf16 copies of the query and key
         // rows, bf16-MFMA score tiles, then one selecting workgroup per query
-        if (pool_blocks > 0) return CSA2_ERR_UNSUPPORTED;
+        // (and per query's row of block keys for a pool)
         PrefillWs pw;
         if (ws_bytes < carve_prefill(ws, w.bytes, Q, max_nvis, Hk * Di, &pw))
             return CSA2_ERR_WORKSPACE;
@@ -1252,8 +1293,22 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
                              Q, q_nvis, max_nvis, w.keys_e, w.se);
             if (st) return st;
         }
-        return CSA2_LAUNCH("row_select", k_row_select, dim3(Q), dim3(kSelThreads), s, w.keys_e,
-                           w.se, q_nvis, topk, topk_idx);
+        if (topk > 0) {
+            st = CSA2_LAUNCH("row_select", k_row_select, dim3(Q), dim3(kSelThreads), s, w.keys_e,
+                             w.se, q_nvis, topk, topk_idx);
+            if (st) return st;
+        }
+        if (pool_blocks > 0) {
+            const int nbmax = (max_nvis + block_size - 1) / block_size;
+            st = CSA2_LAUNCH("block_keys", k_block_keys, dim3((nbmax + 255) / 256 + (nbmax == 0), Q),
+                             dim3(256), s, w.keys_e, w.se, q_nvis, bs_log2,
+                             (int)(block_rule == CSA2_BLOCK_SUM), w.keys_b, w.sb, w.nblk);
+            if (st) return st;
+            st = CSA2_LAUNCH("row_select_b", k_row_select, dim3(Q), dim3(kSelThreads), s,
+                             w.keys_b, w.sb, w.nblk, pool_blocks, pool_block_idx);
+            if (st) return st;
+        }
+        return CSA2_OK;
     }
     st = CSA2_LAUNCH("zero", k_zero_u32, dim3(256), dim3(256), s, w.hist_e, w.zero_words);
     if (st) return st;

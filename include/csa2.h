@@ -97,15 +97,22 @@ int csa2_last_hip_error(void);
  *                  pool_block_idx [Q, pool_blocks] int32 (NULL iff pool_blocks 0)
  * Workspace: csa2_index_full_workspace_bytes for q_seq != NULL;
  * csa2_index_prefill_workspace_bytes (which also holds bf16 copies of the
- * chunk's query rows and the sequence's key rows) for q_seq == NULL.  The
- * prefill form (q_seq == NULL) builds no pool: pool_blocks must be 0, else
- * CSA2_ERR_UNSUPPORTED.  Too small a workspace: CSA2_ERR_WORKSPACE.
+ * chunk's query rows and the sequence's key rows) for q_seq == NULL, or
+ * csa2_index_prefill_workspace_bytes_ex when that form also builds a pool.
+ * The prefill form's pool is the encoder-side form of the hierarchical
+ * indexer (the jaehun.me review's "next steps" suggest extending the
+ * decoder-only candidate pool to the encoder): each query of the chunk gets
+ * the same block pool a decode query with its q_nvis would.  Too small a
+ * workspace: CSA2_ERR_WORKSPACE.
  * Preconditions (device data): rows read stay inside kI.
  * ---------------------------------------------------------------------- */
 size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
                                        int32_t pool_blocks, int32_t block_size);
 size_t csa2_index_prefill_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,
                                           int32_t Hk, int32_t Di);
+size_t csa2_index_prefill_workspace_bytes_ex(int32_t Q, int32_t max_nvis, int32_t topk,
+                                             int32_t pool_blocks, int32_t block_size,
+                                             int32_t Hk, int32_t Di);
 int csa2_index_full(const float* qI, const float* kI, const int64_t* seq_row_off,
                     const int32_t* q_seq, const int32_t* q_nvis, int32_t Q, int32_t Hi,
                     int32_t Hk, int32_t Di, int32_t max_nvis, int32_t topk, int32_t* topk_idx,

@@ -70,7 +70,11 @@ def test_index_full_argument_checks(pkg):
     assert pre > need
     assert _idx(pkg, qseq=NULL, wsb=need) == 4
     assert _idx(pkg, qseq=NULL, wsb=pre - 1) == 4
-    assert _idx(pkg, qseq=NULL, P=16, pool=1) == 3     # no pool in the prefill form
+    # a pool in the prefill form needs the larger workspace of the _ex query
+    pre_pool = pkg.csa2_index_prefill_workspace_bytes_ex(1, 100, 8, 16, 8, 4, 128)
+    assert pre_pool > pre
+    assert _idx(pkg, qseq=NULL, P=16, pool=1, wsb=pre) == 4
+    assert pkg.csa2_index_prefill_workspace_bytes_ex(1, 100, 8, 0, 1, 4, 128) == pre
     assert pkg.csa2_index_prefill_workspace_bytes(-1, 100, 8, 4, 128) == 0
 
 
@@ -83,9 +87,9 @@ def test_index_full_e4m3_argument_checks(pkg):
     assert _idx(pkg, f, Di=100) == 3
     assert _idx(pkg, f, wsb=10) == 4
     assert _idx(pkg, f, Q=0) == 0
-    assert _idx(pkg, f, qseq=NULL, P=16, pool=1) == 3
     pre = pkg.csa2_index_prefill_workspace_bytes(1, 100, 8, 4, 128)
     assert _idx(pkg, f, qseq=NULL, wsb=pre - 1) == 4
+    assert _idx(pkg, f, qseq=NULL, P=16, pool=1, wsb=pre) == 4
 
 
 @pytest.mark.parametrize("fn", ["csa2_reindex", "csa2_reindex_e4m3"])

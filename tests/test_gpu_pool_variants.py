@@ -99,3 +99,56 @@ def test_sum_rule_full_size_1m(csa2):
     del t
     torch.cuda.empty_cache()
 
+
+
+def _prefill_pool(csa2, w, t, keys, rule, P, bs):
+    Q = w.Qn
+    maxn = int(w.q_nvis().max())
+    kI = t["kI8" if keys == "e4m3" else "kI"]
+    idx, pool = C.poison_i32((Q, w.topk)), C.poison_i32((Q, P))
+    buf = C.ws(csa2.csa2_index_prefill_workspace_bytes_ex(Q, maxn, w.topk, P, bs, w.Hk, w.Di))
+    csa2.csa2_index_full_ex(t["qI_full"], kI, t["seq_row_off"], None, t["q_nvis"], maxn, w.topk,
+                            idx, P, bs, pool, block_rule=rule, ws=buf)
+    qR = torch.from_numpy(host_qI(w, T_QI_REINDEX)).cuda()
+    re = C.poison_i32((Q, w.topk))
+    rbuf = C.ws(csa2.csa2_reindex_workspace_bytes(Q, P, bs))
+    fn = csa2.csa2_reindex_e4m3 if keys == "e4m3" else csa2.csa2_reindex
+    fn(qR, kI, t["seq_row_off"], None, t["q_nvis"], pool, bs, w.topk, re, rbuf)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), pool.cpu().numpy(), re.cpu().numpy()
+
+
+def _check_prefill(w, keys, rule, P, bs, idx, pool, re, rows):
+    kI = (host_kI_rows_e4m3 if keys == "e4m3" else host_kI_rows)(w, 0, int(w.ctx[0]))
+    nv = w.q_nvis()
+    qF, qR = host_qI(w, T_QI_FULL), host_qI(w, T_QI_REINDEX)
+    for i in rows:
+        r, p = oracle.index_full(qF[i:i + 1], kI, [0], [0], [nv[i]], w.Hi, w.Hk, w.Di, w.topk, P,
+                                 bs, block_rule=rule)
+        assert np.array_equal(idx[i], r[0]), f"Top-K of prefill query {i}"
+        assert np.array_equal(pool[i], p[0]), f"{rule} pool of prefill query {i}"
+        rr = oracle.reindex(qR[i:i + 1], kI, [0], [0], [nv[i]], p, bs, w.Hi, w.Hk, w.Di, w.topk)
+        assert np.array_equal(re[i], rr[0]), f"Reindex of prefill query {i}"
+
+
+@pytest.mark.parametrize("keys", ["f32", "e4m3"])
+@pytest.mark.parametrize("rule,P,bs", [("max", 256, 8), ("sum", 256, 8), ("max", 2048, 2),
+                                       ("sum", 100, 4)])
+def test_prefill_chunk_pool_and_reindex(csa2, keys, rule, P, bs):
+    # the encoder-side hierarchical indexer: a pool per prefill query, then
+    # Reindex over it for the chunk (q_seq NULL)
+    w = workload(2, small=True)
+    _say(f"[{w.name} prefill pool {keys} {rule} {P}x{bs}] Qn={w.Qn}")
+    t = build_device(w, with_kv=False, layers=0, keys=keys)
+    idx, pool, re = _prefill_pool(csa2, w, t, keys, rule, P, bs)
+    _check_prefill(w, keys, rule, P, bs, idx, pool, re, range(w.Qn))
+
+
+def test_prefill_chunk_pool_full_size(csa2):
+    w = workload(2)
+    _say(f"[{w.name} prefill pool e4m3 max 2048x8] Qn={w.Qn} entries={w.ctx[0]}")
+    t = build_device(w, with_kv=False, layers=0, keys="e4m3")
+    idx, pool, re = _prefill_pool(csa2, w, t, "e4m3", "max", 2048, 8)
+    _check_prefill(w, "e4m3", "max", 2048, 8, idx, pool, re, (0, 1, 2047, 4095))
+    del t
+    torch.cuda.empty_cache()
