@@ -671,7 +671,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 // Merges the key-range splits of one (query, head): weights 2^(m_s - M).
 // All partials are requested in one round (up to kMaxSplitRegs in
 // registers), then weighted.
-constexpr int kMaxSplitRegs = 16;
+constexpr int kMaxSplitRegs = 24;
 
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
@@ -760,6 +760,17 @@ struct AttnPlan {
     size_t ws_bytes;
 };
 
+// Key-range splits.  One workgroup fits a CU (its LDS), so a launch runs in
+// rounds of kCUs workgroups; a workgroup costs about kPrologueTiles tiles of
+// fixed latency (index, query and first gathers in flight) plus its tiles;
+// splitting adds the combine launch (about kCombineTiles).  The plan takes the
+// tiles per split with the lowest modelled cost, rounds x (prologue + tiles),
+// among the splits that keep main-KV and window tiles apart (measured: 64
+// queries with 5 splits = 320 workgroups ran in two rounds, 47 us per layer).
+constexpr int kCUs = 256;
+constexpr int kPrologueTiles = 3;
+constexpr int kCombineTiles = 2;
+
 int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnPlan* p) {
     if (rows_q < 0 || H <= 0 || D <= 0 || topk < 0 || W < 0) return CSA2_ERR_SHAPE;
     if (D != kD || H % 16 != 0 || topk > CSA2_MAX_TOPK || W > 1024 || rows_q > 65535)
@@ -767,23 +778,25 @@ int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnP
     p->hgroups = (H + 63) / 64;
     p->ntiles_main = (topk + kTK - 1) / kTK;
     p->ntiles = p->ntiles_main + (W + kTK - 1) / kTK;
+    const int nwin = p->ntiles - p->ntiles_main;
+    const long units = (long)rows_q * p->hgroups;
     int nsplit = 1;
-    if (allow_split && p->ntiles > 1) {
-        const long wgs = (long)rows_q * p->hgroups;
-        const long target = 256;
-        if (wgs < target) nsplit = (int)((target + wgs - 1) / wgs);
-        if (nsplit > p->ntiles) nsplit = p->ntiles;
-        if (nsplit > kMaxSplitRegs) nsplit = kMaxSplitRegs;
-    }
-    p->tps = p->ntiles > 0 ? (p->ntiles + nsplit - 1) / nsplit : 0;
+    p->tps = p->ntiles;
     p->nsplit_main = 0;
-    if (nsplit > 1) {
-        // no split straddles the main-KV and window tiles
-        const int nwin = p->ntiles - p->ntiles_main;
-        for (;; ++p->tps) {
-            p->nsplit_main = (p->ntiles_main + p->tps - 1) / p->tps;
-            nsplit = p->nsplit_main + (nwin + p->tps - 1) / p->tps;
-            if (nsplit <= kMaxSplitRegs) break;
+    if (allow_split && p->ntiles > 1) {
+        long best = ((units + kCUs - 1) / kCUs) * (kPrologueTiles + p->ntiles);   // no split
+        for (int tps = 1; tps < p->ntiles; ++tps) {
+            const int nm = (p->ntiles_main + tps - 1) / tps, nw = (nwin + tps - 1) / tps;
+            const int ns = nm + nw;
+            if (ns < 2 || ns > kMaxSplitRegs) continue;
+            const long rounds = (units * ns + kCUs - 1) / kCUs;
+            const long cost = rounds * (kPrologueTiles + tps) + kCombineTiles;
+            if (cost < best) {
+                best = cost;
+                nsplit = ns;
+                p->tps = tps;
+                p->nsplit_main = nm;
+            }
         }
     }
     p->nsplit = nsplit;

@@ -7,6 +7,8 @@
 // the sum over indexer heads of the query head dotted with the key row.  Key
 // rows are fp32 (k_score_stream) or, in the compact cache, one E4M3FN byte
 // per value (k_score_stream_e4m3).
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "rowdot.hpp"
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(kStreamThreads32) void k_score_stream(
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
-    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b) {
+    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b, int rpw) {
     // 16-bit bin counters, two per word (a workgroup sees at most
     // kRowsPerWG keys).  Three 4-wave workgroups of 4,096 rows (48 KB of LDS
     // each) fill the twelve wave slots the registers allow per CU; a sweep
@@ -76,9 +78,9 @@ __global__ __launch_bounds__(kStreamThreads32) void k_score_stream(
     constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (32 KB of 2 KB rows)
     const int q = blockIdx.y;
     const int nvis = min(q_nvis[q], (int)kstride);   // q_nvis <= max_nvis <= kstride
-    const int r0 = blockIdx.x * kRowsPerWG;
+    const int r0 = blockIdx.x * rpw;   // rpw <= kRowsPerWG, a multiple of 64
     if (r0 >= nvis) return;
-    const int r1 = min(nvis, r0 + kRowsPerWG);
+    const int r1 = min(nvis, r0 + rpw);
     const bool pool = bkeys != nullptr;
     for (int i = threadIdx.x; i < kHistBins / 2; i += kStreamThreads32) { s_he[i] = 0; s_hb[i] = 0; }
     __syncthreads();
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kStreamThreads8) void k_score_stream_e4m3(
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
-    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b) {
+    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b, int rpw) {
     __shared__ uint32_t s_he[kHistBins / 2];
     __shared__ uint32_t s_hb[kHistBins / 2];
     __shared__ __attribute__((aligned(16))) uint32_t s_ke[kRowsPerWG8];
@@ -162,9 +164,9 @@ __global__ __launch_bounds__(kStreamThreads8) void k_score_stream_e4m3(
     constexpr int GSH = 4 - log2_groups<G>();             // lane bits below the group index
     const int q = blockIdx.y;
     const int nvis = min(q_nvis[q], (int)kstride);
-    const int r0 = blockIdx.x * kRowsPerWG8;
+    const int r0 = blockIdx.x * rpw;   // rpw <= kRowsPerWG8, a multiple of 64
     if (r0 >= nvis) return;
-    const int r1 = min(nvis, r0 + kRowsPerWG8);
+    const int r1 = min(nvis, r0 + rpw);
     const bool pool = bkeys != nullptr;
     for (int i = threadIdx.x; i < kHistBins / 2; i += kStreamThreads8) { s_he[i] = 0; s_hb[i] = 0; }
     __syncthreads();
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(kStreamThreads8) void k_score_stream_e4m3(
     if (pool) {
         // block keys from the row keys staged in LDS: block bi covers rows
         // [bi << bs_log2, (bi + 1) << bs_log2) of this workgroup's range
-        // (ranges start on whole blocks: kRowsPerWG8 is a multiple of 8); for
+        // (ranges start on whole blocks: rpw is a multiple of 8); for
         // the maximum, the rows past the last valid one read as 0, below
         // every real key
         const int nk = r1 - r0, nb = (nk + (int)bmask) >> bs_log2;
@@ -245,13 +247,18 @@ int launch_score_stream(int vpr, bool e4m3, int max_nvis, int Q, hipStream_t s,
                         const int32_t* q_seq, const int32_t* q_nvis, int Hi, int Hk, int Di,
                         uint32_t* keys, int64_t kstride, uint32_t* hist_e, uint32_t* bkeys,
                         int64_t bstride, int bs_log2, int block_sum, uint32_t* hist_b) {
-    const int rpw = e4m3 ? kRowsPerWG8 : kRowsPerWG;
+    // rows per workgroup: the tuned maximum for large launches; small ones
+    // (few queries, short rows) are cut into more workgroups, about 512
+    // (fp32) or 256 (E4M3, two per CU) in all, of at least 64 rows
+    const int rmax = e4m3 ? kRowsPerWG8 : kRowsPerWG;
+    const int64_t want = ((int64_t)Q * max_nvis + (e4m3 ? 255 : 511)) / (e4m3 ? 256 : 512);
+    const int rpw = (int)std::min<int64_t>(rmax, std::max<int64_t>(64, (want + 63) / 64 * 64));
     const dim3 grid((max_nvis + rpw - 1) / rpw, Q);
     const dim3 block(e4m3 ? kStreamThreads8 : kStreamThreads32);
 #define CSA2_STREAM(KERNEL, KT, NAME)                                                         \
     CSA2_LAUNCH(NAME, KERNEL, grid, block, s, qI, static_cast<const KT*>(kI),                \
                 seq_row_off, q_seq, q_nvis, Hi, Hk, Di, keys, kstride, hist_e, bkeys, bstride,\
-                bs_log2, block_sum, hist_b)
+                bs_log2, block_sum, hist_b, rpw)
     if (e4m3)
         return vpr == 1 ? CSA2_STREAM((k_score_stream_e4m3<1, kStreamNB8>), uint8_t,
                                       "score_stream_e4m3")
