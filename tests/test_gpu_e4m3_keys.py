@@ -216,3 +216,35 @@ def test_e4m3_keys_full_size_hierarchical_1m(csa2):
         assert np.array_equal(re[b], _oracle_reindex(w, b, p[0])), f"Reindex of query {b}"
     del t
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("ctx,topk", [([10, 64, 65, 3000, 0, 1], 64), ([2049, 0, 4097], 2048)])
+def test_e4m3_keys_ragged_empty_and_short(csa2, ctx, topk):
+    # empty sequences, a single entry, K above the context, K = 2,048
+    w = Workload("e4m3_ragged", 23, "decode_hier", ctx, H=16, topk=topk, layers=0,
+                 pool_blocks=min(topk, 600))
+    t = build_device(w, with_kv=False, layers=0, keys="e4m3")
+    idx, pool = _index8(csa2, w, t, pool_blocks=w.pool_blocks)
+    for b in range(w.B):
+        if w.ctx[b] == 0:
+            assert np.all(idx[b] == -1) and np.all(pool[b] == -1)
+            continue
+        r, p = _oracle_index(w, b, pool_blocks=w.pool_blocks)
+        assert np.array_equal(idx[b], r[0]), f"Top-K of query {b} ctx {w.ctx[b]}"
+        assert np.array_equal(pool[b], p[0]), f"pool of query {b} ctx {w.ctx[b]}"
+
+
+def test_e4m3_keys_all_ties_and_long_rows(csa2):
+    # qI = 0: every score is 0 (the lowest indices and block ids win); rows
+    # past 65,536 keys take the filter + finalize selection
+    w = Workload("e4m3_ties", 24, "decode_hier", [20000, 70000], H=16, topk=512, layers=0,
+                 pool_blocks=2048)
+    t = build_device(w, with_kv=False, layers=0, keys="e4m3")
+    idx, pool = _index8(csa2, w, t, qI=torch.zeros_like(t["qI_full"]), pool_blocks=2048)
+    for b in range(2):
+        assert np.array_equal(idx[b], np.arange(512))
+        assert np.array_equal(pool[b], np.arange(2048))
+    idx, pool = _index8(csa2, w, t, pool_blocks=2048)
+    for b in range(2):
+        r, p = _oracle_index(w, b, pool_blocks=2048)
+        assert np.array_equal(idx[b], r[0]) and np.array_equal(pool[b], p[0]), f"query {b}"
