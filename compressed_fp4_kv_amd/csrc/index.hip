@@ -64,7 +64,12 @@ __global__ void k_zero_u32(uint32_t* __restrict__ p, size_t n) {
 // 1 <= k <= number of non-empty keys.
 // Digits are taken from bit `top_shift` down; bits above top_shift + 8 must
 // already be equal across all keys.  Stops early once the chosen digit's
-// bucket holds exactly the keys still wanted.
+// bucket holds exactly the keys still wanted.  Once the score word (bits
+// 32-63) is resolved, the keys tied on it (at most kTieCap) are ranked
+// directly by their index word instead of taking four more radix passes:
+// with integer scores the K-th score is usually shared by a few keys.
+constexpr int kTieCap = 1024;
+
 template <int NT, int IPT>
 __device__ uint64_t block_select_kth(const uint64_t (&it)[IPT], uint32_t k, uint32_t* s_hist,
                                      uint32_t* s_dig, int top_shift) {
@@ -114,6 +119,29 @@ __device__ uint64_t block_select_kth(const uint64_t (&it)[IPT], uint32_t k, uint
         mask |= 0xFFull << shift;
         want -= above;
         if (bucket == want) break;   // every key of this bucket is selected
+        if (shift == 32 && bucket <= (uint32_t)kTieCap) {
+            // the bucket's keys share the K-th score; their index words are
+            // distinct, and the want-th largest has exactly want - 1 above it
+            __shared__ uint32_t s_tie[kTieCap];
+            __shared__ uint32_t s_nt;
+            if (threadIdx.x == 0) s_nt = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < IPT; ++j)
+                if (it[j] != 0 && (it[j] & mask) == prefix)
+                    s_tie[atomicAdd(&s_nt, 1u)] = (uint32_t)it[j];
+            __syncthreads();
+            for (int i = threadIdx.x; i < (int)bucket; i += NT) {
+                const uint32_t v = s_tie[i];
+                uint32_t r = 0;
+                for (int x = 0; x < (int)bucket; ++x) r += s_tie[x] > v;
+                if (r == want - 1u) s_dig[0] = v;
+            }
+            __syncthreads();
+            prefix |= (uint64_t)s_dig[0];
+            __syncthreads();
+            break;
+        }
     }
     return prefix;
 }
