@@ -318,6 +318,8 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--keys", choices=("f32", "e4m3"), default="f32",
                     help="indexer-key cache: fp32 (the workloads as stated) or E4M3 bytes")
+    ap.add_argument("--no-e4m3-line", action="store_true",
+                    help="decode workload: skip the E4M3 key-cache figure added to the line")
     ap.add_argument("--pool-blocks", type=int, default=None,
                     help="hierarchical workload: blocks in the candidate pool (default 2,048)")
     ap.add_argument("--block-size", type=int, default=None,
@@ -414,6 +416,36 @@ def main():
     }
     if w.kind == "prefill":
         res["mfma_utilisation"] = mfma_utilisation(w, kern)
+    if args.workload == 1 and args.keys == "f32" and not args.no_e4m3_line:
+        # the same step over the compact indexer-key cache (E4M3 bytes), a
+        # storage variant reported beside the fp32 figure, never as `value`
+        from gen.workloads import dev_kI_e4m3
+        del t["kI"]
+        torch.cuda.empty_cache()
+        t["kI8"] = dev_kI_e4m3(w)
+        step8, _ = make_step(csa2, w, t, torch, "e4m3")
+        for _ in range(args.warmup):
+            step8()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step8()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms8 = e0.elapsed_time(e1) / args.steps
+        csa2.profile_reset()
+        csa2.profile_enable(True)
+        for _ in range(args.steps):
+            step8()
+        torch.cuda.synchronize()
+        prof8 = csa2.profile_read()
+        csa2.profile_enable(False)
+        kern8 = {k: {"launches": n, "avg_us": 1000.0 * ms / n} for k, (n, ms) in prof8.items()}
+        res["e4m3_keys"] = {"value": w.Q / (ms8 * 1e-3), "unit": "queries/s", "ms_per_step": ms8,
+                            "config": "same step, indexer keys stored as E4M3FN bytes (512 B "
+                                      "rows instead of 2 KB)",
+                            "kernels": kern8, "roofline": dominant_roofline(w, kern8, "e4m3")}
+        log(f"e4m3 keys: {ms8:.3f} ms/step")
     del t
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and args.workload == 1:

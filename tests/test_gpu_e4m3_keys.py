@@ -248,3 +248,17 @@ def test_e4m3_keys_all_ties_and_long_rows(csa2):
     for b in range(2):
         r, p = _oracle_index(w, b, pool_blocks=2048)
         assert np.array_equal(idx[b], r[0]) and np.array_equal(pool[b], p[0]), f"query {b}"
+
+
+@pytest.mark.parametrize("Hi,Hk,Di", [(4, 1, 512), (4, 4, 256)])
+def test_e4m3_keys_prefill_row_widths(csa2, Hi, Hk, Di):
+    # the prefill form over E4M3 keys with a shared key head (512-byte rows)
+    # and with 1,024-byte rows
+    w = Workload(f"e4m3_prefill_{Hi}x{Hk}x{Di}", 25, "prefill", [3000], Hi=Hi, Hk=Hk, Di=Di,
+                 topk=128, layers=0, p0=5900, Qn=70, m=2)
+    t = build_device(w, with_kv=False, layers=0, keys="e4m3")
+    idx, _ = _index8(csa2, w, t, prefill=True)
+    k8 = host_kI_rows_e4m3(w, 0, int(w.ctx[0]))
+    ref, _ = oracle.index_full(host_qI(w, T_QI_FULL), k8, [0], np.zeros(w.Qn, np.int32),
+                               w.q_nvis(), w.Hi, w.Hk, w.Di, w.topk)
+    assert np.array_equal(idx, ref)
