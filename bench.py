@@ -155,6 +155,42 @@ def dominant_roofline(w, kern, keys="f32"):
     return None
 
 
+def step_hbm(w, ms_step, keys="f32"):
+    """Algorithmic HBM bytes of one whole step (every call of the workload's
+    sequence) and the rate they imply at the measured step time: the key rows
+    streamed by a Full layer, the key rows a Reindex layer gathers, and per
+    attention layer the query, the output, the selected FP4 rows (288 B), the
+    window K and V (E4M3) and the index row.  Workspace traffic (score keys,
+    split partials) is not algorithmic and not counted."""
+    import numpy as np
+    vb = 1 if keys == "e4m3" else 4
+    rb = w.row_width * vb                           # bytes of one key row
+    qb = w.Hi * w.Di * 4                            # one indexer query
+    total = 0.0
+    if w.kind in ("decode_full", "decode_hier", "prefill"):
+        total += float(np.sum(w.ctx)) * rb + w.Q * qb          # Full-layer stream (prefill: once)
+    if w.kind in ("decode_hier", "decode_reindex"):
+        if w.pool is not None:
+            cand = sum(min(int(np.sum(w.pool[b] >= 0)) * w.block_size, w.ctx[b])
+                       for b in range(w.B))
+        else:
+            cand = sum(min(w.pool_blocks * w.block_size, w.ctx[b]) for b in range(w.B))
+        total += float(cand) * rb + w.Q * qb
+    sel = np.minimum(w.q_nvis(), w.topk).astype(np.float64)
+    win = float(w.swa_rows() if w.kind == "prefill" else w.B * w.W)
+    per_layer = (2.0 * w.Q * w.H * w.D * 4 + float(np.sum(sel)) * (w.D // 2 + w.D // 16)
+                 + win * 2 * w.D + w.Q * w.topk * 4)
+    if w.kind == "prefill":
+        # every query's selected rows come from one 65,536-entry sequence:
+        # the unique rows bound the compulsory bytes
+        per_layer = (2.0 * w.Q * w.H * w.D * 4 + min(float(np.sum(sel)), float(w.ctx[0]))
+                     * (w.D // 2 + w.D // 16) + win * 2 * w.D + w.Q * w.topk * 4)
+    total += w.layers * per_layer
+    ach = total / (ms_step * 1e-3) / 1e9
+    return {"algorithmic_bytes": total, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ach / HBM_PEAK_GBS}
+
+
 def mfma_utilisation(w, kern):
     """Algorithmic flops per launch / measured launch time of the matrix-core
     kernels, against the dense fp16/bf16 peak (the two-part fp16 splits of
@@ -413,6 +449,7 @@ def main():
                    "global_batch": w.Q, "seq_len": int(max(w.ctx)), "parallelism": "single GPU"},
         "kernels": kern,
         "roofline": dominant_roofline(w, kern, args.keys),
+        "step_hbm": step_hbm(w, ms_step, args.keys),
     }
     if w.kind == "prefill":
         res["mfma_utilisation"] = mfma_utilisation(w, kern)
@@ -444,7 +481,8 @@ def main():
         res["e4m3_keys"] = {"value": w.Q / (ms8 * 1e-3), "unit": "queries/s", "ms_per_step": ms8,
                             "config": "same step, indexer keys stored as E4M3FN bytes (512 B "
                                       "rows instead of 2 KB)",
-                            "kernels": kern8, "roofline": dominant_roofline(w, kern8, "e4m3")}
+                            "kernels": kern8, "roofline": dominant_roofline(w, kern8, "e4m3"),
+                            "step_hbm": step_hbm(w, ms8, "e4m3")}
         log(f"e4m3 keys: {ms8:.3f} ms/step")
     del t
     torch.cuda.empty_cache()
