@@ -5,7 +5,8 @@ sequences x 65,536 entries: the Full layer's indexer (score stream over
 32 x 65,536 fp32 key rows of 4 heads x 128 dims, exact Top-512), then
 sparse attention for the Full layer and its 3 Reuse layers (64 heads x 512
 channels over the 512 selected FP4 rows + a 128-token FP8 window, each layer
-with its own query and window).  Inputs are seeded synthetic tensors already
+with its own query and window; the four layers share the indices and the
+KV and go in one csa2_sparse_attn_decode_layers call).  Inputs are seeded synthetic tensors already
 resident in HBM.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--keys f32|e4m3]
@@ -90,21 +91,23 @@ def make_step(csa2, w, t, torch, keys="f32", block_rule="max"):
     if w.kind == "prefill":
         nb = csa2.csa2_prefill_workspace_bytes(Q, w.H, w.D, w.topk, w.W)
     else:
-        nb = csa2.csa2_decode_workspace_bytes(Q, w.H, w.D, w.topk, w.W)
+        # the decode layers of a group share the indices and the KV: one call
+        nb = csa2.csa2_decode_layers_workspace_bytes(w.layers, Q, w.H, w.D, w.topk, w.W)
     ws_a = torch.empty(max(256, nb), dtype=torch.uint8, device=dev)
     outs = [torch.empty((Q, w.H, w.D), dtype=torch.float32, device=dev) for _ in range(w.layers)]
     lses = [torch.empty((Q, w.H), dtype=torch.float32, device=dev) for _ in range(w.layers)]
 
-    def attn(layer, ix):
+    def attn_layers(ix):
         if w.kind == "prefill":
-            csa2.csa2_sparse_attn_prefill_chunk(t["q"][layer], w.p0, t["kv_codes"], t["kv_scales"],
-                                                ix, t["swa_k"][layer], t["swa_v"][layer], w.W,
-                                                w.scale, outs[layer], lses[layer], ws=ws_a)
+            for layer in range(w.layers):
+                csa2.csa2_sparse_attn_prefill_chunk(t["q"][layer], w.p0, t["kv_codes"],
+                                                    t["kv_scales"], ix, t["swa_k"][layer],
+                                                    t["swa_v"][layer], w.W, w.scale, outs[layer],
+                                                    lses[layer], ws=ws_a)
         else:
-            csa2.csa2_sparse_attn_decode(t["q"][layer], t["kv_codes"], t["kv_scales"],
-                                         t["seq_row_off"], ix, t["swa_k"][layer],
-                                         t["swa_v"][layer], t["swa_len"], w.scale, outs[layer],
-                                         lses[layer], ws=ws_a)
+            csa2.csa2_sparse_attn_decode_layers(t["q"], t["kv_codes"], t["kv_scales"],
+                                                t["seq_row_off"], ix, t["swa_k"], t["swa_v"],
+                                                t["swa_len"], w.scale, outs, lses, ws=ws_a)
 
     def step():
         if w.kind in ("decode_full", "prefill"):
@@ -112,8 +115,7 @@ def make_step(csa2, w, t, torch, keys="f32", block_rule="max"):
             index_full(t["qI_full"], kI, t["seq_row_off"],
                        None if w.kind == "prefill" else t["q_seq"], t["q_nvis"], max_nvis, w.topk,
                        idx, ws=ws_i)
-            for layer in range(w.layers):
-                attn(layer, idx)
+            attn_layers(idx)
             return
         if w.kind == "decode_hier":
             # the Full layer's indexer builds Top-K and the candidate pool
@@ -123,8 +125,7 @@ def make_step(csa2, w, t, torch, keys="f32", block_rule="max"):
         # Reindex layer over the pool, then Reindex + Reuse layers' attention
         reindex(t["qI_reindex"], kI, t["seq_row_off"], t["q_seq"], t["q_nvis"], pool,
                 w.block_size, w.topk, ridx, ws=ws_r)
-        for layer in range(w.layers):
-            attn(layer, ridx)
+        attn_layers(ridx)
     return step, idx
 
 
@@ -197,7 +198,8 @@ def mfma_utilisation(w, kern):
     the attention execute twice the algorithmic flops; they are not counted)."""
     res = {}
     if "attn" in kern:
-        flops = 4.0 * w.H * (w.topk + w.W) * w.D * w.Q     # QK^T and PV, 2 flops per MAC
+        # QK^T and PV, 2 flops per MAC; a decode launch covers the group's layers
+        flops = 4.0 * w.H * (w.topk + w.W) * w.D * w.Q * (1 if w.kind == "prefill" else w.layers)
         ach = flops / (kern["attn"]["avg_us"] * 1e-6) / 1e12
         res["attn"] = {"bound": "mfma", "kernel": "attn (fp16 MFMA)", "achieved": ach,
                        "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",

@@ -14,6 +14,7 @@ __all__ = [
     "CSA2Error", "lib", "csa2_index_full", "csa2_index_full_workspace_bytes", "csa2_reindex",
     "csa2_index_full_e4m3", "csa2_reindex_e4m3", "csa2_index_full_ex",
     "csa2_index_prefill_workspace_bytes", "csa2_index_prefill_workspace_bytes_ex",
+    "csa2_sparse_attn_decode_layers", "csa2_decode_layers_workspace_bytes",
     "csa2_reindex_workspace_bytes", "csa2_sparse_attn_decode", "csa2_decode_workspace_bytes",
     "csa2_sparse_attn_prefill_chunk", "csa2_prefill_workspace_bytes", "csa2_kv_quantize_fp4",
     "csa2_swa_append", "profile_enable",
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = [
     "csa2_swa_append",
     "csa2_index_full_e4m3", "csa2_reindex_e4m3", "csa2_index_full_ex",
     "csa2_index_prefill_workspace_bytes_ex",
+    "csa2_sparse_attn_decode_layers", "csa2_decode_layers_workspace_bytes",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -72,6 +74,10 @@ lib.csa2_decode_workspace_bytes.restype = _SZ
 lib.csa2_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
 lib.csa2_sparse_attn_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
                                         _I32, _F32, _P, _P, _P, _SZ, _P]
+lib.csa2_decode_layers_workspace_bytes.restype = _SZ
+lib.csa2_decode_layers_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32]
+lib.csa2_sparse_attn_decode_layers.argtypes = [_I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32,
+                                               _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]
 lib.csa2_prefill_workspace_bytes.restype = _SZ
 lib.csa2_prefill_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
 lib.csa2_sparse_attn_prefill_chunk.argtypes = [_P, _I64, _P, _P, _P, _I32, _P, _P, _I32, _I32,
@@ -257,6 +263,39 @@ def csa2_sparse_attn_decode(q, kv_codes, kv_scales, seq_row_off, topk_idx, swa_k
         _ptr(swa_k, u8, "swa_k"), _ptr(swa_v, u8, "swa_v"), _ptr(swa_len, i32, "swa_len"), W, B,
         H, D, float(softmax_scale), _ptr(out, f32, "out"), _ptr(lse, f32, "lse"), wp, wn,
         _stream(stream)), "csa2_sparse_attn_decode")
+
+
+def csa2_decode_layers_workspace_bytes(L, B, H, D, topk, W):
+    return int(lib.csa2_decode_layers_workspace_bytes(L, B, H, D, topk, W))
+
+
+def _ptr_array(tensors, dtype, name):
+    """Host array of device pointers (ctypes) for a list of tensors or Nones."""
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        p = _ptr(t, dtype, f"{name}[{i}]")
+        arr[i] = p.value if p is not None else None
+    return arr
+
+
+def csa2_sparse_attn_decode_layers(qs, kv_codes, kv_scales, seq_row_off, topk_idx, swa_ks, swa_vs,
+                                   swa_len, softmax_scale, outs, lses=None, ws=None, stream=None):
+    """A layer group sharing topk_idx and the main KV: qs / swa_ks / swa_vs / outs / lses are
+    lists of L tensors, each as for csa2_sparse_attn_decode (lses may be None)."""
+    f32, i32, i64, u8 = _dt()
+    L = len(qs)
+    B, H, D = qs[0].shape
+    topk = topk_idx.shape[1] if topk_idx is not None else 0
+    W = swa_ks[0].shape[1]
+    wp, wn = _ws(ws)
+    _check(lib.csa2_sparse_attn_decode_layers(
+        L, _ptr_array(qs, f32, "q"), _ptr(kv_codes, u8, "kv_codes"),
+        _ptr(kv_scales, u8, "kv_scales"), _ptr(seq_row_off, i64, "seq_row_off"),
+        _ptr(topk_idx, i32, "topk_idx"), topk, _ptr_array(swa_ks, u8, "swa_k"),
+        _ptr_array(swa_vs, u8, "swa_v"), _ptr(swa_len, i32, "swa_len"), W, B, H, D,
+        float(softmax_scale), _ptr_array(outs, f32, "out"),
+        _ptr_array(lses, f32, "lse") if lses is not None else None, wp, wn, _stream(stream)),
+        "csa2_sparse_attn_decode_layers")
 
 
 def csa2_prefill_workspace_bytes(Qn, H, D, topk, W):

@@ -62,14 +62,16 @@ __device__ __forceinline__ int tile_off(int row, int ch) {
 }
 constexpr float kLn2 = 0.69314718055994530942f;
 
+constexpr int kMaxLayers = 8;   // layers of one decode call (a layer group)
+
 struct AttnArgs {
-    const float* q;              // [rows_q, H, D]
+    const float* q[kMaxLayers];  // per layer: [rows_q, H, D]
     const uint8_t* kv_codes;     // [rows, D/2]
     const uint8_t* kv_scales;    // [rows, D/16]
     const int64_t* seq_row_off;  // decode: [B]; prefill: nullptr
     const int32_t* topk_idx;     // [rows_q, topk]
-    const uint8_t* swa_k;        // decode: [B, W, D]; prefill: [Qn + W - 1, D]
-    const uint8_t* swa_v;
+    const uint8_t* swa_k[kMaxLayers];   // per layer; decode: [B, W, D]; prefill: [Qn + W - 1, D]
+    const uint8_t* swa_v[kMaxLayers];
     const int32_t* swa_len;      // decode: [B]; prefill: nullptr
     int topk, W, H;
     float scale_log2;            // softmax_scale * log2(e)
@@ -77,10 +79,11 @@ struct AttnArgs {
     int prefill;
     int ntiles_main, ntiles, tiles_per_split, nsplit;
     int nsplit_main;             // splits [0, nsplit_main) cover main-KV tiles only
-    float* out;                  // [rows_q, H, D]
-    float* lse;                  // [rows_q, H] or nullptr
-    float* part_o;               // [nsplit, rows_q, H, D] (nsplit > 1)
-    float* part_ml;              // [nsplit, rows_q, H, 2]
+    float* out[kMaxLayers];      // per layer: [rows_q, H, D]
+    float* lse[kMaxLayers];      // per layer: [rows_q, H] or nullptr
+    int rows_q, nlayers;         // the grid's z covers rows_q x nlayers (layer-major)
+    float* part_o;               // [nsplit, nlayers * rows_q, H, D] (nsplit > 1)
+    float* part_ml;              // [nsplit, nlayers * rows_q, H, 2]
 };
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
@@ -295,7 +298,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         split = blockIdx.x;
         unit = blockIdx.y + nhg * blockIdx.z;
     }
-    const int hgrp = unit % nhg, qi = unit / nhg;
+    const int hgrp = unit % nhg, qz = unit / nhg;   // qz = layer * rows_q + query
+    const int layer = qz / a.rows_q, qi = qz - layer * a.rows_q;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hh = lane >> 5, l32 = lane & 31;      // lane half, lane in half
     const int hg = wave & 1, cq = wave >> 1;         // head group, channel quarter
@@ -311,13 +315,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         const int64_t p = a.p0 + qi;
         wlo = (int)max((int64_t)0, (int64_t)(a.W - 1) - p);
         whi = a.W;
-        swk = a.swa_k + (size_t)qi * kD;
-        swv = a.swa_v + (size_t)qi * kD;
+        swk = a.swa_k[layer] + (size_t)qi * kD;
+        swv = a.swa_v[layer] + (size_t)qi * kD;
     } else {
         row0 = a.seq_row_off[qi];
         whi = min(a.swa_len[qi], a.W);
-        swk = a.swa_k + (size_t)qi * a.W * kD;
-        swv = a.swa_v + (size_t)qi * a.W * kD;
+        swk = a.swa_k[layer] + (size_t)qi * a.W * kD;
+        swv = a.swa_v[layer] + (size_t)qi * a.W * kD;
     }
     // tile range: with several splits, each holds main-KV tiles only or
     // window tiles only; a single split holds all tiles
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     f16x8 q0[8], q1[8];
     float qunscale;   // exact inverse of the scaling, applied to the partial logits
     {
-        const float* qp = a.q + ((size_t)qi * a.H + (hvalid ? h : 0)) * kD + cbase + 8 * hh;
+        const float* qp = a.q[layer] + ((size_t)qi * a.H + (hvalid ? h : 0)) * kD + cbase + 8 * hh;
         // head 0 stands in for a padding head (zeroed below)
         float4 xq[16];
 #pragma unroll
@@ -641,19 +645,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     // lane (hh, head) holds channels cbase + 32 ct + 8 q + 4 hh + 0..3, q = 0..3
     const size_t orow = ((size_t)qi * a.H + h) * kD + cbase + 4 * hh;
     if (a.nsplit == 1) {
+        float* const out = a.out[layer];
+        float* const lse = a.lse[layer];
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<float4*>(a.out + orow + 32 * ct + 8 * q4) =
+                *reinterpret_cast<float4*>(out + orow + 32 * ct + 8 * q4) =
                     make_float4(o[ct][4 * q4] * inv, o[ct][4 * q4 + 1] * inv,
                                 o[ct][4 * q4 + 2] * inv, o[ct][4 * q4 + 3] * inv);
-        if (a.lse && hh == 0 && cq == 0)
-            a.lse[(size_t)qi * a.H + h] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+        if (lse && hh == 0 && cq == 0)
+            lse[(size_t)qi * a.H + h] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
     } else {
-        const size_t rows_q = gridDim.z;
-        float* po = a.part_o + ((size_t)split * rows_q * a.H) * kD + orow;
+        // partial rows: every layer's rows, layer-major (qz)
+        const size_t rows_all = gridDim.z;
+        float* po = a.part_o + ((size_t)split * rows_all * a.H) * kD +
+                    ((size_t)qz * a.H + h) * kD + cbase + 4 * hh;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -661,7 +669,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
                 *reinterpret_cast<float4*>(po + 32 * ct + 8 * q4) =
                     make_float4(o[ct][4 * q4], o[ct][4 * q4 + 1], o[ct][4 * q4 + 2], o[ct][4 * q4 + 3]);
         if (hh == 0 && cq == 0) {
-            float* pm = a.part_ml + (((size_t)split * rows_q + qi) * a.H + h) * 2;
+            float* pm = a.part_ml + (((size_t)split * rows_all + qz) * a.H + h) * 2;
             pm[0] = m;
             pm[1] = lt;
         }
@@ -673,15 +681,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 // registers), then weighted.
 constexpr int kMaxSplitRegs = 24;
 
+// Output rows of a combine: layer l's rows are partial rows
+// [l * rows_q, (l + 1) * rows_q).
+struct CombineOut {
+    float* out[kMaxLayers];
+    float* lse[kMaxLayers];
+    int rows_q;
+};
+
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
-                                                      int nsplit, int rows_q, int H,
-                                                      float* __restrict__ out,
-                                                      float* __restrict__ lse) {
+                                                      int nsplit, int rows_all, int H,
+                                                      CombineOut co) {
     // (query, head) of this workgroup: when the attention kernel gave all
     // splits of a (query, 64-head group) unit to one XCD, the merge of the
     // unit's heads runs on that XCD too (its partials are in that L2)
-    int qh = blockIdx.x;  // qi * H + h
+    const int rows_q = rows_all;
+    int qh = blockIdx.x;  // qz * H + h, qz = layer * co.rows_q + query
     if (H % 64 == 0 && (rows_q * (H / 64)) % kXcds == 0) {
         const int L = blockIdx.x, slot = L / kXcds;
         const int unit = L % kXcds + kXcds * (slot / 64);   // unit = qi * (H / 64) + group
@@ -713,9 +729,11 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    reinterpret_cast<float4*>(out + (size_t)qh * kD)[threadIdx.x] =
+    const int layer = qh / (co.rows_q * H), r = qh - layer * co.rows_q * H;
+    reinterpret_cast<float4*>(co.out[layer] + (size_t)r * kD)[threadIdx.x] =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    if (lse && threadIdx.x == 0) lse[qh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    float* const lse = co.lse[layer];
+    if (lse && threadIdx.x == 0) lse[r] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Test hook: decodes every FP4 byte and FP8 byte with the helpers above.
@@ -809,7 +827,9 @@ int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnP
     return CSA2_OK;
 }
 
-int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_q, void* ws, hipStream_t s) {
+// rows_all = rows_q x nlayers (the plan was made for that many rows)
+int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_all, void* ws, hipStream_t s) {
+    const int rows_q = rows_all;
     a.ntiles_main = pl.ntiles_main;
     a.ntiles = pl.ntiles;
     a.tiles_per_split = pl.tps;
@@ -823,8 +843,14 @@ int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_q, void* ws, hipStream_
     dim3 grid(pl.nsplit, pl.hgroups, rows_q);
     int st = CSA2_LAUNCH("attn", k_attn, grid, dim3(kAttnThreads), s, a);
     if (st || pl.nsplit == 1) return st;
+    CombineOut co{};
+    for (int l = 0; l < a.nlayers; ++l) {
+        co.out[l] = a.out[l];
+        co.lse[l] = a.lse[l];
+    }
+    co.rows_q = a.rows_q;
     return CSA2_LAUNCH("attn_combine", k_attn_combine, dim3(rows_q * a.H), dim3(128), s,
-                       a.part_o, a.part_ml, pl.nsplit, rows_q, a.H, a.out, a.lse);
+                       a.part_o, a.part_ml, pl.nsplit, rows_q, a.H, co);
 }
 
 }  // namespace
@@ -832,11 +858,54 @@ int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_q, void* ws, hipStream_
 
 using namespace csa2;
 
+extern "C" size_t csa2_decode_layers_workspace_bytes(int32_t L, int32_t B, int32_t H, int32_t D,
+                                                     int32_t topk, int32_t W) {
+    if (L < 1 || L > kMaxLayers || B < 0 || (int64_t)B * L > 65535) return 0;
+    AttnPlan p;
+    if (plan_attn(B * L, H, D, topk, W, true, &p) != CSA2_OK) return 0;
+    return p.ws_bytes;
+}
+
 extern "C" size_t csa2_decode_workspace_bytes(int32_t B, int32_t H, int32_t D, int32_t topk,
                                               int32_t W) {
-    AttnPlan p;
-    if (plan_attn(B, H, D, topk, W, true, &p) != CSA2_OK) return 0;
-    return p.ws_bytes;
+    return csa2_decode_layers_workspace_bytes(1, B, H, D, topk, W);
+}
+
+extern "C" int csa2_sparse_attn_decode_layers(
+    int32_t L, const float* const* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
+    const int64_t* seq_row_off, const int32_t* topk_idx, int32_t topk,
+    const uint8_t* const* swa_k, const uint8_t* const* swa_v, const int32_t* swa_len, int32_t W,
+    int32_t B, int32_t H, int32_t D, float softmax_scale, float* const* out, float* const* lse,
+    void* ws, size_t ws_bytes, void* stream) {
+    if (L < 1 || B < 0) return CSA2_ERR_SHAPE;
+    if (L > kMaxLayers || (int64_t)B * L > 65535) return CSA2_ERR_UNSUPPORTED;
+    AttnPlan pl;
+    int st = plan_attn(B * L, H, D, topk, W, true, &pl);
+    if (st) return st;
+    if (B == 0) return CSA2_OK;
+    if (!q || !out || !swa_len || (W > 0 && (!swa_k || !swa_v))) return CSA2_ERR_NULL;
+    if (topk > 0 && (!kv_codes || !kv_scales || !seq_row_off || !topk_idx)) return CSA2_ERR_NULL;
+    AttnArgs a{};
+    for (int l = 0; l < L; ++l) {
+        if (!q[l] || !out[l] || (W > 0 && (!swa_k[l] || !swa_v[l]))) return CSA2_ERR_NULL;
+        const uintptr_t al = (uintptr_t)q[l] | (uintptr_t)out[l] |
+                             (W > 0 ? ((uintptr_t)swa_k[l] | (uintptr_t)swa_v[l]) : 0);
+        if (al & 15) return CSA2_ERR_UNSUPPORTED;
+        a.q[l] = q[l];
+        a.out[l] = out[l];
+        a.lse[l] = lse ? lse[l] : nullptr;
+        a.swa_k[l] = W > 0 ? swa_k[l] : nullptr;
+        a.swa_v[l] = W > 0 ? swa_v[l] : nullptr;
+    }
+    if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return CSA2_ERR_WORKSPACE;
+    a.kv_codes = kv_codes; a.kv_scales = kv_scales; a.seq_row_off = seq_row_off;
+    a.topk_idx = topk_idx; a.swa_len = swa_len;
+    a.topk = topk; a.W = W; a.H = H;
+    a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+    a.prefill = 0;
+    a.rows_q = B;
+    a.nlayers = L;
+    return launch_attn(a, pl, B * L, ws, (hipStream_t)stream);
 }
 
 extern "C" int csa2_sparse_attn_decode(const float* q, const uint8_t* kv_codes,
@@ -846,24 +915,14 @@ extern "C" int csa2_sparse_attn_decode(const float* q, const uint8_t* kv_codes,
                                        const int32_t* swa_len, int32_t W, int32_t B, int32_t H,
                                        int32_t D, float softmax_scale, float* out, float* lse,
                                        void* ws, size_t ws_bytes, void* stream) {
-    AttnPlan pl;
-    int st = plan_attn(B, H, D, topk, W, true, &pl);
-    if (st) return st;
-    if (B == 0) return CSA2_OK;
-    if (!q || !out || !swa_len) return CSA2_ERR_NULL;
-    if (topk > 0 && (!kv_codes || !kv_scales || !seq_row_off || !topk_idx)) return CSA2_ERR_NULL;
-    if (W > 0 && (!swa_k || !swa_v)) return CSA2_ERR_NULL;
-    if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)swa_k | (uintptr_t)swa_v) & 15)
-        return CSA2_ERR_UNSUPPORTED;
-    if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return CSA2_ERR_WORKSPACE;
-    AttnArgs a{};
-    a.q = q; a.kv_codes = kv_codes; a.kv_scales = kv_scales; a.seq_row_off = seq_row_off;
-    a.topk_idx = topk_idx; a.swa_k = swa_k; a.swa_v = swa_v; a.swa_len = swa_len;
-    a.topk = topk; a.W = W; a.H = H;
-    a.scale_log2 = softmax_scale * 1.44269504088896340736f;
-    a.prefill = 0;
-    a.out = out; a.lse = lse;
-    return launch_attn(a, pl, B, ws, (hipStream_t)stream);
+    const float* qs[1] = {q};
+    const uint8_t* ks[1] = {swa_k};
+    const uint8_t* vs[1] = {swa_v};
+    float* os[1] = {out};
+    float* ls[1] = {lse};
+    return csa2_sparse_attn_decode_layers(1, qs, kv_codes, kv_scales, seq_row_off, topk_idx, topk,
+                                          ks, vs, swa_len, W, B, H, D, softmax_scale, os, ls, ws,
+                                          ws_bytes, stream);
 }
 
 extern "C" size_t csa2_prefill_workspace_bytes(int32_t Qn, int32_t H, int32_t D, int32_t topk,
@@ -892,13 +951,15 @@ extern "C" int csa2_sparse_attn_prefill_chunk(const float* q, int64_t p0, const 
         return CSA2_ERR_UNSUPPORTED;
     if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return CSA2_ERR_WORKSPACE;
     AttnArgs a{};
-    a.q = q; a.kv_codes = kv_codes; a.kv_scales = kv_scales; a.seq_row_off = nullptr;
-    a.topk_idx = topk_idx; a.swa_k = swa_k; a.swa_v = swa_v; a.swa_len = nullptr;
+    a.q[0] = q; a.kv_codes = kv_codes; a.kv_scales = kv_scales; a.seq_row_off = nullptr;
+    a.topk_idx = topk_idx; a.swa_k[0] = swa_k; a.swa_v[0] = swa_v; a.swa_len = nullptr;
     a.topk = topk; a.W = W; a.H = H;
     a.scale_log2 = softmax_scale * 1.44269504088896340736f;
     a.p0 = p0;
     a.prefill = 1;
-    a.out = out; a.lse = lse;
+    a.out[0] = out; a.lse[0] = lse;
+    a.rows_q = Qn;
+    a.nlayers = 1;
     return launch_attn(a, pl, Qn, ws, (hipStream_t)stream);
 }
 

@@ -224,6 +224,34 @@ int csa2_sparse_attn_decode(const float* q, const uint8_t* kv_codes, const uint8
                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Sparse attention, decode, for a layer group in one call: L layers (a Full
+ * or Reindex layer and its Reuse layers) that share topk_idx and the main KV
+ * and differ in their query and window (jaehun.me review, section "2) CSA2"
+ * and its worked example: Reuse layers attend with their own query and SWA
+ * KV over the latest Full layer's KV and indices).  Layer l equals
+ * csa2_sparse_attn_decode with q[l], swa_k[l], swa_v[l], out[l], lse[l] and
+ * the shared arguments; one launch covers all L x B query-layers, so small
+ * batches need fewer key-range splits (and often no merge step).
+ *   q, swa_k, swa_v, out   HOST arrays of L device pointers (each as in
+ *                          csa2_sparse_attn_decode); swa_k/swa_v may be NULL
+ *                          when W == 0
+ *   lse                    NULL, or a HOST array of L device pointers (entries
+ *                          may be NULL)
+ *   1 <= L <= 8 and L x B <= 65535 (else CSA2_ERR_UNSUPPORTED); workspace:
+ *   csa2_decode_layers_workspace_bytes.  Other arguments, shapes and errors
+ *   as csa2_sparse_attn_decode; the per-layer call is this one with L = 1.
+ * ---------------------------------------------------------------------- */
+size_t csa2_decode_layers_workspace_bytes(int32_t L, int32_t B, int32_t H, int32_t D,
+                                          int32_t topk, int32_t W);
+int csa2_sparse_attn_decode_layers(int32_t L, const float* const* q, const uint8_t* kv_codes,
+                                   const uint8_t* kv_scales, const int64_t* seq_row_off,
+                                   const int32_t* topk_idx, int32_t topk,
+                                   const uint8_t* const* swa_k, const uint8_t* const* swa_v,
+                                   const int32_t* swa_len, int32_t W, int32_t B, int32_t H,
+                                   int32_t D, float softmax_scale, float* const* out,
+                                   float* const* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Sparse attention over a prefill chunk of ONE sequence: query i sits at
  * position p = p0 + i and equals a decode query with index row topk_idx[i]
  * and the window of the W tokens ending at p (those at positions >= 0).

@@ -142,3 +142,26 @@ def test_index_full_ex_refuses_unknown_rule_and_key_format(pkg):
     assert f(*b) == 1
     b = list(base); b[18] = 10
     assert f(*b) == 4
+
+
+def test_decode_layers_argument_checks(pkg):
+    arr = (ctypes.c_void_p * 2)(16, 32)
+    v = lambda x: ctypes.c_void_p(16 * x)
+    f = pkg.lib.csa2_sparse_attn_decode_layers
+    base = [2, arr, v(1), v(1), v(1), v(1), 512, arr, arr, v(1), 128, 4, 64, 512, 0.04, arr, None,
+            v(1), 1 << 30, None]
+    b = list(base); b[0] = 0
+    assert f(*b) == 2                       # no layer
+    b = list(base); b[0] = 9
+    assert f(*b) == 3                       # more than 8 layers
+    b = list(base); b[1] = None
+    assert f(*b) == 1
+    b = list(base); b[12] = 24
+    assert f(*b) == 3                       # H not a multiple of 16
+    b = list(base); b[18] = 0
+    assert f(*b) == 4                       # 2 layers x 4 queries need split partials
+    # one layer is the per-layer call; 4 layers x 64 queries fill the chip unsplit
+    assert (pkg.csa2_decode_layers_workspace_bytes(1, 32, 64, 512, 512, 128)
+            == pkg.csa2_decode_workspace_bytes(32, 64, 512, 512, 128))
+    assert pkg.csa2_decode_layers_workspace_bytes(4, 64, 64, 512, 512, 128) == 0
+    assert pkg.csa2_decode_layers_workspace_bytes(9, 64, 64, 512, 512, 128) == 0
