@@ -77,8 +77,7 @@ struct AttnArgs {
     float scale_log2;            // softmax_scale * log2(e)
     int64_t p0;                  // prefill: position of query 0
     int prefill;
-    int ntiles_main, ntiles, tiles_per_split, nsplit;
-    int nsplit_main;             // splits [0, nsplit_main) cover main-KV tiles only
+    int ntiles_main, ntiles, tiles_per_split, nsplit;   // split s: tiles [s tps, (s+1) tps)
     float* out[kMaxLayers];      // per layer: [rows_q, H, D]
     float* lse[kMaxLayers];      // per layer: [rows_q, H] or nullptr
     int rows_q, nlayers;         // the grid's z covers rows_q x nlayers (layer-major)
@@ -323,19 +322,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         swk = a.swa_k[layer] + (size_t)qi * a.W * kD;
         swv = a.swa_v[layer] + (size_t)qi * a.W * kD;
     }
-    // tile range: with several splits, each holds main-KV tiles only or
-    // window tiles only; a single split holds all tiles
-    int t0, t1;
-    if (a.nsplit == 1) {
-        t0 = 0;
-        t1 = a.ntiles;
-    } else if (split < a.nsplit_main) {
-        t0 = split * a.tiles_per_split;
-        t1 = min(a.ntiles_main, t0 + a.tiles_per_split);
-    } else {
-        t0 = a.ntiles_main + (split - a.nsplit_main) * a.tiles_per_split;
-        t1 = min(a.ntiles, t0 + a.tiles_per_split);
-    }
+    // tile range of this split: tiles are numbered main-KV first, then
+    // window, and a split's range may hold both (run in that order)
+    const int t0 = a.nsplit == 1 ? 0 : split * a.tiles_per_split;
+    const int t1 = a.nsplit == 1 ? a.ntiles : min(a.ntiles, t0 + a.tiles_per_split);
     const int tm = min(t1, a.ntiles_main);           // main tiles are [t0, tm)
     const int32_t* qidx = a.topk_idx + (size_t)qi * a.topk;
     const __amdgpu_buffer_rsrc_t rcode = __builtin_amdgcn_make_buffer_rsrc(
@@ -774,7 +764,7 @@ __global__ void k_dequant_tables(float* main_out, float* win_out) {
 }
 
 struct AttnPlan {
-    int hgroups, ntiles_main, ntiles, nsplit, tps, nsplit_main;
+    int hgroups, ntiles_main, ntiles, nsplit, tps;
     size_t ws_bytes;
 };
 
@@ -782,9 +772,10 @@ struct AttnPlan {
 // rounds of kCUs workgroups; a workgroup costs about kPrologueTiles tiles of
 // fixed latency (index, query and first gathers in flight) plus its tiles;
 // splitting adds the combine launch (about kCombineTiles).  The plan takes the
-// tiles per split with the lowest modelled cost, rounds x (prologue + tiles),
-// among the splits that keep main-KV and window tiles apart (measured: 64
-// queries with 5 splits = 320 workgroups ran in two rounds, 47 us per layer).
+// tiles per split with the lowest modelled cost, rounds x (prologue + tiles);
+// a split takes consecutive tiles, main-KV then window ones as a single
+// workgroup runs them (measured before: 64 queries with 5 splits kept apart
+// by kind = 320 workgroups ran in two rounds, 47 us per layer).
 constexpr int kCUs = 256;
 constexpr int kPrologueTiles = 3;
 constexpr int kCombineTiles = 2;
@@ -796,16 +787,13 @@ int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnP
     p->hgroups = (H + 63) / 64;
     p->ntiles_main = (topk + kTK - 1) / kTK;
     p->ntiles = p->ntiles_main + (W + kTK - 1) / kTK;
-    const int nwin = p->ntiles - p->ntiles_main;
     const long units = (long)rows_q * p->hgroups;
     int nsplit = 1;
     p->tps = p->ntiles;
-    p->nsplit_main = 0;
     if (allow_split && p->ntiles > 1) {
         long best = ((units + kCUs - 1) / kCUs) * (kPrologueTiles + p->ntiles);   // no split
         for (int tps = 1; tps < p->ntiles; ++tps) {
-            const int nm = (p->ntiles_main + tps - 1) / tps, nw = (nwin + tps - 1) / tps;
-            const int ns = nm + nw;
+            const int ns = (p->ntiles + tps - 1) / tps;
             if (ns < 2 || ns > kMaxSplitRegs) continue;
             const long rounds = (units * ns + kCUs - 1) / kCUs;
             const long cost = rounds * (kPrologueTiles + tps) + kCombineTiles;
@@ -813,7 +801,6 @@ int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnP
                 best = cost;
                 nsplit = ns;
                 p->tps = tps;
-                p->nsplit_main = nm;
             }
         }
     }
@@ -834,7 +821,6 @@ int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_all, void* ws, hipStrea
     a.ntiles = pl.ntiles;
     a.tiles_per_split = pl.tps;
     a.nsplit = pl.nsplit;
-    a.nsplit_main = pl.nsplit_main;
     if (pl.nsplit > 1) {
         Carver c(ws);
         a.part_o = c.take<float>((size_t)pl.nsplit * rows_q * a.H * kD);
