@@ -679,51 +679,63 @@ struct CombineOut {
     int rows_q;
 };
 
+// One workgroup merges HPW heads of one row (HPW x 512 channels, a float4
+// per thread and head); every partial of the HPW heads is requested before
+// the first is weighted (MAXS >= nsplit).
+template <int HPW, int MAXS>
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int nsplit, int rows_all, int H,
                                                       CombineOut co) {
-    // (query, head) of this workgroup: when the attention kernel gave all
-    // splits of a (query, 64-head group) unit to one XCD, the merge of the
+    // (row, head group) of this workgroup: when the attention kernel gave all
+    // splits of a (row, 64-head group) unit to one XCD, the merge of the
     // unit's heads runs on that XCD too (its partials are in that L2)
-    const int rows_q = rows_all;
-    int qh = blockIdx.x;  // qz * H + h, qz = layer * co.rows_q + query
-    if (H % 64 == 0 && (rows_q * (H / 64)) % kXcds == 0) {
+    constexpr int GPU = 64 / HPW;   // head groups of this size per 64 heads
+    int qh0 = blockIdx.x * HPW;     // qz * H + h, qz = layer * co.rows_q + query
+    if (H % 64 == 0 && (rows_all * (H / 64)) % kXcds == 0) {
         const int L = blockIdx.x, slot = L / kXcds;
-        const int unit = L % kXcds + kXcds * (slot / 64);   // unit = qi * (H / 64) + group
-        qh = unit * 64 + slot % 64;
+        const int unit = L % kXcds + kXcds * (slot / GPU);   // unit = qz * (H / 64) + group
+        qh0 = unit * 64 + (slot % GPU) * HPW;
     }
-    const size_t stride_o = (size_t)rows_q * H * kD;
-    const size_t stride_ml = (size_t)rows_q * H * 2;
-    float2 ml[kMaxSplitRegs];
-    float4 po[kMaxSplitRegs];
+    const size_t stride_o = (size_t)rows_all * H * kD;
+    const size_t stride_ml = (size_t)rows_all * H * 2;
+    float2 ml[HPW][MAXS];
+    float4 po[HPW][MAXS];
 #pragma unroll
-    for (int s = 0; s < kMaxSplitRegs; ++s) {
-        if (s < nsplit) {
-            ml[s] = *reinterpret_cast<const float2*>(part_ml + s * stride_ml + (size_t)qh * 2);
-            po[s] = reinterpret_cast<const float4*>(part_o + s * stride_o + (size_t)qh * kD)[threadIdx.x];
+    for (int j = 0; j < HPW; ++j)
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+            if (s < nsplit) {
+                const size_t qh = (size_t)qh0 + j;
+                ml[j][s] = *reinterpret_cast<const float2*>(part_ml + s * stride_ml + qh * 2);
+                po[j][s] = reinterpret_cast<const float4*>(part_o + s * stride_o + qh * kD)[threadIdx.x];
+            }
         }
-    }
-    float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMaxSplitRegs; ++s)
-        if (s < nsplit) M = fmaxf(M, ml[s].x);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < HPW; ++j) {
+        const int qh = qh0 + j;
+        float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMaxSplitRegs; ++s) {
-        if (s < nsplit && ml[s].x != -INFINITY && ml[s].y != 0.f) {
-            const float w = exp2f(ml[s].x - M);
-            L += w * ml[s].y;
-            acc.x += w * po[s].x; acc.y += w * po[s].y; acc.z += w * po[s].z; acc.w += w * po[s].w;
+        for (int s = 0; s < MAXS; ++s)
+            if (s < nsplit) M = fmaxf(M, ml[j][s].x);
+        float L = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+            if (s < nsplit && ml[j][s].x != -INFINITY && ml[j][s].y != 0.f) {
+                const float w = exp2f(ml[j][s].x - M);
+                L += w * ml[j][s].y;
+                acc.x += w * po[j][s].x; acc.y += w * po[j][s].y;
+                acc.z += w * po[j][s].z; acc.w += w * po[j][s].w;
+            }
         }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const int layer = qh / (co.rows_q * H), r = qh - layer * co.rows_q * H;
+        reinterpret_cast<float4*>(co.out[layer] + (size_t)r * kD)[threadIdx.x] =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        float* const lse = co.lse[layer];
+        if (lse && threadIdx.x == 0) lse[r] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const int layer = qh / (co.rows_q * H), r = qh - layer * co.rows_q * H;
-    reinterpret_cast<float4*>(co.out[layer] + (size_t)r * kD)[threadIdx.x] =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    float* const lse = co.lse[layer];
-    if (lse && threadIdx.x == 0) lse[r] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Test hook: decodes every FP4 byte and FP8 byte with the helpers above.
@@ -835,8 +847,12 @@ int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_all, void* ws, hipStrea
         co.lse[l] = a.lse[l];
     }
     co.rows_q = a.rows_q;
-    return CSA2_LAUNCH("attn_combine", k_attn_combine, dim3(rows_q * a.H), dim3(128), s,
-                       a.part_o, a.part_ml, pl.nsplit, rows_q, a.H, co);
+    // four heads per workgroup when every partial of four fits the registers
+    if (pl.nsplit <= 4 && a.H % 4 == 0)
+        return CSA2_LAUNCH("attn_combine", (k_attn_combine<4, 4>), dim3(rows_q * a.H / 4),
+                           dim3(128), s, a.part_o, a.part_ml, pl.nsplit, rows_q, a.H, co);
+    return CSA2_LAUNCH("attn_combine", (k_attn_combine<1, kMaxSplitRegs>), dim3(rows_q * a.H),
+                       dim3(128), s, a.part_o, a.part_ml, pl.nsplit, rows_q, a.H, co);
 }
 
 }  // namespace
