@@ -98,7 +98,7 @@ def test_layer_group_without_lse_and_eight_layers(csa2):
             C.assert_attn_close(outs[layer][b], ro[0], f"8-layer group layer {layer} query {b}")
 
 
-@pytest.mark.parametrize("wid,queries", [(1, (0, 17, 31)), (4, (0, 21, 63))])
+@pytest.mark.parametrize("wid,queries", [(1, (0, 17, 31)), (3, (0, 7)), (4, (0, 21, 63))])
 def test_layer_group_full_size(csa2, wid, queries):
     w = workload(wid)
     _say(f"[{w.name} layer group, full size] B={w.B}")
