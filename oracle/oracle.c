@@ -145,10 +145,12 @@ uint8_t oracle_e4m3_encode(float x) {
  * pos[b] goes to slot pos[b] mod W, so after position p the ring holds
  * exactly the tokens max(0, p - W + 1) .. p, in slot order rather than
  * position order (attention over the window does not depend on the order).
+ * A negative position (no token) appends nothing.
  * k_new, v_new [B, D] fp32; swa_k, swa_v [B, W, D] E4M3 bytes. */
 void oracle_swa_append(const float* k_new, const float* v_new, const int64_t* pos, int B, int D,
                        int W, uint8_t* swa_k, uint8_t* swa_v) {
     for (int b = 0; b < B; ++b) {
+        if (pos[b] < 0) continue;
         const size_t row = ((size_t)b * W + (size_t)(pos[b] % W)) * D;
         for (int c = 0; c < D; ++c) {
             swa_k[row + c] = oracle_e4m3_encode(k_new[(size_t)b * D + c]);

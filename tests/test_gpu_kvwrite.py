@@ -216,10 +216,12 @@ def test_swa_append_matches_oracle(csa2):
         if pos[b] >= 0:
             ek[b, pos[b] % W] = oracle.e4m3_encode(k[b])
             ev[b, pos[b] % W] = oracle.e4m3_encode(v[b])
-    # the same through the oracle's own ring update
-    rk, rv = sk[keep].copy(), sv[keep].copy()
-    oracle.swa_append(k[keep], v[keep], pos[keep], rk, rv)
-    assert np.array_equal(rk, ek[keep]) and np.array_equal(rv, ev[keep])
+    # the same through the oracle's own ring update (negative positions
+    # append nothing there too)
+    rk, rv = sk.copy(), sv.copy()
+    oracle.swa_append(k, v, pos, rk, rv)
+    assert np.array_equal(rk, ek) and np.array_equal(rv, ev)
+    assert np.array_equal(rk[~keep], sk[~keep]) and np.array_equal(rv[~keep], sv[~keep])
     assert np.array_equal(gk.cpu().numpy(), ek), "window K ring differs"
     assert np.array_equal(gv.cpu().numpy(), ev), "window V ring differs"
 

@@ -576,6 +576,22 @@ def test_swa_ring_holds_the_last_w_tokens():
             assert np.array_equal(sv[b, (start[b] + t) % W], oracle.e4m3_encode(v[t, b]))
 
 
+def test_swa_ring_negative_position_appends_nothing():
+    # a sequence with no token at this step (negative position) keeps its ring
+    B, W, D = 3, 4, 16
+    rng = np.random.default_rng(64)
+    sk = rng.integers(0, 256, (B, W, D)).astype(np.uint8)
+    sv = rng.integers(0, 256, (B, W, D)).astype(np.uint8)
+    k0, v0 = sk.copy(), sv.copy()
+    k = rng.standard_normal((B, D)).astype(np.float32)
+    v = rng.standard_normal((B, D)).astype(np.float32)
+    oracle.swa_append(k, v, np.array([-1, 6, -5], np.int64), sk, sv)
+    for b in (0, 2):
+        assert np.array_equal(sk[b], k0[b]) and np.array_equal(sv[b], v0[b])
+    assert np.array_equal(sk[1, 2], oracle.e4m3_encode(k[1]))
+    assert np.array_equal(sk[1, [0, 1, 3]], k0[1, [0, 1, 3]])
+
+
 def test_attention_over_the_ring_equals_the_window_in_position_order():
     # a window-only (K = 0) layer over the ring after 11 appends with W = 4
     # equals the same layer with the last 4 tokens laid out in position order
