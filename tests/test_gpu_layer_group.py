@@ -113,3 +113,24 @@ def test_layer_group_full_size(csa2, wid, queries):
             C.assert_lse_close(lses[layer][b], rl[0], f"{w.name} layer {layer} query {b}")
     del t
     torch.cuda.empty_cache()
+
+
+def test_layer_group_at_the_limits(csa2):
+    # 8 layers (the most one call takes), the largest Top-K list (2,048: 64
+    # main-KV tiles) and window (1,024 tokens: 32 tiles), 32 heads (half a
+    # head group), a ragged index tail and short windows
+    from gen.workloads import Workload
+    w = Workload("limits", 19, "decode_full", [5000, 2100], H=32, topk=2048, W=1024, layers=8)
+    t = build_device(w, with_kI=False)
+    rng = np.random.default_rng(12)
+    idx = np.full((w.B, w.topk), -1, np.int32)
+    idx[0] = np.sort(rng.choice(5000, 2048, replace=False))
+    idx[1, :1999] = np.sort(rng.choice(2100, 1999, replace=False))
+    sl = np.array([1024, 333], np.int32)
+    t["swa_len"] = torch.from_numpy(sl).cuda()
+    outs, lses = _group(csa2, w, t, torch.from_numpy(idx).cuda())
+    for layer in (0, 3, 7):
+        for b in range(w.B):
+            ro, rl = C.oracle_attn_query(w, b, layer, idx[b], swa_len=int(sl[b]))
+            C.assert_attn_close(outs[layer][b], ro[0], f"layer {layer} query {b}")
+            C.assert_lse_close(lses[layer][b], rl[0], f"layer {layer} query {b}")
