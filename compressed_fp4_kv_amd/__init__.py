@@ -121,6 +121,18 @@ def _ptr(t, dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, shape, name):
+    """Raises ValueError unless tensor t (skipped when None) has `shape`; an
+    entry of None matches any extent.  The kernels trust these extents, so a
+    mismatch is refused here rather than read or written out of bounds."""
+    if t is None:
+        return
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+        want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+        raise ValueError(f"{name}: expected shape {want}, got {list(got)}")
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -154,13 +166,27 @@ def csa2_index_prefill_workspace_bytes_ex(Q, max_nvis, topk, pool_blocks, block_
                                                          block_size, Hk, Di))
 
 
+def _index_shapes(qI, kI, seq_row_off, q_seq, q_nvis, topk, topk_idx, pool_blocks,
+                  pool_block_idx):
+    Q, _, Di = qI.shape
+    _expect(kI, (None, None, Di), "kI")
+    _expect(seq_row_off, (None,), "seq_row_off")
+    _expect(q_seq, (Q,), "q_seq")
+    _expect(q_nvis, (Q,), "q_nvis")
+    _expect(topk_idx, (Q, topk), "topk_idx")
+    if pool_blocks > 0:
+        _expect(pool_block_idx, (Q, pool_blocks), "pool_block_idx")
+
+
 def _index_full(fn, kdt, qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_idx,
                 pool_blocks, block_size, pool_block_idx, ws, stream):
     f32, i32, i64, _ = _dt()
     Q, Hi, Di = qI.shape
     Hk = kI.shape[1]
-    wp, wn = _ws(ws)
     name = fn.__name__
+    _index_shapes(qI, kI, seq_row_off, q_seq, q_nvis, topk, topk_idx, pool_blocks,
+                  pool_block_idx)
+    wp, wn = _ws(ws)
     _check(fn(
         _ptr(qI, f32, "qI"), _ptr(kI, kdt, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
         _ptr(q_seq, i32, "q_seq"), _ptr(q_nvis, i32, "q_nvis"), Q, Hi, Hk, Di, max_nvis, topk,
@@ -202,6 +228,8 @@ def csa2_index_full_ex(qI, kI, seq_row_off, q_seq, q_nvis, max_nvis, topk, topk_
         raise ValueError(f"block_rule: {block_rule!r} is not one of {sorted(BLOCK_RULES)}")
     Q, Hi, Di = qI.shape
     Hk = kI.shape[1]
+    _index_shapes(qI, kI, seq_row_off, q_seq, q_nvis, topk, topk_idx, pool_blocks,
+                  pool_block_idx)
     wp, wn = _ws(ws)
     _check(lib.csa2_index_full_ex(
         _ptr(qI, f32, "qI"), _ptr(kI, kI.dtype, "kI"), fmt, _ptr(seq_row_off, i64, "seq_row_off"),
@@ -221,6 +249,12 @@ def _reindex(fn, kdt, qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, block_
     Q, Hi, Di = qI.shape
     Hk = kI.shape[1]
     P = pool_block_idx.shape[1]
+    _expect(kI, (None, None, Di), "kI")
+    _expect(seq_row_off, (None,), "seq_row_off")
+    _expect(q_seq, (Q,), "q_seq")
+    _expect(q_nvis, (Q,), "q_nvis")
+    _expect(pool_block_idx, (Q, P), "pool_block_idx")
+    _expect(topk_idx, (Q, topk), "topk_idx")
     wp, wn = _ws(ws)
     _check(fn(
         _ptr(qI, f32, "qI"), _ptr(kI, kdt, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
@@ -256,6 +290,14 @@ def csa2_sparse_attn_decode(q, kv_codes, kv_scales, seq_row_off, topk_idx, swa_k
     B, H, D = q.shape
     topk = topk_idx.shape[1] if topk_idx is not None else 0
     W = swa_k.shape[1]
+    _attn_kv_shapes(kv_codes, kv_scales, D)
+    _expect(seq_row_off, (B,), "seq_row_off")
+    _expect(topk_idx, (B, topk), "topk_idx")
+    _expect(swa_k, (B, W, D), "swa_k")
+    _expect(swa_v, (B, W, D), "swa_v")
+    _expect(swa_len, (B,), "swa_len")
+    _expect(out, (B, H, D), "out")
+    _expect(lse, (B, H), "lse")
     wp, wn = _ws(ws)
     _check(lib.csa2_sparse_attn_decode(
         _ptr(q, f32, "q"), _ptr(kv_codes, u8, "kv_codes"), _ptr(kv_scales, u8, "kv_scales"),
@@ -263,6 +305,12 @@ def csa2_sparse_attn_decode(q, kv_codes, kv_scales, seq_row_off, topk_idx, swa_k
         _ptr(swa_k, u8, "swa_k"), _ptr(swa_v, u8, "swa_v"), _ptr(swa_len, i32, "swa_len"), W, B,
         H, D, float(softmax_scale), _ptr(out, f32, "out"), _ptr(lse, f32, "lse"), wp, wn,
         _stream(stream)), "csa2_sparse_attn_decode")
+
+
+def _attn_kv_shapes(kv_codes, kv_scales, D):
+    _expect(kv_codes, (None, D // 2), "kv_codes")
+    if kv_codes is not None:
+        _expect(kv_scales, (kv_codes.shape[0], D // 16), "kv_scales")
 
 
 def csa2_decode_layers_workspace_bytes(L, B, H, D, topk, W):
@@ -287,6 +335,21 @@ def csa2_sparse_attn_decode_layers(qs, kv_codes, kv_scales, seq_row_off, topk_id
     B, H, D = qs[0].shape
     topk = topk_idx.shape[1] if topk_idx is not None else 0
     W = swa_ks[0].shape[1]
+    for name, lst in (("swa_k", swa_ks), ("swa_v", swa_vs), ("out", outs)) + (
+            (("lse", lses),) if lses is not None else ()):
+        if len(lst) != L:
+            raise ValueError(f"{name}: {len(lst)} tensors for {L} layers")
+    for i in range(L):
+        _expect(qs[i], (B, H, D), f"q[{i}]")
+        _expect(swa_ks[i], (B, W, D), f"swa_k[{i}]")
+        _expect(swa_vs[i], (B, W, D), f"swa_v[{i}]")
+        _expect(outs[i], (B, H, D), f"out[{i}]")
+        if lses is not None:
+            _expect(lses[i], (B, H), f"lse[{i}]")
+    _attn_kv_shapes(kv_codes, kv_scales, D)
+    _expect(seq_row_off, (B,), "seq_row_off")
+    _expect(topk_idx, (B, topk), "topk_idx")
+    _expect(swa_len, (B,), "swa_len")
     wp, wn = _ws(ws)
     _check(lib.csa2_sparse_attn_decode_layers(
         L, _ptr_array(qs, f32, "q"), _ptr(kv_codes, u8, "kv_codes"),
@@ -308,6 +371,13 @@ def csa2_sparse_attn_prefill_chunk(q, p0, kv_codes, kv_scales, topk_idx, swa_k, 
     f32, i32, i64, u8 = _dt()
     Qn, H, D = q.shape
     topk = topk_idx.shape[1] if topk_idx is not None else 0
+    _attn_kv_shapes(kv_codes, kv_scales, D)
+    _expect(topk_idx, (Qn, topk), "topk_idx")
+    if W > 0:
+        _expect(swa_k, (Qn + W - 1, D), "swa_k")
+        _expect(swa_v, (Qn + W - 1, D), "swa_v")
+    _expect(out, (Qn, H, D), "out")
+    _expect(lse, (Qn, H), "lse")
     wp, wn = _ws(ws)
     _check(lib.csa2_sparse_attn_prefill_chunk(
         _ptr(q, f32, "q"), int(p0), _ptr(kv_codes, u8, "kv_codes"),
