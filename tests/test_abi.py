@@ -165,3 +165,44 @@ def test_decode_layers_argument_checks(pkg):
             == pkg.csa2_decode_workspace_bytes(32, 64, 512, 512, 128))
     assert pkg.csa2_decode_layers_workspace_bytes(4, 64, 64, 512, 512, 128) == 0
     assert pkg.csa2_decode_layers_workspace_bytes(9, 64, 64, 512, 512, 128) == 0
+
+
+def test_kv_quantize_argument_checks(pkg):
+    # every case below is refused (or is an empty call) on the host: nothing launches
+    f = pkg.lib.csa2_kv_quantize_fp4
+    p = lambda a: None if a is None else ctypes.c_void_p(a)
+    ok = dict(x=0x10000, rows=4, D=512, codes=0x20000, scales=0x30000)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(p(a["x"]), a["rows"], a["D"], p(a["codes"]), p(a["scales"]), None)
+
+    assert call(rows=-1) == 2
+    assert call(D=0) == 2
+    assert call(D=24) == 3                  # not a whole number of 16-channel groups
+    assert call(rows=0, x=None, codes=None, scales=None) == 0
+    assert call(x=None) == 1
+    assert call(scales=None) == 1
+    assert call(x=0x10008) == 3             # fp32 rows must be 16-byte aligned
+    assert call(codes=0x20001) == 3         # code rows must be 2-byte aligned
+
+
+def test_swa_append_argument_checks(pkg):
+    f = pkg.lib.csa2_swa_append
+    p = lambda a: None if a is None else ctypes.c_void_p(a)
+    ok = dict(k=0x10000, v=0x20000, pos=0x30000, B=2, D=512, W=128, sk=0x40000, sv=0x50000)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(p(a["k"]), p(a["v"]), p(a["pos"]), a["B"], a["D"], a["W"], p(a["sk"]),
+                 p(a["sv"]), None)
+
+    assert call(B=-1) == 2
+    assert call(W=0) == 2
+    assert call(D=0) == 2
+    assert call(D=12) == 3
+    assert call(B=0, k=None, v=None, pos=None, sk=None, sv=None) == 0
+    assert call(pos=None) == 1
+    assert call(sv=None) == 1
+    assert call(k=0x10008) == 3
+    assert call(sk=0x40004) == 3
