@@ -10,7 +10,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 from gen import host_ints  # noqa: E402
 from gen.workloads import (T_QI_FULL, T_QI_REINDEX, Workload, build_device, host_kI_rows,  # noqa: E402
-                           host_qI, workload)
+                           host_kv_rows, host_qI, host_swa, workload)
 
 import _cases as C  # noqa: E402
 
@@ -426,3 +426,44 @@ def test_prefill_chunk_two_head_groups(csa2):
     ro, rl = C.oracle_prefill_rows(w, 0, ref, list(range(w.Qn)))
     C.assert_attn_close(out.cpu().numpy(), ro, "prefill, 128 heads")
     C.assert_lse_close(lse.cpu().numpy(), rl, "prefill, 128 heads")
+
+
+@pytest.mark.parametrize("order", ["rising", "falling"])
+def test_attention_rising_falling_and_peaky_logits(csa2, order):
+    # Every head of a query sees the same key order: q[h] = c_h u with c_h > 0,
+    # so sorting the Top-K row by u . k puts the logits of every head in rising
+    # (or falling) order along the tiles and the key-range splits.  Rising
+    # logits move the running maximum tile after tile (the deferred rescale
+    # and the split merge with far-apart maxima); falling ones put the largest
+    # logit first so that later probabilities underflow.  c_h spans 0.02 .. 4
+    # (logits up to ~300): near-uniform to one-hot softmaxes in one launch.
+    w = _edge([3000, 1500], topk=512, W=128)
+    t = build_device(w, layers=1, with_kI=False)
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal(w.D).astype(np.float32)
+    c = np.geomspace(0.02, 4.0, w.H).astype(np.float32)
+    q = np.broadcast_to(c[None, :, None] * u[None, None, :], (w.B, w.H, w.D)).copy()
+    idx = np.full((w.B, w.topk), -1, np.int32)
+    for b in range(w.B):
+        off, n = int(w.seq_row_off[b]), int(w.ctx[b])
+        codes, scales = host_kv_rows(w, off, n)
+        logit = np.array([float(u.astype(np.float64) @ oracle.dequant_row(codes[r], scales[r], w.D))
+                          for r in range(n)])
+        pick = rng.choice(n, w.topk, replace=False)
+        pick = pick[np.argsort(logit[pick], kind="stable")]
+        idx[b] = pick if order == "rising" else pick[::-1]
+        # premise: at the largest scale the top key outweighs the median one by e^20
+        assert c[-1] * w.scale * (logit[pick[-1]] - logit[pick[w.topk // 2]]) > 20
+    qd = torch.from_numpy(q).cuda()
+    out = C.poison_f32((w.B, w.H, w.D))
+    lse = C.poison_f32((w.B, w.H))
+    buf = C.ws(csa2.csa2_decode_workspace_bytes(w.B, w.H, w.D, w.topk, w.W))
+    csa2.csa2_sparse_attn_decode(qd, t["kv_codes"], t["kv_scales"], t["seq_row_off"],
+                                 torch.from_numpy(idx).cuda(), t["swa_k"][0], t["swa_v"][0],
+                                 t["swa_len"], w.scale, out, lse, buf)
+    torch.cuda.synchronize()
+    codes, scales = host_kv_rows(w, 0, w.rows)
+    sk, sv = host_swa(w, 0)
+    ro, rl = oracle.attn_decode(q, codes, scales, w.seq_row_off, idx, sk, sv, w.swa_len(), w.scale)
+    C.assert_attn_close(out.cpu().numpy(), ro, f"{order} logits")
+    C.assert_lse_close(lse.cpu().numpy(), rl, f"{order} logits")
