@@ -240,16 +240,12 @@ __device__ __forceinline__ void dequant_main(const RawMain& r, uint32_t (&kp)[4]
     for (int j = 0; j < 4; ++j) dequant_fp4x8(r.code[j], r.scale[j], kp[j]);
 }
 
-// Converts a window tile (E4M3 K and V); rows outside the window become 0
-// (they are real memory that may hold anything).
-__device__ __forceinline__ void dequant_win(const RawWin& r, uint32_t (&kp)[4][4],
-                                            uint32_t (&vp)[4][4]) {
+// Converts the K or the V half of a window tile (E4M3); rows outside the
+// window become 0 (they are real memory that may hold anything).
+__device__ __forceinline__ void dequant_win(const uint2 (&w)[4], uint32_t ok,
+                                            uint32_t (&kp)[4][4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t keep = 0u - ((r.ok >> j) & 1u);
-        dequant_fp8x8(r.k[j], keep, kp[j]);
-        dequant_fp8x8(r.v[j], keep, vp[j]);
-    }
+    for (int j = 0; j < 4; ++j) dequant_fp8x8(w[j], 0u - ((ok >> j) & 1u), kp[j]);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -610,24 +606,46 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         }
         __syncthreads();   // logits of t+1 and tile t+2 published
     }
-    // window tiles: K in sKV[0], V in sKV[1] (their first gather is issued
-    // here, so that the two raw buffers are never live together)
+    // window tiles: K in sKV[0], V in sKV[1], two block barriers per tile.
+    // Once the logits of tile t are out, nothing reads K(t), so K(t+1) is
+    // written while the P V products of t read V(t); V(t+1) and its mask
+    // follow the second barrier.  The first gather is issued here, so that
+    // the main-KV and window raw buffers are never live together.
     const int w0 = max(t0, a.ntiles_main);
-    if (w0 < t1) fetch_win(swk, swv, a.W, wlo, whi, w0 - a.ntiles_main, rw);
-    for (int t = w0; t < t1; ++t) {
-        __syncthreads();   // previous tile's LDS reads are done
+    if (w0 < t1) {
+        fetch_win(swk, swv, a.W, wlo, whi, w0 - a.ntiles_main, rw);
+        __syncthreads();   // every LDS read of the main-KV tiles is done
         {
-            uint32_t kp[4][4], vp[4][4];
-            dequant_win(rw, kp, vp);
+            uint32_t kp[4][4];
+            dequant_win(rw.k, rw.ok, kp);
             put_rows(kp, sKV[0]);
-            put_rows(vp, sKV[1]);
+            dequant_win(rw.v, rw.ok, kp);
+            put_rows(kp, sKV[1]);
             put_valid(rw.ok, sValid[0]);
         }
-        if (t + 1 < t1) fetch_win(swk, swv, a.W, wlo, whi, t + 1 - a.ntiles_main, rw);
-        __syncthreads();
+        if (w0 + 1 < t1) fetch_win(swk, swv, a.W, wlo, whi, w0 + 1 - a.ntiles_main, rw);
+        __syncthreads();   // K, V and the mask of tile w0 visible
+    }
+    for (int t = w0; t < t1; ++t) {
+        const bool nxt = t + 1 < t1;   // uniform
         s_finish(s_issue(sKV[0]));
-        __syncthreads();
+        __syncthreads();   // logits of t published; every read of K(t) done
+        if (nxt) {
+            uint32_t kp[4][4];
+            dequant_win(rw.k, rw.ok, kp);
+            put_rows(kp, sKV[0]);
+        }
         pv_phase(sKV[1], sValid[0]);
+        __syncthreads();   // every read of V(t), its logits and mask done; K(t+1) visible
+        if (nxt) {
+            uint32_t vp[4][4];
+            dequant_win(rw.v, rw.ok, vp);
+            put_rows(vp, sKV[1]);
+            put_valid(rw.ok, sValid[0]);
+            if (t + 2 < t1) fetch_win(swk, swv, a.W, wlo, whi, t + 2 - a.ntiles_main, rw);
+        }
+        // V(t+1) and its mask are published by the next tile's first barrier,
+        // before its P V products read them
     }
     if (!active) return;
     const float lt = l + __shfl_xor(l, 32);
