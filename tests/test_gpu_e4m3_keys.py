@@ -218,6 +218,43 @@ def test_e4m3_keys_full_size_hierarchical_1m(csa2):
     torch.cuda.empty_cache()
 
 
+def test_e4m3_keys_full_size_mixed_length_reindex(csa2):
+    # 64 sequences of 8,192 .. 1,048,576 entries (7 GB of E4M3 keys): Reindex
+    # over the inherited pools, sampled at the shortest, the longest and two
+    # other sequences
+    w = workload(4)
+    _say(f"[{w.name} e4m3] building {w.rows} key rows")
+    t = build_device(w, with_kv=False, layers=0, keys="e4m3")
+    re = _reindex8(csa2, w, t, w.pool)
+    ctx = np.asarray(w.ctx)
+    for b in sorted({0, int(ctx.argmin()), int(ctx.argmax()), 40}):
+        assert np.array_equal(re[b], _oracle_reindex(w, b, w.pool[b])), \
+            f"Reindex of query {b} (ctx {ctx[b]})"
+        _say(f"[c4 e4m3] query {b} (ctx {ctx[b]}) ok")
+    del t
+    torch.cuda.empty_cache()
+
+
+def test_e4m3_keys_full_size_prefill_chunk(csa2):
+    # 4,096 prefill queries over 65,536 E4M3 key rows (the bf16 MFMA score
+    # GEMM and the row select), sampled at both ends and in the middle
+    w = workload(2)
+    _say(f"[{w.name} e4m3] Qn={w.Qn} p0={w.p0}")
+    t = build_device(w, with_kv=False, layers=0, keys="e4m3")
+    idx, _ = _index8(csa2, w, t, prefill=True)
+    rows = [0, 1, 1000, 2047, 4094, 4095]
+    k8 = host_kI_rows_e4m3(w, 0, int(w.ctx[0]))
+    ref, _ = oracle.index_full(host_qI(w, T_QI_FULL)[rows], k8, [0],
+                               np.zeros(len(rows), np.int32), w.q_nvis()[rows], w.Hi, w.Hk,
+                               w.Di, w.topk)
+    for j, i in enumerate(rows):
+        assert np.array_equal(idx[i], ref[j]), f"prefill Top-K of query {i}"
+    assert np.all((idx >= 0) & (idx < w.q_nvis()[:, None]))
+    assert np.all(np.diff(idx, axis=1) > 0)
+    del t
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("ctx,topk", [([10, 64, 65, 3000, 0, 1], 64), ([2049, 0, 4097], 2048)])
 def test_e4m3_keys_ragged_empty_and_short(csa2, ctx, topk):
     # empty sequences, a single entry, K above the context, K = 2,048
