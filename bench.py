@@ -1,15 +1,35 @@
 """CSA2 decode benchmark on one MI355X.
 
-One step = one CSA2 decoder layer group on the decode workload of 32
-sequences x 65,536 entries: the Full layer's indexer (score stream over
-32 x 65,536 fp32 key rows of 4 heads x 128 dims, exact Top-512), then
-sparse attention for the Full layer and its 3 Reuse layers (64 heads x 512
-channels over the 512 selected FP4 rows + a 128-token FP8 window, each layer
-with its own query and window; the four layers share the indices and the
-KV and go in one csa2_sparse_attn_decode_layers call).  Inputs are seeded synthetic tensors already
-resident in HBM.  Prints one JSON line.
+Default: one JSON line whose `value` is the mixed-length serving decode
+workload, the largest of the five that runs on one GPU: 64 decode queries
+over sequences of 8,192 .. 1,048,576 entries (log-uniform, seeded; 13.7 M
+entries, 28 GB of fp32 indexer keys).  One step = the Reindex layer over
+each sequence's inherited candidate pool (2,048 blocks x 8 positions, fewer
+for short sequences; exact Top-512) and the sparse attention of the Reindex
+layer and its 3 Reuse layers (64 heads x 512 channels over the 512 selected
+FP4 rows + a 128-token FP8 window, one layer-group launch).  value = 64
+queries / the median step time.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--keys f32|e4m3]
+The same line carries the other workloads, each timed the same way, under
+"other_workloads": the 32 x 65,536 decode (Full layer + 3 Reuse), the
+8 x 1,048,576 hierarchical decode (Full layer: score stream, Top-512, pool
+and its own attention; then Reindex + 3 Reuse) and the 4,096-query prefill
+chunk (Full + 5 Reuse layers, with its matrix-core utilisation); and the
+headline step over the compact E4M3 key cache under "e4m3_keys".
+
+Timing: W warm-up steps, then K timed steps, each between its own pair of
+HIP events on the launch stream, with a read-modify-write pass over 1 GiB
+between steps (outside the events) so that no step finds the previous step's
+data in the 256 MB last-level cache.  ms_per_step is the median of the K
+steps.  A second pass with per-launch events gives each kernel's average
+duration, from which the dominant kernel's roofline is computed.
+
+cpu_baseline: the oracle (plain C, double precision) on the host cores, on
+the headline workload: all queries with every core, and a labelled sample
+single-threaded, with the CPU model.  Input generation is not timed.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --workload N [--keys f32|e4m3]  (one workload alone)
        python bench.py --kv-writer   (the FP4 main-KV writer alone, its own line)
 
 --keys e4m3 runs the same step over the compact indexer-key cache (one
@@ -29,16 +49,28 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFS = 2500.0   # dense fp16 / bf16 matrix-core peak of an MI355X
+HEADLINE = 4                 # the mixed-length serving decode workload
+FLUSH_BYTES = 1 << 30        # touched between timed steps (the last-level cache is 256 MB)
 
 WORKLOAD_NAMES = {
     "c0_tiny_full": "decode Full layer: 1 sequence x 4,096 entries, indexer 4x64, Top-64, 16 heads",
     "c1_full_reuse3": "decode Full + 3 Reuse layers: 32 sequences x 65,536 entries, indexer 4x128 "
                       "fp32, Top-512, 64 heads x 512 ch, FP4 main KV, 128-token FP8 window",
     "c2_prefill_m2": "prefill chunk, m=2: 4,096 queries over 65,536 entries, Full + 5 Reuse layers",
-    "c3_hier_1m": "decode, 8 sequences x 1,048,576 entries: Full indexer + 2,048x8 pool, Reindex "
-                  "+ 3 Reuse layers",
-    "c4_mixed_reindex": "decode, 64 sequences of 8K..1M entries: Reindex over inherited pools + "
-                        "3 Reuse layers",
+    "c3_hier_1m": "decode, 8 sequences x 1,048,576 entries: Full layer (score stream, Top-512, "
+                  "2,048x8 pool, its attention), then Reindex + 3 Reuse layers",
+    "c4_mixed_reindex": "decode, 64 sequences of 8,192..1,048,576 entries (log-uniform): Reindex "
+                        "over inherited 2,048x8 pools (Top-512, fp32 indexer keys 4x128) + 3 "
+                        "Reuse layers, 64 heads x 512 ch, FP4 main KV, 128-token FP8 window",
+}
+
+# committed rocprofv3 counter summaries of each workload's dominant kernel
+TRAFFIC_PROFILES = {
+    ("c1_full_reuse3", "f32"): "score_stream_c1_traffic.md",
+    ("c1_full_reuse3", "e4m3"): "score_stream_e4m3_c1_traffic.md",
+    ("c3_hier_1m", "f32"): "score_stream_c3_traffic.md",
+    ("c4_mixed_reindex", "f32"): "reindex_c4_traffic.md",
+    ("c2_prefill_m2", "f32"): "prefill_c2_traffic.md",
 }
 
 
@@ -46,7 +78,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(profile="score_stream_c1_traffic.md"):
+def measured_traffic(profile, kernel=None):
     """HBM bytes per launch of a kernel from its committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration),
     or None if the kernel's sources changed since the counters were taken."""
@@ -56,6 +88,8 @@ def measured_traffic(profile="score_stream_c1_traffic.md"):
         for line in open(path):
             if line.startswith("traffic_record:"):
                 rec = json.loads(line.split(":", 1)[1])
+                if kernel is not None and rec.get("kernel") != kernel:
+                    continue
                 h = hashlib.sha256()
                 for src in rec["sources"]:
                     h.update(open(os.path.join(ROOT, src), "rb").read())
@@ -92,10 +126,14 @@ def make_step(csa2, w, t, torch, keys="f32", block_rule="max"):
         nb = csa2.csa2_prefill_workspace_bytes(Q, w.H, w.D, w.topk, w.W)
     else:
         # the decode layers of a group share the indices and the KV: one call
-        nb = csa2.csa2_decode_layers_workspace_bytes(w.layers, Q, w.H, w.D, w.topk, w.W)
+        nb = max(csa2.csa2_decode_layers_workspace_bytes(w.layers, Q, w.H, w.D, w.topk, w.W),
+                 csa2.csa2_decode_workspace_bytes(Q, w.H, w.D, w.topk, w.W))
     ws_a = torch.empty(max(256, nb), dtype=torch.uint8, device=dev)
     outs = [torch.empty((Q, w.H, w.D), dtype=torch.float32, device=dev) for _ in range(w.layers)]
     lses = [torch.empty((Q, w.H), dtype=torch.float32, device=dev) for _ in range(w.layers)]
+    if w.kind == "decode_hier":
+        out_f = torch.empty((Q, w.H, w.D), dtype=torch.float32, device=dev)
+        lse_f = torch.empty((Q, w.H), dtype=torch.float32, device=dev)
 
     def attn_layers(ix):
         if w.kind == "prefill":
@@ -118,10 +156,14 @@ def make_step(csa2, w, t, torch, keys="f32", block_rule="max"):
             attn_layers(idx)
             return
         if w.kind == "decode_hier":
-            # the Full layer's indexer builds Top-K and the candidate pool
+            # the Full layer's indexer builds Top-K and the candidate pool; the
+            # Full layer attends over its Top-K with its own query and window
             csa2.csa2_index_full_ex(t["qI_full"], kI, t["seq_row_off"], t["q_seq"], t["q_nvis"],
                                     max_nvis, w.topk, idx, P, w.block_size, pool,
                                     block_rule=block_rule, ws=ws_i)
+            csa2.csa2_sparse_attn_decode(t["q_full"], t["kv_codes"], t["kv_scales"],
+                                         t["seq_row_off"], idx, t["swa_k_full"], t["swa_v_full"],
+                                         t["swa_len"], w.scale, out_f, lse_f, ws=ws_a)
         # Reindex layer over the pool, then Reindex + Reuse layers' attention
         reindex(t["qI_reindex"], kI, t["seq_row_off"], t["q_seq"], t["q_nvis"], pool,
                 w.block_size, w.topk, ridx, ws=ws_r)
@@ -129,30 +171,38 @@ def make_step(csa2, w, t, torch, keys="f32", block_rule="max"):
     return step, idx
 
 
+def candidate_rows(w):
+    """Key rows a Reindex layer gathers: each sequence's valid pool blocks,
+    cut at its visible entries."""
+    import numpy as np
+    if w.pool is not None:
+        return sum(min(int(np.sum(w.pool[b] >= 0)) * w.block_size, int(w.ctx[b]))
+                   for b in range(w.B))
+    return sum(min(w.pool_blocks * w.block_size, int(w.ctx[b])) for b in range(w.B))
+
+
 def dominant_roofline(w, kern, keys="f32"):
-    """Roofline record of the workload's dominant kernel (algorithmic work per
-    launch / measured average launch time).  Key bytes per value: 4 (fp32) or
-    1 (E4M3 key cache)."""
+    """Roofline record of the workload's dominant kernel: algorithmic work per
+    launch / its measured average launch duration.  Key bytes per value: 4
+    (fp32) or 1 (E4M3 key cache)."""
     sfx, vb = ("_e4m3", 1) if keys == "e4m3" else ("", 4)
     stream, rscore = "score_stream" + sfx, "reindex_score" + sfx
+    prof = TRAFFIC_PROFILES.get((w.name, keys))
     if w.kind in ("decode_full", "decode_hier") and stream in kern:
         alg = float(w.rows) * w.row_width * vb + float(w.Q) * w.Hi * w.Di * 4
         ach = alg / (kern[stream]["avg_us"] * 1e-6) / 1e9
-        traffic = None
-        if w.name.startswith("c1"):
-            traffic = measured_traffic("score_stream_e4m3_c1_traffic.md" if sfx
-                                       else "score_stream_c1_traffic.md")
         return {"bound": "hbm", "kernel": stream, "achieved": ach, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic}
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": alg,
+                "traffic": measured_traffic(prof, "score_stream") if prof else None}
     if w.kind == "decode_reindex" and rscore in kern:
-        import numpy as np
-        rows = sum(min(int(np.sum(w.pool[b] >= 0)) * w.block_size, w.ctx[b]) for b in range(w.B))
-        alg = float(rows) * w.row_width * vb
+        alg = float(candidate_rows(w)) * w.row_width * vb + float(w.Q) * w.Hi * w.Di * 4
         ach = alg / (kern[rscore]["avg_us"] * 1e-6) / 1e9
         return {"bound": "hbm", "kernel": rscore, "achieved": ach, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": alg,
+                "traffic": measured_traffic(prof, "reindex_score") if prof else None}
     if "attn" in kern:
-        return mfma_utilisation(w, kern)["attn"] | {"traffic": None}
+        return mfma_utilisation(w, kern)["attn"] | {
+            "traffic": measured_traffic(prof, "attn") if prof else None}
     return None
 
 
@@ -171,12 +221,7 @@ def step_hbm(w, ms_step, keys="f32"):
     if w.kind in ("decode_full", "decode_hier", "prefill"):
         total += float(np.sum(w.ctx)) * rb + w.Q * qb          # Full-layer stream (prefill: once)
     if w.kind in ("decode_hier", "decode_reindex"):
-        if w.pool is not None:
-            cand = sum(min(int(np.sum(w.pool[b] >= 0)) * w.block_size, w.ctx[b])
-                       for b in range(w.B))
-        else:
-            cand = sum(min(w.pool_blocks * w.block_size, w.ctx[b]) for b in range(w.B))
-        total += float(cand) * rb + w.Q * qb
+        total += float(candidate_rows(w)) * rb + w.Q * qb
     sel = np.minimum(w.q_nvis(), w.topk).astype(np.float64)
     win = float(w.swa_rows() if w.kind == "prefill" else w.B * w.W)
     per_layer = (2.0 * w.Q * w.H * w.D * 4 + float(np.sum(sel)) * (w.D // 2 + w.D // 16)
@@ -186,7 +231,8 @@ def step_hbm(w, ms_step, keys="f32"):
         # the unique rows bound the compulsory bytes
         per_layer = (2.0 * w.Q * w.H * w.D * 4 + min(float(np.sum(sel)), float(w.ctx[0]))
                      * (w.D // 2 + w.D // 16) + win * 2 * w.D + w.Q * w.topk * 4)
-    total += w.layers * per_layer
+    layers = w.layers + (1 if w.kind == "decode_hier" else 0)   # + the Full layer's attention
+    total += layers * per_layer
     ach = total / (ms_step * 1e-3) / 1e9
     return {"algorithmic_bytes": total, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": ach / HBM_PEAK_GBS}
@@ -194,8 +240,10 @@ def step_hbm(w, ms_step, keys="f32"):
 
 def mfma_utilisation(w, kern):
     """Algorithmic flops per launch / measured launch time of the matrix-core
-    kernels, against the dense fp16/bf16 peak (the two-part fp16 splits of
-    the attention execute twice the algorithmic flops; they are not counted)."""
+    kernels, against the dense fp16/bf16 peak.  The attention's two-part fp16
+    splits of the query and the probabilities execute twice the algorithmic
+    flops (issued / algorithmic = 2); the score GEMM's hi/lo bf16 parts
+    execute 1x (integer-valued inputs: the lo parts are zero and skipped)."""
     res = {}
     if "attn" in kern:
         # QK^T and PV, 2 flops per MAC; a decode launch covers the group's layers
@@ -203,41 +251,252 @@ def mfma_utilisation(w, kern):
         ach = flops / (kern["attn"]["avg_us"] * 1e-6) / 1e12
         res["attn"] = {"bound": "mfma", "kernel": "attn (fp16 MFMA)", "achieved": ach,
                        "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-                       "frac": ach / MFMA_F16_PEAK_TFS}
+                       "frac": ach / MFMA_F16_PEAK_TFS, "issued_per_algorithmic": 2.0}
     if "prefill_scores" in kern:
         import numpy as np
         flops = 2.0 * float(np.sum(w.q_nvis())) * w.Hi * w.Di   # visible (query, entry) dots
         ach = flops / (kern["prefill_scores"]["avg_us"] * 1e-6) / 1e12
         res["prefill_scores"] = {"bound": "mfma", "kernel": "prefill_scores (bf16 MFMA)",
                                  "achieved": ach, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-                                 "frac": ach / MFMA_F16_PEAK_TFS}
+                                 "frac": ach / MFMA_F16_PEAK_TFS, "issued_per_algorithmic": 1.0}
     return res
 
 
-def cpu_baseline(w, max_threads, keys="f32"):
-    """The oracle on the host cores, on the same workload (whole batch)."""
-    import oracle
-    from gen.workloads import (T_QI_FULL, host_kI_rows, host_kI_rows_e4m3, host_kv_rows, host_q,
-                               host_qI, host_swa)
+# ------------------------------------------------------------------ timing
 
-    threads = max(1, min(max_threads, w.B))
+def time_steps(torch, step, steps, warmup, flush):
+    """Per-step times (ms) of `steps` steps, each between its own events,
+    with the flush pass between steps."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        flush.add_(1.0)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def kernel_times(csa2, torch, step, steps, flush):
+    """Average duration of each kernel over `steps` steps (per-launch events
+    on the launch stream), flush pass between steps."""
+    csa2.profile_reset()
+    csa2.profile_enable(True)
+    for _ in range(steps):
+        flush.add_(1.0)
+        step()
+    torch.cuda.synchronize()
+    prof = csa2.profile_read()
+    csa2.profile_enable(False)
+    return {k: {"launches": n, "avg_us": 1000.0 * ms / n} for k, (n, ms) in prof.items()}
+
+
+def summarize(times):
+    import numpy as np
+    a = np.asarray(times)
+    return {"median_ms": float(np.median(a)), "mean_ms": float(a.mean()),
+            "min_ms": float(a.min()), "max_ms": float(a.max()), "n": int(a.size)}
+
+
+def run_workload(csa2, torch, w, args, flush, keys="f32", block_rule="max", tag=""):
+    """Builds workload w on the device, times it, and returns its record."""
+    log(f"[{w.name}{tag}] building inputs: B={w.B} Q={w.Q} max ctx={max(w.ctx)}")
+    from gen.workloads import build_device
+    t = build_device(w, keys=keys)
+    step, _ = make_step(csa2, w, t, torch, keys, block_rule)
+    times = time_steps(torch, step, args.steps, args.warmup, flush)
+    st = summarize(times)
+    ms = st["median_ms"]
+    log(f"[{w.name}{tag}] median {ms:.4f} ms/step (min {st['min_ms']:.4f}, max "
+        f"{st['max_ms']:.4f})")
+    kern = kernel_times(csa2, torch, step, args.steps, flush)
+    log(f"[{w.name}{tag}] kernels: " + json.dumps(kern))
+    rec = {"value": w.Q / (ms * 1e-3), "unit": "queries/s", "ms_per_step": ms, "step_times": st,
+           "workload": WORKLOAD_NAMES.get(w.name, w.name), "global_batch": w.Q,
+           "kernels": kern, "roofline": dominant_roofline(w, kern, keys),
+           "step_hbm": step_hbm(w, ms, keys)}
+    if w.kind == "prefill":
+        rec["mfma_utilisation"] = mfma_utilisation(w, kern)
+    del t, step
+    torch.cuda.empty_cache()
+    return rec
+
+
+# -------------------------------------------------------------- CPU baseline
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads(limit):
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, limit))
+
+
+def _oracle_step(w, queries, inputs):
+    """The oracle's whole step on `queries` (indices into the workload's
+    queries); returns seconds spent in oracle calls (input generation and
+    the packing of selected rows are not timed)."""
+    import numpy as np
+
+    import oracle
+    from oracle import slices
+    spent = 0.0
+    qs = np.asarray(queries, np.int64)
+    if w.kind == "decode_reindex":
+        t0 = time.perf_counter()
+        ridx = slices.reindex_batch(w, inputs["qI_reindex"][qs], inputs["pool_batch"])
+        spent += time.perf_counter() - t0
+        full = np.full((w.B, w.topk), -1, np.int32)
+        full[qs] = ridx
+        rows = slices.selected_rows(w, full, list(queries))
+        for layer in range(w.layers):
+            sk, sv = inputs["swa"][layer]
+            t0 = time.perf_counter()
+            oracle.attn_decode(inputs["q"][layer][qs], rows[0], rows[1], rows[2], rows[3],
+                               sk[qs], sv[qs], w.swa_len()[qs], w.scale)
+            spent += time.perf_counter() - t0
+        return spent
+    if w.kind in ("decode_full", "decode_hier"):
+        kI, offs = inputs["kI"], inputs["offs"]
+        nv = w.q_nvis()[qs]
+        P = w.pool_blocks if w.kind == "decode_hier" else 0
+        t0 = time.perf_counter()
+        idx, pool = oracle.index_full(inputs["qI_full"][qs], kI, offs,
+                                      np.arange(len(qs), dtype=np.int32), nv, w.Hi, w.Hk, w.Di,
+                                      w.topk, P, w.block_size)
+        spent += time.perf_counter() - t0
+        full = np.full((w.B, w.topk), -1, np.int32)
+        full[qs] = idx
+        groups = []
+        if w.kind == "decode_hier":
+            groups.append((full, [inputs["q_full"]], [inputs["swa_full"]]))
+            # Reindex over each query's pool (its rows regenerated and packed)
+            pb = slices.pool_batch(w, _scatter_rows(w, qs, pool), list(queries))
+            t0 = time.perf_counter()
+            ridx = slices.reindex_batch(w, inputs["qI_reindex"][qs], pb)
+            spent += time.perf_counter() - t0
+            full = np.full((w.B, w.topk), -1, np.int32)
+            full[qs] = ridx
+        groups.append((full, inputs["q"], inputs["swa"]))
+        for ix, qlist, swalist in groups:
+            rows = slices.selected_rows(w, ix, list(queries))
+            for ql, (sk, sv) in zip(qlist, swalist):
+                t0 = time.perf_counter()
+                oracle.attn_decode(ql[qs], rows[0], rows[1], rows[2], rows[3], sk[qs], sv[qs],
+                                   w.swa_len()[qs], w.scale)
+                spent += time.perf_counter() - t0
+        return spent
+    if w.kind == "prefill":
+        # a contiguous run of chunk queries: one oracle call per layer
+        i0, n = int(queries[0]), len(queries)
+        nv = w.q_nvis()[i0:i0 + n]
+        t0 = time.perf_counter()
+        idx, _ = oracle.index_full(inputs["qI_full"][i0:i0 + n], inputs["kI"], [0],
+                                   np.zeros(n, np.int32), nv, w.Hi, w.Hk, w.Di, w.topk)
+        spent += time.perf_counter() - t0
+        codes, scales = inputs["kv"]
+        for layer in range(w.layers):
+            sk, sv = inputs["swa"][layer]
+            t0 = time.perf_counter()
+            oracle.attn_prefill(inputs["q"][layer][i0:i0 + n], w.p0 + i0, codes, scales, idx,
+                                sk[i0:i0 + n + w.W - 1], sv[i0:i0 + n + w.W - 1], w.W, w.scale)
+            spent += time.perf_counter() - t0
+        return spent
+    raise ValueError(w.kind)
+
+
+def _scatter_rows(w, qs, rows):
+    """A [B, ...] array holding rows[j] at query qs[j] (others -1)."""
+    import numpy as np
+    out = np.full((w.B,) + rows.shape[1:], -1, rows.dtype)
+    out[qs] = rows
+    return out
+
+
+def _oracle_inputs(w, queries):
+    """Host inputs of `queries` for the oracle (generation, not timed)."""
+    import numpy as np
+
+    from gen.workloads import (FULL_LAYER, T_QI_FULL, T_QI_REINDEX, host_kI_rows, host_kv_rows,
+                               host_q, host_qI, host_swa)
+    from oracle import slices
+    inp = {"q": [host_q(w, l) for l in range(w.layers)],
+           "swa": [host_swa(w, l) for l in range(w.layers)]}
+    if w.kind == "decode_reindex":
+        inp["qI_reindex"] = host_qI(w, T_QI_REINDEX)
+        inp["pool_batch"] = slices.pool_batch(w, w.pool, list(queries))
+        return inp
+    inp["qI_full"] = host_qI(w, T_QI_FULL)
+    if w.kind == "prefill":
+        inp["kI"] = host_kI_rows(w, 0, int(w.ctx[0]))
+        inp["kv"] = host_kv_rows(w, 0, int(w.ctx[0]))
+        return inp
+    # decode Full layer: each query's whole sequence of keys, packed
+    n = [int(w.ctx[b]) for b in queries]
+    inp["offs"] = np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int64)
+    inp["kI"] = np.empty((sum(n), w.Hk, w.Di), np.float32)
+    for j, b in enumerate(queries):
+        o = int(inp["offs"][j])
+        inp["kI"][o:o + n[j]] = host_kI_rows(w, int(w.seq_row_off[b]), n[j])
+    if w.kind == "decode_hier":
+        inp["qI_reindex"] = host_qI(w, T_QI_REINDEX)
+        inp["q_full"] = host_q(w, FULL_LAYER)
+        inp["swa_full"] = host_swa(w, FULL_LAYER)
+    return inp
+
+
+# queries of each workload the oracle runs: (all-core set, single-thread sample)
+def baseline_queries(w):
+    if w.kind == "prefill":
+        mid = w.Qn // 2 - 128
+        return list(range(mid, mid + 256)), list(range(mid, mid + 8))
+    if w.kind == "decode_hier":
+        return list(range(w.B)), [0]
+    if w.kind == "decode_full":
+        return list(range(w.B)), list(range(0, w.B, max(1, w.B // 4)))[:4]
+    return list(range(w.B)), list(range(0, w.B, 4))
+
+
+def cpu_baseline(w, max_threads):
+    """The oracle, as it stands, on the host cores: every query of the
+    workload (a labelled 256-query run of the prefill chunk) with all the
+    threads the oracle can use, and a labelled sample on one thread."""
+    import oracle
+    allq, oneq = baseline_queries(w)
+    threads = host_threads(max_threads)
+    res = {"kind": "oracle", "unit": "queries/s", "cpu_model": cpu_model()}
+    inp = _oracle_inputs(w, allq)
+    used = min(threads, len(allq))
+    oracle.set_threads(used)
+    dt = _oracle_step(w, allq, inp)
+    what = (f"chunk queries {allq[0]}..{allq[-1]} (positions {w.p0 + allq[0]}..{w.p0 + allq[-1]})"
+            if w.kind == "prefill" else f"all {len(allq)} queries")
+    res.update({"value": len(allq) / dt, "cores": used,
+                "sample": f"{what}, whole step (every layer), {dt:.2f} s of oracle time"})
+    oracle.set_threads(1)
+    if w.kind != "prefill":
+        del inp
+        inp = _oracle_inputs(w, oneq)
+    dt1 = _oracle_step(w, oneq, inp)
+    res["single_thread"] = {"value": len(oneq) / dt1, "unit": "queries/s", "cores": 1,
+                            "sample": f"queries {oneq}, whole step, {dt1:.2f} s"}
     oracle.set_threads(threads)
-    kI = (host_kI_rows_e4m3 if keys == "e4m3" else host_kI_rows)(w, 0, w.rows)
-    qI = host_qI(w, T_QI_FULL)
-    codes, scales = host_kv_rows(w, 0, w.rows)
-    qs = [host_q(w, l) for l in range(w.layers)]
-    swa = [host_swa(w, l) for l in range(w.layers)]
-    t0 = time.perf_counter()
-    idx, _ = oracle.index_full(qI, kI, w.seq_row_off, w.q_seq(), w.q_nvis(), w.Hi, w.Hk, w.Di,
-                               w.topk)
-    for l in range(w.layers):
-        oracle.attn_decode(qs[l], codes, scales, w.seq_row_off, idx, swa[l][0], swa[l][1],
-                           w.swa_len(), w.scale, want_lse=True)
-    dt = time.perf_counter() - t0
-    del kI
-    return {"value": w.B / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole step on all {w.B} queries (index_full + {w.layers} attention layers), "
-                      f"{dt:.2f} s"}
+    return res
 
 
 def kv_writer_bench(args, torch, csa2):
@@ -351,13 +610,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", type=int, default=1,
-                    help="workload number (1 = the decode workload the metric is quoted on)")
+    ap.add_argument("--workload", type=int, default=None,
+                    help="run one workload alone (0-4); default: the mixed-length serving "
+                         "decode workload as the line's value, the others as extra keys")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--keys", choices=("f32", "e4m3"), default="f32",
                     help="indexer-key cache: fp32 (the workloads as stated) or E4M3 bytes")
-    ap.add_argument("--no-e4m3-line", action="store_true",
-                    help="decode workload: skip the E4M3 key-cache figure added to the line")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default line: skip the other workloads and the E4M3 key-cache figure")
     ap.add_argument("--pool-blocks", type=int, default=None,
                     help="hierarchical workload: blocks in the candidate pool (default 2,048)")
     ap.add_argument("--block-size", type=int, default=None,
@@ -374,6 +634,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path is single-GPU "
               "and has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     if args.calibrate_copy:
@@ -386,12 +649,13 @@ def main():
                           "calibrate_copy_bytes_written": dst.numel() * 4, "launches": 3}))
         return
     import compressed_fp4_kv_amd as csa2
-    from gen.workloads import build_device, workload
+    from gen.workloads import workload
     if args.kv_writer:
         kv_writer_bench(args, torch, csa2)
         return
 
-    w = workload(args.workload)
+    wid = HEADLINE if args.workload is None else args.workload
+    w = workload(wid)
     pool_variant = (args.pool_blocks, args.block_size, args.block_rule) != (None, None, "max")
     if pool_variant:
         if w.kind != "decode_hier":
@@ -400,97 +664,62 @@ def main():
             sys.exit(2)
         w.pool_blocks = args.pool_blocks or w.pool_blocks
         w.block_size = args.block_size or w.block_size
-    log(f"building inputs: {w.name} B={w.B} ctx={w.ctx[0]} H={w.H} topk={w.topk}")
-    t = build_device(w, keys=args.keys)
-    step, idx = make_step(csa2, w, t, torch, args.keys, args.block_rule)
-    for _ in range(args.warmup):
-        step()
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    log("warmup done")
-
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    log(f"timed: {ms_step:.3f} ms/step")
-
-    # kernel breakdown: same steps again with per-launch events on the launch stream
-    csa2.profile_reset()
-    csa2.profile_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    prof = csa2.profile_read()
-    csa2.profile_enable(False)
-    kern = {k: {"launches": n, "avg_us": 1000.0 * ms / n} for k, (n, ms) in prof.items()}
-    log("kernels:", json.dumps(kern))
-
+    head = run_workload(csa2, torch, w, args, flush, args.keys, args.block_rule)
     res = {
         "metric": "CSA2 decode queries/sec and achieved HBM GB/s (% of peak) at 1 MI355X",
-        "value": w.Q / (ms_step * 1e-3),
+        "value": head["value"],
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded integer indexer inputs, FP4 E2M1/E4M3 KV, N(0,1) queries, "
                 "FP8 window)",
-        "config": {"workload": WORKLOAD_NAMES.get(w.name, w.name) + (
+        "config": {"workload": head["workload"] + (
                        "; indexer keys stored as E4M3FN bytes" if args.keys == "e4m3" else "") + (
                        f"; pool {w.pool_blocks} blocks x {w.block_size}, block score "
                        f"{args.block_rule}" if pool_variant else ""),
-                   "global_batch": w.Q, "seq_len": int(max(w.ctx)), "parallelism": "single GPU"},
-        "kernels": kern,
-        "roofline": dominant_roofline(w, kern, args.keys),
-        "step_hbm": step_hbm(w, ms_step, args.keys),
+                   "global_batch": w.Q, "seq_len": int(max(w.ctx)), "total_entries": w.rows,
+                   "parallelism": "single GPU"},
+        "timing": "median of the timed steps, each between its own HIP events, 1 GiB touched "
+                  "between steps",
+        "step_times": head["step_times"],
+        "kernels": head["kernels"],
+        "roofline": head["roofline"],
+        "step_hbm": head["step_hbm"],
     }
-    if w.kind == "prefill":
-        res["mfma_utilisation"] = mfma_utilisation(w, kern)
-    if args.workload == 1 and args.keys == "f32" and not args.no_e4m3_line:
-        # the same step over the compact indexer-key cache (E4M3 bytes), a
-        # storage variant reported beside the fp32 figure, never as `value`
-        from gen.workloads import dev_kI_e4m3
-        del t["kI"]
-        torch.cuda.empty_cache()
-        t["kI8"] = dev_kI_e4m3(w)
-        step8, _ = make_step(csa2, w, t, torch, "e4m3")
-        for _ in range(args.warmup):
-            step8()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            step8()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms8 = e0.elapsed_time(e1) / args.steps
-        csa2.profile_reset()
-        csa2.profile_enable(True)
-        for _ in range(args.steps):
-            step8()
-        torch.cuda.synchronize()
-        prof8 = csa2.profile_read()
-        csa2.profile_enable(False)
-        kern8 = {k: {"launches": n, "avg_us": 1000.0 * ms / n} for k, (n, ms) in prof8.items()}
-        res["e4m3_keys"] = {"value": w.Q / (ms8 * 1e-3), "unit": "queries/s", "ms_per_step": ms8,
-                            "config": "same step, indexer keys stored as E4M3FN bytes (512 B "
-                                      "rows instead of 2 KB)",
-                            "kernels": kern8, "roofline": dominant_roofline(w, kern8, "e4m3"),
-                            "step_hbm": step_hbm(w, ms8, "e4m3")}
-        log(f"e4m3 keys: {ms8:.3f} ms/step")
-    del t
+    if "mfma_utilisation" in head:
+        res["mfma_utilisation"] = head["mfma_utilisation"]
+    if args.workload is None and not args.no_extras:
+        if args.keys == "f32":
+            # the same step over the compact indexer-key cache (E4M3 bytes), a
+            # storage variant reported beside the fp32 figure, never as `value`
+            r8 = run_workload(csa2, torch, workload(wid), args, flush, "e4m3", tag=" e4m3 keys")
+            res["e4m3_keys"] = {k: r8[k] for k in ("value", "unit", "ms_per_step", "step_times",
+                                                   "kernels", "roofline", "step_hbm")}
+            res["e4m3_keys"]["config"] = "same step, indexer keys stored as E4M3FN bytes"
+        other = {}
+        for oid in (1, 3, 2):
+            ow = workload(oid)
+            other[ow.name] = run_workload(csa2, torch, ow, args, flush)
+        res["other_workloads"] = other
+    del flush
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline and args.workload == 1:
-        log("cpu baseline (oracle) ...")
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_threads, args.keys)
+    if not args.no_cpu_baseline and "other_workloads" in res:
+        for name, rec in res["other_workloads"].items():
+            ow = workload({"c1_full_reuse3": 1, "c3_hier_1m": 3, "c2_prefill_m2": 2}[name])
+            log(f"[{name}] cpu baseline (oracle) ...")
+            rec["cpu_baseline"] = cpu_baseline(ow, args.cpu_threads)
+    if not args.no_cpu_baseline:
+        log(f"[{w.name}] cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_threads)
+        log(f"[{w.name}] cpu baseline: {json.dumps(res['cpu_baseline'])}")
     print(json.dumps(res), flush=True)
 
 

@@ -352,7 +352,8 @@ __device__ void pick_lds_candidates(uint64_t* s_cand, uint32_t NC, uint32_t need
 // b1 are candidates (composite key score|~index); both lists grow by one
 // atomic per workgroup.  cnt[2q + 0/1]: winners, candidates (zeroed first).
 __global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ keys, int64_t stride,
-                                                const int32_t* __restrict__ q_nvis, int bs_log2,
+                                                const int32_t* __restrict__ q_nvis, int nmax,
+                                                int bs_log2,
                                                 int K, const uint32_t* __restrict__ hist,
                                                 uint32_t* __restrict__ cnt,
                                                 int32_t* __restrict__ above,
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ key
     __shared__ uint32_t s_bc[2];
     const int q = blockIdx.y;
     const int nvis = q_nvis[q];
-    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, (int)stride);
+    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, nmax);
     const int e0 = blockIdx.x * kSelElems;
     if (n <= K || e0 >= n) return;
     // the keys (coalesced uint4 loads) are in flight during the bin search
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(256) void k_filter(const uint32_t* __restrict__ key
 // indices in ascending order.
 __global__ __launch_bounds__(kSelThreads) void k_finalize(
     const uint32_t* __restrict__ keys, int64_t stride, const int32_t* __restrict__ q_nvis,
-    int bs_log2, int K, const uint32_t* __restrict__ cnt, const int32_t* __restrict__ above,
+    int nmax, int bs_log2, int K, const uint32_t* __restrict__ cnt, const int32_t* __restrict__ above,
     const uint64_t* __restrict__ cand, int32_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankDirect + 2];
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
     __shared__ uint32_t s_count;
     const int q = blockIdx.x;
     const int nvis = q_nvis[q];
-    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, (int)stride);
+    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, nmax);
     int32_t* o = out + (size_t)q * K;
     if (n <= K) {  // everything is selected
         for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
@@ -616,7 +617,7 @@ __device__ __forceinline__ bool select_row_regs(const uint4 (&v)[kRowRegs], uint
 // Replaces the filter + finalize pair where one workgroup can read the row.
 __global__ __launch_bounds__(kSelThreads) void k_select_small(
     const uint32_t* __restrict__ keys, int64_t stride, const int32_t* __restrict__ q_nvis,
-    int bs_log2, int K, const uint32_t* __restrict__ hist, int32_t* __restrict__ out) {
+    int nmax, int bs_log2, int K, const uint32_t* __restrict__ hist, int32_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
     __shared__ uint32_t s_wbase[kRowRegs * (kSelThreads / kWave)];
     __shared__ uint32_t s_hist[256];
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_small(
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
     const int q = blockIdx.x;
     const int nvis = q_nvis[q];
-    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, (int)stride);
+    const int n = min((nvis + (1 << bs_log2) - 1) >> bs_log2, nmax);
     int32_t* o = out + (size_t)q * K;
     if (n <= K) {
         for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
@@ -852,7 +853,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __restrict__ keys,
                                                             int64_t stride,
                                                             const int32_t* __restrict__ q_nvis,
-                                                            int K, int32_t* __restrict__ out) {
+                                                            int nmax, int K,
+                                                            int32_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint32_t s_h[kHistBins];
     __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
@@ -863,7 +865,7 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
     __shared__ __attribute__((aligned(16))) uint32_t s_rtop[kWave];      // 4 per wave
     __shared__ uint32_t s_wbase[kRowRegs * (kSelThreads / kWave)];       // per (slot, wave)
     const int q = blockIdx.x;
-    const int n = min(q_nvis[q], (int)stride);
+    const int n = min(q_nvis[q], nmax);
     int32_t* o = out + (size_t)q * K;
     if (n <= K) {
         for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = i < n ? i : -1;
@@ -979,11 +981,11 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
 __global__ __launch_bounds__(256) void k_block_keys(const uint32_t* __restrict__ keys,
                                                     int64_t stride,
                                                     const int32_t* __restrict__ q_nvis,
-                                                    int bs_log2, int block_sum,
+                                                    int max_nvis, int bs_log2, int block_sum,
                                                     uint32_t* __restrict__ bkeys, int64_t bstride,
                                                     int32_t* __restrict__ nblk) {
     const int q = blockIdx.y;
-    const int n = min(q_nvis[q], (int)stride);
+    const int n = min(q_nvis[q], max_nvis);
     const int nb = (n + (1 << bs_log2) - 1) >> bs_log2;
     if (blockIdx.x == 0 && threadIdx.x == 0) nblk[q] = nb;
     const int b = blockIdx.x * 256 + threadIdx.x;
@@ -1323,17 +1325,17 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
         }
         if (topk > 0) {
             st = CSA2_LAUNCH("row_select", k_row_select, dim3(Q), dim3(kSelThreads), s, w.keys_e,
-                             w.se, q_nvis, topk, topk_idx);
+                             w.se, q_nvis, max_nvis, topk, topk_idx);
             if (st) return st;
         }
         if (pool_blocks > 0) {
             const int nbmax = (max_nvis + block_size - 1) / block_size;
             st = CSA2_LAUNCH("block_keys", k_block_keys, dim3((nbmax + 255) / 256 + (nbmax == 0), Q),
-                             dim3(256), s, w.keys_e, w.se, q_nvis, bs_log2,
+                             dim3(256), s, w.keys_e, w.se, q_nvis, max_nvis, bs_log2,
                              (int)(block_rule == CSA2_BLOCK_SUM), w.keys_b, w.sb, w.nblk);
             if (st) return st;
             st = CSA2_LAUNCH("row_select_b", k_row_select, dim3(Q), dim3(kSelThreads), s,
-                             w.keys_b, w.sb, w.nblk, pool_blocks, pool_block_idx);
+                             w.keys_b, w.sb, w.nblk, nbmax, pool_blocks, pool_block_idx);
             if (st) return st;
         }
         return CSA2_OK;
@@ -1356,15 +1358,15 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
                       int32_t* out) -> int {
         if (nmax <= kSmallRow)
             return CSA2_LAUNCH(blocks ? "select_small_b" : "select_small", k_select_small,
-                               dim3(Q), dim3(kSelThreads), s, keys, stride, q_nvis, bsl, K,
-                               hist, out);
+                               dim3(Q), dim3(kSelThreads), s, keys, stride, q_nvis, nmax, bsl,
+                               K, hist, out);
         dim3 g((nmax + kSelElems - 1) / kSelElems, Q);
         int r = CSA2_LAUNCH(blocks ? "filter_b" : "filter", k_filter, g, dim3(256), s, keys,
-                            stride, q_nvis, bsl, K, hist, cnt, above, cand);
+                            stride, q_nvis, nmax, bsl, K, hist, cnt, above, cand);
         if (r) return r;
         return CSA2_LAUNCH(blocks ? "finalize_b" : "finalize", k_finalize, dim3(Q),
-                           dim3(kSelThreads), s, keys, stride, q_nvis, bsl, K, cnt, above, cand,
-                           out);
+                           dim3(kSelThreads), s, keys, stride, q_nvis, nmax, bsl, K, cnt, above,
+                           cand, out);
     };
     if (topk > 0) {
         st = select(false, w.keys_e, w.se, 0, max_nvis, topk, w.hist_e, w.cnt_e, w.above_e, w.cand_e,

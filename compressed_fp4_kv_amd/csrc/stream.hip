@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kStreamThreads32) void k_score_stream(
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
-    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b, int rpw) {
+    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b, int rpw,
+    int max_nvis) {
     // 16-bit bin counters, two per word (a workgroup sees at most
     // kRowsPerWG keys).  Three 4-wave workgroups of 4,096 rows (48 KB of LDS
     // each) fill the twelve wave slots the registers allow per CU; a sweep
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kStreamThreads32) void k_score_stream(
     constexpr int RW = 256 * VPR;
     constexpr int kStreamRows = VPR >= 4 ? 8 : 16;   // rows per wave iteration (32 KB of 2 KB rows)
     const int q = blockIdx.y;
-    const int nvis = min(q_nvis[q], (int)kstride);   // q_nvis <= max_nvis <= kstride
+    const int nvis = min(q_nvis[q], max_nvis);   // a larger q_nvis counts as max_nvis
     const int r0 = blockIdx.x * rpw;   // rpw <= kRowsPerWG, a multiple of 64
     if (r0 >= nvis) return;
     const int r1 = min(nvis, r0 + rpw);
@@ -152,7 +153,8 @@ __global__ __launch_bounds__(kStreamThreads8) void k_score_stream_e4m3(
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, uint32_t* __restrict__ keys,
     int64_t kstride, uint32_t* __restrict__ hist_e, uint32_t* __restrict__ bkeys,
-    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b, int rpw) {
+    int64_t bstride, int bs_log2, int block_sum, uint32_t* __restrict__ hist_b, int rpw,
+    int max_nvis) {
     __shared__ uint32_t s_he[kHistBins / 2];
     __shared__ uint32_t s_hb[kHistBins / 2];
     __shared__ __attribute__((aligned(16))) uint32_t s_ke[kRowsPerWG8];
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(kStreamThreads8) void k_score_stream_e4m3(
     constexpr int RPI = NB * RPB;                         // rows per wave iteration
     constexpr int GSH = 4 - log2_groups<G>();             // lane bits below the group index
     const int q = blockIdx.y;
-    const int nvis = min(q_nvis[q], (int)kstride);
+    const int nvis = min(q_nvis[q], max_nvis);
     const int r0 = blockIdx.x * rpw;   // rpw <= kRowsPerWG8, a multiple of 64
     if (r0 >= nvis) return;
     const int r1 = min(nvis, r0 + rpw);
@@ -258,7 +260,7 @@ int launch_score_stream(int vpr, bool e4m3, int max_nvis, int Q, hipStream_t s,
 #define CSA2_STREAM(KERNEL, KT, NAME)                                                         \
     CSA2_LAUNCH(NAME, KERNEL, grid, block, s, qI, static_cast<const KT*>(kI),                \
                 seq_row_off, q_seq, q_nvis, Hi, Hk, Di, keys, kstride, hist_e, bkeys, bstride,\
-                bs_log2, block_sum, hist_b, rpw)
+                bs_log2, block_sum, hist_b, rpw, max_nvis)
     if (e4m3)
         return vpr == 1 ? CSA2_STREAM((k_score_stream_e4m3<1, kStreamNB8>), uint8_t,
                                       "score_stream_e4m3")

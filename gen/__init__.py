@@ -45,6 +45,10 @@ def host():
         _host.gen_host_ints.argtypes = [u64, u64, u64, u64, i32, i32, P]
         _host.gen_host_fp4.argtypes = [u64, u64, u64, u64, P]
         _host.gen_host_pow2_scales.argtypes = [u64, u64, u64, u64, i32, i32, P]
+        i64 = ctypes.c_int64
+        _host.gen_host_ints_runs.argtypes = [u64, u64, P, i64, i64, i32, i32, P]
+        _host.gen_host_fp4_runs.argtypes = [u64, u64, P, i64, i64, P]
+        _host.gen_host_pow2_scales_runs.argtypes = [u64, u64, P, i64, i64, i32, i32, P]
     return _host
 
 
@@ -84,6 +88,34 @@ def host_fp4(seed, tensor, start, count):
 def host_pow2_scales(seed, tensor, start, count, kmin=-4, kmax=4):
     out = np.empty(int(count), np.uint8)
     host().gen_host_pow2_scales(seed, tensor, int(start), int(count), kmin, kmax, _ptr(out))
+    return out
+
+
+def _starts(starts):
+    return np.ascontiguousarray(starts, dtype=np.int64)
+
+
+def host_ints_runs(seed, tensor, starts, run, lo=-8, hi=8):
+    """host_ints for runs of `run` elements starting at each of `starts`,
+    concatenated."""
+    st = _starts(starts)
+    out = np.empty(st.size * int(run), np.float32)
+    host().gen_host_ints_runs(seed, tensor, _ptr(st), st.size, int(run), lo, hi, _ptr(out))
+    return out
+
+
+def host_fp4_runs(seed, tensor, starts, run):
+    st = _starts(starts)
+    out = np.empty(st.size * int(run), np.uint8)
+    host().gen_host_fp4_runs(seed, tensor, _ptr(st), st.size, int(run), _ptr(out))
+    return out
+
+
+def host_pow2_scales_runs(seed, tensor, starts, run, kmin=-4, kmax=4):
+    st = _starts(starts)
+    out = np.empty(st.size * int(run), np.uint8)
+    host().gen_host_pow2_scales_runs(seed, tensor, _ptr(st), st.size, int(run), kmin, kmax,
+                                     _ptr(out))
     return out
 
 

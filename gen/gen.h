@@ -39,6 +39,17 @@ void gen_host_fp4(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t count
 void gen_host_pow2_scales(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t count,
                           int32_t kmin, int32_t kmax, uint8_t* out);
 
+/* The same values for `nruns` runs of `run` elements each, run r starting at
+ * element starts[r]; out holds the runs back to back (nruns * run values).
+ * Regenerates scattered slices (a query's pool blocks, its selected rows). */
+void gen_host_ints_runs(uint64_t seed, uint64_t tensor, const int64_t* starts, int64_t nruns,
+                        int64_t run, int32_t lo, int32_t hi, float* out);
+void gen_host_fp4_runs(uint64_t seed, uint64_t tensor, const int64_t* starts, int64_t nruns,
+                       int64_t run, uint8_t* out);
+void gen_host_pow2_scales_runs(uint64_t seed, uint64_t tensor, const int64_t* starts,
+                               int64_t nruns, int64_t run, int32_t kmin, int32_t kmax,
+                               uint8_t* out);
+
 /* Device fills: same values, written asynchronously on `stream`.  Return 0 on
  * success, otherwise the hipError_t of the launch. */
 int gen_dev_ints(uint64_t seed, uint64_t tensor, uint64_t start, uint64_t count,

@@ -44,3 +44,26 @@ void gen_host_pow2_scales(uint64_t seed, uint64_t tensor, uint64_t start, uint64
         out[j] = (uint8_t)((k + 7) << 3);
     }
 }
+
+void gen_host_ints_runs(uint64_t seed, uint64_t tensor, const int64_t* starts, int64_t nruns,
+                        int64_t run, int32_t lo, int32_t hi, float* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nruns; ++r)
+        gen_host_ints(seed, tensor, (uint64_t)starts[r], (uint64_t)run, lo, hi, out + r * run);
+}
+
+void gen_host_fp4_runs(uint64_t seed, uint64_t tensor, const int64_t* starts, int64_t nruns,
+                       int64_t run, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nruns; ++r)
+        gen_host_fp4(seed, tensor, (uint64_t)starts[r], (uint64_t)run, out + r * run);
+}
+
+void gen_host_pow2_scales_runs(uint64_t seed, uint64_t tensor, const int64_t* starts,
+                               int64_t nruns, int64_t run, int32_t kmin, int32_t kmax,
+                               uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nruns; ++r)
+        gen_host_pow2_scales(seed, tensor, (uint64_t)starts[r], (uint64_t)run, kmin, kmax,
+                             out + r * run);
+}

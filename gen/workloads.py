@@ -6,7 +6,10 @@ regenerate any slice of its tensors on the host (for the oracle), and
 GPU library).  Seed = workload number.  Tensor ids: 1 indexer keys (shared by
 Full and Reindex layers), 2 Full-layer indexer query, 3 Reindex-layer indexer
 query, 4 main-KV FP4 code bytes, 5 main-KV E4M3 scale bytes, 16+l attention
-query of layer l, 32+l window K of layer l, 48+l window V of layer l.
+query of layer l, 32+l window K of layer l, 48+l window V of layer l.  In the
+hierarchical workload the Full layer that builds the pool attends too, with
+the query and window of tensor ids of layer FULL_LAYER (its Reindex group's
+layers are 0..3).
 
 Distributions: indexer inputs are integers uniform on [-8, 8] stored as fp32;
 FP4 codes are uniform over the 15 codes other than negative zero; scales are
@@ -18,10 +21,13 @@ from typing import List, Optional
 
 import numpy as np
 
-from . import (dev_fp4, dev_ints, dev_pow2_scales, e4m3_bytes, host_fp4, host_ints,
-               host_pow2_scales, normal_f32)
+from . import (dev_fp4, dev_ints, dev_pow2_scales, e4m3_bytes, host_fp4, host_fp4_runs,
+               host_ints, host_ints_runs, host_pow2_scales, host_pow2_scales_runs, normal_f32)
 
 T_KI, T_QI_FULL, T_QI_REINDEX, T_CODES, T_SCALES = 1, 2, 3, 4, 5
+
+
+FULL_LAYER = 8   # hierarchical workload: tensor ids of the Full layer's own attention
 
 
 def T_Q(layer):
@@ -157,6 +163,23 @@ def host_kI_rows_e4m3(w, row0, nrows):
     return e4m3_bytes(host_kI_rows(w, row0, nrows))
 
 
+def host_kI_row_runs(w, row_starts, run_rows):
+    """Key rows [len(row_starts) * run_rows, Hk, Di]: run_rows consecutive
+    rows from each absolute row in row_starts, runs back to back."""
+    rw = w.row_width
+    st = np.asarray(row_starts, np.int64) * rw
+    return host_ints_runs(w.seed, T_KI, st, run_rows * rw).reshape(-1, w.Hk, w.Di)
+
+
+def host_kv_rows_at(w, rows):
+    """FP4 code rows [n, D/2] and scale rows [n, D/16] at the absolute rows
+    `rows` (in that order)."""
+    r = np.asarray(rows, np.int64)
+    codes = host_fp4_runs(w.seed, T_CODES, r * (w.D // 2), w.D // 2)
+    scales = host_pow2_scales_runs(w.seed, T_SCALES, r * (w.D // 16), w.D // 16)
+    return codes.reshape(-1, w.D // 2), scales.reshape(-1, w.D // 16)
+
+
 def host_qI(w, tensor):
     return host_ints(w.seed, tensor, 0, w.Q * w.Hi * w.Di).reshape(w.Q, w.Hi, w.Di)
 
@@ -227,6 +250,11 @@ def build_device(w, device="cuda", layers=None, with_kI=True, with_kv=True, keys
         t["qI_reindex"] = torch.from_numpy(host_qI(w, T_QI_REINDEX)).to(dev)
     if w.pool is not None:
         t["pool"] = torch.from_numpy(w.pool).to(dev)
+    if w.kind == "decode_hier":
+        t["q_full"] = torch.from_numpy(host_q(w, FULL_LAYER)).to(dev)
+        k, v = host_swa(w, FULL_LAYER)
+        t["swa_k_full"] = torch.from_numpy(k).to(dev)
+        t["swa_v_full"] = torch.from_numpy(v).to(dev)
     t["q"] = [torch.from_numpy(host_q(w, l)).to(dev) for l in range(L)]
     swa = [host_swa(w, l) for l in range(L)]
     t["swa_k"] = [torch.from_numpy(k).to(dev) for k, _ in swa]

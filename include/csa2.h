@@ -90,7 +90,8 @@ int csa2_last_hip_error(void);
  *                  stream per query.
  *   q_nvis         [Q] int32: visible entries of each query (causality; for
  *                  an encoder chunk with m tokens per entry the caller passes
- *                  floor((p+1)/m)).  0 <= q_nvis[q] <= max_nvis.
+ *                  floor((p+1)/m)).  0 <= q_nvis[q] <= max_nvis; a larger
+ *                  value is read as max_nvis (never past the rows scored).
  *   max_nvis       host bound on q_nvis (sizes the grid and the workspace)
  *   topk           0..CSA2_MAX_TOPK; topk_idx [Q, topk] int32 (may be NULL iff 0)
  *   pool_blocks    0..CSA2_MAX_TOPK; block_size in {1,2,4,8};

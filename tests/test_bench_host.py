@@ -48,8 +48,35 @@ def test_reindex_gather_bytes_per_launch(bench):
     from gen.workloads import workload
     w = workload(4)
     rec = bench.dominant_roofline(w, {"reindex_score": {"avg_us": 340.0}})
-    # 64 sequences: min(2,048, ceil(N / 8)) pool blocks of 8 rows, cut at N
-    assert round(_alg(rec, 340.0)) == 1_037_240 * 2048
+    # 64 sequences: min(2,048, ceil(N / 8)) pool blocks of 8 rows, cut at N,
+    # plus the 64 Reindex indexer queries of 2 KB
+    assert round(_alg(rec, 340.0)) == 1_037_240 * 2048 + 64 * 2048 == 2_124_398_592
+    assert rec["kernel"] == "reindex_score" and rec["bound"] == "hbm"
+
+
+def test_default_line_is_the_mixed_length_workload(bench):
+    from gen.workloads import workload
+    w = workload(bench.HEADLINE)
+    assert w.name == "c4_mixed_reindex" and w.B == 64 and w.kind == "decode_reindex"
+    # the largest of the five workloads that fit one GPU: most entries and key bytes
+    assert w.rows == max(workload(i).rows for i in range(5))
+    assert w.rows * w.row_width * 4 > 28e9
+
+
+def test_step_statistics_are_the_median_of_the_steps(bench):
+    st = bench.summarize([3.0, 1.0, 2.0, 10.0, 2.5])
+    assert st["median_ms"] == 2.5 and st["min_ms"] == 1.0 and st["max_ms"] == 10.0
+    assert st["n"] == 5
+
+
+def test_hierarchical_step_counts_the_full_layer_attention(bench):
+    from gen.workloads import workload
+    w = workload(3)
+    a = bench.step_hbm(w, 1.0)["algorithmic_bytes"]
+    keys = 8 * (1 << 20) * 2048 + 8 * 2048                 # Full-layer stream
+    gather = 8 * 16384 * 2048 + 8 * 2048                   # Reindex over 2,048 x 8 pools
+    layer = 2 * 8 * 64 * 512 * 4 + 8 * 512 * 288 + 8 * 128 * 2 * 512 + 8 * 512 * 4
+    assert a == keys + gather + 5 * layer                  # Full + Reindex + 3 Reuse attention
 
 
 def test_prefill_attention_flops_per_launch(bench):

@@ -36,3 +36,17 @@ def test_workload_shapes():
         p = w4.pool[b]
         v = p[p >= 0]
         assert len(v) == min(2048, (n + 7) // 8) and np.all(np.diff(v) > 0)
+
+
+def test_runs_equal_slices_of_the_contiguous_tensors():
+    starts = np.array([5, 0, 4096, 77, 123456789], np.int64)
+    run = 40
+    ints = gen.host_ints_runs(4, 1, starts, run)
+    fp4 = gen.host_fp4_runs(4, 4, starts, run)
+    sc = gen.host_pow2_scales_runs(4, 5, starts, run)
+    for r, s in enumerate(starts):
+        sl = slice(r * run, (r + 1) * run)
+        assert np.array_equal(ints[sl], gen.host_ints(4, 1, s, run))
+        assert np.array_equal(fp4[sl], gen.host_fp4(4, 4, s, run))
+        assert np.array_equal(sc[sl], gen.host_pow2_scales(4, 5, s, run))
+    assert gen.host_ints_runs(4, 1, np.zeros(0, np.int64), run).size == 0

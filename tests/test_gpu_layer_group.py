@@ -2,7 +2,8 @@
 its Reuse layers in one call, sharing the index list and the main KV, each
 with its own query and window.  Every layer's output and log-sum-exp within
 max-abs 2e-3 / rel-L2 1e-3 of the oracle; one layer reproduces the per-layer
-call bit for bit."""
+call bit for bit.  (The groups of the decode workloads at full size, every
+query, are in test_gpu_fullsize.py.)"""
 import numpy as np
 import pytest
 import torch
@@ -96,23 +97,6 @@ def test_layer_group_without_lse_and_eight_layers(csa2):
         for b in range(w.B):
             ro, _ = C.oracle_attn_query(w, b, layer, ih[b])
             C.assert_attn_close(outs[layer][b], ro[0], f"8-layer group layer {layer} query {b}")
-
-
-@pytest.mark.parametrize("wid,queries", [(1, (0, 17, 31)), (3, (0, 7)), (4, (0, 21, 63))])
-def test_layer_group_full_size(csa2, wid, queries):
-    w = workload(wid)
-    _say(f"[{w.name} layer group, full size] B={w.B}")
-    t = build_device(w)
-    idx = _indices(w, t)
-    outs, lses = _group(csa2, w, t, idx)
-    ih = idx.cpu().numpy()
-    for layer in range(w.layers):
-        for b in queries:
-            ro, rl = C.oracle_attn_query(w, b, layer, ih[b])
-            C.assert_attn_close(outs[layer][b], ro[0], f"{w.name} layer {layer} query {b}")
-            C.assert_lse_close(lses[layer][b], rl[0], f"{w.name} layer {layer} query {b}")
-    del t
-    torch.cuda.empty_cache()
 
 
 def test_layer_group_at_the_limits(csa2):
