@@ -16,6 +16,7 @@ __all__ = [
     "csa2_index_prefill_workspace_bytes", "csa2_index_prefill_workspace_bytes_ex",
     "csa2_sparse_attn_decode_layers", "csa2_decode_layers_workspace_bytes",
     "csa2_reindex_workspace_bytes", "csa2_sparse_attn_decode", "csa2_decode_workspace_bytes",
+    "csa2_reindex_noalloc", "NOALLOC_MAX_CAND",
     "csa2_sparse_attn_prefill_chunk", "csa2_prefill_workspace_bytes", "csa2_kv_quantize_fp4",
     "csa2_swa_append", "profile_enable",
     "profile_read", "profile_reset", "EXPORTED_SYMBOLS",
@@ -38,7 +39,10 @@ EXPORTED_SYMBOLS = [
     "csa2_index_full_e4m3", "csa2_reindex_e4m3", "csa2_index_full_ex",
     "csa2_index_prefill_workspace_bytes_ex",
     "csa2_sparse_attn_decode_layers", "csa2_decode_layers_workspace_bytes",
+    "csa2_reindex_noalloc",
 ]
+
+NOALLOC_MAX_CAND = 2097152   # CSA2_NOALLOC_MAX_CAND
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
@@ -70,6 +74,8 @@ lib.csa2_reindex_workspace_bytes.argtypes = [_I32, _I32, _I32]
 lib.csa2_reindex.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                              _P, _SZ, _P]
 lib.csa2_reindex_e4m3.argtypes = lib.csa2_reindex.argtypes
+lib.csa2_reindex_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                     _I32, _P, _P]
 lib.csa2_decode_workspace_bytes.restype = _SZ
 lib.csa2_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
 lib.csa2_sparse_attn_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32,
@@ -277,6 +283,28 @@ def csa2_reindex_e4m3(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, block_
 
 
 # ---------------------------------------------------------------- attention
+
+def csa2_reindex_noalloc(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, block_size, topk,
+                         topk_idx, stream=None):
+    """csa2_reindex without a workspace argument: the library's static
+    per-device scratch (at most NOALLOC_MAX_CAND candidates per call) is used
+    and nothing is allocated.  Calls that overlap on one GPU race."""
+    f32, i32, i64, _ = _dt()
+    Q, Hi, Di = qI.shape
+    Hk = kI.shape[1]
+    P = pool_block_idx.shape[1]
+    _expect(kI, (None, None, Di), "kI")
+    _expect(seq_row_off, (None,), "seq_row_off")
+    _expect(q_seq, (Q,), "q_seq")
+    _expect(q_nvis, (Q,), "q_nvis")
+    _expect(pool_block_idx, (Q, P), "pool_block_idx")
+    _expect(topk_idx, (Q, topk), "topk_idx")
+    _check(lib.csa2_reindex_noalloc(
+        _ptr(qI, f32, "qI"), _ptr(kI, f32, "kI"), _ptr(seq_row_off, i64, "seq_row_off"),
+        _ptr(q_seq, i32, "q_seq"), _ptr(q_nvis, i32, "q_nvis"),
+        _ptr(pool_block_idx, i32, "pool_block_idx"), P, block_size, Q, Hi, Hk, Di, topk,
+        _ptr(topk_idx, i32, "topk_idx"), _stream(stream)), "csa2_reindex_noalloc")
+
 
 def csa2_decode_workspace_bytes(B, H, D, topk, W):
     return int(lib.csa2_decode_workspace_bytes(B, H, D, topk, W))

@@ -31,6 +31,8 @@
 //   <= 16,384 composite keys of a query in one workgroup.
 #include <limits.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "rowdot.hpp"
@@ -1491,4 +1493,61 @@ extern "C" int csa2_reindex_e4m3(const float* qI, const uint8_t* kI, const int64
                                  size_t ws_bytes, void* stream) {
     return reindex_impl<uint8_t>(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, pool_blocks,
                                  block_size, Q, Hi, Hk, Di, topk, topk_idx, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------ allocation-free Reindex
+
+// Scratch of csa2_reindex_noalloc: the composite candidate keys (8 bytes per
+// candidate) that k_reindex_score writes and k_reindex_select reads, in a
+// static array that each GPU the library runs on holds until the process
+// ends.  Host code never passes this name to a kernel: on the host it stands
+// for no device address; the address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint64_t scratch[CSA2_NOALLOC_MAX_CAND];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+}  // namespace
+
+// The device address of the current device's scratch; looked up once per
+// device (with that device current) and kept.
+static int current_device_scratch(uint64_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        set_last_hip_error(e);
+        return CSA2_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return CSA2_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_last_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return CSA2_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = static_cast<uint64_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA2_OK;
+}
+
+extern "C" int csa2_reindex_noalloc(const float* qI, const float* kI,
+                                    const int64_t* seq_row_off, const int32_t* q_seq,
+                                    const int32_t* q_nvis, const int32_t* pool_block_idx,
+                                    int32_t pool_blocks, int32_t block_size, int32_t Q,
+                                    int32_t Hi, int32_t Hk, int32_t Di, int32_t topk,
+                                    int32_t* topk_idx, void* stream) {
+    if (Q < 0 || pool_blocks < 0 || block_size <= 0 || topk < 0) return CSA2_ERR_SHAPE;
+    if ((int64_t)Q * pool_blocks * block_size > CSA2_NOALLOC_MAX_CAND) return CSA2_ERR_UNSUPPORTED;
+    uint64_t* ws = nullptr;
+    if (Q > 0 && topk > 0) {
+        const int st = current_device_scratch(&ws);
+        if (st != CSA2_OK) return st;
+    }
+    return reindex_impl<float>(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, pool_blocks,
+                               block_size, Q, Hi, Hk, Di, topk, topk_idx, ws,
+                               sizeof(uint64_t) * (size_t)CSA2_NOALLOC_MAX_CAND, stream);
 }

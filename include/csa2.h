@@ -139,6 +139,28 @@ int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
                  void* stream);
 
 /* ------------------------------------------------------------------------
+ * Allocation-free Reindex, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): csa2_reindex with its workspace replaced by a static device
+ * array of CSA2_NOALLOC_MAX_CAND composite keys (16 MiB) that each GPU the
+ * library runs on holds until the process ends.  Same arguments, results and
+ * errors as csa2_reindex, without ws / ws_bytes; the array of the CURRENT
+ * device (hipGetDevice) is used, so `stream` must belong to that device.
+ * Q * pool_blocks * block_size above CSA2_NOALLOC_MAX_CAND (for example 128
+ * queries of 2,048 x 8 candidates) gives CSA2_ERR_UNSUPPORTED before anything
+ * is enqueued.  The call allocates nothing (no hipMalloc, no hipFree).  All
+ * calls on one GPU share its array, and every call overwrites what it uses
+ * before reading it: calls that overlap on one GPU (different streams or
+ * host threads without ordering) race and must not be issued.
+ * ---------------------------------------------------------------------- */
+#define CSA2_NOALLOC_MAX_CAND 2097152
+int csa2_reindex_noalloc(const float* qI, const float* kI, const int64_t* seq_row_off,
+                         const int32_t* q_seq, const int32_t* q_nvis,
+                         const int32_t* pool_block_idx, int32_t pool_blocks, int32_t block_size,
+                         int32_t Q, int32_t Hi, int32_t Hk, int32_t Di, int32_t topk,
+                         int32_t* topk_idx, void* stream);
+
+/* ------------------------------------------------------------------------
  * Compact indexer-key cache: the same Full-mode and Reindex calls over keys
  * stored as one E4M3FN byte per value (a quarter of the fp32 cache's bytes).
  * The pages (jaehun.me review, TL;DR and section "2) CSA2": the global KV

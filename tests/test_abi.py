@@ -206,3 +206,17 @@ def test_swa_append_argument_checks(pkg):
     assert call(sv=None) == 1
     assert call(k=0x10008) == 3
     assert call(sk=0x40004) == 3
+
+
+def test_reindex_noalloc_argument_checks(pkg):
+    v = lambda x: ctypes.c_void_p(16 * x)
+
+    def call(Q=1, P=2048, bs=8, topk=512):
+        return pkg.lib.csa2_reindex_noalloc(v(1), v(1), v(1), v(1), v(1), v(1), P, bs, Q, 4, 4,
+                                            128, topk, v(1), None)
+    # more candidates than the static scratch holds: refused before anything is enqueued
+    assert pkg.NOALLOC_MAX_CAND == 2097152
+    assert call(Q=129) == 3
+    assert call(Q=1, P=2048, bs=8 * 129) == 3
+    assert call(Q=-1) == 2 and call(bs=0) == 2 and call(topk=-1) == 2 and call(P=-5) == 2
+    assert call(Q=0) == 0             # nothing to do, nothing launched
