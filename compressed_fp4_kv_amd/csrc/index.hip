@@ -31,6 +31,8 @@
 //   <= 16,384 composite keys of a query in one workgroup.
 #include <limits.h>
 
+#include <algorithm>
+
 #include <mutex>
 
 #include "common.hpp"
@@ -203,28 +205,29 @@ __device__ void select_global_row(const uint32_t* __restrict__ keys, int n, int 
 
 // Writes the `count` distinct non-negative indices of s_list (unordered,
 // 16-byte aligned, room for 4 pad slots after them) to o in ascending order
-// and pads the K slots with -1.  Lists of up to 512: each
-// index is written at its rank.  Longer ones: a counting sort into
-// kSelThreads buckets spread evenly over [min, max] of the list, then each
+// and pads the K slots with -1, with NT threads.  Lists of up to
+// min(512, NT): each index is written at its rank.  Longer ones: a counting
+// sort into NT buckets spread evenly over [min, max] of the list, then each
 // index is placed by its rank inside its bucket.
+template <int NT = kSelThreads>
 __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __restrict__ o) {
-    constexpr int NB = kSelThreads;
+    constexpr int NB = NT;
     __shared__ uint32_t s_start[NB + 1];
     __shared__ uint32_t s_cur[NB];
     __shared__ int32_t s_srt[CSA2_MAX_TOPK];
-    __shared__ int32_t s_mm[2 * (kSelThreads / kWave)];
-    __shared__ uint32_t s_scan[kSelThreads / kWave + 1];
-    if (count <= 512) {
+    __shared__ int32_t s_mm[2 * (NT / kWave)];
+    __shared__ uint32_t s_scan[NT / kWave + 1];
+    if (count <= (NT < 512 ? NT : 512)) {
         // rank = #{smaller indices}, each element's comparisons split over
-        // kSelThreads / count threads whose partial counts add up in LDS
+        // NT / count threads whose partial counts add up in LDS
         if (count == 0) {
-            for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
+            for (int i = threadIdx.x; i < K; i += NT) o[i] = -1;
             return;
         }
-        for (int i = threadIdx.x; i < count; i += kSelThreads) s_cur[i] = 0u;
+        for (int i = threadIdx.x; i < count; i += NT) s_cur[i] = 0u;
         if (threadIdx.x < 4) s_list[count + threadIdx.x] = INT_MAX;   // never smaller
         __syncthreads();
-        const int P = kSelThreads / count, i = threadIdx.x % count, part = threadIdx.x / count;
+        const int P = NT / count, i = threadIdx.x % count, part = threadIdx.x / count;
         if (part < P) {
             const int n4 = (count + 3) / 4, chunk = (n4 + P - 1) / P;
             const int j0 = part * chunk, j1 = min(n4, j0 + chunk);
@@ -239,11 +242,11 @@ __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __res
             if (r) atomicAdd(&s_cur[i], r);
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < count; i += kSelThreads) o[s_cur[i]] = s_list[i];
+        for (int i = threadIdx.x; i < count; i += NT) o[s_cur[i]] = s_list[i];
     } else {
         // range of the list
         int32_t mn = INT_MAX, mx = 0;
-        for (int i = threadIdx.x; i < count; i += kSelThreads) {
+        for (int i = threadIdx.x; i < count; i += NT) {
             mn = min(mn, s_list[i]);
             mx = max(mx, s_list[i]);
         }
@@ -257,28 +260,28 @@ __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __res
         s_cur[threadIdx.x] = 0u;
         __syncthreads();
         mn = INT_MAX; mx = 0;
-        for (int w = 0; w < kSelThreads / kWave; ++w) {
+        for (int w = 0; w < NT / kWave; ++w) {
             mn = min(mn, s_mm[2 * w]);
             mx = max(mx, s_mm[2 * w + 1]);
         }
         // bucket(e) is non-decreasing in e
         const float scale = (float)NB / ((float)(mx - mn) + 1.0f);
         auto bucket = [&](int32_t e) { return min(NB - 1, (int)((float)(e - mn) * scale)); };
-        for (int i = threadIdx.x; i < count; i += kSelThreads) atomicAdd(&s_cur[bucket(s_list[i])], 1u);
+        for (int i = threadIdx.x; i < count; i += NT) atomicAdd(&s_cur[bucket(s_list[i])], 1u);
         __syncthreads();
         const uint32_t c = s_cur[threadIdx.x];
         uint32_t tot;
-        const uint32_t ex = block_exclusive_sum<kSelThreads>(c, s_scan, tot);
+        const uint32_t ex = block_exclusive_sum<NT>(c, s_scan, tot);
         s_start[threadIdx.x] = ex;
         s_cur[threadIdx.x] = ex;
         if (threadIdx.x == NB - 1) s_start[NB] = ex + c;
         __syncthreads();
-        for (int i = threadIdx.x; i < count; i += kSelThreads) {
+        for (int i = threadIdx.x; i < count; i += NT) {
             const int32_t e = s_list[i];
             s_srt[atomicAdd(&s_cur[bucket(e)], 1u)] = e;
         }
         __syncthreads();
-        for (int p = threadIdx.x; p < count; p += kSelThreads) {
+        for (int p = threadIdx.x; p < count; p += NT) {
             const int32_t e = s_srt[p];
             const int bk = bucket(e);
             const int lo = (int)s_start[bk], hi = (int)s_start[bk + 1];
@@ -287,7 +290,7 @@ __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __res
             o[lo + r] = e;
         }
     }
-    for (int i = count + threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
+    for (int i = count + threadIdx.x; i < K; i += NT) o[i] = -1;
 }
 
 // Appends to s_out[NA ..] the indices of the `need` best of the NC distinct
@@ -470,11 +473,14 @@ __global__ __launch_bounds__(kSelThreads) void k_finalize(
 // the first `need` values == thr (in any fixed order).  A pass whose chosen
 // bucket holds exactly the values still wanted ends the search: then every
 // value >= the bucket's lower bound is taken (thr = bound - 1, need = 0).
+//   With last_shift > 0 the passes stop at that digit: then (unless a pass
+// ended the search) thr is the lower bound of the last bucket (its low bits
+// zero), and the K largest are among the values >= thr.
 template <int NT, int IPT>
 __device__ int64_t block_kth_u32(const uint32_t (&it)[IPT], uint32_t K, uint32_t* s_hist,
-                                 uint32_t* s_dig, uint32_t& need) {
+                                 uint32_t* s_dig, uint32_t& need, int last_shift = 0) {
     uint32_t prefix = 0, mask = 0, want = K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = 24; shift >= last_shift; shift -= 8) {
         for (int i = threadIdx.x; i < 256; i += NT) s_hist[i] = 0u;
         __syncthreads();
 #pragma unroll
@@ -647,13 +653,22 @@ __global__ __launch_bounds__(kSelThreads) void k_select_small(
 
 // A prefill chunk of Q queries of one sequence scores the same key rows for
 // every query, so it is a dense contraction S = Qi K^T ([Q x RW] x [RW x N])
-// on the bf16 matrix cores, in two kernels:
+// on the bf16 matrix cores:
 //   k_prefill_convert: one bf16 copy of the chunk's query rows (heads summed
 //     when the key row is shared, Hk == 1) and of the sequence's key rows,
 //     each value split x = hi + lo (lo = x - hi rounded to bf16), rows padded
-//     to tiles with zeros, and one flag per 64 rows: some lo part is non-zero;
-//   k_prefill_gemm: 128 x 128 score tiles; hi*hi always, hi*lo + lo*hi only
-//     for tiles whose flags are set.
+//     to tiles with zeros, and one flag per 128-row tile: some lo part is
+//     non-zero (only then are the tile's lo rows written);
+//   k_prefill_gemm: 128 x 128 score tiles; hi*hi always, hi*lo when the key
+//     tile is flagged, lo*hi when the query tile is (lo*lo is dropped: about
+//     2^-16 of each product, and exactly zero when either side is integer).
+// The Top-K never materialises the [Q x N] scores: a GEMM over 16 sampled
+// key tiles gives each query a threshold (k_sample_thr), the full GEMM
+// appends only the scores at or above it to the query's candidate list, and
+// k_cand_select selects exactly over the list.  A list that cannot hold the
+// answer (too short above the threshold, or overflowing) sends its query
+// tile through the full score rows and k_row_select instead; the result is
+// the exact Top-K either way.
 // Integer-valued inputs of magnitude <= 256 are exact in bf16 (no lo part)
 // and, while every partial sum stays below 2^24 in magnitude, the fp32
 // accumulation is exact in any order: the scores equal the definition bit
@@ -664,7 +679,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kGM = 128, kGN = 128, kGK = 64;   // score tile and K chunk
 constexpr int kGStr = kGK + 8;                  // LDS row stride (bf16): 144 B
 constexpr int kGVec = kGM * kGK / 8 / 256;      // 16-byte pieces per thread and operand
-constexpr int kCvtRows = 64;                    // rows per conversion workgroup (and flag)
+constexpr int kCvtRows = 128;                   // rows per conversion workgroup and flag (a tile)
+constexpr int kCvtThreads = 1024;               // threads per conversion workgroup
+static_assert(kCvtRows == kGM && kCvtRows == kGN, "one lo flag per score tile side");
 
 __device__ __forceinline__ float4 load_qrow4(const float* __restrict__ qI, int q, int Hi, int Hk,
                                              int Di, int c) {
@@ -708,14 +725,20 @@ __device__ __forceinline__ float4 load_key4(const uint8_t* p) {
 }
 
 // Workgroups [0, Qp/64) convert query rows, the rest key rows (64 each).
-template <typename KT>
-__global__ __launch_bounds__(256) void k_prefill_convert(
+// A thread converts NG groups of 8 consecutive values (16-byte stores),
+// four groups' loads issued together.  The first pass writes the hi parts
+// and finds whether some lo part of the block is non-zero; only then does a
+// second pass re-read the rows (from the caches) and write the lo parts,
+// since the score GEMM reads lo rows only for flagged blocks.
+template <typename KT, int NG>
+__global__ __launch_bounds__(kCvtThreads) void k_prefill_convert(
     const float* __restrict__ qI, const KT* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, int Q, int Qp, int Hi, int Hk,
     int Di, int N, uint16_t* __restrict__ qh, uint16_t* __restrict__ ql,
     uint16_t* __restrict__ kh, uint16_t* __restrict__ kl, uint32_t* __restrict__ qflag,
     uint32_t* __restrict__ kflag) {
-    const int RW = Hk * Di, f4 = RW / 4;
+    constexpr int kU = 4;
+    const int RW = Hk * Di, f8 = RW / 8;   // RW = 64 NG (kCvtRows rows, kCvtThreads threads)
     const KT* kb = kI + seq_row_off[0] * (int64_t)RW;
     const int nqb = Qp / kCvtRows;
     const bool isq = (int)blockIdx.x < nqb;
@@ -724,28 +747,55 @@ __global__ __launch_bounds__(256) void k_prefill_convert(
     uint16_t* dh = isq ? qh : kh;
     uint16_t* dl = isq ? ql : kl;
     int any = 0;
-    for (int f = threadIdx.x; f < kCvtRows * f4; f += 256) {
-        const int r = r0 + f / f4, c = 4 * (f % f4);
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < nrow)
-            x = isq ? load_qrow4(qI, r, Hi, Hk, Di, c) : load_key4(kb + (size_t)r * RW + c);
-        uint2 h, l;
-        any |= split4_bf16(x, h, l) ? 1 : 0;
-        *reinterpret_cast<uint2*>(dh + (size_t)r * RW + c) = h;
-        *reinterpret_cast<uint2*>(dl + (size_t)r * RW + c) = l;
-    }
+    // groups g0 .. g0 + kU - 1; pass 0 writes hi (and finds any), pass 1 lo
+    auto groups = [&](int g0, int pass) {
+        float4 x[kU][2];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int f = threadIdx.x + kCvtThreads * (g0 + u), r = r0 + f / f8, c = 8 * (f % f8);
+            x[u][0] = x[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < nrow) {
+                if (isq) {
+                    x[u][0] = load_qrow4(qI, r, Hi, Hk, Di, c);
+                    x[u][1] = load_qrow4(qI, r, Hi, Hk, Di, c + 4);
+                } else {
+                    x[u][0] = load_key4(kb + (size_t)r * RW + c);
+                    x[u][1] = load_key4(kb + (size_t)r * RW + c + 4);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int f = threadIdx.x + kCvtThreads * (g0 + u), r = r0 + f / f8, c = 8 * (f % f8);
+            uint2 h0, l0, h1, l1;
+            any |= split4_bf16(x[u][0], h0, l0) ? 1 : 0;
+            any |= split4_bf16(x[u][1], h1, l1) ? 1 : 0;
+            uint16_t* d = (pass == 0 ? dh : dl) + (size_t)r * RW + c;
+            *reinterpret_cast<uint4*>(d) = pass == 0 ? make_uint4(h0.x, h0.y, h1.x, h1.y)
+                                                     : make_uint4(l0.x, l0.y, l1.x, l1.y);
+        }
+    };
+#pragma unroll 1
+    for (int g0 = 0; g0 < NG; g0 += kU) groups(g0, 0);
     any = __syncthreads_or(any);
+    if (any) {
+#pragma unroll 1
+        for (int g0 = 0; g0 < NG; g0 += kU) groups(g0, 1);
+    }
     if (threadIdx.x == 0) (isq ? qflag : kflag)[blk] = any ? 1u : 0u;
 }
 
 // A thread's share of one K chunk: kGVec x 16 B of the query tile and of the
 // key tile (row f / (kGK/8), 8 bf16 at column 8 (f % (kGK/8)), f = thread + 256 j).
-// Chunk c of the (pass, K chunk) sequence: pass 0 = hi*hi, 1 = hi*lo,
-// 2 = lo*hi.  (Native vector types keep the staging in registers.)
+// Chunk c of the (pass, K chunk) sequence: the passes are hi*hi, then
+// hi*lo when the key tile has lo parts, then lo*hi when the query tile has
+// them (p1: the second pass).  (Native vector types keep the staging in
+// registers.)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define CSA2_GEMM_LOAD(RA, RB, c)                                                          \
     do {                                                                                   \
-        const int pass_ = (c) / nch, kc_ = ((c) - pass_ * nch) * kGK;                      \
+        const int seq_ = (c) / nch, kc_ = ((c) - seq_ * nch) * kGK;                        \
+        const int pass_ = seq_ == 0 ? 0 : seq_ == 1 ? p1 : 2;                              \
         const uint16_t* A_ = pass_ == 2 ? ql : qh;                                         \
         const uint16_t* B_ = pass_ == 1 ? kl : kh;                                         \
         _Pragma("unroll") for (int j_ = 0; j_ < kGVec; ++j_) {                             \
@@ -783,29 +833,125 @@ __device__ __forceinline__ void gemm_mma(const uint16_t* sA, const uint16_t* sB,
     }
 }
 
-// One 128 x 128 tile of scores per workgroup (4 waves of 64 x 64 on the
-// 32x32x16 bf16 MFMA).  The chunk sequence is (pass, K chunk) with pass 0 =
-// hi*hi, 1 = hi*lo, 2 = lo*hi; a chunk is loaded into registers during the
-// previous chunk's products and stored to LDS right before its own, so one
-// 36 KB LDS buffer serves.  Four workgroups per CU (the register budget is
-// capped to fit them) hide the operand loads' latency better than deeper
-// staging in fewer workgroups: 128-wide chunks with two workgroups per CU
-// took 25 % longer.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_prefill_gemm(
-    const uint16_t* __restrict__ qh, const uint16_t* __restrict__ ql,
-    const uint16_t* __restrict__ kh, const uint16_t* __restrict__ kl,
-    const uint32_t* __restrict__ qflag, const uint32_t* __restrict__ kflag, int RW, int Q,
-    const int32_t* __restrict__ q_nvis, int max_nvis, uint32_t* __restrict__ keys,
-    int64_t kstride) {
+// Modes of the score GEMM's epilogue (what a tile of scores turns into).
+constexpr int kGemmKeys = 0;        // every visible score's key into its row
+constexpr int kGemmSample = 1;      // sampled key tiles: keys (0 if invisible) into a sample row
+constexpr int kGemmCand = 2;        // keys at or above the query's threshold, appended to its list
+constexpr int kSampleTiles = 16;    // key tiles sampled per query (2,048 keys)
+constexpr int kCandCapPre = 4096;   // candidates a prefill query keeps
+constexpr int kFbGrid = 1024;       // workgroups of the exact-path score GEMM
+
+// The min(K, #non-empty) largest of the register-resident composite keys
+// of a workgroup of NT threads (score word | ~index word; 0 = empty;
+// non-empty keys distinct), written to o as their indices in ascending
+// order, -1 padded.
+template <int NT, int IPT>
+__device__ void select_top_ckeys(const uint64_t (&it)[IPT], int K, int32_t* __restrict__ o) {
+    __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t s_tmp[NT / kWave + 3];
+    __shared__ uint32_t s_count;
+    uint32_t nv = 0;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) nv += it[j] != 0;
+    uint32_t total;
+    (void)block_exclusive_sum<NT>(nv, s_tmp, total);
+    const int k = min((int)total, K);
+    if (k == 0) {
+        for (int i = threadIdx.x; i < K; i += NT) o[i] = -1;
+        return;
+    }
+    const uint64_t T = block_select_kth<NT, IPT>(it, (uint32_t)k, s_hist, s_dig, 56);
+    if (threadIdx.x == 0) s_count = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+        if (it[j] != 0 && it[j] >= T) {
+            const uint32_t pos = atomicAdd(&s_count, 1u);
+            if (pos < (uint32_t)K) s_out[pos] = (int32_t)comp_idx(it[j]);
+        }
+    }
+    __syncthreads();
+    rank_and_write<NT>(s_out, min((int)s_count, K), K, o);
+}
+
+constexpr int kXcdsIdx = 8;   // XCDs of an MI355X (L2 domains)
+
+// Score tile (key tile kt, query tile qt) of workgroup g in a grid of ntk x
+// nqt tiles.  Workgroups are dealt to the XCDs round-robin by linear id.
+// When the key tiles split evenly over the XCDs, XCD x takes key tiles
+// [x ntk/8, (x+1) ntk/8) for every query tile and walks them in groups of
+// up to 8 query tiles, query tile fastest: its L2 keeps the group's query
+// rows while its share of the key rows streams past them, and no other XCD
+// reads those key rows.  (A key-tile-fastest order over the whole grid
+// makes every XCD stream every key row once per query tile.)
+__device__ __forceinline__ void gemm_tile(int g, int ntk, int nqt, int& kt, int& qt) {
+    if (ntk % kXcdsIdx == 0) {
+        const int gq = nqt % 8 == 0 ? 8 : nqt % 4 == 0 ? 4 : nqt % 2 == 0 ? 2 : 1;
+        const int x = g % kXcdsIdx, local = g / kXcdsIdx, kr = ntk / kXcdsIdx;
+        const int qi = local % gq, rest = local / gq;
+        kt = x * kr + rest % kr;
+        qt = (rest / kr) * gq + qi;
+    } else {
+        kt = g % ntk;
+        qt = g / ntk;
+    }
+}
+
+// Tile g of the score GEMM: 128 x 128 scores (4 waves of 64 x 64 on the
+// 32x32x16 bf16 MFMA), ntk x nqt tiles in a 1-D grid (order: gemm_tile).
+// The chunk sequence is (pass, K chunk) with pass 0 = hi*hi, 1 = hi*lo,
+// 2 = lo*hi; a chunk is loaded into registers during the previous chunk's
+// products and stored to LDS right before its own, so one 36 KB LDS buffer
+// serves.  Four workgroups per CU (the register budget is capped to fit
+// them) hide the operand loads' latency better than deeper staging in fewer
+// workgroups: 128-wide chunks with two workgroups per CU took 25 % longer.
+//   MODE kGemmKeys: keys[q * kstride + t] for every visible t; with
+//     tile_fail set (word 0: any tile flagged, word 1 + t: query tile t),
+//     only query tiles whose flag is set run (the exact
+//     path of the queries whose candidate list missed).
+//   MODE kGemmSample: grid key tile kt is key tile kt * tile_step; its keys
+//     go to keys[q * kstride + 128 kt + col] (0 for an invisible key).
+//   MODE kGemmCand: the composite keys (score, index) of the visible scores
+//     whose key is >= thr[q] are appended to cand[q * kCandCapPre ..]; cnt[q]
+//     counts them all (also those past the list's capacity).  A workgroup
+//     counts its candidates per query first and reserves their slots with
+//     one atomic per query, then writes them.
+#define CSA2_GEMM_PARAMS                                                                   \
+    const uint16_t* __restrict__ qh, const uint16_t* __restrict__ ql,                      \
+        const uint16_t* __restrict__ kh, const uint16_t* __restrict__ kl,                  \
+        const uint32_t* __restrict__ qflag, const uint32_t* __restrict__ kflag, int RW, int Q, \
+        const int32_t* __restrict__ q_nvis, int max_nvis, uint32_t* __restrict__ keys,     \
+        int64_t kstride, int ntk, int nqt, int tile_step,                                  \
+        const uint32_t* __restrict__ tile_fail, const uint32_t* __restrict__ thr,          \
+        uint64_t* __restrict__ cand, uint32_t* __restrict__ cnt
+#define CSA2_GEMM_ARGS                                                                     \
+    qh, ql, kh, kl, qflag, kflag, RW, Q, q_nvis, max_nvis, keys, kstride, ntk, nqt,        \
+        tile_step, tile_fail, thr, cand, cnt
+
+template <int MODE>
+__device__ __forceinline__ void prefill_gemm_tile(int g, CSA2_GEMM_PARAMS) {
     __shared__ __attribute__((aligned(16))) uint16_t sA[kGM * kGStr];
     __shared__ __attribute__((aligned(16))) uint16_t sB[kGN * kGStr];
-    const int n0 = blockIdx.x * kGN, m0 = blockIdx.y * kGM;
+    __shared__ int s_nv[kGM];
+    __shared__ uint32_t s_thr[kGM];
+    int kt, qt;
+    gemm_tile(g, ntk, nqt, kt, qt);
+    if (MODE == kGemmKeys && tile_fail && tile_fail[1 + qt] == 0u) return;
+    const int n0 = kt * tile_step * kGN, m0 = qt * kGM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hh = lane >> 5, l32 = lane & 31;
     const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
-    const int mb = m0 / kCvtRows, nb = n0 / kCvtRows;
-    const bool need_lo = (qflag[mb] | qflag[mb + 1] | kflag[nb] | kflag[nb + 1]) != 0u;
-    const int nch = RW / kGK, total = (need_lo ? 3 : 1) * nch;
+    if (threadIdx.x < kGM) {
+        const int q = m0 + threadIdx.x;
+        s_nv[threadIdx.x] = q < Q ? min(q_nvis[q], max_nvis) : 0;
+        if (MODE == kGemmCand) s_thr[threadIdx.x] = q < Q ? thr[q] : 0u;
+    }
+    // lo rows exist (are written) only for flagged tiles
+    const bool lo_q = qflag[m0 / kCvtRows] != 0u, lo_k = kflag[n0 / kCvtRows] != 0u;
+    const int p1 = lo_k ? 1 : 2;
+    const int nch = RW / kGK, total = (1 + (int)lo_q + (int)lo_k) * nch;
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -822,22 +968,172 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
 #undef CSA2_GEMM_LOAD
 #undef CSA2_GEMM_STORE
-    // lane (hh, l32) of tile (i, j), register r holds
-    // S[query m0 + wm + 32i + 8(r/4) + 4hh + r%4][key n0 + wn + 32j + l32]
+    __syncthreads();   // s_nv / s_thr
+    // lane (hh, l32) of tile (i, j), register r holds S[query m0 + lr]
+    // [key n0 + wn + 32j + l32], lr = wm + 32i + 8(r/4) + 4hh + r%4
+    if constexpr (MODE == kGemmCand) {
+        // the 32 lanes of a half-wave share one query row; per row, the wave
+        // with wn = 0 takes the first slots of the workgroup's run
+        __shared__ uint32_t s_cnt[2][kGM];
+        __shared__ uint32_t s_base[kGM];
+        const uint32_t below = (1u << l32) - 1u;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int q = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (q >= Q) continue;
-            const int nv = min(q_nvis[q], max_nvis);
-            uint32_t* krow = keys + (size_t)q * kstride;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int t = n0 + wn + 32 * j + l32;
-                if (t < nv) krow[t] = ord_key(acc[i][j][r]);
+            for (int r = 0; r < 16; ++r) {
+                const int lr = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int nv = s_nv[lr];
+                const uint32_t T = s_thr[lr];
+                const int t0 = n0 + wn + l32;
+                const bool v0 = t0 < nv && ord_key(acc[i][0][r]) >= T;
+                const bool v1 = t0 + 32 < nv && ord_key(acc[i][1][r]) >= T;
+                const uint32_t b0 = (uint32_t)(__ballot(v0) >> (32 * hh));
+                const uint32_t b1 = (uint32_t)(__ballot(v1) >> (32 * hh));
+                if (l32 == 0) s_cnt[wn >> 6][lr] = __popc(b0) + __popc(b1);
             }
+        __syncthreads();
+        if (threadIdx.x < kGM) {
+            const uint32_t n = s_cnt[0][threadIdx.x] + s_cnt[1][threadIdx.x];
+            s_base[threadIdx.x] = n ? atomicAdd(&cnt[m0 + threadIdx.x], n) : 0u;   // n > 0: q < Q
         }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int nv = s_nv[lr];
+                const uint32_t T = s_thr[lr];
+                const int t0 = n0 + wn + l32;
+                const uint32_t k0 = ord_key(acc[i][0][r]), k1 = ord_key(acc[i][1][r]);
+                const bool v0 = t0 < nv && k0 >= T;
+                const bool v1 = t0 + 32 < nv && k1 >= T;
+                const uint32_t b0 = (uint32_t)(__ballot(v0) >> (32 * hh));
+                const uint32_t b1 = (uint32_t)(__ballot(v1) >> (32 * hh));
+                const uint32_t base = s_base[lr] + (wn ? s_cnt[0][lr] : 0u);
+                uint64_t* crow = cand + (size_t)(m0 + lr) * kCandCapPre;   // used only if q < Q
+                if (v0) {
+                    const uint32_t pos = base + __popc(b0 & below);
+                    if (pos < (uint32_t)kCandCapPre) crow[pos] = comp_key(k0, (uint32_t)t0);
+                }
+                if (v1) {
+                    const uint32_t pos = base + __popc(b0) + __popc(b1 & below);
+                    if (pos < (uint32_t)kCandCapPre) crow[pos] = comp_key(k1, (uint32_t)(t0 + 32));
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int q = m0 + lr;
+                if (q >= Q) continue;
+                const int nv = s_nv[lr];
+                uint32_t* krow = keys + (size_t)q * kstride;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = n0 + wn + 32 * j + l32;
+                    if (MODE == kGemmSample)
+                        krow[kt * kGN + wn + 32 * j + l32] = t < nv ? ord_key(acc[i][j][r]) : 0u;
+                    else if (t < nv)
+                        krow[t] = ord_key(acc[i][j][r]);
+                }
+            }
+    }
+    __syncthreads();   // before a next tile's s_nv / s_thr
+}
+
+// The score GEMM: one tile per workgroup; kGemmKeysFb is kGemmKeys with
+// tile_fail over a small grid that takes tiles g, g + grid, ... in turn.
+constexpr int kGemmKeysFb = 3;
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_prefill_gemm(
+    CSA2_GEMM_PARAMS) {
+    if constexpr (MODE == kGemmKeysFb) {
+        if (tile_fail[0] == 0u) return;   // no query tile was flagged
+        for (int g = blockIdx.x; g < ntk * nqt; g += gridDim.x)
+            prefill_gemm_tile<kGemmKeys>(g, CSA2_GEMM_ARGS);
+    } else {
+        prefill_gemm_tile<MODE>(blockIdx.x, CSA2_GEMM_ARGS);
+    }
+}
+#undef CSA2_GEMM_PARAMS
+#undef CSA2_GEMM_ARGS
+
+// Threshold of each prefill query from its sampled keys (one workgroup per
+// query): a query with at most kCandCapPre visible entries takes every entry
+// (threshold 0); otherwise the threshold is the j-th largest visible sampled
+// key cut to its top 24 bits, j chosen so that about 3 K entries are
+// expected at or above it.  The
+// candidate list then holds every entry whose key is >= the threshold; a
+// list with fewer than K of them, or more than it can hold, sends the query
+// to the exact path (the threshold only decides how much work is skipped).
+__global__ __launch_bounds__(256) void k_sample_thr(const uint32_t* __restrict__ samp, int ns,
+                                                    const int32_t* __restrict__ q_nvis,
+                                                    int max_nvis, int K,
+                                                    uint32_t* __restrict__ thr) {
+    constexpr int NT = 256, IPT = kSampleTiles * kGN / NT;
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t s_tmp[NT / kWave + 3];
+    const int q = blockIdx.x;
+    const int nv = min(q_nvis[q], max_nvis);
+    if (nv <= kCandCapPre) {
+        if (threadIdx.x == 0) thr[q] = 0u;
+        return;
+    }
+    uint32_t it[IPT];   // 0 = invisible (no visible score has key 0)
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+        const int i = threadIdx.x + NT * j;
+        it[j] = i < ns ? samp[(size_t)q * ns + i] : 0u;
+        c += it[j] != 0u;
+    }
+    uint32_t total;
+    (void)block_exclusive_sum<NT>(c, s_tmp, total);
+    if (total == 0u) {   // no visible sample: every entry is a candidate
+        if (threadIdx.x == 0) thr[q] = 0u;
+        return;
+    }
+    const uint64_t want = ((uint64_t)3 * K * total + nv - 1) / (uint64_t)nv;
+    const uint32_t j = (uint32_t)max<uint64_t>(1, min<uint64_t>(want, total));
+    // the top 24 bits of the j-th largest sample: its value to about 2^-15
+    // relative (exactly, for integer scores below 2^15 in magnitude)
+    uint32_t need;
+    const int64_t t = block_kth_u32<NT, IPT>(it, j, s_hist, s_dig, need, 8);
+    // the j largest samples are >= t when need > 0, else > t
+    if (threadIdx.x == 0) thr[q] = (uint32_t)(need ? t : t + 1);
+}
+
+// Exact Top-K of each prefill query over its candidate list; a query whose
+// list cannot hold the answer (fewer than K entries above a non-zero
+// threshold, or more entries than the list holds) flags its query tile for
+// the exact path instead (tile_fail word 1 + tile, and word 0: any tile).
+constexpr int kCandThreads = 256;
+__global__ __launch_bounds__(kCandThreads) void k_cand_select(const uint64_t* __restrict__ cand,
+                                                             const uint32_t* __restrict__ cnt,
+                                                             const uint32_t* __restrict__ thr,
+                                                             int K, int32_t* __restrict__ out,
+                                                             uint32_t* __restrict__ tile_fail) {
+    constexpr int IPT = kCandCapPre / kCandThreads;
+    const int q = blockIdx.x;
+    const uint32_t n = cnt[q];
+    if (n > (uint32_t)kCandCapPre || (thr[q] != 0u && n < (uint32_t)K)) {
+        if (threadIdx.x == 0) {
+            atomicOr(&tile_fail[1 + q / kGM], 1u);
+            atomicOr(&tile_fail[0], 1u);
+        }
+        return;
+    }
+    uint64_t it[IPT];
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+        const int i = threadIdx.x + j * kCandThreads;
+        it[j] = i < (int)n ? cand[(size_t)q * kCandCapPre + i] : 0ull;
+    }
+    select_top_ckeys<kCandThreads, IPT>(it, K, out + (size_t)q * K);
 }
 
 // Exact Top-K of one row of score keys (prefill: one workgroup per query).
@@ -856,7 +1152,8 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
                                                             int64_t stride,
                                                             const int32_t* __restrict__ q_nvis,
                                                             int nmax, int K,
-                                                            int32_t* __restrict__ out) {
+                                                            int32_t* __restrict__ out,
+                                                            const uint32_t* __restrict__ tile_fail) {
     __shared__ __attribute__((aligned(16))) uint32_t s_h[kHistBins];
     __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
@@ -867,6 +1164,7 @@ __global__ __launch_bounds__(kSelThreads) void k_row_select(const uint32_t* __re
     __shared__ __attribute__((aligned(16))) uint32_t s_rtop[kWave];      // 4 per wave
     __shared__ uint32_t s_wbase[kRowRegs * (kSelThreads / kWave)];       // per (slot, wave)
     const int q = blockIdx.x;
+    if (tile_fail && tile_fail[1 + q / kGM] == 0u) return;   // its candidate list held the answer
     const int n = min(q_nvis[q], nmax);
     int32_t* o = out + (size_t)q * K;
     if (n <= K) {
@@ -1143,40 +1441,14 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score_e4m3(
 
 __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
     const uint64_t* __restrict__ ckeys, int ncand, int K, int32_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
-    __shared__ uint32_t s_hist[256];
-    __shared__ uint32_t s_dig[2];
-    __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
-    __shared__ uint32_t s_count;
     const int q = blockIdx.x;
     uint64_t it[kSelItems];
-    uint32_t nv = 0;
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
         const int i = threadIdx.x + j * kSelThreads;
         it[j] = i < ncand ? ckeys[(size_t)q * ncand + i] : 0ull;
-        nv += it[j] != 0;
     }
-    uint32_t total;
-    (void)block_exclusive_sum<kSelThreads>(nv, s_tmp, total);
-    const int k = min((int)total, K);
-    int32_t* o = out + (size_t)q * K;
-    if (k == 0) {
-        for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
-        return;
-    }
-    const uint64_t T = block_select_kth<kSelThreads, kSelItems>(it, (uint32_t)k, s_hist, s_dig, 56);
-    if (threadIdx.x == 0) s_count = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kSelItems; ++j) {
-        if (it[j] != 0 && it[j] >= T) {
-            const uint32_t pos = atomicAdd(&s_count, 1u);
-            if (pos < (uint32_t)K) s_out[pos] = (int32_t)comp_idx(it[j]);
-        }
-    }
-    __syncthreads();
-    rank_and_write(s_out, min((int)s_count, K), K, o);
+    select_top_ckeys<kSelThreads, kSelItems>(it, K, out + (size_t)q * K);
 }
 
 // ------------------------------------------------------ host helpers
@@ -1244,6 +1516,12 @@ struct PrefillWs {
     uint16_t *qh, *ql, *kh, *kl;
     uint32_t *qflag, *kflag;
     int Qp, Np;   // rows padded to whole score tiles
+    // candidate path of the Top-K: sampled keys, thresholds, candidate
+    // lists, their counts and the flags of query tiles sent to the exact path
+    uint32_t *samp, *thr, *cnt, *tfail;
+    uint64_t* cand;
+    int ns;       // sampled keys per query
+    size_t zero_words;   // cnt and tfail, cleared together
 };
 
 size_t carve_prefill(void* ws, size_t at, int Q, int max_nvis, int RW, PrefillWs* p) {
@@ -1257,6 +1535,15 @@ size_t carve_prefill(void* ws, size_t at, int Q, int max_nvis, int RW, PrefillWs
     p->kl = c.take<uint16_t>((size_t)p->Np * RW);
     p->qflag = c.take<uint32_t>(p->Qp / kCvtRows);
     p->kflag = c.take<uint32_t>(p->Np / kCvtRows);
+    const int ntiles = p->Np / kGN;
+    p->ns = kGN * std::min(ntiles, kSampleTiles);
+    p->samp = c.take<uint32_t>((size_t)Q * p->ns);
+    p->thr = c.take<uint32_t>((size_t)Q);
+    p->cand = c.take<uint64_t>((size_t)Q * kCandCapPre);
+    // counts, then the any-tile flag and the tile flags
+    p->cnt = c.take<uint32_t>((size_t)Q + 1 + p->Qp / kGM);
+    p->tfail = p->cnt ? p->cnt + Q : nullptr;
+    p->zero_words = (size_t)Q + 1 + p->Qp / kGM;
     return c.bytes();
 }
 
@@ -1315,19 +1602,71 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
         if (ws_bytes < carve_prefill(ws, w.bytes, Q, max_nvis, Hk * Di, &pw))
             return CSA2_ERR_WORKSPACE;
         if (max_nvis > 0) {
-            st = CSA2_LAUNCH("prefill_convert", k_prefill_convert<KT>,
-                             dim3((pw.Qp + pw.Np) / kCvtRows), dim3(256), s, qI, kI, seq_row_off,
+            const int RW = Hk * Di;
+            auto cvt = RW == 256 ? k_prefill_convert<KT, 4>
+                     : RW == 512 ? k_prefill_convert<KT, 8> : k_prefill_convert<KT, 16>;
+            st = CSA2_LAUNCH("prefill_convert", cvt,
+                             dim3((pw.Qp + pw.Np) / kCvtRows), dim3(kCvtThreads), s, qI, kI,
+                             seq_row_off,
                              Q, pw.Qp, Hi, Hk, Di, max_nvis, pw.qh, pw.ql, pw.kh, pw.kl,
                              pw.qflag, pw.kflag);
             if (st) return st;
-            st = CSA2_LAUNCH("prefill_scores", k_prefill_gemm, dim3(pw.Np / kGN, pw.Qp / kGM),
-                             dim3(256), s, pw.qh, pw.ql, pw.kh, pw.kl, pw.qflag, pw.kflag, Hk * Di,
-                             Q, q_nvis, max_nvis, w.keys_e, w.se);
+        }
+        const int ntiles = pw.Np / kGN, nqt = pw.Qp / kGM;
+        if (topk > 0 && pool_blocks == 0 && max_nvis > 0) {
+            // Top-K without the full score rows: thresholds from sampled key
+            // tiles, candidate lists from the score tiles, exact selection over
+            // the lists, and the full rows only for query tiles whose lists
+            // could not hold the answer
+            const int step = (ntiles + kSampleTiles - 1) / kSampleTiles;
+            const int nst = (ntiles + step - 1) / step;
+            st = CSA2_LAUNCH("zero", k_zero_u32, dim3(64), dim3(256), s, pw.cnt, pw.zero_words);
+            if (st) return st;
+            st = CSA2_LAUNCH("prefill_sample", k_prefill_gemm<kGemmSample>,
+                             dim3(nst * nqt), dim3(256), s, pw.qh, pw.ql, pw.kh, pw.kl,
+                             pw.qflag, pw.kflag, Hk * Di, Q, q_nvis, max_nvis, pw.samp,
+                             (int64_t)nst * kGN, nst, nqt, step, (const uint32_t*)nullptr,
+                             (const uint32_t*)nullptr, (uint64_t*)nullptr, (uint32_t*)nullptr);
+            if (st) return st;
+            st = CSA2_LAUNCH("sample_thr", k_sample_thr, dim3(Q), dim3(256), s, pw.samp, nst * kGN,
+                             q_nvis, max_nvis, topk, pw.thr);
+            if (st) return st;
+            st = CSA2_LAUNCH("prefill_scores", k_prefill_gemm<kGemmCand>,
+                             dim3(ntiles * nqt), dim3(256), s, pw.qh, pw.ql, pw.kh, pw.kl,
+                             pw.qflag, pw.kflag, Hk * Di, Q, q_nvis, max_nvis, (uint32_t*)nullptr,
+                             (int64_t)0, ntiles, nqt, 1, (const uint32_t*)nullptr, pw.thr, pw.cand,
+                             pw.cnt);
+            if (st) return st;
+            st = CSA2_LAUNCH("cand_select", k_cand_select, dim3(Q), dim3(kCandThreads), s, pw.cand,
+                             pw.cnt, pw.thr, topk, topk_idx, pw.tfail);
+            if (st) return st;
+            // exact path, flagged query tiles only (a small grid that skips
+            // the other tiles: the launch costs little when nothing failed)
+            st = CSA2_LAUNCH("prefill_scores_fb", k_prefill_gemm<kGemmKeysFb>,
+                             dim3(std::min(ntiles * nqt, kFbGrid)), dim3(256), s, pw.qh, pw.ql, pw.kh, pw.kl,
+                             pw.qflag, pw.kflag, Hk * Di, Q, q_nvis, max_nvis, w.keys_e, w.se,
+                             ntiles, nqt, 1,
+                             (const uint32_t*)pw.tfail, (const uint32_t*)nullptr,
+                             (uint64_t*)nullptr, (uint32_t*)nullptr);
+            if (st) return st;
+            st = CSA2_LAUNCH("row_select_fb", k_row_select, dim3(Q), dim3(kSelThreads), s,
+                             w.keys_e, w.se, q_nvis, max_nvis, topk, topk_idx,
+                             (const uint32_t*)pw.tfail);
+            if (st) return st;
+            return CSA2_OK;
+        }
+        if (max_nvis > 0) {
+            st = CSA2_LAUNCH("prefill_scores", k_prefill_gemm<kGemmKeys>,
+                             dim3(ntiles * nqt), dim3(256), s, pw.qh, pw.ql, pw.kh, pw.kl,
+                             pw.qflag, pw.kflag, Hk * Di, Q, q_nvis, max_nvis, w.keys_e, w.se,
+                             ntiles, nqt, 1,
+                             (const uint32_t*)nullptr, (const uint32_t*)nullptr,
+                             (uint64_t*)nullptr, (uint32_t*)nullptr);
             if (st) return st;
         }
         if (topk > 0) {
             st = CSA2_LAUNCH("row_select", k_row_select, dim3(Q), dim3(kSelThreads), s, w.keys_e,
-                             w.se, q_nvis, max_nvis, topk, topk_idx);
+                             w.se, q_nvis, max_nvis, topk, topk_idx, (const uint32_t*)nullptr);
             if (st) return st;
         }
         if (pool_blocks > 0) {
@@ -1337,7 +1676,8 @@ static int index_full_impl(const float* qI, const KT* kI, const int64_t* seq_row
                              (int)(block_rule == CSA2_BLOCK_SUM), w.keys_b, w.sb, w.nblk);
             if (st) return st;
             st = CSA2_LAUNCH("row_select_b", k_row_select, dim3(Q), dim3(kSelThreads), s,
-                             w.keys_b, w.sb, w.nblk, nbmax, pool_blocks, pool_block_idx);
+                             w.keys_b, w.sb, w.nblk, nbmax, pool_blocks, pool_block_idx,
+                             (const uint32_t*)nullptr);
             if (st) return st;
         }
         return CSA2_OK;

@@ -105,6 +105,16 @@ int csa2_last_hip_error(void);
  * decoder-only candidate pool to the encoder): each query of the chunk gets
  * the same block pool a decode query with its q_nvis would.  Too small a
  * workspace: CSA2_ERR_WORKSPACE.
+ * Accuracy of the prefill form: its scores come from bf16 matrix products of
+ * a two-part split of every input value, x = hi + lo (hi = bf16(x),
+ * lo = bf16(x - hi)); hi*hi + hi*lo + lo*hi is accumulated in fp32 and the
+ * lo*lo product is dropped.  Integer-valued inputs (|x| <= 256 splits with
+ * lo = 0) give the exact scores of the decode form and the selection of the
+ * definition.  Other fp32 inputs: each score is within about
+ * 2^-14 * sum_i |q_i k_i| of the exact one (the dropped lo*lo term and the
+ * split's residual, each at most 2^-18 of a product, plus fp32 accumulation),
+ * so an entry can trade places with another only when their exact scores
+ * are that close.
  * Preconditions (device data): rows read stay inside kI.
  * ---------------------------------------------------------------------- */
 size_t csa2_index_full_workspace_bytes(int32_t Q, int32_t max_nvis, int32_t topk,

@@ -343,28 +343,46 @@ def test_index_candidate_radix_paths(csa2):
         assert np.array_equal(pool[b], p[0]), f"pool of query {b}"
 
 
-def test_prefill_indexer_general_fp32_inputs(csa2):
-    # inputs that are not exact in bf16 take the hi/lo split path; the
-    # selection must be the oracle's except for entries whose exact score is
-    # within the path's rounding of the K-th score
-    w = Workload("prefill_fp32", 11, "prefill", [3000], topk=64, layers=0, p0=4000, Qn=40, m=2)
+@pytest.mark.parametrize("split", ["both", "queries", "keys"])
+@pytest.mark.parametrize("ctx,p0", [(3000, 4000), (12000, 20000)])
+def test_prefill_indexer_general_fp32_inputs(csa2, split, ctx, p0):
+    # values that are not exact in bf16 (on both sides, or on one side with
+    # integers on the other) take the hi/lo split passes of the score GEMM.
+    # Each score is within 2^-14 * sum_i |q_i k_i| of the exact one (the
+    # dropped lo*lo term and the split's residual, each at most 2^-18 of a
+    # product, and fp32 accumulation: at most 3 x 32 roundings of 16-product
+    # MFMA steps, 96 * 2^-24 < 2^-17), so an entry the GPU picks
+    # in place of the oracle's is within the sum of the two entries' bounds
+    # of the K-th exact score.  The longer context puts the queries' visible
+    # entries past the candidate lists' capacity, so the sampled thresholds
+    # decide the lists.
+    w = Workload("prefill_fp32", 11, "prefill", [ctx], topk=64, layers=0, p0=p0, Qn=40, m=2)
     t = build_device(w, with_kv=False, layers=0)
-    kI = (host_ints(79, 1, 0, w.rows * w.row_width) / 3.0).astype(np.float32).reshape(-1, w.Hk, w.Di)
-    qI = (host_ints(79, 2, 0, w.Qn * w.Hi * w.Di) / 7.0).astype(np.float32).reshape(w.Qn, w.Hi, w.Di)
+    kI = host_ints(79, 1, 0, w.rows * w.row_width).astype(np.float32).reshape(-1, w.Hk, w.Di)
+    qI = host_ints(79, 2, 0, w.Qn * w.Hi * w.Di).astype(np.float32).reshape(w.Qn, w.Hi, w.Di)
+    if split in ("both", "keys"):
+        kI = (kI / 3.0).astype(np.float32)
+    if split in ("both", "queries"):
+        qI = (qI / 7.0).astype(np.float32)
     t["kI"] = torch.from_numpy(kI).cuda()
     idx, _ = C.gpu_index_full(w, t, qI=torch.from_numpy(qI).cuda())
     idx = idx.cpu().numpy()
     nv = w.q_nvis()
+    assert nv.max() <= ctx
     ref, _ = oracle.index_full(qI, kI, [0], np.zeros(w.Qn, np.int32), nv, w.Hi, w.Hk, w.Di, w.topk)
+    ka = np.abs(kI.astype(np.float64))
     for i in range(w.Qn):
         s = oracle.scores(qI, kI, [0], np.zeros(w.Qn, np.int32), nv, i, w.Hi, w.Hk, w.Di)
+        n = int(nv[i])
+        bound = 2.0 ** -14 * np.einsum("hd,nhd->n", np.abs(qI[i].astype(np.float64)), ka[:n])
         g = idx[i]
-        assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[:min(w.topk, nv[i])] >= 0)
-        kth = np.sort(s)[::-1][min(w.topk, nv[i]) - 1]
-        eps = 1e-3 * np.abs(s).max()
+        k = min(w.topk, n)
+        assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[:k] >= 0) and np.all(g[k:] == -1)
+        kth = np.sort(s)[::-1][k - 1]
         gsel, rsel = set(g[g >= 0].tolist()), set(ref[i][ref[i] >= 0].tolist())
-        assert all(s[j] >= kth - eps for j in gsel - rsel), f"query {i}"
-        assert all(s[j] <= kth + eps for j in rsel - gsel), f"query {i}"
+        bmax = bound.max()
+        assert all(s[j] >= kth - bound[j] - bmax for j in gsel - rsel), f"query {i}"
+        assert all(s[j] <= kth + bound[j] + bmax for j in rsel - gsel), f"query {i}"
 
 
 def test_prefill_row_select_paths(csa2):
@@ -393,6 +411,30 @@ def test_prefill_row_select_paths(csa2):
     zero = torch.zeros((w.Qn, w.Hi, w.Di), dtype=torch.float32, device="cuda")
     idx, _ = C.gpu_index_full(w, t, qI=zero)
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(512), (w.Qn, 1)))
+
+
+@pytest.mark.parametrize("ctx,p0,m,zero_rows", [(4100, 7900, 2, (5, 299)),
+                                                 (40300, 40000, 1, (130, 131, 299))])
+def test_prefill_candidate_lists_and_exact_fallback(csa2, ctx, p0, m, zero_rows):
+    # 300 queries (three query tiles, the last ragged).  A query with more
+    # than 4,096 visible entries keeps a candidate list of the entries at or
+    # above a threshold from sampled key tiles; a query whose scores all tie
+    # (qI = 0) overflows its list and sends its query tile to the full-row
+    # select, while the other tiles keep their lists
+    w = Workload("prefill_cand", 14, "prefill", [ctx], topk=512, layers=0, p0=p0, Qn=300, m=m)
+    nv = w.q_nvis()
+    assert nv.max() <= ctx
+    t = build_device(w, with_kv=False, layers=0)
+    qI = host_qI(w, T_QI_FULL).copy()
+    qI[list(zero_rows)] = 0.0
+    idx, _ = C.gpu_index_full(w, t, qI=torch.from_numpy(qI).cuda())
+    idx = idx.cpu().numpy()
+    kI = host_kI_rows(w, 0, ctx)
+    ref, _ = oracle.index_full(qI, kI, [0], np.zeros(w.Qn, np.int32), nv, w.Hi, w.Hk, w.Di, w.topk)
+    for i in range(w.Qn):
+        assert np.array_equal(idx[i], ref[i]), f"query {i} (nvis {nv[i]})"
+    for i in zero_rows:
+        assert np.array_equal(idx[i], np.arange(512)), f"all-tie query {i}"
 
 
 def test_attention_largest_topk_and_window(csa2):
