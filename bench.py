@@ -70,6 +70,7 @@ TRAFFIC_PROFILES = {
     ("c1_full_reuse3", "e4m3"): "score_stream_e4m3_c1_traffic.md",
     ("c3_hier_1m", "f32"): "score_stream_c3_traffic.md",
     ("c4_mixed_reindex", "f32"): "reindex_c4_traffic.md",
+    ("c4_mixed_reindex", "e4m3"): "reindex_c4_traffic.md",
     ("c2_prefill_m2", "f32"): "prefill_c2_traffic.md",
 }
 
@@ -193,13 +194,13 @@ def dominant_roofline(w, kern, keys="f32"):
         ach = alg / (kern[stream]["avg_us"] * 1e-6) / 1e9
         return {"bound": "hbm", "kernel": stream, "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": alg,
-                "traffic": measured_traffic(prof, "score_stream") if prof else None}
+                "traffic": measured_traffic(prof, stream) if prof else None}
     if w.kind == "decode_reindex" and rscore in kern:
         alg = float(candidate_rows(w)) * w.row_width * vb + float(w.Q) * w.Hi * w.Di * 4
         ach = alg / (kern[rscore]["avg_us"] * 1e-6) / 1e9
         return {"bound": "hbm", "kernel": rscore, "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": alg,
-                "traffic": measured_traffic(prof, "reindex_score") if prof else None}
+                "traffic": measured_traffic(prof, rscore) if prof else None}
     if "attn" in kern:
         return mfma_utilisation(w, kern)["attn"] | {
             "traffic": measured_traffic(prof, "attn") if prof else None}

@@ -39,7 +39,7 @@ def test_score_stream_bytes_per_launch(bench):
     assert rec["bound"] == "hbm" and rec["peak"] == 8000.0
     assert rec["frac"] == pytest.approx(rec["achieved"] / 8000.0)
     # the counter record is used only while the stream's sources are unchanged
-    assert rec["traffic"] in (None, 4_304_260_457)
+    assert rec["traffic"] is None or abs(rec["traffic"] / 4_295_032_832 - 1.0) < 0.01
     rec8 = bench.dominant_roofline(w, {"score_stream_e4m3": {"avg_us": 160.0}}, keys="e4m3")
     assert round(_alg(rec8, 160.0)) == 32 * 65536 * 512 + 32 * 2048 == 1_073_807_360
 
