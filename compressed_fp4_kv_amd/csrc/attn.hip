@@ -20,19 +20,22 @@
 //     channel quarter is first scaled by a power of two that puts its largest
 //     element in [2^13, 2^14), so both parts stay in fp16's normal range; the
 //     partial logits are scaled back exactly.
-// Work split: a workgroup (8 waves, 2 per SIMD) owns one query token, 64
-// heads and a range of 32-key tiles.  Wave w handles heads 32*(w&1).. and
-// channels 128*(w>>1)..; the four channel quarters add their partial logits
-// through LDS in a fixed order, then all run the same softmax and each
-// accumulates its quarter of the output.  A tile is dequantised once into
-// LDS as row-major [key][channel]: it is the A operand of S^T = K Q^T as it
-// stands, and the gfx950 transposed LDS read (ds_read_b64_tr_b16) turns it
-// into the A operand of O^T = V^T P^T.  Main-KV tiles are double-buffered:
-// while the products of tile t read one buffer, tile t+1 is dequantised into
-// the other and tile t+2 is gathered into registers.  S^T leaves each lane
-// with 16 keys of one head, exactly the B-operand layout the P V product
-// needs, so P never leaves registers.  Key-range splits across workgroups
-// are merged by k_attn_combine.
+// Work split: a workgroup (4 waves, one per SIMD) owns one query token, 32
+// heads and a range of 32-key tiles; wave w handles channels 128*w.. of the
+// 32 heads.  The four channel quarters add their partial logits through LDS
+// in a fixed order, then all run the same softmax and each accumulates its
+// quarter of the output.  A wave needs 256 registers per lane (accumulators,
+// the two-part query slice, a tile's K and V^T fragments), so a CU holds two
+// such workgroups; each runs its tile loop on its own, and one's matrix-core
+// chains overlap the other's softmax, dequantisation and barriers.  A tile
+// is dequantised into LDS as row-major [key][channel]: it is the A operand of
+// S^T = K Q^T as it stands, and the gfx950 transposed LDS read
+// (ds_read_b64_tr_b16) turns it into the A operand of O^T = V^T P^T.  One
+// tile buffer (32 KB) per workgroup; the next tile is gathered into
+// registers while the current one is processed.  S^T leaves each lane with
+// 16 keys of one head, exactly the B-operand layout the P V product needs,
+// so P never leaves registers.  Key-range splits across workgroups are
+// merged by k_attn_combine.
 #include <math.h>
 
 #include "common.hpp"
@@ -116,35 +119,34 @@ __device__ __forceinline__ f16x8 as_f16x8(uint32_t w0, uint32_t w1, uint32_t w2,
     return __builtin_bit_cast(f16x8, w);
 }
 
-constexpr int kAttnThreads = 512;   // 8 waves
+constexpr int kAttnThreads = 256;   // 4 waves
+constexpr int kHeadsWG = 32;        // heads per workgroup
+constexpr int kKPT = 8;             // keys per thread of a tile
 constexpr int kXcds = 8;            // XCDs of an MI355X (L2 domains)
 
-// Raw bytes of one tile for one thread: 4 keys x 8 channels (item mapping:
-// channels 8*(thread & 63) .. +8, keys 4*(thread >> 6) .. +4, so consecutive
+// Raw bytes of one tile for one thread: 8 keys x 8 channels (item mapping:
+// channels 8*(thread & 63) .. +8, keys 8*(thread >> 6) .. +8, so consecutive
 // threads write consecutive 16 B of a K row and V rows land 2 banks apart).
-// Main-KV tiles and window tiles keep their bytes in separate registers, so
-// that a gather in flight is never copied (and so never waited for) where the
-// two kinds of tile meet.
 struct RawMain {
-    uint32_t code[4];    // 8 E2M1 codes of key j
-    uint32_t scale[4];   // its E4M3 scale byte
-    uint32_t ok;         // bit j: key j is real
+    uint32_t code[kKPT];    // 8 E2M1 codes of key j
+    uint32_t scale[kKPT];   // its E4M3 scale byte
+    uint32_t ok;            // bit j: key j is real
 };
 struct RawWin {
-    uint2 k[4], v[4];    // 8 E4M3 bytes of K and of V of key j
+    uint2 b[kKPT];   // 8 E4M3 bytes of K (or of V) of key j
     uint32_t ok;
 };
 
-// The main-KV indices of this thread's 4 keys of a tile: from `idxp` (the
+// The main-KV indices of this thread's keys of a tile: from `idxp` (the
 // tile's first slot; slots >= nslots >= 1 are padding).  The loads are
 // unconditional (clamped slot) so that they issue back to back.
-__device__ __forceinline__ void tile_idx(const int32_t* idxp, int nslots, int32_t (&idx)[4]) {
+__device__ __forceinline__ void tile_idx(const int32_t* idxp, int nslots, int32_t (&idx)[kKPT]) {
     const int kq = threadIdx.x >> 6;
-    int32_t v[4];
+    int32_t v[kKPT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = idxp[min(4 * kq + j, nslots - 1)];
+    for (int j = 0; j < kKPT; ++j) v[j] = idxp[min(kKPT * kq + j, nslots - 1)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) idx[j] = 4 * kq + j < nslots ? v[j] : -1;
+    for (int j = 0; j < kKPT; ++j) idx[j] = kKPT * kq + j < nslots ? v[j] : -1;
 }
 
 // Byte range of the main-KV buffer resources: a sequence's rows are read at
@@ -153,60 +155,64 @@ __device__ __forceinline__ void tile_idx(const int32_t* idxp, int nslots, int32_
 constexpr uint32_t kKvRange = 0x80000000u;
 constexpr int kBufFlags = 0x00020000;   // raw 32-bit buffer (gfx9 family)
 
-// Gather of a main-KV tile (issued early; consumed by store_main) through
-// buffer resources based at the sequence's first row: a padding key's offset
-// is out of range, so every load issues back to back with no branch.
+// Gather of a main-KV tile (issued early; consumed by dequant_main) through
+// buffer resources based at the sequence's first row, with no branch and no
+// select: the byte offset of a padding key (index -1, or any index in
+// [-2^23, 0)) wraps to 2^32 minus at most 2^31 and is outside the range,
+// so its load reads 0; a more negative index reads some row of the sequence
+// and is masked by its -inf bias like any padding key.
 __device__ __forceinline__ void fetch_main(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                           const int32_t (&idx)[4], RawMain& r) {
+                                           const int32_t (&idx)[kKPT], RawMain& r) {
     const int c8 = threadIdx.x & 63;
     uint32_t ok = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const bool v = idx[j] >= 0;
-        ok |= (v ? 1u : 0u) << j;
-        const uint32_t oc = v ? (uint32_t)idx[j] * (kD / 2) + 4 * c8 : kKvRange;
-        const uint32_t os = v ? (uint32_t)idx[j] * (kD / 16) + (c8 >> 1) : kKvRange;
+    for (int j = 0; j < kKPT; ++j) {
+        ok |= (idx[j] >= 0 ? 1u : 0u) << j;
+        const uint32_t oc = (uint32_t)idx[j] * (kD / 2) + 4 * c8;
+        const uint32_t os = (uint32_t)idx[j] * (kD / 16) + (c8 >> 1);
         r.code[j] = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, 0);
         r.scale[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
     }
     r.ok = ok;
 }
 
-// Gather of window tile tw (rows 32 tw ..): rows outside [wlo, whi) are
-// masked; rows past the window read its last row instead.
-__device__ __forceinline__ void fetch_win(const uint8_t* swk, const uint8_t* swv, int W, int wlo,
-                                          int whi, int tw, RawWin& r) {
+// Gather of the K (or V) rows of window tile tw (rows 32 tw ..) from sw:
+// rows outside [wlo, whi) are masked; rows past the window read its last
+// row instead.
+__device__ __forceinline__ void fetch_win(const uint8_t* sw, int W, int wlo, int whi, int tw,
+                                          RawWin& r) {
     const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
     uint32_t ok = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int w_ = kTK * tw + 4 * kq + j;
+    for (int j = 0; j < kKPT; ++j) {
+        const int w_ = kTK * tw + kKPT * kq + j;
         ok |= (w_ >= wlo && w_ < whi ? 1u : 0u) << j;
-        const size_t off = (size_t)min(w_, W - 1) * kD + 8 * c8;
-        r.k[j] = *reinterpret_cast<const uint2*>(swk + off);
-        r.v[j] = *reinterpret_cast<const uint2*>(swv + off);
+        r.b[j] = *reinterpret_cast<const uint2*>(sw + (size_t)min(w_, W - 1) * kD + 8 * c8);
     }
     r.ok = ok;
 }
 
-// Writes one thread's 4 keys (fp16 pairs kp[j][x] = channels 2x, 2x+1 of the
+// Writes one thread's 8 keys (fp16 pairs kp[j][x] = channels 2x, 2x+1 of the
 // thread's 8) as rows of a tile buffer (row-major [key][channel]; the 64
 // lanes of a wave fill one 1 KB row per store).
-__device__ __forceinline__ void put_rows(const uint32_t (&kp)[4][4], uint16_t* buf) {
+__device__ __forceinline__ void put_rows(const uint32_t (&kp)[kKPT][4], uint16_t* buf) {
     const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(buf + tile_off(4 * kq + j, c8)) =
+    for (int j = 0; j < kKPT; ++j)
+        *reinterpret_cast<uint4*>(buf + tile_off(kKPT * kq + j, c8)) =
             make_uint4(kp[j][0], kp[j][1], kp[j][2], kp[j][3]);
 }
 
 // The keys' logit bias: 0 for a real key, -inf for padding (entry g holds
 // keys 4g..4g+3).
 __device__ __forceinline__ void put_valid(uint32_t ok, float4* sBias) {
-    if ((threadIdx.x & 63) == 0) {
+    const int lane = threadIdx.x & 63;
+    if (lane < 2) {
         const float ninf = -INFINITY;
-        sBias[threadIdx.x >> 6] = make_float4((ok & 1u) ? 0.f : ninf, (ok & 2u) ? 0.f : ninf,
-                                              (ok & 4u) ? 0.f : ninf, (ok & 8u) ? 0.f : ninf);
+        const uint32_t o = ok >> (4 * lane);
+        sBias[2 * (threadIdx.x >> 6) + lane] =
+            make_float4((o & 1u) ? 0.f : ninf, (o & 2u) ? 0.f : ninf, (o & 4u) ? 0.f : ninf,
+                        (o & 8u) ? 0.f : ninf);
     }
 }
 
@@ -235,17 +241,17 @@ __device__ __forceinline__ void dequant_fp8x8(uint2 w, uint32_t keep, uint32_t (
 
 // Dequantises a main-KV tile to fp16 (K = V).  A padding key's bytes were
 // read as 0 (outside the buffer range), so its row is 0.
-__device__ __forceinline__ void dequant_main(const RawMain& r, uint32_t (&kp)[4][4]) {
+__device__ __forceinline__ void dequant_main(const RawMain& r, uint32_t (&kp)[kKPT][4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dequant_fp4x8(r.code[j], r.scale[j], kp[j]);
+    for (int j = 0; j < kKPT; ++j) dequant_fp4x8(r.code[j], r.scale[j], kp[j]);
 }
 
 // Converts the K or the V half of a window tile (E4M3); rows outside the
 // window become 0 (they are real memory that may hold anything).
-__device__ __forceinline__ void dequant_win(const uint2 (&w)[4], uint32_t ok,
-                                            uint32_t (&kp)[4][4]) {
+__device__ __forceinline__ void dequant_win(const uint2 (&w)[kKPT], uint32_t ok,
+                                            uint32_t (&kp)[kKPT][4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dequant_fp8x8(w[j], 0u - ((ok >> j) & 1u), kp[j]);
+    for (int j = 0; j < kKPT; ++j) dequant_fp8x8(w[j], 0u - ((ok >> j) & 1u), kp[j]);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -263,45 +269,36 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
 // so p <= 2^8 and most tiles skip the rescale of the accumulators.
 constexpr float kRescale = 8.f;
 
-__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
-    // two tile buffers (main-KV: double buffering; window: K and V)
-    __shared__ __attribute__((aligned(16))) uint16_t sKV[2][kTileElems];
-    __shared__ __attribute__((aligned(16))) float4 sS[8][4][64];   // partial logits per wave
-    __shared__ float4 sValid[2][kTK / 4];   // logit bias per key
+__global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sKV[kTileElems];   // one tile
+    __shared__ __attribute__((aligned(16))) float4 sS[4][4][64];   // partial logits per wave
+    __shared__ float4 sValid[kTK / 4];   // logit bias per key
     __shared__ int32_t s_idx[CSA2_MAX_TOPK];
+    __shared__ uint4 sP[2][2][64];        // probabilities: [16-key half][fp16 part][lane]
+    __shared__ float s_tmax[4][kHeadsWG];   // per wave: maximum logit of its keys per head
 
-    // Work item.  Workgroups are dealt to the XCDs round-robin by linear
-    // id; when the (query, 64-head group) units divide evenly among them, all
-    // key-range splits of a unit go to one XCD, so that they share its L2
-    // (each reads the unit's 128 KB query slice); without splits, each XCD
-    // takes a contiguous run of units, so that neighbouring prefill queries
-    // (whose windows overlap in all but one row) share its L2.  Any other
+    // Work item (unit = query-layer row x 32-head group, split).  Workgroups
+    // are dealt to the XCDs round-robin by linear id; when the items divide
+    // evenly among them, each XCD takes a contiguous run of items in (unit,
+    // split) order, so that the layers, head groups and key-range splits of
+    // a query share its L2 (they gather the same FP4 rows) and so do
+    // neighbouring prefill queries (whose windows overlap in all but one row).  Any other
     // count keeps the plain order; the mapping is a bijection either way.
     const int nsp = gridDim.x, nhg = gridDim.y;
-    const int units = nhg * gridDim.z;
-    int split, unit;
-    if (nsp > 1 && units % kXcds == 0) {
-        const int L = blockIdx.x + nsp * (blockIdx.y + nhg * blockIdx.z);
-        const int slot = L / kXcds;
-        split = slot % nsp;
-        unit = L % kXcds + kXcds * (slot / nsp);
-    } else if (nsp == 1 && units % kXcds == 0) {
-        const int L = blockIdx.y + nhg * blockIdx.z;
-        split = 0;
-        unit = (L % kXcds) * (units / kXcds) + L / kXcds;
-    } else {
-        split = blockIdx.x;
-        unit = blockIdx.y + nhg * blockIdx.z;
-    }
-    const int hgrp = unit % nhg, qz = unit / nhg;   // qz = layer * rows_q + query
-    const int layer = qz / a.rows_q, qi = qz - layer * a.rows_q;
+    const long items = (long)nsp * nhg * gridDim.z;
+    const int L = blockIdx.x + nsp * (blockIdx.y + nhg * blockIdx.z);
+    const int item = items % kXcds == 0 ? (int)((L % kXcds) * (items / kXcds) + L / kXcds) : L;
+    const int split = item % nsp, unit = item / nsp;
+    // units run query-major (query, layer, head group), so that the layers of
+    // a decode query, which gather the same FP4 rows, share an XCD's L2
+    const int hgrp = unit % nhg, qq = unit / nhg;   // qq = query * nlayers + layer
+    const int qi = qq / a.nlayers, layer = qq - qi * a.nlayers;
+    const int qz = layer * a.rows_q + qi;           // row of the split partials (layer-major)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hh = lane >> 5, l32 = lane & 31;      // lane half, lane in half
-    const int hg = wave & 1, cq = wave >> 1;         // head group, channel quarter
-    const int h = hgrp * 64 + hg * 32 + l32;         // this lane's head
+    const int h = hgrp * kHeadsWG + l32;             // this lane's head
     const bool hvalid = h < a.H;
-    const bool active = hgrp * 64 + hg * 32 < a.H;   // wave-uniform
-    const int cbase = 128 * cq;
+    const int cbase = 128 * wave;                    // this wave's channel quarter
 
     int64_t row0 = 0;   // first main-KV row of this query's sequence
     int wlo = 0, whi = 0;
@@ -328,23 +325,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         (void*)(a.kv_codes + row0 * (kD / 2)), (short)0, (int)kKvRange, kBufFlags);
     const __amdgpu_buffer_rsrc_t rscale = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.kv_scales + row0 * (kD / 16)), (short)0, (int)kKvRange, kBufFlags);
-    // Prologue, in issue order: the first two tiles' indices, the query slice
-    // (16 loads per lane), the split's index staging; then the first two
-    // gathers once their indices are in.
-    RawMain rm0, rm;   // first tile (prologue only); the tile after the current one
-    RawWin rw;
+    // Prologue, in issue order: the first tile's indices, the query slice
+    // (16 loads per lane), the split's index staging; then the first gather
+    // once its indices are in.
+    RawMain rm;   // raw bytes of the next main-KV tile
+    RawWin rk, rv;   // raw bytes of a window tile's K and V rows
     const int nslot = kTK * (tm - t0);
     // the query's Top-K row as a buffer resource: slots past topk read 0
     // (and are masked), so no prologue load sits under a branch
     const __amdgpu_buffer_rsrc_t ridx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)qidx, (short)0, a.topk * 4, kBufFlags);
     const int kq = threadIdx.x >> 6;
-    int32_t idx0[4], idx1[4];   // this thread's slots of the first two tiles
+    int32_t idx0[kKPT];   // this thread's slots of the first tile
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        idx0[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, (kTK * t0 + 4 * kq + j) * 4, 0, 0);
-        idx1[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, (kTK * (t0 + 1) + 4 * kq + j) * 4, 0, 0);
-    }
+    for (int j = 0; j < kKPT; ++j)
+        idx0[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, (kTK * t0 + kKPT * kq + j) * 4, 0, 0);
     // query slice in two fp16 parts after a power-of-two scaling: step s (16
     // channels) of this lane is channels cbase + 16 s + 8 hh .. +8 of head h
     f16x8 q0[8], q1[8];
@@ -359,19 +354,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         // the index values are first used after every query load has issued
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (t0 >= tm || kTK * t0 + 4 * kq + j >= a.topk) idx0[j] = -1;
-            if (t0 + 1 >= tm || kTK * (t0 + 1) + 4 * kq + j >= a.topk) idx1[j] = -1;
-        }
+        for (int j = 0; j < kKPT; ++j)
+            if (t0 >= tm || kTK * t0 + kKPT * kq + j >= a.topk) idx0[j] = -1;
         int32_t stage[CSA2_MAX_TOPK / kAttnThreads];
 #pragma unroll
         for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i)
             stage[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
                 ridx, (kTK * t0 + (int)threadIdx.x + kAttnThreads * i) * 4, 0, 0);
-        // the first two tiles' gathers go out together (a window-only split's
-        // slots are all padding: nothing is read)
-        fetch_main(rcode, rscale, idx0, rm0);
-        fetch_main(rcode, rscale, idx1, rm);
+        // the first tile's gather (a window-only split's slots are all
+        // padding: nothing is read)
+        fetch_main(rcode, rscale, idx0, rm);
 
         // largest magnitude of this head's 128 channels (both lane halves)
         float mx = 0.f;
@@ -420,25 +412,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     const int kr1 = l32 * kKStr + 8 * ((cbase >> 3) + ((2 + hh) ^ ((l32 >> 2) & 3)));
     auto s_issue = [&](const uint16_t* kb) __attribute__((always_inline)) -> f32x16 {
         f32x16 s0 = f32x16{};
-        if (!active) return s0;
-        // every K fragment is requested before the first product (one LDS
-        // round trip per tile): row l32, chunk (cbase >> 3) + 2 st + hh, whose
-        // swizzle splits like the transposed reads' (kr0/kr1 by st & 1)
-        f16x8 ka[8];
+        // the K fragments in two halves of four (registers): row l32, chunk
+        // (cbase >> 3) + 2 st + hh, whose swizzle splits like the transposed
+        // reads' (kr0/kr1 by st & 1)
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
-            ka[st] = *reinterpret_cast<const f16x8*>(kb + ((st & 1) ? kr1 : kr0) +
-                                                     32 * ((st >> 1) ^ (l32 & 3)));
-        __builtin_amdgcn_sched_barrier(0);
+        for (int half = 0; half < 2; ++half) {
+            f16x8 ka[4];
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            s0 = mfma32(ka[st], q0[st], s0);
-            s0 = mfma32(ka[st], q1[st], s0);
+            for (int i = 0; i < 4; ++i) {
+                const int st = 4 * half + i;
+                ka[i] = *reinterpret_cast<const f16x8*>(kb + ((st & 1) ? kr1 : kr0) +
+                                                        32 * ((st >> 1) ^ (l32 & 3)));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s0 = mfma32(ka[i], q0[4 * half + i], s0);
+                s0 = mfma32(ka[i], q1[4 * half + i], s0);
+            }
         }
         return s0;
     };
     auto s_finish = [&](f32x16 s0) __attribute__((always_inline)) {
-        if (!active) return;
         s0 = s0 * qunscale;   // lane l32's column is head h: its own scaling
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
@@ -460,36 +455,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     const int trb1 = (trrow + 8) * kKStr + 8 * ((cbase >> 3) + (tsub ^ (((trrow >> 2) + 2) & 3))) +
                      4 * (lane & 1);
 
-    // Softmax of the tile's logits (sS, published) and O^T += V^T P^T with V
-    // the row-major tile in `vb`.
-    // Softmax of the tile's logits (sS, published) -> the P^T operands.
-    auto softmax = [&](const float4* bias, f16x8 (&pp)[2][2]) __attribute__((always_inline)) {
-        if (!active) return;
-        // full logits: the four channel quarters of this head group, added in
-        // the same order in every wave (every read is unconditional; a padding
-        // key's zero logit gets its -inf bias added, so no branch depends on
-        // LDS data)
-        float z[16];
-        float tm_ = -INFINITY;
+    // Softmax of a tile, split over the four waves: wave w takes keys
+    // 8w .. 8w+7 (its registers' rows 4w .. 4w+3 of S^T), so it reads one
+    // quarter of the partial logits.  tile_max: the full logits of those keys
+    // (the four channel quarters added in a fixed order; a padding key's zero
+    // logit gets its -inf bias, so no branch depends on LDS data) and their
+    // maximum per head, published in s_tmax.  probs (after a barrier): the
+    // tile's maximum per head from the four waves (the same in every wave, so
+    // every wave moves m alike), the lazy rescale, and this wave's
+    // probabilities, split into two fp16 parts and written to sP in the
+    // B-operand layout of the P V products; after another barrier every wave
+    // reads all of them (read_p).
+    auto tile_max = [&](const float4* bias, float (&z)[4]) __attribute__((always_inline)) {
+        const float4 c0 = sS[0][wave][lane], c1 = sS[1][wave][lane];
+        const float4 c2 = sS[2][wave][lane], c3 = sS[3][wave][lane];
+        const float4 bb = bias[2 * wave + hh];   // keys 8 wave + 4 hh + 0..3
+        const float v0[4] = {c0.x, c0.y, c0.z, c0.w}, v1[4] = {c1.x, c1.y, c1.z, c1.w};
+        const float v2[4] = {c2.x, c2.y, c2.z, c2.w}, v3[4] = {c3.x, c3.y, c3.z, c3.w};
+        const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+        float tw = -INFINITY;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const float4 c0 = sS[hg][r4][lane], c1 = sS[hg + 2][r4][lane];
-            const float4 c2 = sS[hg + 4][r4][lane], c3 = sS[hg + 6][r4][lane];
-            const float4 bb = bias[2 * r4 + hh];   // keys 8 r4 + 4 hh + 0..3
-            const float v0[4] = {c0.x, c0.y, c0.z, c0.w}, v1[4] = {c1.x, c1.y, c1.z, c1.w};
-            const float v2[4] = {c2.x, c2.y, c2.z, c2.w}, v3[4] = {c3.x, c3.y, c3.z, c3.w};
-            const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * r4 + i;
-                const float sv = (v0[i] + v1[i]) + (v2[i] + v3[i]);
-                z[r] = fmaf(sv, a.scale_log2, bv[i]);
-                tm_ = fmaxf(tm_, z[r]);
-            }
-            // one group of partial-logit reads in flight at a time (registers)
-            __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i) {
+            z[i] = fmaf((v0[i] + v1[i]) + (v2[i] + v3[i]), a.scale_log2, bv[i]);
+            tw = fmaxf(tw, z[i]);
         }
-        tm_ = fmaxf(tm_, __shfl_xor(tm_, 32));
+        tw = fmaxf(tw, __shfl_xor(tw, 32));
+        if (hh == 0) s_tmax[wave][l32] = tw;
+    };
+    auto probs = [&](const float (&z)[4]) __attribute__((always_inline)) {
+        const float tm_ = fmaxf(fmaxf(s_tmax[0][l32], s_tmax[1][l32]),
+                                fmaxf(s_tmax[2][l32], s_tmax[3][l32]));
         const bool bump = tm_ > m + kRescale;   // true for any finite tm_ while m = -inf
         if (__ballot(bump)) {
             const float mn = bump ? tm_ : m;   // finite where bump
@@ -499,156 +494,126 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             for (int ct = 0; ct < 4; ++ct) o[ct] = o[ct] * alpha;
             m = mn;
         }
-        // P^T operands: MFMA u covers registers 8u..8u+7 (keys 16u + 8(j/4) + 4hh + j%4),
-        // each probability (<= 2^8) split into two fp16 parts.  m = -inf only
-        // while every logit so far is -inf: those give exp2(-inf) = 0.
+        // each probability (<= 2^8) in two fp16 parts.  m = -inf only while
+        // every logit so far is -inf: those give exp2(-inf) = 0.
         const float ms = m == -INFINITY ? 0.f : m;
-        float ps = 0.f;
+        float pv[4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float pv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float zr = z[8 * u + j];
-                // raw v_exp_f32: results below 2^-126 flush to 0 (negligible next
-                // to the running maximum's 1)
-                pv[j] = __builtin_amdgcn_exp2f(zr - ms);
-                ps += pv[j];
-            }
-            uint32_t x0[4], x1[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) split2_pk(pv[2 * j], pv[2 * j + 1], x0[j], x1[j]);
-            pp[u][0] = as_f16x8(x0[0], x0[1], x0[2], x0[3]);
-            pp[u][1] = as_f16x8(x1[0], x1[1], x1[2], x1[3]);
+        for (int i = 0; i < 4; ++i) {
+            // raw v_exp_f32: results below 2^-126 flush to 0 (negligible next
+            // to the running maximum's 1)
+            pv[i] = __builtin_amdgcn_exp2f(z[i] - ms);
         }
-        l += ps;
+        l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        uint32_t x0[2], x1[2];
+        split2_pk(pv[0], pv[1], x0[0], x1[0]);
+        split2_pk(pv[2], pv[3], x0[1], x1[1]);
+        // MFMA u's B operand, element j: key 16u + 8(j/4) + 4hh + j%4; this
+        // wave's keys are u = wave/2, j/4 = wave%2: dwords 2(wave%2) .. +1
+        uint32_t* d0 = reinterpret_cast<uint32_t*>(&sP[wave >> 1][0][lane]) + 2 * (wave & 1);
+        uint32_t* d1 = reinterpret_cast<uint32_t*>(&sP[wave >> 1][1][lane]) + 2 * (wave & 1);
+        *reinterpret_cast<uint2*>(d0) = make_uint2(x0[0], x0[1]);
+        *reinterpret_cast<uint2*>(d1) = make_uint2(x1[0], x1[1]);
+    };
+    auto read_p = [&](f16x8 (&pp)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+                pp[u][part] = __builtin_bit_cast(f16x8, sP[u][part][lane]);
     };
     // O^T += V^T P^T with V the row-major tile in `vb`.
     auto pv_mma = [&](const uint16_t* vb, const f16x8 (&pp)[2][2]) __attribute__((always_inline)) {
-        if (!active) return;
         // O^T[channel cbase + 32 ct + m][head] += V^T P^T over the 32 keys;
         // the A operand's 8 keys are 16u + 4hh + 0..3 and 16u + 8 + 4hh + 0..3.
-        // Every V^T fragment is requested before the first product.
-        f16x8 vv[4][2];
+        // The V^T fragments of one 16-key half are requested before its
+        // products; consecutive products go to different accumulators.
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int u = 0; u < 2; ++u) {
+            f16x8 vv[4];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int ct = 0; ct < 4; ++ct) {
                 const int cto = 32 * (ct ^ trhi);
                 const v4i16 lo = lds_read_tr16(vb + trb0 + 16 * u * kKStr + cto);
                 const v4i16 hi = lds_read_tr16(vb + trb1 + 16 * u * kKStr + cto);
-                vv[ct][u] = __builtin_bit_cast(
+                vv[ct] = __builtin_bit_cast(
                     f16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
                                                                         hi[0], hi[1], hi[2], hi[3]});
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // consecutive products go to different accumulators
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int part = 0; part < 2; ++part) {
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) o[ct] = mfma32(vv[ct][u], pp[u][part], o[ct]);
+                for (int ct = 0; ct < 4; ++ct) o[ct] = mfma32(vv[ct], pp[u][part], o[ct]);
             }
         }
     };
-    auto pv_phase = [&](const uint16_t* vb, const float4* bias) __attribute__((always_inline)) {
-        f16x8 pp[2][2];
-        softmax(bias, pp);
-        pv_mma(vb, pp);
-    };
-
-    // main-KV tiles, double-buffered: tile t lives in sKV[(t - t0) & 1].
-    // Entering step t, the logits of tile t are in sS and tile t+1 is in the
-    // other buffer; step t computes the logits of tile t+1 and the softmax and
-    // P V of tile t, then dequantises tile t+2 while the products finish.
-    if (t0 < tm) {
-        uint32_t kp[4][4];
-        dequant_main(rm0, kp);
-        put_rows(kp, sKV[0]);
-        put_valid(rm0.ok, sValid[0]);
-        __syncthreads();   // tile t0 and the index staging visible
-        const f32x16 s0 = s_issue(sKV[0]);
-        if (t0 + 1 < tm) {   // tile t0+1 into the other buffer; gather of t0+2
-            dequant_main(rm, kp);
-            put_rows(kp, sKV[1]);
-            put_valid(rm.ok, sValid[1]);
-            if (t0 + 2 < tm) {
-                int32_t idx[4];
-                tile_idx(s_idx + 2 * kTK, kTK, idx);
-                fetch_main(rcode, rscale, idx, rm);
-            }
-        }
-        s_finish(s0);
-        __syncthreads();   // logits of t0 and tile t0+1 published
-    }
+    // main-KV tiles through the one buffer, three block barriers per tile:
+    // tile t's bytes are in `rm` when its step starts; they are dequantised
+    // in registers, the gather of tile t+1 goes out, and after the barrier
+    // the tile is written, its logits computed and exchanged, and its softmax
+    // and P V products run.
     for (int t = t0; t < tm; ++t) {
-        const int b = (t - t0) & 1;
-        const bool next = t + 1 < tm, deq = t + 2 < tm;   // uniform
-        f32x16 sn = f32x16{};
+        uint32_t kp[kKPT][4];
+        dequant_main(rm, kp);
+        const uint32_t ok = rm.ok;
+        __syncthreads();   // every read of the previous tile (sKV, sS, sValid) is done
+        put_rows(kp, sKV);
+        put_valid(ok, sValid);
+        if (t + 1 < tm) {   // s_idx was published by the barrier above
+            int32_t idx[kKPT];
+            tile_idx(s_idx + kTK * (t + 1 - t0), kTK, idx);
+            fetch_main(rcode, rscale, idx, rm);
+        }
+        __syncthreads();   // tile t visible
+        s_finish(s_issue(sKV));
+        __syncthreads();   // logits of t published
+        float z[4];
+        tile_max(sValid, z);
+        __syncthreads();   // the waves' maxima published
+        probs(z);
+        __syncthreads();   // probabilities published
         f16x8 pp[2][2];
-        if (next) sn = s_issue(sKV[b ^ 1]);
-        softmax(sValid[b], pp);
-        pv_mma(sKV[b], pp);
-        __syncthreads();   // every read of sS and of tile t is done
-        if (next) s_finish(sn);
-        if (deq) {   // tile t+2 into this buffer (while the P V products run); gather of t+3
-            uint32_t kp[4][4];
-            dequant_main(rm, kp);
-            put_rows(kp, sKV[b]);
-            put_valid(rm.ok, sValid[b]);
-            if (t + 3 < tm) {
-                int32_t idx[4];
-                tile_idx(s_idx + kTK * (t + 3 - t0), kTK, idx);
-                fetch_main(rcode, rscale, idx, rm);
-            }
-        }
-        __syncthreads();   // logits of t+1 and tile t+2 published
+        read_p(pp);
+        pv_mma(sKV, pp);
     }
-    // window tiles: K in sKV[0], V in sKV[1], two block barriers per tile.
-    // Once the logits of tile t are out, nothing reads K(t), so K(t+1) is
-    // written while the P V products of t read V(t); V(t+1) and its mask
-    // follow the second barrier.  The first gather is issued here, so that
-    // the main-KV and window raw buffers are never live together.
+    // window tiles: K, then V, through the same buffer.  K(t+1) is gathered
+    // during the softmax and P V products of t, V(t) while the logits of t
+    // are exchanged (so that no gather is in flight across the S^T chain)
     const int w0 = max(t0, a.ntiles_main);
-    if (w0 < t1) {
-        fetch_win(swk, swv, a.W, wlo, whi, w0 - a.ntiles_main, rw);
-        __syncthreads();   // every LDS read of the main-KV tiles is done
-        {
-            uint32_t kp[4][4];
-            dequant_win(rw.k, rw.ok, kp);
-            put_rows(kp, sKV[0]);
-            dequant_win(rw.v, rw.ok, kp);
-            put_rows(kp, sKV[1]);
-            put_valid(rw.ok, sValid[0]);
-        }
-        if (w0 + 1 < t1) fetch_win(swk, swv, a.W, wlo, whi, w0 + 1 - a.ntiles_main, rw);
-        __syncthreads();   // K, V and the mask of tile w0 visible
-    }
+    if (w0 < t1) fetch_win(swk, a.W, wlo, whi, w0 - a.ntiles_main, rk);
     for (int t = w0; t < t1; ++t) {
-        const bool nxt = t + 1 < t1;   // uniform
-        s_finish(s_issue(sKV[0]));
+        uint32_t kp[kKPT][4];
+        dequant_win(rk.b, rk.ok, kp);
+        const uint32_t ok = rk.ok;
+        __syncthreads();   // every read of the previous tile is done
+        put_rows(kp, sKV);
+        put_valid(ok, sValid);
+        __syncthreads();   // K(t) visible
+        s_finish(s_issue(sKV));
+        fetch_win(swv, a.W, wlo, whi, t - a.ntiles_main, rv);
         __syncthreads();   // logits of t published; every read of K(t) done
-        if (nxt) {
-            uint32_t kp[4][4];
-            dequant_win(rw.k, rw.ok, kp);
-            put_rows(kp, sKV[0]);
-        }
-        pv_phase(sKV[1], sValid[0]);
-        __syncthreads();   // every read of V(t), its logits and mask done; K(t+1) visible
-        if (nxt) {
-            uint32_t vp[4][4];
-            dequant_win(rw.v, rw.ok, vp);
-            put_rows(vp, sKV[1]);
-            put_valid(rw.ok, sValid[0]);
-            if (t + 2 < t1) fetch_win(swk, swv, a.W, wlo, whi, t + 2 - a.ntiles_main, rw);
-        }
-        // V(t+1) and its mask are published by the next tile's first barrier,
-        // before its P V products read them
+        float z[4];
+        tile_max(sValid, z);
+        dequant_win(rv.b, ok, kp);
+        put_rows(kp, sKV);
+        if (t + 1 < t1) fetch_win(swk, a.W, wlo, whi, t + 1 - a.ntiles_main, rk);
+        __syncthreads();   // V(t) and the waves' maxima visible
+        probs(z);
+        __syncthreads();   // probabilities published
+        f16x8 pp[2][2];
+        read_p(pp);
+        pv_mma(sKV, pp);
     }
-    if (!active) return;
-    const float lt = l + __shfl_xor(l, 32);
+    // l holds this lane's keys' share: add the two lane halves, then the
+    // four waves (s_tmax is free: every read of it is behind a barrier)
+    {
+        const float lw = l + __shfl_xor(l, 32);
+        __syncthreads();
+        if (hh == 0) s_tmax[wave][l32] = lw;
+        __syncthreads();
+    }
+    const float lt = (s_tmax[0][l32] + s_tmax[1][l32]) + (s_tmax[2][l32] + s_tmax[3][l32]);
     if (!hvalid) return;
     // lane (hh, head) holds channels cbase + 32 ct + 8 q + 4 hh + 0..3, q = 0..3
     const size_t orow = ((size_t)qi * a.H + h) * kD + cbase + 4 * hh;
@@ -663,7 +628,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
                 *reinterpret_cast<float4*>(out + orow + 32 * ct + 8 * q4) =
                     make_float4(o[ct][4 * q4] * inv, o[ct][4 * q4 + 1] * inv,
                                 o[ct][4 * q4 + 2] * inv, o[ct][4 * q4 + 3] * inv);
-        if (lse && hh == 0 && cq == 0)
+        if (lse && hh == 0 && wave == 0)
             lse[(size_t)qi * a.H + h] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
     } else {
         // partial rows: every layer's rows, layer-major (qz)
@@ -676,7 +641,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             for (int q4 = 0; q4 < 4; ++q4)
                 *reinterpret_cast<float4*>(po + 32 * ct + 8 * q4) =
                     make_float4(o[ct][4 * q4], o[ct][4 * q4 + 1], o[ct][4 * q4 + 2], o[ct][4 * q4 + 3]);
-        if (hh == 0 && cq == 0) {
+        if (hh == 0 && wave == 0) {
             float* pm = a.part_ml + (((size_t)split * rows_all + qz) * a.H + h) * 2;
             pm[0] = m;
             pm[1] = lt;
@@ -694,7 +659,7 @@ constexpr int kMaxSplitRegs = 24;
 struct CombineOut {
     float* out[kMaxLayers];
     float* lse[kMaxLayers];
-    int rows_q;
+    int rows_q, nlayers;
 };
 
 // One workgroup merges HPW heads of one row (HPW x 512 channels, a float4
@@ -705,16 +670,15 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
                                                       const float* __restrict__ part_ml,
                                                       int nsplit, int rows_all, int H,
                                                       CombineOut co) {
-    // (row, head group) of this workgroup: when the attention kernel gave all
-    // splits of a (row, 64-head group) unit to one XCD, the merge of the
-    // unit's heads runs on that XCD too (its partials are in that L2)
-    constexpr int GPU = 64 / HPW;   // head groups of this size per 64 heads
-    int qh0 = blockIdx.x * HPW;     // qz * H + h, qz = layer * co.rows_q + query
-    if (H % 64 == 0 && (rows_all * (H / 64)) % kXcds == 0) {
-        const int L = blockIdx.x, slot = L / kXcds;
-        const int unit = L % kXcds + kXcds * (slot / GPU);   // unit = qz * (H / 64) + group
-        qh0 = unit * 64 + (slot % GPU) * HPW;
-    }
+    // (row, head group) of this workgroup: the attention kernel gives each
+    // XCD a contiguous run of its query-major (query, layer, 32-head group)
+    // units when they divide evenly; the merges take the same contiguous
+    // runs, so that a unit's partials are merged on the XCD whose L2 holds them
+    const int n = gridDim.x, L = blockIdx.x;
+    const int item = n % kXcds == 0 ? (L % kXcds) * (n / kXcds) + L / kXcds : L;
+    const int qq = item * HPW / H, h0 = item * HPW - qq * H;   // qq = query * nlayers + layer
+    const int qi = qq / co.nlayers, lyr = qq - qi * co.nlayers;
+    const int qh0 = (lyr * co.rows_q + qi) * H + h0;   // qz * H + h, qz = layer * rows_q + query
     const size_t stride_o = (size_t)rows_all * H * kD;
     const size_t stride_ml = (size_t)rows_all * H * 2;
     float2 ml[HPW][MAXS];
@@ -798,35 +762,40 @@ struct AttnPlan {
     size_t ws_bytes;
 };
 
-// Key-range splits.  One workgroup fits a CU (its LDS), so a launch runs in
-// rounds of kCUs workgroups; a workgroup costs about kPrologueTiles tiles of
-// fixed latency (index, query and first gathers in flight) plus its tiles;
-// splitting adds the combine launch (about kCombineTiles).  The plan takes the
-// tiles per split with the lowest modelled cost, rounds x (prologue + tiles);
-// a split takes consecutive tiles, main-KV then window ones as a single
-// workgroup runs them (measured before: 64 queries with 5 splits kept apart
-// by kind = 320 workgroups ran in two rounds, 47 us per layer).
+// Key-range splits.  Two workgroups fit a CU (registers: 256 per lane at
+// four waves); a lone workgroup costs about kPrologueTiles tiles of fixed
+// latency (index, query and first gathers in flight) plus its tiles, and a CU
+// runs two together in kPairTenths / 10 of that.  Splitting adds the combine
+// launch (about kCombineTiles).  The plan takes the tiles per split with the
+// lowest modelled cost; a split takes consecutive tiles, main-KV then window
+// ones as a single workgroup runs them.
 constexpr int kCUs = 256;
 constexpr int kPrologueTiles = 3;
 constexpr int kCombineTiles = 2;
+constexpr long kPairTenths = 14;
+
+// Modelled time, in tenths of a lone tile, of `wgs` workgroups of `tiles` tiles.
+long attn_cost(long wgs, int tiles) {
+    const long per_cu = (wgs + kCUs - 1) / kCUs;
+    return ((per_cu / 2) * kPairTenths + (per_cu % 2) * 10) * (kPrologueTiles + tiles);
+}
 
 int plan_attn(int rows_q, int H, int D, int topk, int W, bool allow_split, AttnPlan* p) {
     if (rows_q < 0 || H <= 0 || D <= 0 || topk < 0 || W < 0) return CSA2_ERR_SHAPE;
     if (D != kD || H % 16 != 0 || topk > CSA2_MAX_TOPK || W > 1024 || rows_q > 65535)
         return CSA2_ERR_UNSUPPORTED;
-    p->hgroups = (H + 63) / 64;
+    p->hgroups = (H + kHeadsWG - 1) / kHeadsWG;
     p->ntiles_main = (topk + kTK - 1) / kTK;
     p->ntiles = p->ntiles_main + (W + kTK - 1) / kTK;
     const long units = (long)rows_q * p->hgroups;
     int nsplit = 1;
     p->tps = p->ntiles;
     if (allow_split && p->ntiles > 1) {
-        long best = ((units + kCUs - 1) / kCUs) * (kPrologueTiles + p->ntiles);   // no split
+        long best = attn_cost(units, p->ntiles);   // no split
         for (int tps = 1; tps < p->ntiles; ++tps) {
             const int ns = (p->ntiles + tps - 1) / tps;
             if (ns < 2 || ns > kMaxSplitRegs) continue;
-            const long rounds = (units * ns + kCUs - 1) / kCUs;
-            const long cost = rounds * (kPrologueTiles + tps) + kCombineTiles;
+            const long cost = attn_cost(units * ns, tps) + 10 * kCombineTiles;
             if (cost < best) {
                 best = cost;
                 nsplit = ns;
@@ -865,6 +834,7 @@ int launch_attn(AttnArgs a, const AttnPlan& pl, int rows_all, void* ws, hipStrea
         co.lse[l] = a.lse[l];
     }
     co.rows_q = a.rows_q;
+    co.nlayers = a.nlayers;
     // four heads per workgroup when every partial of four fits the registers
     if (pl.nsplit <= 4 && a.H % 4 == 0)
         return CSA2_LAUNCH("attn_combine", (k_attn_combine<4, 4>), dim3(rows_q * a.H / 4),
