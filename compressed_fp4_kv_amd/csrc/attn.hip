@@ -22,19 +22,21 @@
 //     partial logits are scaled back exactly.
 // Work split: a workgroup (4 waves, one per SIMD) owns one query token, 32
 // heads and a range of 32-key tiles; wave w handles channels 128*w.. of the
-// 32 heads.  The four channel quarters add their partial logits through LDS
-// in a fixed order, then all run the same softmax and each accumulates its
-// quarter of the output.  A wave needs 256 registers per lane (accumulators,
-// the two-part query slice, a tile's K and V^T fragments), so a CU holds two
-// such workgroups; each runs its tile loop on its own, and one's matrix-core
-// chains overlap the other's softmax, dequantisation and barriers.  A tile
-// is dequantised into LDS as row-major [key][channel]: it is the A operand of
-// S^T = K Q^T as it stands, and the gfx950 transposed LDS read
-// (ds_read_b64_tr_b16) turns it into the A operand of O^T = V^T P^T.  One
-// tile buffer (32 KB) per workgroup; the next tile is gathered into
-// registers while the current one is processed.  S^T leaves each lane with
-// 16 keys of one head, exactly the B-operand layout the P V product needs,
-// so P never leaves registers.  Key-range splits across workgroups are
+// 32 heads.  Each wave gathers and dequantises only its own channel quarter
+// of a tile (lane = key of the tile and a 64-channel half of the quarter):
+// the fp16 key fragments feed S^T = K Q^T straight from registers as its A
+// operand, and are also written to the wave's private quarter tile in LDS,
+// row-major [key][channel], from which the gfx950 transposed LDS read
+// (ds_read_b64_tr_b16) forms the A operand of O^T = V^T P^T.  The four
+// channel quarters add their partial logits through LDS in a fixed order,
+// each wave runs the softmax of 8 of the 32 keys, and every wave
+// accumulates its quarter of the output from all 32 probabilities: three
+// block barriers per tile.  The next tile's bytes are gathered into
+// registers while the current one is processed.  A wave needs 256 registers
+// per lane (accumulators, the two-part query slice, a tile's gathered bytes
+// and key fragments), so a CU holds two such workgroups; each runs its tile
+// loop on its own, and one's matrix-core chains overlap the other's softmax,
+// dequantisation and barriers.  Key-range splits across workgroups are
 // merged by k_attn_combine.
 #include <math.h>
 
@@ -50,19 +52,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 512;
 constexpr int kTK = 32;             // keys per tile
-constexpr int kKStr = kD;           // LDS row stride of a tile (fp16 elements): 1 KB
-constexpr int kTileElems = kTK * kKStr;
 
-// Tile rows are not padded; instead 16-byte chunk ch of row `row` is stored
-// at chunk ch ^ tile_swz(row) of that row.  The 16 rows one K-operand read
-// instruction takes (one column chunk each) then cover all 64 banks, and the
-// 4 rows each 32-lane half of a transposed V read touches fall in 4 distinct
-// 16-bank windows: both reads are free of bank conflicts (a 16-element pad
-// served the first but gave the second 2-way conflicts).
+// A quarter tile's rows (256 B, 16 chunks of 8 fp16) are not padded;
+// instead chunk ch of row `row` is stored at chunk ch ^ tile_swz(row) of
+// that row, so that the 4 rows each 32-lane half of a transposed V read
+// touches fall in 4 distinct 16-bank windows (free of bank conflicts).
 __device__ __forceinline__ int tile_swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
-__device__ __forceinline__ int tile_off(int row, int ch) {
-    return row * kKStr + 8 * (ch ^ tile_swz(row));
-}
 constexpr float kLn2 = 0.69314718055994530942f;
 
 constexpr int kMaxLayers = 8;   // layers of one decode call (a layer group)
@@ -121,33 +116,22 @@ __device__ __forceinline__ f16x8 as_f16x8(uint32_t w0, uint32_t w1, uint32_t w2,
 
 constexpr int kAttnThreads = 256;   // 4 waves
 constexpr int kHeadsWG = 32;        // heads per workgroup
-constexpr int kKPT = 8;             // keys per thread of a tile
 constexpr int kXcds = 8;            // XCDs of an MI355X (L2 domains)
 
-// Raw bytes of one tile for one thread: 8 keys x 8 channels (item mapping:
-// channels 8*(thread & 63) .. +8, keys 8*(thread >> 6) .. +8, so consecutive
-// threads write consecutive 16 B of a K row and V rows land 2 banks apart).
-struct RawMain {
-    uint32_t code[kKPT];    // 8 E2M1 codes of key j
-    uint32_t scale[kKPT];   // its E4M3 scale byte
-    uint32_t ok;            // bit j: key j is real
-};
-struct RawWin {
-    uint2 b[kKPT];   // 8 E4M3 bytes of K (or of V) of key j
-    uint32_t ok;
-};
+constexpr int kQStr = 128;   // row stride (fp16 elements) of a wave's quarter tile: 256 B
 
-// The main-KV indices of this thread's keys of a tile: from `idxp` (the
-// tile's first slot; slots >= nslots >= 1 are padding).  The loads are
-// unconditional (clamped slot) so that they issue back to back.
-__device__ __forceinline__ void tile_idx(const int32_t* idxp, int nslots, int32_t (&idx)[kKPT]) {
-    const int kq = threadIdx.x >> 6;
-    int32_t v[kKPT];
-#pragma unroll
-    for (int j = 0; j < kKPT; ++j) v[j] = idxp[min(kKPT * kq + j, nslots - 1)];
-#pragma unroll
-    for (int j = 0; j < kKPT; ++j) idx[j] = kKPT * kq + j < nslots ? v[j] : -1;
-}
+// Main-KV bytes of one lane for a tile: its key (l32 of the tile) and its
+// 64 channels 128 wave + 64 hh .. +64: 32 bytes of E2M1 codes (two 16-byte
+// loads) and the 4 E4M3 scales of those channels (one 4-byte load).
+struct RawQ {
+    uint4 code[2];    // byte b holds channels 2b, 2b+1 of the 64
+    uint32_t scale;   // byte g: scale of channels 16 g .. 16 g + 15 of the 64
+};
+// Window bytes of one lane for a tile: 64 E4M3 bytes of K (or of V) of its
+// key row, the same 64 channels.
+struct RawWQ {
+    uint4 b[4];
+};
 
 // Byte range of the main-KV buffer resources: a sequence's rows are read at
 // offsets below 2^31 (fewer than 2^23 entries per sequence); a larger offset
@@ -155,65 +139,40 @@ __device__ __forceinline__ void tile_idx(const int32_t* idxp, int nslots, int32_
 constexpr uint32_t kKvRange = 0x80000000u;
 constexpr int kBufFlags = 0x00020000;   // raw 32-bit buffer (gfx9 family)
 
-// Gather of a main-KV tile (issued early; consumed by dequant_main) through
-// buffer resources based at the sequence's first row, with no branch and no
-// select: the byte offset of a padding key (index -1, or any index in
-// [-2^23, 0)) wraps to 2^32 minus at most 2^31 and is outside the range,
-// so its load reads 0; a more negative index reads some row of the sequence
-// and is masked by its -inf bias like any padding key.
-__device__ __forceinline__ void fetch_main(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                           const int32_t (&idx)[kKPT], RawMain& r) {
-    const int c8 = threadIdx.x & 63;
-    uint32_t ok = 0;
-#pragma unroll
-    for (int j = 0; j < kKPT; ++j) {
-        ok |= (idx[j] >= 0 ? 1u : 0u) << j;
-        const uint32_t oc = (uint32_t)idx[j] * (kD / 2) + 4 * c8;
-        const uint32_t os = (uint32_t)idx[j] * (kD / 16) + (c8 >> 1);
-        r.code[j] = __builtin_amdgcn_raw_buffer_load_b32(rc, oc, 0, 0);
-        r.scale[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
-    }
-    r.ok = ok;
+// Gather of a lane's main-KV bytes (issued early; consumed by dequant_q)
+// through buffer resources based at the sequence's first row, with no
+// branch and no select: the byte offset of a padding key (index -1, or any
+// index in [-2^23, 0)) wraps to 2^32 minus at most 2^31 and is outside the
+// range, so its loads read 0; a more negative index reads some row of the
+// sequence and is masked like any padding key.
+__device__ __forceinline__ void fetch_q(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                        int32_t idx, int wave, int hh, RawQ& r) {
+    const uint32_t oc = (uint32_t)idx * (kD / 2) + 64 * wave + 32 * hh;
+    r.code[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 0));
+    r.code[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc + 16, 0, 0));
+    r.scale = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)idx * (kD / 16) + 8 * wave + 4 * hh,
+                                                   0, 0);
 }
 
-// Gather of the K (or V) rows of window tile tw (rows 32 tw ..) from sw:
-// rows outside [wlo, whi) are masked; rows past the window read its last
-// row instead.
-__device__ __forceinline__ void fetch_win(const uint8_t* sw, int W, int wlo, int whi, int tw,
-                                          RawWin& r) {
-    const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
-    uint32_t ok = 0;
+// Gather of a lane's window bytes of tile tw (row 32 tw + l32) from sw; a
+// row past the window reads its last row instead (and is masked).
+__device__ __forceinline__ void fetch_wq(const uint8_t* sw, int W, int tw, int wave, int hh,
+                                         RawWQ& r) {
+    const int row = min(kTK * tw + (int)(threadIdx.x & 31), W - 1);
+    const uint8_t* p = sw + (size_t)row * kD + 128 * wave + 64 * hh;
 #pragma unroll
-    for (int j = 0; j < kKPT; ++j) {
-        const int w_ = kTK * tw + kKPT * kq + j;
-        ok |= (w_ >= wlo && w_ < whi ? 1u : 0u) << j;
-        r.b[j] = *reinterpret_cast<const uint2*>(sw + (size_t)min(w_, W - 1) * kD + 8 * c8);
-    }
-    r.ok = ok;
+    for (int i = 0; i < 4; ++i) r.b[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
 }
 
-// Writes one thread's 8 keys (fp16 pairs kp[j][x] = channels 2x, 2x+1 of the
-// thread's 8) as rows of a tile buffer (row-major [key][channel]; the 64
-// lanes of a wave fill one 1 KB row per store).
-__device__ __forceinline__ void put_rows(const uint32_t (&kp)[kKPT][4], uint16_t* buf) {
-    const int c8 = threadIdx.x & 63, kq = threadIdx.x >> 6;
-#pragma unroll
-    for (int j = 0; j < kKPT; ++j)
-        *reinterpret_cast<uint4*>(buf + tile_off(kKPT * kq + j, c8)) =
-            make_uint4(kp[j][0], kp[j][1], kp[j][2], kp[j][3]);
+// Writes fragment s of a lane's key (channels 8 s .. +8 of its 64) into its
+// row of a wave's quarter tile: chunk 8 hh + s of row l32, swizzled.
+__device__ __forceinline__ void put_q1(const f16x8& f, int s, uint16_t* vt) {
+    const int l32 = threadIdx.x & 31, hh = (threadIdx.x >> 5) & 1;
+    *reinterpret_cast<f16x8*>(vt + l32 * kQStr + 8 * ((8 * hh + s) ^ tile_swz(l32))) = f;
 }
-
-// The keys' logit bias: 0 for a real key, -inf for padding (entry g holds
-// keys 4g..4g+3).
-__device__ __forceinline__ void put_valid(uint32_t ok, float4* sBias) {
-    const int lane = threadIdx.x & 63;
-    if (lane < 2) {
-        const float ninf = -INFINITY;
-        const uint32_t o = ok >> (4 * lane);
-        sBias[2 * (threadIdx.x >> 6) + lane] =
-            make_float4((o & 1u) ? 0.f : ninf, (o & 2u) ? 0.f : ninf, (o & 4u) ? 0.f : ninf,
-                        (o & 8u) ? 0.f : ninf);
-    }
+__device__ __forceinline__ void put_q(const f16x8 (&kf)[8], uint16_t* vt) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) put_q1(kf[s], s, vt);
 }
 
 // Eight E2M1 codes (dword w; byte x holds channels 2x, 2x+1, low nibble
@@ -239,19 +198,29 @@ __device__ __forceinline__ void dequant_fp8x8(uint2 w, uint32_t keep, uint32_t (
     o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true)) & keep;
 }
 
-// Dequantises a main-KV tile to fp16 (K = V).  A padding key's bytes were
-// read as 0 (outside the buffer range), so its row is 0.
-__device__ __forceinline__ void dequant_main(const RawMain& r, uint32_t (&kp)[kKPT][4]) {
+// A lane's main-KV bytes as its 8 key fragments (fp16, exact: K = V).  A
+// padding key's bytes were read as 0 (outside the buffer range), so its
+// fragments are 0.
+__device__ __forceinline__ void dequant_q(const RawQ& r, f16x8 (&kf)[8]) {
+    const uint32_t w[8] = {r.code[0].x, r.code[0].y, r.code[0].z, r.code[0].w,
+                           r.code[1].x, r.code[1].y, r.code[1].z, r.code[1].w};
 #pragma unroll
-    for (int j = 0; j < kKPT; ++j) dequant_fp4x8(r.code[j], r.scale[j], kp[j]);
+    for (int s = 0; s < 8; ++s) {
+        uint32_t o[4];
+        dequant_fp4x8(w[s], (r.scale >> (8 * (s >> 1))) & 0xffu, o);
+        kf[s] = as_f16x8(o[0], o[1], o[2], o[3]);
+    }
 }
 
-// Converts the K or the V half of a window tile (E4M3); rows outside the
-// window become 0 (they are real memory that may hold anything).
-__device__ __forceinline__ void dequant_win(const uint2 (&w)[kKPT], uint32_t ok,
-                                            uint32_t (&kp)[kKPT][4]) {
-#pragma unroll
-    for (int j = 0; j < kKPT; ++j) dequant_fp8x8(w[j], 0u - ((ok >> j) & 1u), kp[j]);
+// Fragment s (channels 8 s .. +8 of the lane's 64) of a lane's window bytes
+// (E4M3) in fp16; a row outside the window becomes 0 (it is real memory
+// that may hold anything): keep is all ones or zero.
+__device__ __forceinline__ f16x8 dequant_wq(const RawWQ& r, uint32_t keep, int s) {
+    const uint4 b = r.b[s >> 1];
+    const uint2 w = (s & 1) ? make_uint2(b.z, b.w) : make_uint2(b.x, b.y);
+    uint32_t o[4];
+    dequant_fp8x8(w, keep, o);
+    return as_f16x8(o[0], o[1], o[2], o[3]);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -275,10 +244,11 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
 constexpr float kRescale = 8.f;
 
 __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sKV[kTileElems];   // one tile
+    // each wave's own quarter of a tile (32 keys x its 128 channels, fp16,
+    // row-major [key][channel], rows of 256 B): the V^T operand of its P V
+    // products through the transposed LDS read
+    __shared__ __attribute__((aligned(16))) uint16_t sV[4][kTK * kQStr];
     __shared__ __attribute__((aligned(16))) float4 sS[4][4][64];   // partial logits per wave
-    __shared__ float4 sValid[kTK / 4];   // logit bias per key
-    __shared__ int32_t s_idx[CSA2_MAX_TOPK];
     __shared__ uint4 sP[2][2][64];        // probabilities: [16-key half][fp16 part][lane]
     __shared__ float s_tmax[4][kHeadsWG];   // per wave: maximum logit of its keys per head
 
@@ -330,45 +300,34 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
         (void*)(a.kv_codes + row0 * (kD / 2)), (short)0, (int)kKvRange, kBufFlags);
     const __amdgpu_buffer_rsrc_t rscale = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.kv_scales + row0 * (kD / 16)), (short)0, (int)kKvRange, kBufFlags);
-    // Prologue, in issue order: the first tile's indices, the query slice
-    // (16 loads per lane), the split's index staging; then the first gather
-    // once its indices are in.
-    RawMain rm;   // raw bytes of the next main-KV tile
-    RawWin rk, rv;   // raw bytes of a window tile's K and V rows
-    const int nslot = kTK * (tm - t0);
-    // the query's Top-K row as a buffer resource: slots past topk read 0
-    // (and are masked), so no prologue load sits under a branch
+    // the query's Top-K row as a buffer resource: slots past topk read 0 and
+    // are masked to -1
     const __amdgpu_buffer_rsrc_t ridx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)qidx, (short)0, a.topk * 4, kBufFlags);
-    const int kq = threadIdx.x >> 6;
-    int32_t idx0[kKPT];   // this thread's slots of the first tile
-#pragma unroll
-    for (int j = 0; j < kKPT; ++j)
-        idx0[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, (kTK * t0 + kKPT * kq + j) * 4, 0, 0);
-    // query slice in two fp16 parts after a power-of-two scaling: step s (16
-    // channels) of this lane is channels cbase + 16 s + 8 hh .. +8 of head h
+    // the entry of this lane's key (key l32) of main tile t, -1 for padding
+    auto key_idx = [&](int t) __attribute__((always_inline)) -> int32_t {
+        const int slot = kTK * t + l32;
+        const int32_t v = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, slot * 4, 0, 0);
+        return (t < tm && slot < a.topk) ? v : -1;
+    };
+    // Prologue, in issue order: the first two tiles' key entries, the query
+    // slice (16 loads per lane), then the first gather once its entry is in.
+    int32_t idx_t = key_idx(t0), idx_n = key_idx(t0 + 1);
+    RawQ rq;   // bytes of the next main-KV tile (this lane's key and channels)
+    // query slice in two fp16 parts after a power-of-two scaling: MFMA step
+    // s of this lane is channels cbase + 64 hh + 8 s .. +8 of head h (the
+    // key fragments take the same channels)
     f16x8 q0[8], q1[8];
     float qunscale;   // exact inverse of the scaling, applied to the partial logits
     {
-        const float* qp = a.q[layer] + ((size_t)qi * a.H + (hvalid ? h : 0)) * kD + cbase + 8 * hh;
+        const float* qp = a.q[layer] + ((size_t)qi * a.H + (hvalid ? h : 0)) * kD + cbase + 64 * hh;
         // head 0 stands in for a padding head (zeroed below)
         float4 xq[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            xq[i] = *reinterpret_cast<const float4*>(qp + 16 * (i >> 1) + 4 * (i & 1));
-        // the index values are first used after every query load has issued
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < kKPT; ++j)
-            if (t0 >= tm || kTK * t0 + kKPT * kq + j >= a.topk) idx0[j] = -1;
-        int32_t stage[CSA2_MAX_TOPK / kAttnThreads];
-#pragma unroll
-        for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i)
-            stage[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
-                ridx, (kTK * t0 + (int)threadIdx.x + kAttnThreads * i) * 4, 0, 0);
-        // the first tile's gather (a window-only split's slots are all
+        for (int i = 0; i < 16; ++i) xq[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+        // the first tile's gather (a window-only split's keys are all
         // padding: nothing is read)
-        fetch_main(rcode, rscale, idx0, rm);
+        fetch_q(rcode, rscale, idx_t, wave, hh, rq);
 
         // largest magnitude of this head's 128 channels (both lane halves)
         float mx = 0.f;
@@ -395,50 +354,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
             q0[st] = as_f16x8(a0[0], a0[1], a0[2], a0[3]);
             q1[st] = as_f16x8(a1[0], a1[1], a1[2], a1[3]);
         }
-        if (t0 < tm) {
-#pragma unroll
-            for (int i = 0; i < CSA2_MAX_TOPK / kAttnThreads; ++i) {
-                const int k = threadIdx.x + kAttnThreads * i;
-                if (k < nslot) s_idx[k] = kTK * t0 + k < a.topk ? stage[i] : -1;
-            }
-        }
     }
     f32x16 o[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) o[ct] = f32x16{};
     float m = -INFINITY, l = 0.f;
+    uint16_t* const vt = sV[wave];   // this wave's quarter tile
 
-    // S^T of the tile in `kb` over this wave's 128 channels, to sS (the small
-    // query part is folded into the same chain, after the main part of each
-    // step).  Published by the caller's next barrier.
-    // (split in two so that independent work can run while the matrix core
-    // finishes the chain)
-    const int kr0 = l32 * kKStr + 8 * ((cbase >> 3) + (hh ^ ((l32 >> 2) & 3)));
-    const int kr1 = l32 * kKStr + 8 * ((cbase >> 3) + ((2 + hh) ^ ((l32 >> 2) & 3)));
-    auto s_issue = [&](const uint16_t* kb) __attribute__((always_inline)) -> f32x16 {
+    // S^T of a tile over this wave's 128 channels from its key fragments in
+    // registers, scaled back and published in sS (by the caller's barrier).
+    auto s_chain = [&](auto&& frag) __attribute__((always_inline)) {
         f32x16 s0 = f32x16{};
-        // the K fragments in two halves of four (registers): row l32, chunk
-        // (cbase >> 3) + 2 st + hh, whose swizzle splits like the transposed
-        // reads' (kr0/kr1 by st & 1)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            f16x8 ka[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int st = 4 * half + i;
-                ka[i] = *reinterpret_cast<const f16x8*>(kb + ((st & 1) ? kr1 : kr0) +
-                                                        32 * ((st >> 1) ^ (l32 & 3)));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s0 = mfma32(ka[i], q0[4 * half + i], s0);
-                s0 = mfma32(ka[i], q1[4 * half + i], s0);
-            }
+        for (int st = 0; st < 8; ++st) {
+            const f16x8 f = frag(st);
+            s0 = mfma32(f, q0[st], s0);
+            s0 = mfma32(f, q1[st], s0);
         }
-        return s0;
-    };
-    auto s_finish = [&](f32x16 s0) __attribute__((always_inline)) {
         s0 = s0 * qunscale;   // lane l32's column is head h: its own scaling
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
@@ -446,42 +378,40 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
     };
 
     // Lane part of the transposed reads of V: lane l = 16 g + 4 b + c points
-    // at key row 4 (g >> 1) + b, channels cbase + 16 (g & 1) + 4 c .. +3, so
-    // that lane l receives channel cbase + (l & 31) of 4 consecutive keys
-    // (row, 16-byte chunk and the half of it).
-    // In tile_off terms: row 16 u + 8 hi + trrow, chunk (cbase >> 3) + 4 ct +
-    // tsub; since tile_swz(row) = 4 (row & 3) + ((row >> 2) & 3), the chunk's
-    // swizzle splits into tsub ^ ((row >> 2) & 3), which depends on hi only,
-    // and ct ^ (row & 3), which depends on the lane only.
+    // at key row 4 (g >> 1) + b, channels 16 (g & 1) + 4 c .. +3 of a
+    // 32-channel block of the quarter, so that lane l receives channel
+    // (l & 31) of the block for 4 consecutive keys.  In quarter-tile terms:
+    // row 16 u + 8 hi + trrow, chunk 4 ct + tsub; since tile_swz(row) = 4
+    // (row & 3) + ((row >> 2) & 3), the chunk's swizzle splits into tsub ^
+    // ((row >> 2) & 3), which depends on hi only, and ct ^ (row & 3), which
+    // depends on the lane only.
     const int trrow = 4 * (lane >> 5) + ((lane >> 2) & 3);
     const int tsub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int trhi = (lane >> 2) & 3;   // row & 3
-    const int trb0 = trrow * kKStr + 8 * ((cbase >> 3) + (tsub ^ ((trrow >> 2) & 3))) + 4 * (lane & 1);
-    const int trb1 = (trrow + 8) * kKStr + 8 * ((cbase >> 3) + (tsub ^ (((trrow >> 2) + 2) & 3))) +
-                     4 * (lane & 1);
+    const int trb0 = trrow * kQStr + 8 * (tsub ^ ((trrow >> 2) & 3)) + 4 * (lane & 1);
+    const int trb1 = (trrow + 8) * kQStr + 8 * (tsub ^ (((trrow >> 2) + 2) & 3)) + 4 * (lane & 1);
 
     // Softmax of a tile, split over the four waves: wave w takes keys
     // 8w .. 8w+7 (its registers' rows 4w .. 4w+3 of S^T), so it reads one
     // quarter of the partial logits.  tile_max: the full logits of those keys
-    // (the four channel quarters added in a fixed order; a padding key's zero
-    // logit gets its -inf bias, so no branch depends on LDS data) and their
-    // maximum per head, published in s_tmax.  probs (after a barrier): the
-    // tile's maximum per head from the four waves (the same in every wave, so
-    // every wave moves m alike), the lazy rescale, and this wave's
-    // probabilities, split into two fp16 parts and written to sP in the
-    // B-operand layout of the P V products; after another barrier every wave
-    // reads all of them (read_p).
-    auto tile_max = [&](const float4* bias, float (&z)[4]) __attribute__((always_inline)) {
+    // (the four channel quarters added in a fixed order; a padding key's
+    // logit is -inf by the tile's key mask) and their maximum per head,
+    // published in s_tmax.  probs (after a barrier): the tile's maximum per
+    // head from the four waves (the same in every wave, so every wave moves m
+    // alike), the lazy rescale, and this wave's probabilities, split into two
+    // fp16 parts and written to sP in the B-operand layout of the P V
+    // products; after another barrier every wave reads all of them (read_p).
+    auto tile_max = [&](uint64_t vmask, float (&z)[4]) __attribute__((always_inline)) {
         const float4 c0 = sS[0][wave][lane], c1 = sS[1][wave][lane];
         const float4 c2 = sS[2][wave][lane], c3 = sS[3][wave][lane];
-        const float4 bb = bias[2 * wave + hh];   // keys 8 wave + 4 hh + 0..3
         const float v0[4] = {c0.x, c0.y, c0.z, c0.w}, v1[4] = {c1.x, c1.y, c1.z, c1.w};
         const float v2[4] = {c2.x, c2.y, c2.z, c2.w}, v3[4] = {c3.x, c3.y, c3.z, c3.w};
-        const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+        const uint32_t kbits = (uint32_t)(vmask >> (8 * wave + 4 * hh));   // keys 8 wave + 4 hh + i
         float tw = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = fmaf((v0[i] + v1[i]) + (v2[i] + v3[i]), a.scale_log2, bv[i]);
+            const float zz = ((v0[i] + v1[i]) + (v2[i] + v3[i])) * a.scale_log2;
+            z[i] = (kbits >> i) & 1u ? zz : -INFINITY;
             tw = fmaxf(tw, z[i]);
         }
         tw = fmaxf(tw, __shfl_xor(tw, 32));
@@ -527,7 +457,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
             for (int part = 0; part < 2; ++part)
                 pp[u][part] = __builtin_bit_cast(f16x8, sP[u][part][lane]);
     };
-    // O^T += V^T P^T with V the row-major tile in `vb`.
+    // O^T += V^T P^T with V this wave's row-major quarter tile in `vb`.
     auto pv_mma = [&](const uint16_t* vb, const f16x8 (&pp)[2][2]) __attribute__((always_inline)) {
         // O^T[channel cbase + 32 ct + m][head] += V^T P^T over the 32 keys;
         // the A operand's 8 keys are 16u + 4hh + 0..3 and 16u + 8 + 4hh + 0..3.
@@ -539,8 +469,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 const int cto = 32 * (ct ^ trhi);
-                const v4i16 lo = lds_read_tr16(vb + trb0 + 16 * u * kKStr + cto);
-                const v4i16 hi = lds_read_tr16(vb + trb1 + 16 * u * kKStr + cto);
+                const v4i16 lo = lds_read_tr16(vb + trb0 + 16 * u * kQStr + cto);
+                const v4i16 hi = lds_read_tr16(vb + trb1 + 16 * u * kQStr + cto);
                 vv[ct] = __builtin_bit_cast(
                     f16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
                                                                         hi[0], hi[1], hi[2], hi[3]});
@@ -553,70 +483,70 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
             }
         }
     };
-    // main-KV tiles through the one buffer, three block barriers per tile:
-    // tile t's bytes are in `rm` when its step starts; they are dequantised
-    // in registers, the gather of tile t+1 goes out, and after the barrier
-    // the tile is written, its logits computed and exchanged, and its softmax
-    // and P V products run.
+    // Main-KV tiles: three block barriers per tile (the partial logits, the
+    // tile maxima and the probabilities are exchanged; each wave's tile data
+    // is its own).  Tile t's bytes are in rq when its step starts; they
+    // become the key fragments, the gather of tile t+1 goes out, and the
+    // fragments are written to the wave's quarter tile for the P V products
+    // (the wave's earlier reads of it precede these writes in its own LDS
+    // order).
     for (int t = t0; t < tm; ++t) {
-        uint32_t kp[kKPT][4];
-        dequant_main(rm, kp);
-        const uint32_t ok = rm.ok;
-        __syncthreads();   // every read of the previous tile (sKV, sS, sValid) is done
-        put_rows(kp, sKV);
-        put_valid(ok, sValid);
-        if (t + 1 < tm) {   // s_idx was published by the barrier above
-            int32_t idx[kKPT];
-            tile_idx(s_idx + kTK * (t + 1 - t0), kTK, idx);
-            fetch_main(rcode, rscale, idx, rm);
-        }
-        __syncthreads();   // tile t visible
+        f16x8 kf[8];
+        dequant_q(rq, kf);
+        const uint64_t vm = __ballot(idx_t >= 0);
+        if (t + 1 < tm) fetch_q(rcode, rscale, idx_n, wave, hh, rq);
+        idx_t = idx_n;
+        idx_n = key_idx(t + 2);
+        put_q(kf, vt);
         __builtin_amdgcn_s_setprio(1);   // raised priority: see above k_attn
-        s_finish(s_issue(sKV));
+        s_chain([&](int st) __attribute__((always_inline)) { return kf[st]; });
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();   // logits of t published
         float z[4];
-        tile_max(sValid, z);
+        tile_max(vm, z);
         __syncthreads();   // the waves' maxima published
         probs(z);
         __syncthreads();   // probabilities published
         f16x8 pp[2][2];
         read_p(pp);
         __builtin_amdgcn_s_setprio(1);
-        pv_mma(sKV, pp);
+        pv_mma(vt, pp);
         __builtin_amdgcn_s_setprio(0);
     }
-    // window tiles: K, then V, through the same buffer.  K(t+1) is gathered
-    // during the softmax and P V products of t, V(t) while the logits of t
-    // are exchanged (so that no gather is in flight across the S^T chain)
+    // Window tiles: the same steps with the key fragments from the window's
+    // K rows and the quarter tile from its V rows (rows outside the window
+    // are zeroed and masked), converted one fragment at a time; each of the
+    // next tile's row sets is gathered as soon as this tile's is consumed.
     const int w0 = max(t0, a.ntiles_main);
-    if (w0 < t1) fetch_win(swk, a.W, wlo, whi, w0 - a.ntiles_main, rk);
-    for (int t = w0; t < t1; ++t) {
-        uint32_t kp[kKPT][4];
-        dequant_win(rk.b, rk.ok, kp);
-        const uint32_t ok = rk.ok;
-        __syncthreads();   // every read of the previous tile is done
-        put_rows(kp, sKV);
-        put_valid(ok, sValid);
-        __syncthreads();   // K(t) visible
-        __builtin_amdgcn_s_setprio(1);   // raised priority: see above k_attn
-        s_finish(s_issue(sKV));
-        __builtin_amdgcn_s_setprio(0);
-        fetch_win(swv, a.W, wlo, whi, t - a.ntiles_main, rv);
-        __syncthreads();   // logits of t published; every read of K(t) done
-        float z[4];
-        tile_max(sValid, z);
-        dequant_win(rv.b, ok, kp);
-        put_rows(kp, sKV);
-        if (t + 1 < t1) fetch_win(swk, a.W, wlo, whi, t + 1 - a.ntiles_main, rk);
-        __syncthreads();   // V(t) and the waves' maxima visible
-        probs(z);
-        __syncthreads();   // probabilities published
-        f16x8 pp[2][2];
-        read_p(pp);
-        __builtin_amdgcn_s_setprio(1);
-        pv_mma(sKV, pp);
-        __builtin_amdgcn_s_setprio(0);
+    if (w0 < t1) {
+        RawWQ rk, rv;
+        fetch_wq(swk, a.W, w0 - a.ntiles_main, wave, hh, rk);
+        fetch_wq(swv, a.W, w0 - a.ntiles_main, wave, hh, rv);
+        for (int t = w0; t < t1; ++t) {
+            const int tw = t - a.ntiles_main;
+            const int w_ = kTK * tw + l32;   // this lane's window row
+            const bool valid = w_ >= wlo && w_ < whi;
+            const uint64_t vm = __ballot(valid);
+            const uint32_t keep = valid ? ~0u : 0u;
+#pragma unroll
+            for (int st = 0; st < 8; ++st) put_q1(dequant_wq(rv, keep, st), st, vt);
+            if (t + 1 < t1) fetch_wq(swv, a.W, tw + 1, wave, hh, rv);
+            __builtin_amdgcn_s_setprio(1);
+            s_chain([&](int st) __attribute__((always_inline)) { return dequant_wq(rk, keep, st); });
+            __builtin_amdgcn_s_setprio(0);
+            if (t + 1 < t1) fetch_wq(swk, a.W, tw + 1, wave, hh, rk);
+            __syncthreads();   // logits of t published
+            float z[4];
+            tile_max(vm, z);
+            __syncthreads();   // the waves' maxima published
+            probs(z);
+            __syncthreads();   // probabilities published
+            f16x8 pp[2][2];
+            read_p(pp);
+            __builtin_amdgcn_s_setprio(1);
+            pv_mma(vt, pp);
+            __builtin_amdgcn_s_setprio(0);
+        }
     }
     // l holds this lane's keys' share: add the two lane halves, then the
     // four waves (s_tmax is free: every read of it is behind a barrier)
