@@ -304,15 +304,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
     // are masked to -1
     const __amdgpu_buffer_rsrc_t ridx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)qidx, (short)0, a.topk * 4, kBufFlags);
-    // the entry of this lane's key (key l32) of main tile t, -1 for padding
-    auto key_idx = [&](int t) __attribute__((always_inline)) -> int32_t {
-        const int slot = kTK * t + l32;
-        const int32_t v = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, slot * 4, 0, 0);
-        return (t < tm && slot < a.topk) ? v : -1;
+    // The entry of this lane's key (key l32) of main tile t is loaded as
+    // key_raw(t) and masked by key_sel(t, raw) (-1 for padding) only when it
+    // is used, a tile later: a select next to the load would make the wave
+    // wait for it at once, and with it for every gather issued before it.
+    auto key_raw = [&](int t) __attribute__((always_inline)) -> int32_t {
+        return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ridx, (kTK * t + l32) * 4, 0, 0);
+    };
+    auto key_sel = [&](int t, int32_t raw) __attribute__((always_inline)) -> int32_t {
+        return (t < tm && kTK * t + l32 < a.topk) ? raw : -1;
     };
     // Prologue, in issue order: the first two tiles' key entries, the query
     // slice (16 loads per lane), then the first gather once its entry is in.
-    int32_t idx_t = key_idx(t0), idx_n = key_idx(t0 + 1);
+    int32_t idx_t = key_raw(t0), raw_n = key_raw(t0 + 1);
+    idx_t = key_sel(t0, idx_t);
     RawQ rq;   // bytes of the next main-KV tile (this lane's key and channels)
     // query slice in two fp16 parts after a power-of-two scaling: MFMA step
     // s of this lane is channels cbase + 64 hh + 8 s .. +8 of head h (the
@@ -494,9 +499,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
         f16x8 kf[8];
         dequant_q(rq, kf);
         const uint64_t vm = __ballot(idx_t >= 0);
-        if (t + 1 < tm) fetch_q(rcode, rscale, idx_n, wave, hh, rq);
-        idx_t = idx_n;
-        idx_n = key_idx(t + 2);
+        // unconditional: past the last tile the entry is -1 and nothing is read
+        idx_t = key_sel(t + 1, raw_n);
+        fetch_q(rcode, rscale, idx_t, wave, hh, rq);
+        raw_n = key_raw(t + 2);
         put_q(kf, vt);
         __builtin_amdgcn_s_setprio(1);   // raised priority: see above k_attn
         s_chain([&](int st) __attribute__((always_inline)) { return kf[st]; });
@@ -516,7 +522,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
     // Window tiles: the same steps with the key fragments from the window's
     // K rows and the quarter tile from its V rows (rows outside the window
     // are zeroed and masked), converted one fragment at a time; each of the
-    // next tile's row sets is gathered as soon as this tile's is consumed.
+    // next tile's row sets is gathered as soon as this tile's is consumed
+    // (unconditionally: past the last tile every lane reads the window's
+    // last row, which is unused).
     const int w0 = max(t0, a.ntiles_main);
     if (w0 < t1) {
         RawWQ rk, rv;
@@ -530,11 +538,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
             const uint32_t keep = valid ? ~0u : 0u;
 #pragma unroll
             for (int st = 0; st < 8; ++st) put_q1(dequant_wq(rv, keep, st), st, vt);
-            if (t + 1 < t1) fetch_wq(swv, a.W, tw + 1, wave, hh, rv);
+            fetch_wq(swv, a.W, tw + 1, wave, hh, rv);
             __builtin_amdgcn_s_setprio(1);
             s_chain([&](int st) __attribute__((always_inline)) { return dequant_wq(rk, keep, st); });
             __builtin_amdgcn_s_setprio(0);
-            if (t + 1 < t1) fetch_wq(swk, a.W, tw + 1, wave, hh, rk);
+            fetch_wq(swk, a.W, tw + 1, wave, hh, rk);
             __syncthreads();   // logits of t published
             float z[4];
             tile_max(vm, z);
