@@ -16,10 +16,10 @@
 //     itself has 4 bits and lies in [2^-9, 448]);
 //   - the fp32 query and the fp32 probabilities are split into two fp16
 //     parts (x = x1 + x2, relative residual about 2^-22), each multiplied
-//     exactly and accumulated in fp32.  The query slice of each head and
-//     channel quarter is first scaled by a power of two that puts its largest
-//     element in [2^13, 2^14), so both parts stay in fp16's normal range; the
-//     partial logits are scaled back exactly.
+//     exactly and accumulated in fp32.  The query of each head is first
+//     scaled by a power of two that puts its largest element in
+//     [2^13, 2^14), so both parts stay in fp16's normal range; the logits
+//     are scaled back exactly, together with the softmax scale.
 // Work split: a workgroup (4 waves, one per SIMD) owns one query token, 32
 // heads and a range of 32-key tiles; wave w handles channels 128*w.. of the
 // 32 heads.  Each wave gathers and dequantises only its own channel quarter
@@ -175,20 +175,6 @@ __device__ __forceinline__ void put_q(const f16x8 (&kf)[8], uint16_t* vt) {
     for (int s = 0; s < 8; ++s) put_q1(kf[s], s, vt);
 }
 
-// Eight E2M1 codes (dword w; byte x holds channels 2x, 2x+1, low nibble
-// first) times their E4M3 group scale (byte sb), as four fp16 pairs.  Exact:
-// the gfx950 FP4 -> fp16 conversion is exact, the scale is exact in fp16
-// (4 significant bits, |s| in [2^-9, 448]) and so is each product (at most 6
-// significant bits, magnitude in [2^-10, 2688]).
-__device__ __forceinline__ void dequant_fp4x8(uint32_t w, uint32_t sb, uint32_t (&o)[4]) {
-    const _Float16 s = (_Float16)fp8x2_to_f32<false>(sb).x;
-    const f16x2v sc = {s, s};
-    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc);
-    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc);
-    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc);
-    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc);
-}
-
 // Eight E4M3 bytes as four fp16 pairs (exact), ANDed with `keep` (all ones
 // or zero).
 __device__ __forceinline__ void dequant_fp8x8(uint2 w, uint32_t keep, uint32_t (&o)[4]) {
@@ -198,17 +184,29 @@ __device__ __forceinline__ void dequant_fp8x8(uint2 w, uint32_t keep, uint32_t (
     o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true)) & keep;
 }
 
-// A lane's main-KV bytes as its 8 key fragments (fp16, exact: K = V).  A
-// padding key's bytes were read as 0 (outside the buffer range), so its
-// fragments are 0.
+// A lane's main-KV bytes as its 8 key fragments (fp16; K = V): fragment s
+// is code word s (byte x holds channels 2x, 2x+1, low nibble first) times
+// the E4M3 scale of its 16-channel group (scale byte s / 2).  Exact: the
+// gfx950 FP4 -> fp16 conversion is exact, the four scale bytes become fp16
+// in two packed conversions, exactly (4 significant bits, |s| in
+// [2^-9, 448]), and so is each product (at most 6 significant bits,
+// magnitude in [2^-10, 2688]).  A padding key's bytes were read as 0
+// (outside the buffer range), so its fragments are 0.
 __device__ __forceinline__ void dequant_q(const RawQ& r, f16x8 (&kf)[8]) {
     const uint32_t w[8] = {r.code[0].x, r.code[0].y, r.code[0].z, r.code[0].w,
                            r.code[1].x, r.code[1].y, r.code[1].z, r.code[1].w};
+    const f16x2v sc01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.scale, 1.0f, false);
+    const f16x2v sc23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.scale, 1.0f, true);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        uint32_t o[4];
-        dequant_fp4x8(w[s], (r.scale >> (8 * (s >> 1))) & 0xffu, o);
-        kf[s] = as_f16x8(o[0], o[1], o[2], o[3]);
+        const int g = s >> 1;   // scale group of fragment s
+        const _Float16 sg = g == 0 ? sc01[0] : g == 1 ? sc01[1] : g == 2 ? sc23[0] : sc23[1];
+        const f16x2v sc = {sg, sg};
+        const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[s], 1.0f, 0) * sc);
+        const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[s], 1.0f, 1) * sc);
+        const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[s], 1.0f, 2) * sc);
+        const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[s], 1.0f, 3) * sc);
+        kf[s] = as_f16x8(o0, o1, o2, o3);
     }
 }
 
@@ -323,7 +321,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
     // s of this lane is channels cbase + 64 hh + 8 s .. +8 of head h (the
     // key fragments take the same channels)
     f16x8 q0[8], q1[8];
-    float qunscale;   // exact inverse of the scaling, applied to the partial logits
+    float zscale;     // softmax scale (log2 units) times the exact inverse of the scaling
     {
         const float* qp = a.q[layer] + ((size_t)qi * a.H + (hvalid ? h : 0)) * kD + cbase + 64 * hh;
         // head 0 stands in for a padding head (zeroed below)
@@ -334,7 +332,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
         // padding: nothing is read)
         fetch_q(rcode, rscale, idx_t, wave, hh, rq);
 
-        // largest magnitude of this head's 128 channels (both lane halves)
+        // largest magnitude of this head's 128 channels (both lane halves),
+        // then of all its 512
         float mx = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -342,11 +341,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
                                  fmaxf(fabsf(xq[i].z), fabsf(xq[i].w))));
         if (!hvalid) mx = 0.f;
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // one scale per head for its four channel quarters (the waves), so
+        // that their partial logits add as they are and the inverse scaling
+        // joins the softmax scale
+        if (hh == 0) s_tmax[wave][l32] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(s_tmax[0][l32], s_tmax[1][l32]), fmaxf(s_tmax[2][l32], s_tmax[3][l32]));
         int e = 0;
         (void)frexpf(mx, &e);                          // mx in [2^(e-1), 2^e)
         const int sh = mx > 0.f ? 14 - e : 0;          // mx * 2^sh in [2^13, 2^14)
         const float qscale = ldexpf(1.f, sh);
-        qunscale = ldexpf(1.f, -sh);
+        zscale = a.scale_log2 * ldexpf(1.f, -sh);
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
             float4 x0 = xq[2 * st], x1 = xq[2 * st + 1];
@@ -367,7 +372,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
     uint16_t* const vt = sV[wave];   // this wave's quarter tile
 
     // S^T of a tile over this wave's 128 channels from its key fragments in
-    // registers, scaled back and published in sS (by the caller's barrier).
+    // registers, published in sS (by the caller's barrier) in the query's
+    // scaled units.
     auto s_chain = [&](auto&& frag) __attribute__((always_inline)) {
         f32x16 s0 = f32x16{};
 #pragma unroll
@@ -376,7 +382,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
             s0 = mfma32(f, q0[st], s0);
             s0 = mfma32(f, q1[st], s0);
         }
-        s0 = s0 * qunscale;   // lane l32's column is head h: its own scaling
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
             sS[wave][r4][lane] = make_float4(s0[4 * r4], s0[4 * r4 + 1], s0[4 * r4 + 2], s0[4 * r4 + 3]);
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
         float tw = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float zz = ((v0[i] + v1[i]) + (v2[i] + v3[i])) * a.scale_log2;
+            const float zz = ((v0[i] + v1[i]) + (v2[i] + v3[i])) * zscale;   // lane l32: head h
             z[i] = (kbits >> i) & 1u ? zz : -INFINITY;
             tw = fmaxf(tw, z[i]);
         }
@@ -694,9 +699,18 @@ __global__ void k_dequant_tables(float* main_out, float* win_out) {
     const uint32_t sb = blockIdx.x, c = threadIdx.x & 15u, pos = threadIdx.x >> 4;
     uint32_t w = 0;
     for (uint32_t x = 0; x < 8; ++x) w |= (x == pos ? c : (c + 3 * x + 1) & 15u) << (4 * x);
-    uint32_t o[4];
-    dequant_fp4x8(w, sb, o);
-    main_out[(sb * 16 + c) * 8 + pos] = (float)__builtin_bit_cast(f16x2v, o[pos >> 1])[pos & 1];
+    // through the attention's own path: every code word is w and every
+    // group scale byte is sb, and fragment pos (scale byte pos / 2) is read
+    RawQ r;
+    r.code[0] = r.code[1] = make_uint4(w, w, w, w);
+    r.scale = sb * 0x01010101u;
+    f16x8 kf[8];
+    dequant_q(r, kf);
+    float v = 0.f;
+#pragma unroll
+    for (uint32_t f = 0; f < 8; ++f)
+        if (f == pos) v = (float)kf[f][pos];
+    main_out[(sb * 16 + c) * 8 + pos] = v;
     if (threadIdx.x < 8) {
         uint32_t wb[2] = {0u, 0u};
         for (uint32_t x = 0; x < 8; ++x)
