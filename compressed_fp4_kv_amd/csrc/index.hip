@@ -1439,16 +1439,76 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score_e4m3(
     }
 }
 
+// Top-K of one query's Reindex candidates (composite keys, 0: none) by one
+// workgroup: a 4096-bin histogram of the keys' top 12 bits (the score's)
+// places the K-th largest key in bin b1; the keys above b1 win outright and
+// the best of b1's keys are picked in LDS (direct ranking, or a radix select
+// from bit 48 when there are many).  More than kRankMax keys in b1
+// (degenerate score distributions) falls back to the radix select over all
+// candidates.  The K indices are written in ascending order.
 __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
     const uint64_t* __restrict__ ckeys, int ncand, int K, int32_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
+    __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
+    __shared__ uint32_t s_h[kHistBins];
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
+    __shared__ uint32_t s_count, s_nc;
     const int q = blockIdx.x;
+    int32_t* o = out + (size_t)q * K;
     uint64_t it[kSelItems];
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
         const int i = threadIdx.x + j * kSelThreads;
         it[j] = i < ncand ? ckeys[(size_t)q * ncand + i] : 0ull;
     }
-    select_top_ckeys<kSelThreads, kSelItems>(it, K, out + (size_t)q * K);
+    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
+    if (threadIdx.x == 0) { s_count = 0u; s_nc = 0u; }
+    __syncthreads();
+    uint32_t nv = 0;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        const bool m = it[j] != 0ull;
+        nv += m;
+        const uint32_t d = (uint32_t)(it[j] >> 52);
+        // one atomic per wave when all of its keys share the bin
+        const uint64_t mm = __ballot(m);
+        if (mm) {
+            const int lead = __builtin_ctzll(mm);
+            const uint32_t d0 = __shfl(d, lead);
+            if (__ballot(m && d == d0) == mm) {
+                if (lane_id() == lead) atomicAdd(&s_h[d0], (uint32_t)__popcll(mm));
+            } else if (m) {
+                atomicAdd(&s_h[d], 1u);
+            }
+        }
+    }
+    uint32_t total;
+    (void)block_exclusive_sum<kSelThreads>(nv, s_tmp, total);   // ends with a barrier
+    const uint32_t k = min(total, (uint32_t)K);
+    if (k == 0u) {
+        for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
+        return;
+    }
+    uint32_t b1, nabove;
+    find_digit_4096<kSelThreads>(s_h, k, s_tmp, b1, nabove);
+    const uint32_t nb = s_h[b1];
+    if (nb > (uint32_t)kRankMax) {
+        select_top_ckeys<kSelThreads, kSelItems>(it, K, o);
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        if (it[j] == 0ull) continue;
+        const uint32_t d = (uint32_t)(it[j] >> 52);
+        if (d > b1) s_out[atomicAdd(&s_count, 1u)] = (int32_t)comp_idx(it[j]);
+        else if (d == b1) s_cand[atomicAdd(&s_nc, 1u)] = it[j];
+    }
+    __syncthreads();
+    // nabove keys above b1 (fewer than k) and nb >= k - nabove keys in b1
+    pick_lds_candidates(s_cand, nb, k - nabove, nabove, s_out, s_hist, s_dig, &s_count, 48);
+    rank_and_write<kSelThreads>(s_out, (int)k, K, o);
 }
 
 // ------------------------------------------------------ host helpers
