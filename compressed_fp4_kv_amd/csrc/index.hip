@@ -206,9 +206,10 @@ __device__ void select_global_row(const uint32_t* __restrict__ keys, int n, int 
 // Writes the `count` distinct non-negative indices of s_list (unordered,
 // 16-byte aligned, room for 4 pad slots after them) to o in ascending order
 // and pads the K slots with -1, with NT threads.  Lists of up to
-// min(512, NT): each index is written at its rank.  Longer ones: a counting
-// sort into NT buckets spread evenly over [min, max] of the list, then each
-// index is placed by its rank inside its bucket.
+// min(128, NT): each index is written at its rank among all of them.  Longer
+// ones: a counting sort into NT buckets spread evenly over [min, max] of the
+// list, then each index is placed by its rank inside its bucket (ranking a
+// list of 512 against itself costs about three times as long).
 template <int NT = kSelThreads>
 __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __restrict__ o) {
     constexpr int NB = NT;
@@ -217,7 +218,7 @@ __device__ void rank_and_write(int32_t* s_list, int count, int K, int32_t* __res
     __shared__ int32_t s_srt[CSA2_MAX_TOPK];
     __shared__ int32_t s_mm[2 * (NT / kWave)];
     __shared__ uint32_t s_scan[NT / kWave + 1];
-    if (count <= (NT < 512 ? NT : 512)) {
+    if (count <= (NT < 128 ? NT : 128)) {
         // rank = #{smaller indices}, each element's comparisons split over
         // NT / count threads whose partial counts add up in LDS
         if (count == 0) {
@@ -1454,7 +1455,7 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
-    __shared__ uint32_t s_count, s_nc;
+    __shared__ uint32_t s_count;
     const int q = blockIdx.x;
     int32_t* o = out + (size_t)q * K;
     uint64_t it[kSelItems];
@@ -1464,7 +1465,6 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
         it[j] = i < ncand ? ckeys[(size_t)q * ncand + i] : 0ull;
     }
     for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
-    if (threadIdx.x == 0) { s_count = 0u; s_nc = 0u; }
     __syncthreads();
     uint32_t nv = 0;
 #pragma unroll
@@ -1498,12 +1498,23 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
         select_top_ckeys<kSelThreads, kSelItems>(it, K, o);
         return;
     }
+    // winners to s_out, b1's keys to s_cand, at offsets from one block scan
+    // of the per-thread counts (packed: fewer than 2^16 of either)
+    uint32_t na = 0, nc = 0;
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
-        if (it[j] == 0ull) continue;
         const uint32_t d = (uint32_t)(it[j] >> 52);
-        if (d > b1) s_out[atomicAdd(&s_count, 1u)] = (int32_t)comp_idx(it[j]);
-        else if (d == b1) s_cand[atomicAdd(&s_nc, 1u)] = it[j];
+        na += it[j] != 0ull && d > b1;
+        nc += it[j] != 0ull && d == b1;
+    }
+    uint32_t tot2;
+    const uint32_t ex = block_exclusive_sum<kSelThreads>((na << 16) | nc, s_tmp, tot2);
+    uint32_t pa = ex >> 16, pc = ex & 0xFFFFu;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        const uint32_t d = (uint32_t)(it[j] >> 52);
+        if (it[j] != 0ull && d > b1) s_out[pa++] = (int32_t)comp_idx(it[j]);
+        else if (it[j] != 0ull && d == b1) s_cand[pc++] = it[j];
     }
     __syncthreads();
     // nabove keys above b1 (fewer than k) and nb >= k - nabove keys in b1
