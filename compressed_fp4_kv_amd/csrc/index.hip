@@ -1451,7 +1451,7 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
     const uint64_t* __restrict__ ckeys, int ncand, int K, int32_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
-    __shared__ uint32_t s_h[kHistBins];
+    __shared__ uint32_t s_h[4][kHistBins];   // four sub-histograms, then their sum in s_h[0]
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t s_tmp[kSelThreads / kWave + 3];
@@ -1464,36 +1464,32 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
         const int i = threadIdx.x + j * kSelThreads;
         it[j] = i < ncand ? ckeys[(size_t)q * ncand + i] : 0ull;
     }
-    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) s_h[i] = 0u;
+    for (int i = threadIdx.x; i < 4 * kHistBins; i += kSelThreads) (&s_h[0][0])[i] = 0u;
     __syncthreads();
+    // lane l counts into sub-histogram l % 4: lanes of one instruction that
+    // hit the same bin (scores cluster in a few bins) serialise a quarter as
+    // often
+    uint32_t* const hsub = s_h[lane_id() & 3];
     uint32_t nv = 0;
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
-        const bool m = it[j] != 0ull;
-        nv += m;
-        const uint32_t d = (uint32_t)(it[j] >> 52);
-        // one atomic per wave when all of its keys share the bin
-        const uint64_t mm = __ballot(m);
-        if (mm) {
-            const int lead = __builtin_ctzll(mm);
-            const uint32_t d0 = __shfl(d, lead);
-            if (__ballot(m && d == d0) == mm) {
-                if (lane_id() == lead) atomicAdd(&s_h[d0], (uint32_t)__popcll(mm));
-            } else if (m) {
-                atomicAdd(&s_h[d], 1u);
-            }
-        }
+        if (it[j] == 0ull) continue;
+        ++nv;
+        atomicAdd(&hsub[(uint32_t)(it[j] >> 52)], 1u);
     }
     uint32_t total;
     (void)block_exclusive_sum<kSelThreads>(nv, s_tmp, total);   // ends with a barrier
+    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads)
+        s_h[0][i] = (s_h[0][i] + s_h[1][i]) + (s_h[2][i] + s_h[3][i]);
+    __syncthreads();
     const uint32_t k = min(total, (uint32_t)K);
     if (k == 0u) {
         for (int i = threadIdx.x; i < K; i += kSelThreads) o[i] = -1;
         return;
     }
     uint32_t b1, nabove;
-    find_digit_4096<kSelThreads>(s_h, k, s_tmp, b1, nabove);
-    const uint32_t nb = s_h[b1];
+    find_digit_4096<kSelThreads>(s_h[0], k, s_tmp, b1, nabove);
+    const uint32_t nb = s_h[0][b1];
     if (nb > (uint32_t)kRankMax) {
         select_top_ckeys<kSelThreads, kSelItems>(it, K, o);
         return;
