@@ -55,9 +55,15 @@ constexpr int kTK = 32;             // keys per tile
 
 // A quarter tile's rows (256 B, 16 chunks of 8 fp16) are not padded;
 // instead chunk ch of row `row` is stored at chunk ch ^ tile_swz(row) of
-// that row, so that the 4 rows each 32-lane half of a transposed V read
-// touches fall in 4 distinct 16-bank windows (free of bank conflicts).
-__device__ __forceinline__ int tile_swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+// that row.  The swizzle keeps both of the tile's LDS access patterns free
+// of bank conflicts whether the LDS serves 128 or 256 bytes a cycle: the
+// fragment writes (8 or 16 consecutive rows, one chunk each) and the
+// transposed V reads (4 consecutive rows, 2 or 4 chunks each).  Its high
+// part is row & 3 and its low part swz_lo(row).
+__device__ __forceinline__ int swz_lo(int row) {
+    return (row & 3) ^ ((row >> 2) & 1) ^ (((row >> 3) & 1) << 1);
+}
+__device__ __forceinline__ int tile_swz(int row) { return 4 * (row & 3) + swz_lo(row); }
 constexpr float kLn2 = 0.69314718055994530942f;
 
 constexpr int kMaxLayers = 8;   // layers of one decode call (a layer group)
@@ -392,14 +398,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
     // 32-channel block of the quarter, so that lane l receives channel
     // (l & 31) of the block for 4 consecutive keys.  In quarter-tile terms:
     // row 16 u + 8 hi + trrow, chunk 4 ct + tsub; since tile_swz(row) = 4
-    // (row & 3) + ((row >> 2) & 3), the chunk's swizzle splits into tsub ^
-    // ((row >> 2) & 3), which depends on hi only, and ct ^ (row & 3), which
-    // depends on the lane only.
+    // (row & 3) + swz_lo(row), the chunk's swizzle splits into tsub ^
+    // swz_lo(row), fixed per lane and hi (u adds 16 rows, which swz_lo does
+    // not see), and ct ^ (row & 3), fixed per lane.
     const int trrow = 4 * (lane >> 5) + ((lane >> 2) & 3);
     const int tsub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int trhi = (lane >> 2) & 3;   // row & 3
-    const int trb0 = trrow * kQStr + 8 * (tsub ^ ((trrow >> 2) & 3)) + 4 * (lane & 1);
-    const int trb1 = (trrow + 8) * kQStr + 8 * (tsub ^ (((trrow >> 2) + 2) & 3)) + 4 * (lane & 1);
+    const int trb0 = trrow * kQStr + 8 * (tsub ^ swz_lo(trrow)) + 4 * (lane & 1);
+    const int trb1 = (trrow + 8) * kQStr + 8 * (tsub ^ swz_lo(trrow + 8)) + 4 * (lane & 1);
 
     // Softmax of a tile, split over the four waves: wave w takes keys
     // 8w .. 8w+7 (its registers' rows 4w .. 4w+3 of S^T), so it reads one
