@@ -28,12 +28,15 @@ __device__ __forceinline__ void stream_flush(int q, int r0, int r1, bool pool, i
                                              uint32_t* __restrict__ hist_e,
                                              uint32_t* __restrict__ hist_b) {
     __syncthreads();
-    // r0 and the key strides are multiples of 4 (64): whole uint4 stores,
-    // a scalar tail for the last workgroup of a row
+    // r0 and the key strides are multiples of 4 (64): whole 16-byte stores
+    // (nontemporal: the keys are read once, by the select, and stay out of
+    // the way of the row stream), a scalar tail for the last workgroup of a row
+    typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
     const int nk = r1 - r0;
     for (int i = 4 * threadIdx.x; i < nk; i += 4 * NT) {
         if (i + 4 <= nk)
-            *reinterpret_cast<uint4*>(krow + r0 + i) = *reinterpret_cast<const uint4*>(s_ke + i);
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4s*>(s_ke + i),
+                                        reinterpret_cast<u32x4s*>(krow + r0 + i));
         else
             for (int x = i; x < nk; ++x) krow[r0 + x] = s_ke[x];
     }
