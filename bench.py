@@ -18,11 +18,14 @@ chunk (Full + 5 Reuse layers, with its matrix-core utilisation); and the
 headline step over the compact E4M3 key cache under "e4m3_keys".
 
 Timing: W warm-up steps, then K timed steps, each between its own pair of
-HIP events on the launch stream, with a read-modify-write pass over 1 GiB
-between steps (outside the events) so that no step finds the previous step's
-data in the 256 MB last-level cache.  ms_per_step is the median of the K
-steps.  A second pass with per-launch events gives each kernel's average
-duration, from which the dominant kernel's roofline is computed.
+HIP events on the launch stream, with a read pass over 1 GiB between steps
+(outside the events) so that no step finds the previous step's data in the
+256 MB last-level cache.  ms_per_step is the median of the K steps.  The
+same K steps are also timed after a read-modify-write pass over the 1 GiB
+instead ("rmw_touch"): that pass leaves the last-level cache full of dirty
+lines, and the step then also pays for writing them back.  A second pass
+with per-launch events gives each kernel's average duration, from which the
+dominant kernel's roofline is computed.
 
 cpu_baseline: the oracle (plain C, double precision) on the host cores, on
 the headline workload: all queries with every core, and a labelled sample
@@ -265,9 +268,27 @@ def mfma_utilisation(w, kern):
 
 # ------------------------------------------------------------------ timing
 
-def time_steps(torch, step, steps, warmup, flush):
+class Touch:
+    """The pass over FLUSH_BYTES of device memory between timed steps: a read
+    (every cache level then holds clean lines of this buffer only), or a
+    read-modify-write (the same, but the last-level cache is left full of
+    dirty lines that the next step has to write back)."""
+
+    def __init__(self, torch):
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+        self.kind = "read"
+
+    def __call__(self):
+        if self.kind == "read":
+            self.sink.add_(self.buf.sum())
+        else:
+            self.buf.add_(1.0)
+
+
+def time_steps(torch, step, steps, warmup, touch):
     """Per-step times (ms) of `steps` steps, each between its own events,
-    with the flush pass between steps."""
+    with the touch pass between steps."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -275,7 +296,7 @@ def time_steps(torch, step, steps, warmup, flush):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for e0, e1 in ev:
-        flush.add_(1.0)
+        touch()
         e0.record(stream)
         step()
         e1.record(stream)
@@ -283,13 +304,13 @@ def time_steps(torch, step, steps, warmup, flush):
     return [e0.elapsed_time(e1) for e0, e1 in ev]
 
 
-def kernel_times(csa2, torch, step, steps, flush):
+def kernel_times(csa2, torch, step, steps, touch):
     """Average duration of each kernel over `steps` steps (per-launch events
-    on the launch stream), flush pass between steps."""
+    on the launch stream), touch pass between steps."""
     csa2.profile_reset()
     csa2.profile_enable(True)
     for _ in range(steps):
-        flush.add_(1.0)
+        touch()
         step()
     torch.cuda.synchronize()
     prof = csa2.profile_read()
@@ -304,20 +325,26 @@ def summarize(times):
             "min_ms": float(a.min()), "max_ms": float(a.max()), "n": int(a.size)}
 
 
-def run_workload(csa2, torch, w, args, flush, keys="f32", block_rule="max", tag=""):
+def run_workload(csa2, torch, w, args, touch, keys="f32", block_rule="max", tag=""):
     """Builds workload w on the device, times it, and returns its record."""
     log(f"[{w.name}{tag}] building inputs: B={w.B} Q={w.Q} max ctx={max(w.ctx)}")
     from gen.workloads import build_device
     t = build_device(w, keys=keys)
     step, _ = make_step(csa2, w, t, torch, keys, block_rule)
-    times = time_steps(torch, step, args.steps, args.warmup, flush)
+    touch.kind = "read"
+    times = time_steps(torch, step, args.steps, args.warmup, touch)
+    touch.kind = "rmw"
+    st_rmw = summarize(time_steps(torch, step, args.steps, 0, touch))
+    touch.kind = "read"
     st = summarize(times)
     ms = st["median_ms"]
     log(f"[{w.name}{tag}] median {ms:.4f} ms/step (min {st['min_ms']:.4f}, max "
-        f"{st['max_ms']:.4f})")
-    kern = kernel_times(csa2, torch, step, args.steps, flush)
+        f"{st['max_ms']:.4f}); after a read-modify-write touch {st_rmw['median_ms']:.4f}")
+    kern = kernel_times(csa2, torch, step, args.steps, touch)
     log(f"[{w.name}{tag}] kernels: " + json.dumps(kern))
     rec = {"value": w.Q / (ms * 1e-3), "unit": "queries/s", "ms_per_step": ms, "step_times": st,
+           "rmw_touch": {"ms_per_step": st_rmw["median_ms"], "step_times": st_rmw,
+                         "value": w.Q / (st_rmw["median_ms"] * 1e-3)},
            "workload": WORKLOAD_NAMES.get(w.name, w.name), "global_batch": w.Q,
            "kernels": kern, "roofline": dominant_roofline(w, kern, keys),
            "step_hbm": step_hbm(w, ms, keys)}
@@ -665,9 +692,9 @@ def main():
             sys.exit(2)
         w.pool_blocks = args.pool_blocks or w.pool_blocks
         w.block_size = args.block_size or w.block_size
-    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    touch = Touch(torch)
     torch.cuda.synchronize()
-    head = run_workload(csa2, torch, w, args, flush, args.keys, args.block_rule)
+    head = run_workload(csa2, torch, w, args, touch, args.keys, args.block_rule)
     res = {
         "metric": "CSA2 decode queries/sec and achieved HBM GB/s (% of peak) at 1 MI355X",
         "value": head["value"],
@@ -688,9 +715,11 @@ def main():
                        f"{args.block_rule}" if pool_variant else ""),
                    "global_batch": w.Q, "seq_len": int(max(w.ctx)), "total_entries": w.rows,
                    "parallelism": "single GPU"},
-        "timing": "median of the timed steps, each between its own HIP events, 1 GiB touched "
-                  "between steps",
+        "timing": "median of the timed steps, each between its own HIP events, 1 GiB read "
+                  "between steps; rmw_touch: the same steps after a read-modify-write of the "
+                  "1 GiB",
         "step_times": head["step_times"],
+        "rmw_touch": head["rmw_touch"],
         "kernels": head["kernels"],
         "roofline": head["roofline"],
         "step_hbm": head["step_hbm"],
@@ -701,16 +730,17 @@ def main():
         if args.keys == "f32":
             # the same step over the compact indexer-key cache (E4M3 bytes), a
             # storage variant reported beside the fp32 figure, never as `value`
-            r8 = run_workload(csa2, torch, workload(wid), args, flush, "e4m3", tag=" e4m3 keys")
+            r8 = run_workload(csa2, torch, workload(wid), args, touch, "e4m3", tag=" e4m3 keys")
             res["e4m3_keys"] = {k: r8[k] for k in ("value", "unit", "ms_per_step", "step_times",
-                                                   "kernels", "roofline", "step_hbm")}
+                                                   "rmw_touch", "kernels", "roofline",
+                                                   "step_hbm")}
             res["e4m3_keys"]["config"] = "same step, indexer keys stored as E4M3FN bytes"
         other = {}
         for oid in (1, 3, 2):
             ow = workload(oid)
-            other[ow.name] = run_workload(csa2, torch, ow, args, flush)
+            other[ow.name] = run_workload(csa2, torch, ow, args, touch)
         res["other_workloads"] = other
-    del flush
+    del touch
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and "other_workloads" in res:
         for name, rec in res["other_workloads"].items():

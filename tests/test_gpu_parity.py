@@ -343,6 +343,53 @@ def test_index_candidate_radix_paths(csa2):
         assert np.array_equal(pool[b], p[0]), f"pool of query {b}"
 
 
+@pytest.mark.parametrize("case", ["top2048", "narrow", "ties", "signs"])
+def test_reindex_select_paths(csa2, case):
+    # Paths of the Reindex select beyond the common one (the K-th key's
+    # histogram bin holding a few hundred keys, ranked directly): Top-2,048
+    # (the long-list output sort); keys in [0, 2] against a 0/1 query (about
+    # 2,300 keys in the K-th key's bin: radix pick in LDS); 0/1 keys against
+    # an all-ones query (thousands tied: the radix select over all keys); key
+    # rows turned so that all but about 2 % of the scores are negative or zero
+    # (the K-th key far below the top one, across the sign).  Pools are
+    # random distinct blocks, a short sequence's pool padded with -1.
+    w = _edge([140000, 30000, 9000, 700], topk=2048 if case == "top2048" else 512,
+              pool_blocks=2048, block_size=8)
+    topk = w.topk
+    t = build_device(w, layers=0, with_kv=False)
+    n = w.rows * w.row_width
+    rng = np.random.default_rng([31, len(case)])
+    if case == "ties":
+        kh = host_ints(82, 1, 0, n, 0, 1).reshape(-1, w.Hk, w.Di)
+        qh = np.ones((w.B, w.Hi, w.Di), np.float32)
+    elif case == "narrow":
+        kh = host_ints(82, 1, 0, n, 0, 2).reshape(-1, w.Hk, w.Di)
+        qh = host_ints(82, 2, 0, w.B * w.Hi * w.Di, 0, 1).reshape(w.B, w.Hi, w.Di)
+    else:
+        kh = host_ints(82, 1, 0, n, -8, 8).reshape(-1, w.Hk, w.Di)
+        qh = host_ints(82, 2, 0, w.B * w.Hi * w.Di, -8, 8).reshape(w.B, w.Hi, w.Di)
+    if case == "signs":
+        for b in range(w.B):
+            off, nb = int(w.seq_row_off[b]), int(w.ctx[b])
+            s = np.einsum("rd,d->r", kh[off:off + nb].reshape(nb, -1).astype(np.float64),
+                          qh[b].reshape(-1).astype(np.float64))
+            flip = (s > 0) & (rng.random(nb) >= 0.02)
+            kh[off:off + nb][flip] *= -1.0
+    pool = np.full((w.B, w.pool_blocks), -1, np.int32)
+    for b in range(w.B):
+        nblk = (int(w.ctx[b]) + w.block_size - 1) // w.block_size
+        m = min(nblk, w.pool_blocks)
+        pool[b, :m] = rng.choice(nblk, m, replace=False)
+    t["kI"] = torch.from_numpy(kh).cuda()
+    re = C.gpu_reindex(w, t, torch.from_numpy(pool).cuda(), qI=torch.from_numpy(qh).cuda(),
+                       topk=topk).cpu().numpy()
+    for b in range(w.B):
+        off = int(w.seq_row_off[b])
+        r = oracle.reindex(qh[b:b + 1], kh[off:off + w.ctx[b]], [0], [0], [w.ctx[b]],
+                           pool[b:b + 1], w.block_size, w.Hi, w.Hk, w.Di, topk)
+        assert np.array_equal(re[b], r[0]), f"{case}: query {b} (ctx {w.ctx[b]})"
+
+
 @pytest.mark.parametrize("split", ["both", "queries", "keys"])
 @pytest.mark.parametrize("ctx,p0", [(3000, 4000), (12000, 20000)])
 def test_prefill_indexer_general_fp32_inputs(csa2, split, ctx, p0):
