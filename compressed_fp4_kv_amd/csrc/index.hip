@@ -27,8 +27,9 @@
 //   (Kernel boundaries order the phases: a grid-wide "last workgroup" hand-
 //   off would need agent-scope fences, which write back L2 on this part.)
 //   Reindex: k_reindex_score gathers the pool rows (8 contiguous 2 KB rows
-//   per block) with the same 8-row dot, k_reindex_select selects among the
-//   <= 16,384 composite keys of a query in one workgroup.
+//   per block) with the same 8-row dot and writes one 4-byte score key per
+//   candidate; k_reindex_select rebuilds the <= 16,384 composite keys of a
+//   query from them and the pool row, and selects in one workgroup.
 #include <limits.h>
 
 #include <algorithm>
@@ -1311,7 +1312,7 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
     const float* __restrict__ qI, const float* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, const int32_t* __restrict__ pool,
-    int P, int bs, uint64_t* __restrict__ ckeys) {
+    int P, int bs, uint32_t* __restrict__ ckeys) {
     constexpr int RW = 256 * VPR;
     const int q = blockIdx.y;
     const int ncand = P * bs;
@@ -1362,11 +1363,13 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score(
             const int64_t t = (int64_t)(((uint64_t)(uint32_t)__shfl((int)thi, r) << 32) |
                                         (uint32_t)__shfl((int)tlo, r));
             const int c = cw + r;
-            // nontemporal: written once, read once by the select kernel, and
-            // kept out of the way of this kernel's row stream (with plain
-            // stores the gather ran about 4 % slower)
+            // the score key only (0: no candidate; no score maps to 0): the
+            // select rebuilds the entry from the pool.  Nontemporal: written
+            // once, read once by the select kernel, and kept out of the way
+            // of this kernel's row stream (with plain stores the gather ran
+            // about 4 % slower)
             if ((lane & 7) == 0 && c < c1)
-                __builtin_nontemporal_store(t >= 0 ? comp_key(ord_key(sv[hh]), (uint32_t)t) : 0ull,
+                __builtin_nontemporal_store(t >= 0 ? ord_key(sv[hh]) : 0u,
                                             ckeys + (size_t)q * ncand + c);
         }
     }
@@ -1386,7 +1389,7 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score_e4m3(
     const float* __restrict__ qI, const uint8_t* __restrict__ kI,
     const int64_t* __restrict__ seq_row_off, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_nvis, int Hi, int Hk, int Di, const int32_t* __restrict__ pool,
-    int P, int bs, uint64_t* __restrict__ ckeys) {
+    int P, int bs, uint32_t* __restrict__ ckeys) {
     constexpr int RB = 256 * VPR;
     constexpr int G = 16 / VPR;
     constexpr int RPB = 4 * G;                        // rows per sub-block
@@ -1438,22 +1441,29 @@ __global__ __launch_bounds__(kReindexThreads) void k_reindex_score_e4m3(
             const int t = __shfl(tl, r);
             const int c = cw + r;
             if (writer && c < c1)
-                __builtin_nontemporal_store(t >= 0 ? comp_key(ord_key(sv[b]), (uint32_t)t) : 0ull,
+                __builtin_nontemporal_store(t >= 0 ? ord_key(sv[b]) : 0u,
                                             ckeys + (size_t)q * ncand + c);
         }
     }
 }
 
-// Top-K of one query's Reindex candidates (composite keys, 0: none) by one
-// workgroup: a 4096-bin histogram of the keys' top 12 bits (the score's)
+// Top-K of one query's Reindex candidates by one workgroup.  The gather
+// leaves a 4-byte score key per candidate (0: none); the histogram and the
+// placement work on those, and the entry of a candidate (from the pool row
+// staged in LDS) is looked up only for the keys that need it, the winners
+// and the composite keys (score, then the lower entry) of the K-th key's
+// bin.  A 4096-bin histogram of the keys' top 12 bits (the score's)
 // places the K-th largest key in bin b1; the keys above b1 win outright and
 // the best of b1's keys are picked in LDS (direct ranking, or a radix select
 // from bit 48 when there are many).  More than kRankMax keys in b1
 // (degenerate score distributions) falls back to the radix select over all
 // candidates.  The K indices are written in ascending order.
+template <bool POW2>
 __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
-    const uint64_t* __restrict__ ckeys, int ncand, int K, int32_t* __restrict__ out) {
+    const uint32_t* __restrict__ skeys, int ncand, int K, int32_t* __restrict__ out,
+    const int32_t* __restrict__ pool, int P, int bs) {
     __shared__ __attribute__((aligned(16))) int32_t s_out[CSA2_MAX_TOPK + 4];
+    __shared__ int32_t s_pool[CSA2_MAX_TOPK];
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[kRankMax + 2];
     __shared__ uint32_t s_h[4][kHistBins];   // four sub-histograms, then their sum in s_h[0]
     __shared__ uint32_t s_hist[256];
@@ -1462,14 +1472,24 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
     __shared__ uint32_t s_count;
     const int q = blockIdx.x;
     int32_t* o = out + (size_t)q * K;
-    uint64_t it[kSelItems];
+    uint32_t sk[kSelItems];
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
         const int i = threadIdx.x + j * kSelThreads;
-        it[j] = i < ncand ? ckeys[(size_t)q * ncand + i] : 0ull;
+        sk[j] = i < ncand ? skeys[(size_t)q * ncand + i] : 0u;
     }
+    for (int i = threadIdx.x; i < P; i += kSelThreads) s_pool[i] = pool[(size_t)q * P + i];
     for (int i = threadIdx.x; i < 4 * kHistBins; i += kSelThreads) (&s_h[0][0])[i] = 0u;
     __syncthreads();
+    // entry of candidate c: position c % bs of pool block s_pool[c / bs]
+    // (taken only for the keys that need it; POW2: bs a power of two)
+    const int lbs = __ffs(bs) - 1;
+    auto entry = [&](int c) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (POW2)
+            return (uint32_t)(s_pool[min(c >> lbs, CSA2_MAX_TOPK - 1)] * bs + (c & (bs - 1)));
+        else
+            return (uint32_t)(s_pool[min(c / bs, CSA2_MAX_TOPK - 1)] * bs + c % bs);
+    };
     // lane l counts into sub-histogram l % 4: lanes of one instruction that
     // hit the same bin (scores cluster in a few bins) serialise a quarter as
     // often
@@ -1477,9 +1497,9 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
     uint32_t nv = 0;
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
-        if (it[j] == 0ull) continue;
+        if (sk[j] == 0u) continue;
         ++nv;
-        atomicAdd(&hsub[(uint32_t)(it[j] >> 52)], 1u);
+        atomicAdd(&hsub[sk[j] >> kDigitShift], 1u);
     }
     uint32_t total;
     (void)block_exclusive_sum<kSelThreads>(nv, s_tmp, total);   // ends with a barrier
@@ -1495,26 +1515,31 @@ __global__ __launch_bounds__(kSelThreads) void k_reindex_select(
     find_digit_4096<kSelThreads>(s_h[0], k, s_tmp, b1, nabove);
     const uint32_t nb = s_h[0][b1];
     if (nb > (uint32_t)kRankMax) {
+        uint64_t it[kSelItems];
+#pragma unroll
+        for (int j = 0; j < kSelItems; ++j)
+            it[j] = sk[j] ? comp_key(sk[j], entry(threadIdx.x + j * kSelThreads)) : 0ull;
         select_top_ckeys<kSelThreads, kSelItems>(it, K, o);
         return;
     }
-    // winners to s_out, b1's keys to s_cand, at offsets from one block scan
-    // of the per-thread counts (packed: fewer than 2^16 of either)
+    // winners to s_out, b1's keys to s_cand (composite), at offsets from one
+    // block scan of the per-thread counts (packed: fewer than 2^16 of either)
     uint32_t na = 0, nc = 0;
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
-        const uint32_t d = (uint32_t)(it[j] >> 52);
-        na += it[j] != 0ull && d > b1;
-        nc += it[j] != 0ull && d == b1;
+        const uint32_t d = sk[j] >> kDigitShift;
+        na += sk[j] != 0u && d > b1;
+        nc += sk[j] != 0u && d == b1;
     }
     uint32_t tot2;
     const uint32_t ex = block_exclusive_sum<kSelThreads>((na << 16) | nc, s_tmp, tot2);
     uint32_t pa = ex >> 16, pc = ex & 0xFFFFu;
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
-        const uint32_t d = (uint32_t)(it[j] >> 52);
-        if (it[j] != 0ull && d > b1) s_out[pa++] = (int32_t)comp_idx(it[j]);
-        else if (it[j] != 0ull && d == b1) s_cand[pc++] = it[j];
+        const uint32_t d = sk[j] >> kDigitShift;
+        const int c = threadIdx.x + j * kSelThreads;
+        if (sk[j] != 0u && d > b1) s_out[pa++] = (int32_t)entry(c);
+        else if (sk[j] != 0u && d == b1) s_cand[pc++] = comp_key(sk[j], entry(c));
     }
     __syncthreads();
     // nabove keys above b1 (fewer than k) and nb >= k - nabove keys in b1
@@ -1841,7 +1866,7 @@ extern "C" int csa2_index_full_ex(const float* qI, const void* kI, int32_t key_f
 extern "C" size_t csa2_reindex_workspace_bytes(int32_t Q, int32_t pool_blocks, int32_t block_size) {
     if (Q < 0 || pool_blocks < 0 || block_size <= 0) return 0;
     Carver c(nullptr);
-    c.take<uint64_t>((size_t)Q * pool_blocks * block_size);
+    c.take<uint32_t>((size_t)Q * pool_blocks * block_size);
     return c.bytes();
 }
 
@@ -1865,7 +1890,7 @@ static int reindex_impl(const float* qI, const KT* kI, const int64_t* seq_row_of
     if (ws_bytes < csa2_reindex_workspace_bytes(Q, pool_blocks, block_size))
         return CSA2_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream_;
-    uint64_t* ck = static_cast<uint64_t*>(ws);
+    uint32_t* ck = static_cast<uint32_t*>(ws);
     const int ncand = pool_blocks * block_size;
     if (ncand > 0) {
         dim3 g((ncand + kReindexPerWG - 1) / kReindexPerWG, Q);
@@ -1883,8 +1908,11 @@ static int reindex_impl(const float* qI, const KT* kI, const int64_t* seq_row_of
 #undef CSA2_RS
         if (st) return st;
     }
-    return CSA2_LAUNCH("reindex_select", k_reindex_select, dim3(Q), dim3(kSelThreads), s, ck,
-                       ncand, topk, topk_idx);
+    if ((block_size & (block_size - 1)) == 0)
+        return CSA2_LAUNCH("reindex_select", k_reindex_select<true>, dim3(Q), dim3(kSelThreads),
+                           s, ck, ncand, topk, topk_idx, pool_block_idx, pool_blocks, block_size);
+    return CSA2_LAUNCH("reindex_select", k_reindex_select<false>, dim3(Q), dim3(kSelThreads), s,
+                       ck, ncand, topk, topk_idx, pool_block_idx, pool_blocks, block_size);
 }
 
 extern "C" int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
@@ -1908,22 +1936,22 @@ extern "C" int csa2_reindex_e4m3(const float* qI, const uint8_t* kI, const int64
 
 // ------------------------------------------------ allocation-free Reindex
 
-// Scratch of csa2_reindex_noalloc: the composite candidate keys (8 bytes per
+// Scratch of csa2_reindex_noalloc: the candidates' score keys (4 bytes per
 // candidate) that k_reindex_score writes and k_reindex_select reads, in a
 // static array that each GPU the library runs on holds until the process
 // ends.  Host code never passes this name to a kernel: on the host it stands
 // for no device address; the address comes from hipGetSymbolAddress.
-static __device__ __align__(256) uint64_t scratch[CSA2_NOALLOC_MAX_CAND];
+static __device__ __align__(256) uint32_t scratch[CSA2_NOALLOC_MAX_CAND];
 
 namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
-uint64_t* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+uint32_t* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
 }  // namespace
 
 // The device address of the current device's scratch; looked up once per
 // device (with that device current) and kept.
-static int current_device_scratch(uint64_t** out) {
+static int current_device_scratch(uint32_t** out) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) {
@@ -1939,7 +1967,7 @@ static int current_device_scratch(uint64_t** out) {
             set_last_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
             return CSA2_ERR_HIP;
         }
-        g_scratch_ptr[dev] = static_cast<uint64_t*>(p);
+        g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
     }
     *out = g_scratch_ptr[dev];
     return CSA2_OK;
@@ -1953,12 +1981,12 @@ extern "C" int csa2_reindex_noalloc(const float* qI, const float* kI,
                                     int32_t* topk_idx, void* stream) {
     if (Q < 0 || pool_blocks < 0 || block_size <= 0 || topk < 0) return CSA2_ERR_SHAPE;
     if ((int64_t)Q * pool_blocks * block_size > CSA2_NOALLOC_MAX_CAND) return CSA2_ERR_UNSUPPORTED;
-    uint64_t* ws = nullptr;
+    uint32_t* ws = nullptr;
     if (Q > 0 && topk > 0) {
         const int st = current_device_scratch(&ws);
         if (st != CSA2_OK) return st;
     }
     return reindex_impl<float>(qI, kI, seq_row_off, q_seq, q_nvis, pool_block_idx, pool_blocks,
                                block_size, Q, Hi, Hk, Di, topk, topk_idx, ws,
-                               sizeof(uint64_t) * (size_t)CSA2_NOALLOC_MAX_CAND, stream);
+                               sizeof(uint32_t) * (size_t)CSA2_NOALLOC_MAX_CAND, stream);
 }

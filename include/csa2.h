@@ -152,7 +152,7 @@ int csa2_reindex(const float* qI, const float* kI, const int64_t* seq_row_off,
  * Allocation-free Reindex, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): csa2_reindex with its workspace replaced by a static device
- * array of CSA2_NOALLOC_MAX_CAND composite keys (16 MiB) that each GPU the
+ * array of CSA2_NOALLOC_MAX_CAND candidate score keys (8 MiB) that each GPU the
  * library runs on holds until the process ends.  Same arguments, results and
  * errors as csa2_reindex, without ws / ws_bytes; the array of the CURRENT
  * device (hipGetDevice) is used, so `stream` must belong to that device.

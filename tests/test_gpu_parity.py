@@ -343,8 +343,9 @@ def test_index_candidate_radix_paths(csa2):
         assert np.array_equal(pool[b], p[0]), f"pool of query {b}"
 
 
+@pytest.mark.parametrize("order", ["random", "ascending", "holes"])
 @pytest.mark.parametrize("case", ["top2048", "narrow", "ties", "signs"])
-def test_reindex_select_paths(csa2, case):
+def test_reindex_select_paths(csa2, case, order):
     # Paths of the Reindex select beyond the common one (the K-th key's
     # histogram bin holding a few hundred keys, ranked directly): Top-2,048
     # (the long-list output sort); keys in [0, 2] against a 0/1 query (about
@@ -352,7 +353,11 @@ def test_reindex_select_paths(csa2, case):
     # an all-ones query (thousands tied: the radix select over all keys); key
     # rows turned so that all but about 2 % of the scores are negative or zero
     # (the K-th key far below the top one, across the sign).  Pools are
-    # random distinct blocks, a short sequence's pool padded with -1.
+    # random distinct blocks, a short sequence's pool padded with -1, in
+    # random order, in ascending order (the Full layer's order: the select
+    # then writes the winners from a bitmap in candidate order when at most
+    # 512 keys share the K-th key's bin), or ascending with empty slots
+    # between valid ones (which must not take that path).
     w = _edge([140000, 30000, 9000, 700], topk=2048 if case == "top2048" else 512,
               pool_blocks=2048, block_size=8)
     topk = w.topk
@@ -379,7 +384,12 @@ def test_reindex_select_paths(csa2, case):
     for b in range(w.B):
         nblk = (int(w.ctx[b]) + w.block_size - 1) // w.block_size
         m = min(nblk, w.pool_blocks)
-        pool[b, :m] = rng.choice(nblk, m, replace=False)
+        row = rng.choice(nblk, m, replace=False)
+        if order != "random":
+            row = np.sort(row)
+        pool[b, :m] = row
+        if order == "holes" and m > 8:
+            pool[b, rng.choice(m - 1, 4, replace=False)] = -1
     t["kI"] = torch.from_numpy(kh).cuda()
     re = C.gpu_reindex(w, t, torch.from_numpy(pool).cuda(), qI=torch.from_numpy(qh).cuda(),
                        topk=topk).cpu().numpy()
@@ -387,7 +397,7 @@ def test_reindex_select_paths(csa2, case):
         off = int(w.seq_row_off[b])
         r = oracle.reindex(qh[b:b + 1], kh[off:off + w.ctx[b]], [0], [0], [w.ctx[b]],
                            pool[b:b + 1], w.block_size, w.Hi, w.Hk, w.Di, topk)
-        assert np.array_equal(re[b], r[0]), f"{case}: query {b} (ctx {w.ctx[b]})"
+        assert np.array_equal(re[b], r[0]), f"{case}, {order} pool: query {b} (ctx {w.ctx[b]})"
 
 
 @pytest.mark.parametrize("split", ["both", "queries", "keys"])
