@@ -400,6 +400,31 @@ def test_reindex_select_paths(csa2, case, order):
         assert np.array_equal(re[b], r[0]), f"{case}, {order} pool: query {b} (ctx {w.ctx[b]})"
 
 
+@pytest.mark.parametrize("bs", [3, 5, 16])
+def test_reindex_other_block_sizes(csa2, bs):
+    # Reindex accepts any positive block size (the Full layer's pools use 1,
+    # 2, 4 or 8): candidate c is position c mod bs of pool block c / bs, here
+    # for sizes that are not powers of two and for one above 8, with random
+    # pools in random order, a short sequence's pool padded with -1.
+    P = 16384 // bs if bs > 8 else 1000
+    w = _edge([60000, 9000, 500], topk=512, pool_blocks=P, block_size=bs)
+    t = build_device(w, layers=0, with_kv=False)
+    rng = np.random.default_rng([41, bs])
+    pool = np.full((w.B, P), -1, np.int32)
+    for b in range(w.B):
+        nblk = (int(w.ctx[b]) + bs - 1) // bs
+        m = min(nblk, P)
+        pool[b, :m] = rng.choice(nblk, m, replace=False)
+    qh = host_qI(w, T_QI_FULL)
+    re = C.gpu_reindex(w, t, torch.from_numpy(pool).cuda(), qI=t["qI_full"], topk=512).cpu().numpy()
+    for b in range(w.B):
+        off = int(w.seq_row_off[b])
+        kh = host_kI_rows(w, off, int(w.ctx[b]))
+        r = oracle.reindex(qh[b:b + 1], kh, [0], [0], [int(w.ctx[b])], pool[b:b + 1], bs, w.Hi,
+                           w.Hk, w.Di, 512)
+        assert np.array_equal(re[b], r[0]), f"block size {bs}: query {b} (ctx {w.ctx[b]})"
+
+
 @pytest.mark.parametrize("split", ["both", "queries", "keys"])
 @pytest.mark.parametrize("ctx,p0", [(3000, 4000), (12000, 20000)])
 def test_prefill_indexer_general_fp32_inputs(csa2, split, ctx, p0):
